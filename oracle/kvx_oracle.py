@@ -1,0 +1,238 @@
+"""Plain float64 CPU oracle of the cross-model KV handoff.
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the bench's CPU-baseline leg
+are the only callers; the product path (the HIP library and its binding) never
+imports, calls or runs anything here.  It shares no code with the HIP path.
+
+What it follows, step by step (page titles as printed on the pages):
+
+* "PANORAMA: Cross-Model KV Sharing via Contextual Recomputation", abstract:
+  the mapper is factorized into one shared source projection, which turns each prompt
+  position's source KV into a compact latent, and a layer-specific target
+  reconstruction of each target layer's K/V from that latent; a small subset of
+  important target positions is then recomputed so that it attends over the full KV
+  cache the mapper produced.
+* RaReCache abstract (the CacheReforge card and the arxivdaily page): each token is
+  scored by the energy of its mapped KV in output directions that the calibration
+  data supports weakly, and a fixed share of positions (30% or 40%) is recomputed.
+
+Readings taken where the pages are silent (each stated where it is used):
+linear bias-free mapper; calibration subspace given as an orthonormal basis per
+layer and "weakly supported" read as "outside its span"; score = sum over target
+layers of the squared residual of the concatenated [K | V] vector; budget
+k = ceil(pct * T / 100); ties go to the lower position; rotate-half RoPE with base
+10000 applied only to recomputed q and k at their true positions; all selected K/V
+of a layer are written before any selected query attends; inclusive causal mask,
+scale 1/sqrt(d_h), KV head = h // (H_q / H_kv).
+
+Every function takes float64 numpy arrays (exact upcasts of the stored values) and
+computes its result by its plain definition.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence
+
+import numpy as np
+
+
+# ------------------------------------------------------------------------------------
+# budget
+# ------------------------------------------------------------------------------------
+
+def budget(T: int, pct: int) -> int:
+    """Number of positions to recompute: ceil(pct * T / 100) in integer arithmetic.
+
+    RaReCache abstract: "recomputing just 30% of positions" (and 40%).  The count is
+    rounded up so the budget is never under-spent.
+    """
+    if not (0 <= pct <= 100) or T < 0:
+        raise ValueError("budget: need 0 <= pct <= 100 and T >= 0")
+    return (pct * T + 99) // 100
+
+
+# ------------------------------------------------------------------------------------
+# mapper: shared source projection, then layer-specific reconstruction
+# ------------------------------------------------------------------------------------
+
+def map_latent(x_src: np.ndarray, w_s: np.ndarray) -> np.ndarray:
+    """Shared source projection (PANORAMA abstract): z_t = W_s x_t for every position.
+
+    x_src [N, d_src] (source K and V of all source layers concatenated per position),
+    w_s [r, d_src] stored output-major.  Returns the latent Z [N, r].
+    """
+    return x_src @ w_s.T
+
+
+def reconstruct(z: np.ndarray, w_l: np.ndarray, H_kv: int, d_h: int):
+    """Layer-specific target reconstruction (PANORAMA abstract): y_{t,l} = W_l z_t.
+
+    w_l [L_t, d_t, r] stored output-major; the first H_kv*d_h outputs of a layer are its
+    K heads and the rest its V heads, head-major.  Returns the translated cache
+    K, V [L_t, N, H_kv, d_h] and the mapped vectors Y [L_t, N, d_t].
+    """
+    L = w_l.shape[0]
+    N = z.shape[0]
+    Y = np.stack([z @ w_l[l].T for l in range(L)])
+    K = Y[:, :, :H_kv * d_h].reshape(L, N, H_kv, d_h)
+    V = Y[:, :, H_kv * d_h:].reshape(L, N, H_kv, d_h)
+    return K, V, Y
+
+
+# ------------------------------------------------------------------------------------
+# rank-disagreement score and top-budget selection
+# ------------------------------------------------------------------------------------
+
+def rank_disagreement(Y: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Score of every position (RaReCache abstract, "rank disagreement").
+
+    The energy of a token's mapped KV in directions the calibration data supports
+    weakly, read as: the squared norm of the part of y_{t,l} outside span(U_l), summed
+    over the target layers.  Y [L_t, N, d_t], u [L_t, d_t, c] with orthonormal columns.
+    The residual is formed explicitly: R = Y - (Y U) U^T.
+    """
+    L, N, _ = Y.shape
+    s = np.zeros(N)
+    for l in range(L):
+        proj = (Y[l] @ u[l]) @ u[l].T
+        res = Y[l] - proj
+        s += np.sum(res * res, axis=1)
+    return s
+
+
+def select(s: np.ndarray, k: int):
+    """The k positions with the largest score; ties go to the lower position.
+
+    Sort by the key (-s_t, t) and take the first k.  Returns (S, C): the selected set and
+    its complement, both ascending.  -0.0 and +0.0 compare equal here, as numbers.
+    """
+    T = s.shape[0]
+    if not (0 <= k <= T):
+        raise ValueError("select: need 0 <= k <= T")
+    order = np.lexsort((np.arange(T), -s))
+    S = np.sort(order[:k]).astype(np.int64)
+    C = np.sort(order[k:]).astype(np.int64)
+    return S, C
+
+
+# ------------------------------------------------------------------------------------
+# contextual recomputation of the selected positions
+# ------------------------------------------------------------------------------------
+
+def rope_angles(pos: np.ndarray, d_h: int, base: float) -> np.ndarray:
+    """Angles pos * base**(-2j/d_h) for j < d_h/2, in float64; shape pos.shape + (d_h/2,)."""
+    j = np.arange(d_h // 2, dtype=np.float64)
+    theta = base ** (-2.0 * j / d_h)
+    return np.asarray(pos, dtype=np.float64)[..., None] * theta
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotate-half rotary embedding at positions ``pos``.
+
+    x [..., d_h] with ``pos`` broadcast over the leading axes; pair (j, j + d_h/2) is
+    rotated by the angle of frequency j.
+    """
+    d_h = x.shape[-1]
+    half = d_h // 2
+    ang = rope_angles(pos, d_h, base)
+    cos, sin = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def recompute_qkv(x_rows: np.ndarray, w_qkv: np.ndarray, pos: np.ndarray,
+                  H_q: int, H_kv: int, d_h: int, base: float):
+    """Target Q/K/V of the selected positions (PANORAMA abstract, contextual recompute).
+
+    x_rows [k, D] are the target layer's hidden inputs at the selected positions,
+    w_qkv [(H_q + 2 H_kv) d_h, D] stored output-major with rows [Q heads | K heads |
+    V heads].  q and k are rotated at their true positions; v is not.
+    """
+    qkv = x_rows @ w_qkv.T
+    n = x_rows.shape[0]
+    q = qkv[:, :H_q * d_h].reshape(n, H_q, d_h)
+    k = qkv[:, H_q * d_h:(H_q + H_kv) * d_h].reshape(n, H_kv, d_h)
+    v = qkv[:, (H_q + H_kv) * d_h:].reshape(n, H_kv, d_h)
+    pos = np.asarray(pos)
+    q = rope(q, pos[:, None], base)
+    k = rope(k, pos[:, None], base)
+    return q, k, v
+
+
+def scatter(K: np.ndarray, V: np.ndarray, S: np.ndarray, k_new: np.ndarray, v_new: np.ndarray):
+    """Mixed cache: recomputed K/V replace the translated ones at the selected positions."""
+    K = K.copy()
+    V = V.copy()
+    K[S] = k_new
+    V[S] = v_new
+    return K, V
+
+
+def sparse_causal_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray):
+    """Causal attention of the selected queries over the full (mixed) cache.
+
+    q [k, H_q, d_h] at positions ``pos``; K, V [T, H_kv, d_h].  Query (i, h) attends to
+    keys j <= pos[i] of KV head h // (H_q / H_kv) with weights
+    softmax(q . K_j / sqrt(d_h)).  Returns O [k, H_q, d_h] and the natural-log
+    log-sum-exp of the scaled logits, LSE [k, H_q].
+    """
+    n, H_q, d_h = q.shape
+    H_kv = K.shape[1]
+    g = H_q // H_kv
+    O = np.zeros((n, H_q, d_h))
+    lse = np.zeros((n, H_q))
+    scale = 1.0 / math.sqrt(d_h)
+    for i in range(n):
+        p = int(pos[i])
+        for h in range(H_q):
+            kv = h // g
+            logits = (K[:p + 1, kv, :] @ q[i, h]) * scale
+            m = logits.max()
+            e = np.exp(logits - m)
+            tot = e.sum()
+            w = e / tot
+            assert abs(w.sum() - 1.0) <= 1e-12
+            O[i, h] = w @ V[:p + 1, kv, :]
+            lse[i, h] = m + math.log(tot)
+    return O, lse
+
+
+# ------------------------------------------------------------------------------------
+# the whole handoff, one request at a time
+# ------------------------------------------------------------------------------------
+
+def handoff_request(x_src: np.ndarray, w_s: np.ndarray, w_l: np.ndarray, u: np.ndarray,
+                    x_l: np.ndarray, w_qkv: np.ndarray, pct: int, H_q: int, H_kv: int,
+                    d_h: int, base: float = 10000.0) -> Dict[str, np.ndarray]:
+    """One request: map -> score -> select -> recompute + scatter -> attend, per layer.
+
+    x_src [T, d_src], x_l [L_t, T, D], w_qkv [L_t, n_qkv, D].  Returns the latent Z, the
+    translated cache (K_tr, V_tr), the scores s, the sets S and C, the mixed cache
+    (K, V) [L_t, T, H_kv, d_h] and the attention outputs O [L_t, k, H_q, d_h], LSE.
+    """
+    T = x_src.shape[0]
+    L = w_l.shape[0]
+    z = map_latent(x_src, w_s)
+    K_tr, V_tr, Y = reconstruct(z, w_l, H_kv, d_h)
+    s = rank_disagreement(Y, u)
+    k = budget(T, pct)
+    S, C = select(s, k)
+    K = K_tr.copy()
+    V = V_tr.copy()
+    O = np.zeros((L, k, H_q, d_h))
+    LSE = np.zeros((L, k, H_q))
+    for l in range(L):
+        q, kk, vv = recompute_qkv(x_l[l][S], w_qkv[l], S, H_q, H_kv, d_h, base)
+        K[l], V[l] = scatter(K[l], V[l], S, kk, vv)
+        O[l], LSE[l] = sparse_causal_attention(q, K[l], V[l], S)
+    return dict(z=z, K_tr=K_tr, V_tr=V_tr, s=s, S=S, C=C, K=K, V=V, O=O, LSE=LSE)
+
+
+def score_gap(s: np.ndarray, k: int) -> float:
+    """Relative gap between the k-th and (k+1)-th largest scores (inf when k is 0 or T)."""
+    T = s.shape[0]
+    if k == 0 or k == T:
+        return math.inf
+    srt = np.sort(s)[::-1]
+    tau = srt[k - 1]
+    return float((srt[k - 1] - srt[k]) / abs(tau)) if tau != 0 else float(srt[k - 1] - srt[k])

@@ -1,0 +1,536 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each pin checks the oracle against something it does not compute itself: a value
+worked by hand (tests/golden), a closed form, an invariant of the mathematics, a
+special case that reduces to a library routine, or brute force on tiny inputs.
+``test_planted_mistakes`` plants plausible mistakes in the oracle and checks that at
+least one pin catches each of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvx_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _orthonormal(rng, n, c):
+    q, _ = np.linalg.qr(rng.standard_normal((n, c)))
+    return q
+
+
+# ------------------------------------------------------------------------- budget
+
+def pin_budget_golden():
+    for case in _golden("budget.json")["cases"]:
+        assert O.budget(case["T"], case["pct"]) == case["k"], case
+
+
+def pin_budget_ceiling():
+    for T in range(0, 300):
+        for pct in range(0, 101):
+            want = math.ceil(Fraction(pct * T, 100))
+            assert O.budget(T, pct) == want
+
+
+# ------------------------------------------------------------------------- mapper
+
+def pin_map_identity():
+    rng = _rng(1)
+    x = rng.standard_normal((9, 16))
+    z = O.map_latent(x, np.eye(16))
+    assert np.array_equal(z, x)
+
+
+def pin_map_orthogonal_roundtrip():
+    """Orthogonal shared projection + the matching per-layer reconstruction returns the
+    source KV split into layer blocks (an orthogonal mapper reproduces its input)."""
+    rng = _rng(2)
+    L, H_kv, d_h = 3, 2, 4
+    d_t = 2 * H_kv * d_h
+    d = L * d_t
+    x = rng.standard_normal((11, d))
+    Q = _orthonormal(rng, d, d)
+    z = O.map_latent(x, Q)                          # z = x Q^T
+    w_l = np.stack([Q.T[l * d_t:(l + 1) * d_t] for l in range(L)])
+    K, V, Y = O.reconstruct(z, w_l, H_kv, d_h)
+    for l in range(L):
+        blk = x[:, l * d_t:(l + 1) * d_t]
+        assert np.abs(Y[l] - blk).max() < 1e-12
+        assert np.abs(K[l].reshape(11, -1) - blk[:, :H_kv * d_h]).max() < 1e-12
+        assert np.abs(V[l].reshape(11, -1) - blk[:, H_kv * d_h:]).max() < 1e-12
+
+
+def pin_map_linearity():
+    rng = _rng(3)
+    w = rng.standard_normal((5, 12))
+    a, b = rng.standard_normal((4, 12)), rng.standard_normal((4, 12))
+    lhs = O.map_latent(2.0 * a - 3.0 * b, w)
+    rhs = 2.0 * O.map_latent(a, w) - 3.0 * O.map_latent(b, w)
+    assert np.abs(lhs - rhs).max() < 1e-12
+    # a non-square mapper: each latent entry is one weight row dotted with the input
+    for i in range(4):
+        for j in range(5):
+            assert abs(O.map_latent(a, w)[i, j] - sum(a[i, c] * w[j, c] for c in range(12))) < 1e-12
+
+
+def pin_reconstruct_block_identity():
+    """w_l = identity picks latent columns: K head h of layer 0 is z[:, h*d_h:(h+1)*d_h],
+    V heads follow the K heads."""
+    rng = _rng(4)
+    H_kv, d_h = 2, 3
+    d_t = 2 * H_kv * d_h
+    z = rng.standard_normal((5, d_t))
+    w_l = np.stack([np.eye(d_t), np.eye(d_t)[::-1]])
+    K, V, _ = O.reconstruct(z, w_l, H_kv, d_h)
+    for h in range(H_kv):
+        assert np.array_equal(K[0][:, h], z[:, h * d_h:(h + 1) * d_h])
+        assert np.array_equal(V[0][:, h], z[:, (H_kv + h) * d_h:(H_kv + h + 1) * d_h])
+    # layer 1 reverses the columns
+    assert np.array_equal(V[1][:, H_kv - 1, ::-1], z[:, :d_h])
+
+
+# ------------------------------------------------------------------------- score
+
+def pin_score_hand():
+    g = _golden("score_hand.json")
+    u = np.array(g["u"])
+    Y = np.array(g["y"])
+    assert abs(O.rank_disagreement(Y, u)[0] - g["score"]) < 1e-12
+
+
+def pin_score_in_span_zero():
+    rng = _rng(5)
+    L, d_t, c, N = 3, 10, 4, 7
+    u = np.stack([_orthonormal(rng, d_t, c) for _ in range(L)])
+    Y = np.stack([rng.standard_normal((N, c)) @ u[l].T for l in range(L)])
+    s = O.rank_disagreement(Y, u)
+    assert np.all(np.abs(s) <= 1e-12 * np.sum(Y * Y, axis=(0, 2)))
+
+
+def pin_score_complement_full():
+    rng = _rng(6)
+    L, d_t, c, N = 2, 8, 3, 6
+    s_full = []
+    u = []
+    Y = []
+    for _ in range(L):
+        q = _orthonormal(rng, d_t, d_t)
+        u.append(q[:, :c])
+        Y.append(rng.standard_normal((N, d_t - c)) @ q[:, c:].T)   # orthogonal to span(U)
+    u, Y = np.stack(u), np.stack(Y)
+    s = O.rank_disagreement(Y, u)
+    want = np.sum(Y * Y, axis=(0, 2))
+    assert np.abs(s - want).max() <= 1e-12 * want.max()
+
+
+def pin_score_empty_basis():
+    rng = _rng(7)
+    Y = rng.standard_normal((2, 5, 6))
+    s = O.rank_disagreement(Y, np.zeros((2, 6, 0)))
+    assert np.abs(s - np.sum(Y * Y, axis=(0, 2))).max() < 1e-12
+
+
+def pin_score_homogeneous_equivariant():
+    rng = _rng(8)
+    L, d_t, c, N = 2, 8, 3, 9
+    u = np.stack([_orthonormal(rng, d_t, c) for _ in range(L)])
+    Y = rng.standard_normal((L, N, d_t))
+    s = O.rank_disagreement(Y, u)
+    assert np.abs(O.rank_disagreement(2.5 * Y, u) - 6.25 * s).max() < 1e-11 * s.max()
+    perm = rng.permutation(N)
+    assert np.abs(O.rank_disagreement(Y[:, perm], u) - s[perm]).max() < 1e-12 * s.max()
+
+
+def pin_score_least_squares():
+    """The residual outside span(U) equals the least-squares residual of fitting y by U's
+    columns (library routine), so the energies agree."""
+    rng = _rng(9)
+    L, d_t, c, N = 2, 9, 4, 5
+    u = np.stack([_orthonormal(rng, d_t, c) for _ in range(L)])
+    Y = rng.standard_normal((L, N, d_t))
+    want = np.zeros(N)
+    for l in range(L):
+        coef, *_ = np.linalg.lstsq(u[l], Y[l].T, rcond=None)
+        res = Y[l].T - u[l] @ coef
+        want += np.sum(res * res, axis=0)
+    assert np.abs(O.rank_disagreement(Y, u) - want).max() < 1e-12 * want.max()
+
+
+def pin_score_latent_identity():
+    """For a linear bias-free mapper the score is a quadratic form of the latent:
+    s_t = z_t^T A z_t with A = sum_l R_l^T R_l, R_l = (I - U_l U_l^T) W_l."""
+    rng = _rng(10)
+    L, H_kv, d_h, r, c, N = 3, 2, 4, 6, 5, 8
+    d_t = 2 * H_kv * d_h
+    w_l = rng.standard_normal((L, d_t, r))
+    u = np.stack([_orthonormal(rng, d_t, c) for _ in range(L)])
+    z = rng.standard_normal((N, r))
+    _, _, Y = O.reconstruct(z, w_l, H_kv, d_h)
+    s = O.rank_disagreement(Y, u)
+    A = np.zeros((r, r))
+    for l in range(L):
+        R = w_l[l] - u[l] @ (u[l].T @ w_l[l])
+        A += R.T @ R
+    s2 = np.einsum("ti,ij,tj->t", z, A, z)
+    assert np.abs(s - s2).max() <= 1e-12 * s.max()
+
+
+# ------------------------------------------------------------------------- select
+
+def pin_select_brute_force():
+    rng = _rng(11)
+    for trial in range(40):
+        T = int(rng.integers(1, 40))
+        s = rng.integers(0, 5, size=T).astype(float) * (1 if trial % 2 else 0.5)
+        for k in range(T + 1):
+            S, C = O.select(s, k)
+            order = sorted(range(T), key=lambda t: (-s[t], t))
+            assert list(S) == sorted(order[:k])
+            assert list(C) == sorted(order[k:])
+
+
+def pin_select_all_equal():
+    s = np.full(20, 3.0)
+    S, C = O.select(s, 6)
+    assert list(S) == list(range(6)) and list(C) == list(range(6, 20))
+
+
+def pin_select_signed_zero():
+    s = np.array([-0.0, 0.0, -0.0, 0.0, 1.0, -1.0])
+    S, _ = O.select(s, 3)          # 1.0 first, then the two lowest-index zeros
+    assert list(S) == [0, 1, 4]
+
+
+def pin_select_extremes():
+    s = np.arange(10.0)[::-1]
+    S, C = O.select(s, 0)
+    assert len(S) == 0 and list(C) == list(range(10))
+    S, C = O.select(s, 10)
+    assert list(S) == list(range(10)) and len(C) == 0
+
+
+def pin_select_planted():
+    """Positions whose source KV is scaled by 3 score 9x (homogeneity) and must be
+    selected whenever their count fits the budget."""
+    rng = _rng(12)
+    T, d, r, L, H_kv, d_h, c = 60, 256, 64, 2, 2, 16, 16
+    d_t = 2 * H_kv * d_h
+    x = rng.standard_normal((T, d))
+    planted = rng.choice(T, size=7, replace=False)
+    x[planted] *= 3.0
+    w_s = rng.standard_normal((r, d)) / 16
+    w_l = rng.standard_normal((L, d_t, r)) / 8
+    u = np.stack([_orthonormal(rng, d_t, c) for _ in range(L)])
+    _, _, Y = O.reconstruct(O.map_latent(x, w_s), w_l, H_kv, d_h)
+    s = O.rank_disagreement(Y, u)
+    S, _ = O.select(s, O.budget(T, 30))
+    assert set(planted.tolist()) <= set(S.tolist())
+
+
+# ------------------------------------------------------------------------- rope / recompute
+
+def pin_rope_zero_position():
+    rng = _rng(13)
+    x = rng.standard_normal((3, 5, 8))
+    assert np.array_equal(O.rope(x, np.zeros((3, 5)), 10000.0), x)
+
+
+def pin_rope_d2_closed_form():
+    """d_h = 2 has one pair at frequency 1: a plane rotation by the position itself."""
+    for p in (1, 7, 1000):
+        out = O.rope(np.array([[0.3, -1.1]]), np.array([p]), 10000.0)[0]
+        want = [0.3 * math.cos(p) + 1.1 * math.sin(p), -1.1 * math.cos(p) + 0.3 * math.sin(p)]
+        assert np.abs(out - want).max() < 1e-12
+
+
+def pin_rope_d4_pairs():
+    """d_h = 4: pairs are (0, 2) at frequency 1 and (1, 3) at frequency base^(-1/2)."""
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    out = O.rope(x, np.array([1]), 10000.0)[0]
+    a0, a1 = 1.0, 0.01
+    want = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+            3 * math.cos(a0) + 1 * math.sin(a0), 4 * math.cos(a1) + 2 * math.sin(a1)]
+    assert np.abs(out - want).max() < 1e-12
+
+
+def pin_rope_norm_and_relative():
+    rng = _rng(14)
+    q, k = rng.standard_normal(16), rng.standard_normal(16)
+    for m, n in ((5, 2), (300, 17), (16383, 9000)):
+        rq = O.rope(q[None], np.array([m]), 10000.0)[0]
+        rk = O.rope(k[None], np.array([n]), 10000.0)[0]
+        assert abs(np.linalg.norm(rq) - np.linalg.norm(q)) < 1e-12
+        rel = O.rope(q[None], np.array([m - n]), 10000.0)[0]
+        assert abs(rq @ rk - rel @ k) < 1e-10
+
+
+def pin_recompute_identity_weights():
+    """w_qkv made of identity blocks returns the hidden rows themselves (q, k rotated)."""
+    rng = _rng(15)
+    H_q, H_kv, d_h = 2, 1, 4
+    D = H_q * d_h
+    x = rng.standard_normal((6, D))
+    w = np.concatenate([np.eye(D), np.eye(D)[:H_kv * d_h], np.eye(D)[H_kv * d_h:2 * H_kv * d_h]])
+    pos = np.array([0, 3, 4, 9, 10, 20])
+    q, k, v = O.recompute_qkv(x, w, pos, H_q, H_kv, d_h, 10000.0)
+    assert np.abs(q - O.rope(x.reshape(6, H_q, d_h), pos[:, None], 10000.0)).max() < 1e-12
+    assert np.abs(k[:, 0] - O.rope(x[:, :d_h], pos, 10000.0)).max() < 1e-12
+    assert np.array_equal(v[:, 0], x[:, d_h:2 * d_h])
+
+
+# ------------------------------------------------------------------------- attention
+
+def pin_attention_hand():
+    g = _golden("attention_hand.json")
+    q = np.array(g["q"])[None, None]
+    K = np.array(g["K"])[:, None]
+    V = np.array(g["V"])[:, None]
+    o, lse = O.sparse_causal_attention(q, K, V, np.array([g["pos"]]))
+    assert np.abs(o[0, 0] - g["o"]).max() < 1e-12
+    assert abs(lse[0, 0] - g["lse"]) < 1e-12
+
+
+def _sdpa_causal(q, K, V):
+    """Library routine: torch's scaled_dot_product_attention, causal, float64 CPU.
+    q [T, H_q, d], K/V [T, H_kv, d]; KV heads repeated g times (head h reads h // g)."""
+    g = q.shape[1] // K.shape[1]
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(np.repeat(K, g, axis=1)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(np.repeat(V, g, axis=1)).permute(1, 0, 2)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def pin_attention_full_is_causal_sdpa():
+    rng = _rng(16)
+    T, H_q, H_kv, d_h = 23, 6, 2, 8
+    q = rng.standard_normal((T, H_q, d_h))
+    K = rng.standard_normal((T, H_kv, d_h))
+    V = rng.standard_normal((T, H_kv, d_h))
+    o, lse = O.sparse_causal_attention(q, K, V, np.arange(T))
+    assert np.abs(o - _sdpa_causal(q, K, V)).max() < 1e-12
+    # log-sum-exp against scipy's routine
+    from scipy.special import logsumexp
+    g = H_q // H_kv
+    for i in (0, 5, T - 1):
+        for h in range(H_q):
+            ref = logsumexp(K[:i + 1, h // g] @ q[i, h] / math.sqrt(d_h))
+            assert abs(lse[i, h] - ref) < 1e-12
+
+
+def pin_attention_special_cases():
+    rng = _rng(17)
+    T, H_q, H_kv, d_h = 12, 4, 2, 4
+    q = rng.standard_normal((3, H_q, d_h))
+    K = rng.standard_normal((T, H_kv, d_h))
+    V = rng.standard_normal((T, H_kv, d_h))
+    o, _ = O.sparse_causal_attention(q, K, V, np.array([0, 5, 11]))
+    # the first position sees only itself
+    assert np.abs(o[0] - np.repeat(V[0], 2, axis=0)).max() < 1e-12
+    # constant values give the constant back
+    Vc = np.broadcast_to(np.array([1.0, -2.0, 0.5, 3.0]), (T, H_kv, d_h)).copy()
+    oc, _ = O.sparse_causal_attention(q, K, Vc, np.array([0, 5, 11]))
+    assert np.abs(oc - Vc[0, 0]).max() < 1e-12
+    # GQA equals MHA over KV heads repeated g times
+    om, _ = O.sparse_causal_attention(q, np.repeat(K, 2, axis=1), np.repeat(V, 2, axis=1),
+                                      np.array([0, 5, 11]))
+    assert np.abs(o - om).max() < 1e-12
+
+
+# ------------------------------------------------------------------------- end to end
+
+def _tiny_problem(seed, T=20):
+    rng = _rng(seed)
+    L_t, H_q, H_kv, d_h, r, D, c = 2, 4, 2, 4, 6, 8, 3
+    d_t = 2 * H_kv * d_h
+    d_src = 24
+    return dict(
+        x_src=rng.standard_normal((T, d_src)), w_s=rng.standard_normal((r, d_src)) / 5,
+        w_l=rng.standard_normal((L_t, d_t, r)) / 2.5,
+        u=np.stack([_orthonormal(rng, d_t, c) for _ in range(L_t)]),
+        x_l=rng.standard_normal((L_t, T, D)),
+        w_qkv=rng.standard_normal((L_t, (H_q + 2 * H_kv) * d_h, D)) / 3,
+        H_q=H_q, H_kv=H_kv, d_h=d_h)
+
+
+def pin_handoff_zero_budget():
+    p = _tiny_problem(18)
+    out = O.handoff_request(pct=0, **p)
+    assert len(out["S"]) == 0 and out["O"].shape[1] == 0
+    assert np.array_equal(out["K"], out["K_tr"]) and np.array_equal(out["V"], out["V_tr"])
+
+
+def pin_handoff_full_budget_is_prefill():
+    """A 100% budget recomputes every position, so the cache is the target's own K/V and
+    the outputs equal plain causal attention over the target's own Q/K/V."""
+    p = _tiny_problem(19)
+    out = O.handoff_request(pct=100, **p)
+    T = p["x_src"].shape[0]
+    H_q, H_kv, d_h = p["H_q"], p["H_kv"], p["d_h"]
+    for l in range(p["w_l"].shape[0]):
+        qkv = p["x_l"][l] @ p["w_qkv"][l].T
+        q = qkv[:, :H_q * d_h].reshape(T, H_q, d_h)
+        k = qkv[:, H_q * d_h:(H_q + H_kv) * d_h].reshape(T, H_kv, d_h)
+        v = qkv[:, (H_q + H_kv) * d_h:].reshape(T, H_kv, d_h)
+        # rotary embedding by explicit 2x2 rotations of each (j, j + d_h/2) pair
+        def rot(a):
+            b = a.copy()
+            for t in range(T):
+                for j in range(d_h // 2):
+                    ang = t * 10000.0 ** (-2.0 * j / d_h)
+                    x1, x2 = a[t, :, j], a[t, :, j + d_h // 2]
+                    b[t, :, j] = x1 * math.cos(ang) - x2 * math.sin(ang)
+                    b[t, :, j + d_h // 2] = x2 * math.cos(ang) + x1 * math.sin(ang)
+            return b
+        q, k = rot(q), rot(k)
+        assert np.abs(out["K"][l] - k).max() < 1e-12
+        assert np.abs(out["V"][l] - v).max() < 1e-12
+        assert np.abs(out["O"][l] - _sdpa_causal(q, k, v)).max() < 1e-12
+
+
+def pin_handoff_partial_budget_mixed_cache():
+    """At a partial budget the mixed cache holds translated K/V off the selected set and
+    recomputed K/V on it; every selected query attends to both kinds."""
+    p = _tiny_problem(20)
+    out = O.handoff_request(pct=30, **p)
+    S, C = out["S"], out["C"]
+    assert len(S) == O.budget(20, 30) and sorted(set(S) | set(C)) == list(range(20))
+    assert np.array_equal(out["K"][:, C], out["K_tr"][:, C])
+    assert not np.allclose(out["K"][:, S], out["K_tr"][:, S])
+    # the last selected query's output changes if a translated entry it sees changes
+    l, i = 0, len(S) - 1
+    Kp = out["K"][l].copy()
+    j = int(C[C < S[i]][0])
+    Kp[j] += 1.0
+    q, _, _ = O.recompute_qkv(p["x_l"][l][S], p["w_qkv"][l], S, p["H_q"], p["H_kv"], p["d_h"], 10000.0)
+    o2, _ = O.sparse_causal_attention(q[i:i + 1], Kp, out["V"][l], S[i:i + 1])
+    assert np.abs(o2[0] - out["O"][l, i]).max() > 1e-6
+
+
+PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin(name):
+    PINS[name]()
+
+
+# ------------------------------------------------------------------------- planted mistakes
+
+def _mut_rope_sign(x, pos, base):
+    d_h = x.shape[-1]
+    h = d_h // 2
+    ang = O.rope_angles(pos, d_h, base)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * np.cos(ang) + x2 * np.sin(ang), x2 * np.cos(ang) - x1 * np.sin(ang)], -1)
+
+
+def _mut_rope_interleaved(x, pos, base):
+    d_h = x.shape[-1]
+    ang = O.rope_angles(pos, d_h, base)
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x1 * np.cos(ang) - x2 * np.sin(ang)
+    out[..., 1::2] = x2 * np.cos(ang) + x1 * np.sin(ang)
+    return out
+
+
+def _mut_attn_factory(scale_fn=None, exclusive=False, gqa_mod=False):
+    def attn(q, K, V, pos):
+        n, H_q, d_h = q.shape
+        H_kv = K.shape[1]
+        g = H_q // H_kv
+        Oo = np.zeros((n, H_q, d_h))
+        lse = np.zeros((n, H_q))
+        for i in range(n):
+            p = int(pos[i]) + (0 if exclusive else 1)
+            p = max(p, 1)
+            for h in range(H_q):
+                kv = h % H_kv if gqa_mod else h // g
+                lg = (K[:p, kv] @ q[i, h]) * (scale_fn(d_h) if scale_fn else 1 / math.sqrt(d_h))
+                e = np.exp(lg - lg.max())
+                Oo[i, h] = (e / e.sum()) @ V[:p, kv]
+                lse[i, h] = lg.max() + math.log(e.sum())
+        return Oo, lse
+    return attn
+
+
+def _mut_select_high_index(s, k):
+    T = s.shape[0]
+    order = np.lexsort((-np.arange(T), -s))
+    return np.sort(order[:k]), np.sort(order[k:])
+
+
+def _mut_score_projection(Y, u):
+    s = np.zeros(Y.shape[1])
+    for l in range(Y.shape[0]):
+        p = Y[l] @ u[l]
+        s += np.sum(p * p, axis=1)
+    return s
+
+
+def _mut_score_one_layer(Y, u):
+    res = Y[0] - (Y[0] @ u[0]) @ u[0].T
+    return np.sum(res * res, axis=1)
+
+
+def _mut_map_no_transpose(x, w):
+    return x @ w if w.shape[0] == x.shape[1] else x @ w.T[:, ::-1]
+
+
+def _mut_reconstruct_kv_swapped(z, w_l, H_kv, d_h):
+    K, V, Y = RECONSTRUCT(z, w_l, H_kv, d_h)
+    return V, K, Y
+
+
+def _mut_budget_floor(T, pct):
+    return pct * T // 100
+
+
+RECONSTRUCT = O.reconstruct
+
+MUTANTS = {
+    "rope_sign": ("rope", _mut_rope_sign),
+    "rope_interleaved": ("rope", _mut_rope_interleaved),
+    "attn_no_scale": ("sparse_causal_attention", _mut_attn_factory(scale_fn=lambda d: 1.0)),
+    "attn_exclusive_causal": ("sparse_causal_attention", _mut_attn_factory(exclusive=True)),
+    "attn_gqa_modulo": ("sparse_causal_attention", _mut_attn_factory(gqa_mod=True)),
+    "select_ties_high_index": ("select", _mut_select_high_index),
+    "score_projection_energy": ("rank_disagreement", _mut_score_projection),
+    "score_one_layer": ("rank_disagreement", _mut_score_one_layer),
+    "map_untransposed": ("map_latent", _mut_map_no_transpose),
+    "reconstruct_kv_swapped": ("reconstruct", _mut_reconstruct_kv_swapped),
+    "budget_floor": ("budget", _mut_budget_floor),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistakes(mutant, monkeypatch):
+    attr, fn = MUTANTS[mutant]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for name, pin in PINS.items():
+        if name == "pin_budget_ceiling" and attr != "budget":
+            continue
+        try:
+            pin()
+        except Exception:
+            caught.append(name)
+    assert caught, f"no pin caught the planted mistake {mutant}"
