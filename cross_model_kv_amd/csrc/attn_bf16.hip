@@ -1,0 +1,286 @@
+// Sparse-query causal GQA flash attention for gfx950 (bf16 storage, fp32 softmax/accumulate).
+//
+// A workgroup serves one KV head of one block of consecutive selected queries of a request:
+// rows = (query, head) pairs for the g = H_q / H_kv query heads that share the KV head, 32
+// rows per wave.  The block walks the request's mixed cache in 64-key tiles up to the
+// position of its last query; each row masks keys beyond its own position (inclusive).
+//
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K is the A operand (16-byte LDS reads), the
+//    rotated Q rows are the B operand held in registers for the whole sweep.  In the result
+//    every lane holds 16 keys of one row, so the online softmax needs only lane-local work
+//    and one exchange with lane ^ 32.
+//  * O^T = V^T P^T: P comes straight from the S^T registers (bf16), V^T fragments are read
+//    from the row-major V tile with ds_read_b64_tr_b16, and the output rows stay lane-local,
+//    so the rescale by exp2(m_old - m_new) needs no cross-lane traffic.
+//  * K and V tiles are double-buffered in LDS with per-row XOR-swizzled 16-byte chunks; the
+//    next tile is loaded into registers while the current one is consumed.
+//  * q is rotated (rotate-half, table angles at the query's true position) while it is
+//    loaded; k was rotated when it was scattered into the cache.
+//  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
+//    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
+#include "kvx_internal.h"
+
+namespace kvx {
+namespace {
+
+constexpr int KT = 64;   // keys per tile
+
+template <int D_H>
+__device__ __forceinline__ int kv_swz(int key) {
+    if constexpr (D_H == 128) return key & 15;
+    else return swz(key);
+}
+
+template <int D_H, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bf16_kernel(AttnArgs a) {
+    constexpr int NT = W * 64;
+    constexpr int NCH = D_H / 8;               // 16-byte chunks per K/V row
+    constexpr int QC = D_H / 16;               // 16-deep k-steps of S^T = K Q^T
+    constexpr int DB = D_H / 32;               // 32-wide output blocks
+    constexpr int TILE = KT * D_H;             // elements of one K (or V) tile
+    constexpr int CHUNKS = 2 * KT * NCH;       // K and V chunks per tile
+    constexpr int CPT = (CHUNKS + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) bf16 lds[2][2 * TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int hf = lane >> 5, lr = lane & 31;
+    const int H_kv = a.H_kv, g = a.H_q / H_kv;
+    const int hk = blockIdx.x % H_kv;
+    const int qb = a.n_blocks - 1 - (int)(blockIdx.x / H_kv);   // longest first
+
+    // request of this query block
+    int b = 0;
+    {
+        int lo = 0, hi = a.n_req - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.blk_cu[mid] <= qb) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+    }
+    const int ks0 = a.cu_sel[b], k_b = a.cu_sel[b + 1] - ks0;
+    const int qi0 = (qb - a.blk_cu[b]) * a.bq;
+    const int nq = min(a.bq, k_b - qi0);
+    const int i0 = ks0 + qi0;
+    const int T_b = a.slots.cu_tok[b + 1] - a.slots.cu_tok[b];
+    const int p_max = a.sel[i0 + nq - 1];
+
+    // this lane's row
+    const int row = w * 32 + lr;
+    const int qi = row / g, hh = row - qi * g;
+    const bool valid = qi < nq;
+    const int h = hk * g + hh;
+    const int p_row = valid ? a.sel[i0 + qi] : p_max;
+
+    // ---- rotated Q fragments (B operand: row lr, dims 16c + 8hf + e)
+    bf16x8 qf[QC];
+    {
+        const bf16* qrow = (const bf16*)a.qkv + (int64_t)(i0 + (valid ? qi : 0)) * a.ld + (int64_t)h * D_H;
+#pragma unroll
+        for (int c = 0; c < QC; ++c) {
+            if (valid) qf[c] = *(const bf16x8*)(qrow + 16 * c + 8 * hf);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[c][e] = (bf16)0.f;
+        }
+        constexpr int HC = QC / 2;     // chunks of the first half of the dims
+        const float* rp = a.rope + (int64_t)p_row * D_H;   // [d_h/2][2] per position
+#pragma unroll
+        for (int c = 0; c < HC; ++c) {
+            const int j0 = 16 * c + 8 * hf;
+            const float4* cs = (const float4*)(rp + 2 * j0);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float4 t = cs[e2];       // (cos, sin) of j0+2e2 and j0+2e2+1
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int e = 2 * e2 + u;
+                    const float co = u ? t.z : t.x, si = u ? t.w : t.y;
+                    const float x1 = (float)qf[c][e], x2 = (float)qf[c + HC][e];
+                    qf[c][e] = (bf16)(x1 * co - x2 * si);
+                    qf[c + HC][e] = (bf16)(x2 * co + x1 * si);
+                }
+            }
+        }
+    }
+
+    // ---- K/V tile staging
+    const bf16* kbase = (const bf16*)a.kc;
+    const bf16* vbase = (const bf16*)a.vc;
+    uint4 pre[CPT];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int idx = tid + c * NT;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (idx < CHUNKS) {
+                const int kv = idx / (KT * NCH);
+                const int kk = (idx / NCH) % KT, ch = idx % NCH;
+                const int j = kt * KT + kk;
+                if (j < T_b) {
+                    const int64_t slot = a.slots.slot(b, j);
+                    const bf16* src = (kv ? vbase : kbase) + (slot * H_kv + hk) * D_H + ch * 8;
+                    v = *(const uint4*)src;
+                }
+            }
+            pre[c] = v;
+        }
+    };
+    auto lstore = [&](int stage) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int idx = tid + c * NT;
+            if (idx < CHUNKS) {
+                const int kv = idx / (KT * NCH);
+                const int kk = (idx / NCH) % KT, ch = idx % NCH;
+                *(uint4*)(&lds[stage][kv * TILE + kk * D_H + ((ch ^ kv_swz<D_H>(kk)) << 3)]) = pre[c];
+            }
+        }
+    };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = 1.4426950408889634f / sqrtf((float)D_H);
+
+    const int n_tiles = p_max / KT + 1;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < n_tiles; ++kt) {
+        const int stage = kt & 1;
+        if (kt + 1 < n_tiles) gload(kt + 1);
+        const bf16* lk = &lds[stage][0];
+        const bf16* lv = &lds[stage][TILE];
+
+        // S^T for the two 32-key halves of the tile
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+            const int key = kb * 32 + lr;
+#pragma unroll
+            for (int c = 0; c < QC; ++c) {
+                const bf16x8 kf = *(const bf16x8*)(lk + key * D_H + (((2 * c + hf) ^ kv_swz<D_H>(key)) << 3));
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
+            }
+        }
+
+        // online softmax in the log2 domain
+        float mx = -INFINITY;
+        const int jbase = kt * KT + 4 * hf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = jbase + kb * 32 + 8 * (i >> 2) + (i & 3);
+                const float x = j <= p_row ? sacc[kb][i] * sl2 : -INFINITY;
+                sacc[kb][i] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        float rs = 0.f;
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = __builtin_amdgcn_exp2f(sacc[kb][i] - m_new);
+                rs += pv;
+                pf[kb][i >> 3][i & 7] = (bf16)pv;
+            }
+        rs += __shfl_xor(rs, 32);
+        l_run = l_run * corr + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
+
+        // O^T += V^T P^T
+        const int G = lane >> 4, gi = lane & 15;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int d = 0; d < DB; ++d) {
+                    bf16x8 vf;
+#pragma unroll
+                    for (int E = 0; E < 2; ++E) {
+                        const int key = kb * 32 + s * 16 + 8 * E + 4 * (G >> 1) + (gi >> 2);
+                        const int d0 = d * 32 + 16 * (G & 1) + 4 * (gi & 3);
+                        const bf16* addr = lv + key * D_H + (((d0 >> 3) ^ kv_swz<D_H>(key)) << 3) + (d0 & 7);
+                        const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(addr));
+                        const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) vf[4 * E + v] = tb[v];
+                    }
+                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][s], oacc[d], 0, 0, 0);
+                }
+            }
+        }
+
+        if (kt + 1 < n_tiles) lstore(stage ^ 1);
+        __syncthreads();
+    }
+
+    if (!valid) return;
+    const float inv = 1.f / l_run;
+    bf16* orow = (bf16*)a.out + ((int64_t)(i0 + qi) * a.H_q + h) * D_H;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            bf16x4 o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = (bf16)(oacc[d][4 * q4 + v] * inv);
+            *(bf16x4*)(orow + d * 32 + 8 * q4 + 4 * hf) = o;
+        }
+    if (a.lse && hf == 0)
+        a.lse[(int64_t)(i0 + qi) * a.H_q + h] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
+}
+
+template <int D_H>
+hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.n_blocks * a.H_kv));
+    switch (W) {
+        case 3: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 3>), grid, dim3(3 * 64), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 4>), grid, dim3(4 * 64), 0, s, a); break;
+        case 5: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 5>), grid, dim3(5 * 64), 0, s, a); break;
+        case 6: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 6>), grid, dim3(6 * 64), 0, s, a); break;
+        case 7: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 7>), grid, dim3(7 * 64), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Rows per workgroup are 32 per wave: 4 waves when g divides 128, else g waves of 32 queries.
+int attn_bf16_block_queries(int g) {
+    if (g <= 0) return 0;
+    if (128 % g == 0 && g <= 16) return 128 / g;
+    if (g <= 7) return 32;
+    return 0;
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+    if (a.n_blocks == 0) return hipSuccess;
+    const int g = a.H_q / a.H_kv;
+    const int W = a.bq * g / 32;
+    if (a.d_h == 128) return launch_dh<128>(a, W, s);
+    if (a.d_h == 64) return launch_dh<64>(a, W, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kvx

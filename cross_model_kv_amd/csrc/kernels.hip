@@ -1,0 +1,538 @@
+// Non-matrix-core kernels of the handoff: the fp64 score-operator preparation, the radix
+// top-k selection, the rotary table, rotate-and-scatter of recomputed K/V, and the fp32
+// storage path (GEMM, row dot, attention).
+#include <math.h>
+
+#include "kvx_internal.h"
+
+namespace kvx {
+namespace {
+
+template <typename T> __device__ __forceinline__ double to_d(T x) { return (double)x; }
+template <> __device__ __forceinline__ double to_d<bf16>(bf16 x) { return (double)(float)x; }
+template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+// =========================================================================== fp64 GEMM
+// 64x64 output tile, 16-deep K slices, 256 threads with 4x4 outputs each.  Used once per
+// (mapper, calibration) pair, so it favours generality (arbitrary strides and input types).
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void gemm_f64_kernel(int M, int N, int K, double alpha,
+                                                       const TA* A, int64_t sam, int64_t sak,
+                                                       const TB* B, int64_t sbk, int64_t sbn,
+                                                       double* C, int64_t ldc, int accumulate) {
+    __shared__ double As[16][65];
+    __shared__ double Bs[16][65];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    double acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        for (int e = tid; e < 1024; e += 256) {
+            const int mm = e & 63, kk = e >> 6;        // consecutive threads walk m (A) / n (B)
+            const int m = m0 + mm, n = n0 + mm, k = k0 + kk;
+            As[kk][mm] = (m < M && k < K) ? to_d(A[m * sam + k * sak]) : 0.0;
+            Bs[kk][mm] = (n < N && k < K) ? to_d(B[k * sbk + n * sbn]) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty * 4 + i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx * 4 + j;
+            if (n >= N) continue;
+            double v = alpha * acc[i][j];
+            if (accumulate) v += C[m * ldc + n];
+            C[m * ldc + n] = v;
+        }
+    }
+}
+
+template <typename T>
+__global__ void to_f64_kernel(const T* src, double* dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = to_d(src[i]);
+}
+
+__global__ void zero_f64_kernel(double* dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = 0.0;
+}
+
+__global__ void pack_operator_kernel(const double* A, int r, int dtype, void* op) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)r * r) return;
+    const double a = A[i];
+    if (dtype == KVX_F32) {
+        ((float*)op)[i] = (float)a;
+        return;
+    }
+    const int row = (int)(i / r), col = (int)(i % r);
+    const bf16 hi = (bf16)(float)a;
+    const bf16 lo = (bf16)(float)(a - (double)(float)hi);
+    bf16* o = (bf16*)op + (int64_t)row * 2 * r;
+    o[col] = hi;
+    o[r + col] = lo;
+}
+
+// =========================================================================== select
+// One workgroup of 1024 threads per request.  Keys are the fp32 score bits made
+// order-preserving as unsigned integers (-0.0 folded onto +0.0).  The k-th largest key is
+// found by radix passes of 8 bits over the bits below the common prefix of the request's
+// min and max keys; the histogram's top-down cumulative count picks each digit.  Keys equal
+// to the k-th are taken lowest position first, then positions are written in ascending
+// order with two block-wide prefix sums.  Integer-only after the scores: deterministic.
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ int block_excl_scan(int v, int* s_wave, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        int t = lane < SEL_WAVES ? s_wave[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(t, o);
+            if (lane >= o) t += y;
+        }
+        if (lane < SEL_WAVES) s_wave[lane] = t;
+    }
+    __syncthreads();
+    const int base = w > 0 ? s_wave[w - 1] : 0;
+    if (total) *total = s_wave[SEL_WAVES - 1];
+    __syncthreads();
+    return base + x - v;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partial, int n_part,
+                                                            int64_t n_rows, float* scores,
+                                                            const int32_t* cu_tok,
+                                                            const int32_t* cu_sel, int32_t* sel,
+                                                            int32_t* rest) {
+    __shared__ int hist[SEL_WAVES][256];
+    __shared__ int s_wave[SEL_WAVES];
+    __shared__ uint32_t s_mm[2][SEL_WAVES];
+    __shared__ int s_bc[2];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int b = blockIdx.x;
+    const int base = cu_tok[b], T = cu_tok[b + 1] - base;
+    const int k = cu_sel[b + 1] - cu_sel[b];
+    int32_t* so = sel + cu_sel[b];
+    int32_t* ro = rest + (base - cu_sel[b]);
+
+    auto score_at = [&](int t) -> float {
+        if (n_part == 0) return scores[base + t];
+        float s = 0.f;
+        for (int p = 0; p < n_part; ++p) s += partial[(int64_t)p * n_rows + base + t];
+        return s;
+    };
+    if (n_part > 0)
+        for (int t = tid; t < T; t += SEL_THREADS) scores[base + t] = score_at(t);
+    if (k == 0) {
+        for (int t = tid; t < T; t += SEL_THREADS) ro[t] = t;
+        return;
+    }
+    if (k == T) {
+        for (int t = tid; t < T; t += SEL_THREADS) so[t] = t;
+        return;
+    }
+
+    // common prefix of all keys of this request
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int t = tid; t < T; t += SEL_THREADS) {
+        const uint32_t key = order_key(score_at(t));
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    if (lane == 0) { s_mm[0][w] = kmin; s_mm[1][w] = kmax; }
+    __syncthreads();
+    kmin = s_mm[0][0];
+    kmax = s_mm[1][0];
+    for (int i = 1; i < SEL_WAVES; ++i) { kmin = min(kmin, s_mm[0][i]); kmax = max(kmax, s_mm[1][i]); }
+    const uint32_t diff = kmin ^ kmax;
+    int nb = diff ? 32 - __clz(diff) : 0;              // bits below the common prefix
+    uint32_t prefix = nb == 32 ? 0u : (kmax >> nb) << nb;
+    uint32_t mask = nb == 32 ? 0u : ~((1u << nb) - 1u);
+    int want = k;                                       // rank from the top among matches
+
+    while (nb > 0) {
+        const int d = nb < 8 ? nb : 8;
+        const int shift = nb - d;
+        const int nbins = 1 << d;
+        for (int i = tid; i < SEL_WAVES * 256; i += SEL_THREADS) (&hist[0][0])[i] = 0;
+        __syncthreads();
+        for (int t = tid; t < T; t += SEL_THREADS) {
+            const uint32_t key = order_key(score_at(t));
+            if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & (nbins - 1)], 1);
+        }
+        __syncthreads();
+        if (tid < 256) {
+            int s = 0;
+            for (int i = 0; i < SEL_WAVES; ++i) s += hist[i][tid];
+            hist[0][tid] = s;
+        }
+        __syncthreads();
+        if (w == 0) {
+            // lane l owns bins top-4l .. top-4l-3 (top = nbins-1), cumulative from the top
+            int cnt[4], c = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int bin = nbins - 1 - 4 * lane - q;
+                cnt[q] = bin >= 0 ? hist[0][bin] : 0;
+                c += cnt[q];
+            }
+            int cum = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(cum, o);
+                if (lane >= o) cum += y;
+            }
+            const unsigned long long hit = __ballot(cum >= want);
+            const int L = __ffsll((long long)hit) - 1;
+            if (lane == L) {
+                int before = cum - c, bin = nbins - 1 - 4 * lane;
+                for (int q = 0; q < 4; ++q, --bin) {
+                    if (before + cnt[q] >= want) break;
+                    before += cnt[q];
+                }
+                s_bc[0] = bin;
+                s_bc[1] = want - before;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_bc[0] << shift;
+        mask |= (uint32_t)(nbins - 1) << shift;
+        want = s_bc[1];
+        nb = shift;
+        __syncthreads();
+    }
+    const uint32_t tau = prefix;      // the k-th largest key
+    const int take_eq = want;         // how many keys equal to tau are selected
+
+    const int chunk = (T + SEL_THREADS - 1) / SEL_THREADS;
+    const int t0 = min(T, tid * chunk), t1 = min(T, t0 + chunk);
+    int n_eq = 0;
+    for (int t = t0; t < t1; ++t) n_eq += order_key(score_at(t)) == tau;
+    const int eq_before = block_excl_scan(n_eq, s_wave, nullptr);
+    int n_take = 0;
+    {
+        int e = eq_before;
+        for (int t = t0; t < t1; ++t) {
+            const uint32_t key = order_key(score_at(t));
+            n_take += key > tau || (key == tau && e++ < take_eq);
+        }
+    }
+    int j = block_excl_scan(n_take, s_wave, nullptr);
+    int e = eq_before;
+    for (int t = t0; t < t1; ++t) {
+        const uint32_t key = order_key(score_at(t));
+        const bool take = key > tau || (key == tau && e++ < take_eq);
+        if (take) so[j++] = t;
+        else ro[t - j] = t;
+    }
+}
+
+// =========================================================================== rope
+__global__ void rope_table_kernel(double base, int d_h, int max_pos, float* table) {
+    const int half = d_h / 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)max_pos * half) return;
+    const int p = (int)(idx / half), j = (int)(idx % half);
+    const double theta = pow(base, -2.0 * (double)j / (double)d_h);
+    const double ang = (double)p * theta;
+    table[2 * idx] = (float)cos(ang);
+    table[2 * idx + 1] = (float)sin(ang);
+}
+
+// one thread per (selected row, KV head, rotation pair j): rotates k's pair and copies v's
+// two elements at j and j + d_h/2
+template <typename TE>
+__global__ void rope_scatter_kernel(ScatterArgs a) {
+    const int half = a.d_h / 2;
+    const int64_t per_row = (int64_t)a.H_kv * half;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= a.n_sel * per_row) return;
+    const int i = (int)(idx / per_row);
+    const int rem = (int)(idx % per_row);
+    const int h = rem / half, j = rem % half;
+    const int b = find_request(a.cu_sel, a.n_req, i);
+    const int p = a.sel[i];
+    const int64_t slot = a.slots.slot(b, p);
+    const TE* row = (const TE*)a.qkv + (int64_t)i * a.ld;
+    const TE* kr = row + (int64_t)(a.H_q + h) * a.d_h;
+    const TE* vr = row + (int64_t)(a.H_q + a.H_kv + h) * a.d_h;
+    const float c = a.rope[((int64_t)p * half + j) * 2], s = a.rope[((int64_t)p * half + j) * 2 + 1];
+    const float x1 = to_f(kr[j]), x2 = to_f(kr[j + half]);
+    TE* kd = (TE*)a.kc + (slot * a.H_kv + h) * a.d_h;
+    TE* vd = (TE*)a.vc + (slot * a.H_kv + h) * a.d_h;
+    kd[j] = (TE)(x1 * c - x2 * s);
+    kd[j + half] = (TE)(x2 * c + x1 * s);
+    vd[j] = vr[j];
+    vd[j + half] = vr[j + half];
+}
+
+// =========================================================================== fp32 path
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args a) {
+    __shared__ float As[16][65];
+    __shared__ float Bs[16][65];
+    __shared__ int s_src[64];
+    __shared__ int64_t s_slot[64];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int g = blockIdx.z, m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    if (tid < 64) {
+        const int m = m0 + tid;
+        int src = -1;
+        int64_t slot = 0;
+        if (m < a.M) {
+            const RowInfo ri = row_info(a.rows, m);
+            src = ri.src;
+            if (a.epi == EPI_CACHE) slot = a.slots.slot(ri.b, ri.pos);
+        }
+        s_src[tid] = src;
+        s_slot[tid] = slot;
+    }
+    __syncthreads();
+    const float* Bg = a.B + (int64_t)g * a.b_group_stride;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < a.K; k0 += 16) {
+        for (int e = tid; e < 1024; e += 256) {
+            const int kk = e & 15, mm = e >> 4;         // consecutive threads walk k
+            const int k = k0 + kk;
+            const int src = s_src[mm];
+            As[kk][mm] = (src >= 0 && k < a.K) ? a.A[(int64_t)src * a.lda + k % a.K_a] : 0.f;
+            const int n = n0 + mm;
+            Bs[kk][mm] = (n < a.N && k < a.K) ? Bg[(int64_t)n * a.ldb + k] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float x[4], y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(x[i], y[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ml = ty * 4 + i;
+        if (s_src[ml] < 0) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx * 4 + j;
+            if (n >= a.N) continue;
+            if (a.epi == EPI_STORE) {
+                a.C[(int64_t)(m0 + ml) * a.ldc + n] = acc[i][j];
+            } else {
+                const bool is_k = n < a.hd;
+                float* dst = (is_k ? a.kc : a.vc) + (int64_t)g * a.layer_elems + s_slot[ml] * a.hd +
+                             (is_k ? n : n - a.hd);
+                *dst = acc[i][j];
+            }
+        }
+    }
+}
+
+// one wave per row: out[t] = sum_n P[t][n] * Z[t][n] in a fixed order
+__global__ void rowdot_f32_kernel(const float* P, const float* Z, int64_t n, int r, float* out) {
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= n) return;
+    float s = 0.f;
+    for (int c = lane; c < r; c += 64) s = fmaf(P[row * r + c], Z[row * r + c], s);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) out[row] = s;
+}
+
+// fp32 attention: one wave per (selected query, head).  Keys are spread over the lanes
+// (one dot product per lane), the softmax is online over chunks of 64 keys in the log2
+// domain, and every lane accumulates the output dims lane and lane + 64.
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+    __shared__ float s_q[4][128];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wv;            // one (row, head) per wave
+    if (item >= (int64_t)a.n_blocks * a.H_q) return;               // whole wave leaves
+    const int i = (int)(item / a.H_q), h = (int)(item % a.H_q);
+    const int g = a.H_q / a.H_kv, hk = h / g;
+    const int d_h = a.d_h, half = d_h / 2;
+    const int b = find_request(a.cu_sel, a.n_req, i);
+    const int p = a.sel[i];
+    const float* q = (const float*)a.qkv + (int64_t)i * a.ld + (int64_t)h * d_h;
+    if (lane < half) {
+        const float c = a.rope[((int64_t)p * half + lane) * 2], s = a.rope[((int64_t)p * half + lane) * 2 + 1];
+        const float x1 = q[lane], x2 = q[lane + half];
+        s_q[wv][lane] = x1 * c - x2 * s;
+        s_q[wv][lane + half] = x2 * c + x1 * s;
+    }
+    // s_q[wv] is private to this wave: a wave-level barrier orders its LDS writes and reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float* K = (const float*)a.kc;
+    const float* V = (const float*)a.vc;
+    const float scale = 1.4426950408889634f / sqrtf((float)d_h);
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int j0 = 0; j0 <= p; j0 += 64) {
+        const int j = j0 + lane;
+        float x = -INFINITY;
+        int64_t slot_j = 0;
+        if (j <= p) {
+            slot_j = a.slots.slot(b, j);
+            const float* kr = K + (slot_j * a.H_kv + hk) * d_h;
+            float dot = 0.f;
+            for (int d = 0; d < d_h; ++d) dot = fmaf(s_q[wv][d], kr[d], dot);
+            x = dot * scale;
+        }
+        float cm = x;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+        const float mn = fmaxf(m, cm);
+        const float corr = exp2f(m - mn);
+        const float pj = j <= p ? exp2f(x - mn) : 0.f;
+        float ps = pj;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ps += __shfl_xor(ps, o);
+        l = l * corr + ps;
+        o0 *= corr;
+        o1 *= corr;
+        const int nj = min(64, p + 1 - j0);
+        for (int jj = 0; jj < nj; ++jj) {
+            const float w = __shfl(pj, jj);
+            const int64_t sj = __shfl((long long)slot_j, jj);
+            const float* vr = V + (sj * a.H_kv + hk) * d_h;
+            o0 = fmaf(w, vr[lane], o0);
+            if (lane + 64 < d_h) o1 = fmaf(w, vr[lane + 64], o1);
+        }
+        m = mn;
+    }
+    float* out = (float*)a.out + ((int64_t)i * a.H_q + h) * d_h;
+    if (lane < d_h) out[lane] = o0 / l;
+    if (lane + 64 < d_h) out[lane + 64] = o1 / l;
+    if (a.lse && lane == 0) a.lse[(int64_t)i * a.H_q + h] = (m + log2f(l)) * 0.6931471805599453f;
+}
+
+}  // namespace
+
+// =========================================================================== launchers
+hipError_t launch_gemm_f64(int M, int N, int K, double alpha, const void* A, int ta, int64_t sam,
+                           int64_t sak, const void* B, int tb, int64_t sbk, int64_t sbn, double* C,
+                           int64_t ldc, bool accumulate, hipStream_t s) {
+    if (M == 0 || N == 0) return hipSuccess;
+    dim3 grid(cdiv(N, 64), cdiv(M, 64));
+    const int acc = accumulate ? 1 : 0;
+#define KVX_F64_CASE(TA_, TB_)                                                                    \
+    hipLaunchKernelGGL((gemm_f64_kernel<TA_, TB_>), grid, dim3(256), 0, s, M, N, K, alpha,         \
+                       (const TA_*)A, sam, sak, (const TB_*)B, sbk, sbn, C, ldc, acc)
+    if (ta == ET_F32 && tb == ET_BF16) KVX_F64_CASE(float, bf16);
+    else if (ta == ET_F32 && tb == ET_F32) KVX_F64_CASE(float, float);
+    else if (ta == ET_F32 && tb == ET_F64) KVX_F64_CASE(float, double);
+    else if (ta == ET_F64 && tb == ET_F64) KVX_F64_CASE(double, double);
+    else return hipErrorInvalidValue;
+#undef KVX_F64_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_to_f64(const void* src, int t, double* dst, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (t == ET_BF16) hipLaunchKernelGGL(to_f64_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)src, dst, n);
+    else hipLaunchKernelGGL(to_f64_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f64(double* dst, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_f64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_operator(const double* A, int r, int dtype, void* op, hipStream_t s) {
+    const int64_t n = (int64_t)r * r;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_operator_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, A, r, dtype, op);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const float* partial, int n_part, int64_t n_rows, float* scores,
+                         const int32_t* cu_tok, const int32_t* cu_sel, int n_req, int32_t* sel,
+                         int32_t* rest, hipStream_t s) {
+    if (n_req == 0) return hipSuccess;
+    hipLaunchKernelGGL(select_kernel, dim3(n_req), dim3(SEL_THREADS), 0, s, partial, n_part, n_rows,
+                       scores, cu_tok, cu_sel, sel, rest);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(double base, int d_h, int max_pos, float* table, hipStream_t s) {
+    const int64_t n = (int64_t)max_pos * (d_h / 2);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, base, d_h, max_pos, table);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_scatter(const ScatterArgs& a, int dtype, hipStream_t s) {
+    const int64_t n = a.n_sel * a.H_kv * (a.d_h / 2);
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (dtype == KVX_BF16) hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const GemmF32Args& a, hipStream_t s) {
+    if (a.M == 0 || a.N == 0 || a.groups == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(cdiv(a.N, 64), cdiv(a.M, 64), a.groups), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowdot_f32(const float* P, const float* Z, int64_t n, int r, float* out, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(rowdot_f32_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, P, Z, n, r, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
+    const int64_t items = (int64_t)a.n_blocks * a.H_q;   // n_blocks = selected rows here
+    if (items == 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvx

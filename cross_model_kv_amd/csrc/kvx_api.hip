@@ -1,0 +1,515 @@
+// C ABI of libkvx: argument validation (host only, before any GPU work is enqueued), workspace
+// sizing and the launch sequence of every entry point declared in include/kvx.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <string>
+#include <vector>
+
+#include "kvx_internal.h"
+
+using namespace kvx;
+
+namespace {
+
+thread_local std::string g_err;
+
+kvx_status fail(kvx_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+kvx_status ok() {
+    g_err.clear();
+    return KVX_OK;
+}
+
+kvx_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(KVX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define KVX_TRY_HIP(expr, what)                              \
+    do {                                                     \
+        hipError_t e_ = (expr);                              \
+        if (e_ != hipSuccess) return hip_status(e_, what);   \
+    } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool debug_checks() {
+    static const int on = [] {
+        const char* v = getenv("KVX_DEBUG");
+        return (v && v[0] && v[0] != '0') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+#define KVX_REQUIRE(cond, ...)                                         \
+    do {                                                               \
+        if (!(cond)) return fail(KVX_ERR_INVALID, __VA_ARGS__);        \
+    } while (0)
+
+#define KVX_REQUIRE_PTR(p, name)                                                        \
+    do {                                                                                \
+        if (!(p)) return fail(KVX_ERR_INVALID, "%s must not be null", name);            \
+        if (!aligned16(p)) return fail(KVX_ERR_INVALID, "%s must be 16-byte aligned", name); \
+    } while (0)
+
+kvx_status check_dtype(int32_t dtype) {
+    if (dtype != KVX_F32 && dtype != KVX_BF16)
+        return fail(KVX_ERR_UNSUPPORTED, "dtype %d is not KVX_F32 (0) or KVX_BF16 (1)", dtype);
+    return KVX_OK;
+}
+
+size_t elem_size(int32_t dtype) { return dtype == KVX_BF16 ? 2 : 4; }
+
+struct BatchInfo {
+    int n_req;
+    int64_t n_tokens, n_sel, n_rest;
+    int max_T;
+};
+
+kvx_status check_batch(const kvx_batch* bt, BatchInfo* out) {
+    KVX_REQUIRE(bt, "batch must not be null");
+    KVX_REQUIRE(bt->n_req >= 1, "batch.n_req must be >= 1 (got %d)", bt->n_req);
+    KVX_REQUIRE(bt->cu_tokens_h && bt->cu_sel_h, "batch host prefix arrays must not be null");
+    KVX_REQUIRE(bt->cu_tokens_d && bt->cu_sel_d, "batch device prefix arrays must not be null");
+    KVX_REQUIRE(bt->cu_tokens_h[0] == 0 && bt->cu_sel_h[0] == 0, "batch prefix arrays must start at 0");
+    int max_T = 0;
+    for (int b = 0; b < bt->n_req; ++b) {
+        const int T = bt->cu_tokens_h[b + 1] - bt->cu_tokens_h[b];
+        const int k = bt->cu_sel_h[b + 1] - bt->cu_sel_h[b];
+        KVX_REQUIRE(T >= 0, "batch.cu_tokens must be non-decreasing (request %d)", b);
+        KVX_REQUIRE(k >= 0 && k <= T, "request %d selects %d of %d positions", b, k, T);
+        if (T > max_T) max_T = T;
+    }
+    if (debug_checks()) {
+        std::vector<int32_t> t(bt->n_req + 1), s(bt->n_req + 1);
+        KVX_TRY_HIP(hipMemcpy(t.data(), bt->cu_tokens_d, t.size() * 4, hipMemcpyDeviceToHost), "debug copy");
+        KVX_TRY_HIP(hipMemcpy(s.data(), bt->cu_sel_d, s.size() * 4, hipMemcpyDeviceToHost), "debug copy");
+        for (int b = 0; b <= bt->n_req; ++b)
+            KVX_REQUIRE(t[b] == bt->cu_tokens_h[b] && s[b] == bt->cu_sel_h[b],
+                        "batch device prefix arrays differ from the host copies at %d", b);
+    }
+    out->n_req = bt->n_req;
+    out->n_tokens = bt->cu_tokens_h[bt->n_req];
+    out->n_sel = bt->cu_sel_h[bt->n_req];
+    out->n_rest = out->n_tokens - out->n_sel;
+    out->max_T = max_T;
+    return KVX_OK;
+}
+
+kvx_status check_cache(const kvx_cache* c, const BatchInfo& bi, int32_t dtype, int32_t H_kv,
+                       int32_t d_h, int min_layers) {
+    KVX_REQUIRE(c, "cache must not be null");
+    KVX_REQUIRE(c->layout == KVX_CONTIGUOUS || c->layout == KVX_PAGED, "cache.layout %d is unknown", c->layout);
+    KVX_REQUIRE_PTR(c->k, "cache.k");
+    KVX_REQUIRE_PTR(c->v, "cache.v");
+    KVX_REQUIRE(c->n_layers >= min_layers, "cache.n_layers (%d) must be >= %d", c->n_layers, min_layers);
+    if (c->layout == KVX_CONTIGUOUS) {
+        KVX_REQUIRE(c->n_slots >= bi.n_tokens, "contiguous cache.n_slots (%lld) < tokens (%lld)",
+                    (long long)c->n_slots, (long long)bi.n_tokens);
+        return KVX_OK;
+    }
+    KVX_REQUIRE(c->page_size > 0, "paged cache.page_size must be > 0");
+    KVX_REQUIRE(c->page_table, "paged cache.page_table must not be null");
+    KVX_REQUIRE(c->n_slots % c->page_size == 0, "paged cache.n_slots must be a multiple of page_size");
+    const int need = (bi.max_T + c->page_size - 1) / c->page_size;
+    KVX_REQUIRE(c->max_pages >= need, "paged cache.max_pages (%d) < %d pages of the longest request",
+                c->max_pages, need);
+    (void)dtype; (void)H_kv; (void)d_h;
+    return KVX_OK;
+}
+
+kvx_status check_page_table_debug(const kvx_cache* c, const kvx_batch* bt) {
+    if (!debug_checks() || c->layout != KVX_PAGED) return KVX_OK;
+    std::vector<int32_t> pt((size_t)bt->n_req * c->max_pages);
+    KVX_TRY_HIP(hipMemcpy(pt.data(), c->page_table, pt.size() * 4, hipMemcpyDeviceToHost), "debug copy");
+    const int64_t n_pages = c->n_slots / c->page_size;
+    std::vector<char> used((size_t)n_pages, 0);
+    for (int b = 0; b < bt->n_req; ++b) {
+        const int T = bt->cu_tokens_h[b + 1] - bt->cu_tokens_h[b];
+        const int np = (T + c->page_size - 1) / c->page_size;
+        for (int i = 0; i < np; ++i) {
+            const int32_t p = pt[(size_t)b * c->max_pages + i];
+            KVX_REQUIRE(p >= 0 && p < n_pages, "page_table[%d][%d] = %d is outside [0, %lld)", b, i, p,
+                        (long long)n_pages);
+            KVX_REQUIRE(!used[p], "page %d is mapped twice", p);
+            used[p] = 1;
+        }
+    }
+    return KVX_OK;
+}
+
+SlotMap slot_map(const kvx_cache* c, const kvx_batch* bt) {
+    SlotMap s;
+    s.cu_tok = bt->cu_tokens_d;
+    s.paged = c->layout == KVX_PAGED ? 1 : 0;
+    s.page_table = s.paged ? c->page_table : nullptr;
+    s.max_pages = s.paged ? c->max_pages : 0;
+    s.page_size = s.paged ? c->page_size : 1;
+    return s;
+}
+
+int32_t budget_of(int32_t T, int32_t pct) { return (int32_t)(((int64_t)pct * T + 99) / 100); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvx_last_error(void) { return g_err.c_str(); }
+
+const char* kvx_version(void) { return "kvx 0.1 (gfx950)"; }
+
+int32_t kvx_budget(int32_t T, int32_t pct) {
+    if (T < 0 || pct < 0 || pct > 100) {
+        fail(KVX_ERR_INVALID, "kvx_budget: need T >= 0 and 0 <= pct <= 100");
+        return -1;
+    }
+    return budget_of(T, pct);
+}
+
+kvx_status kvx_map_latent(void* stream, int32_t dtype, const void* x_src, const void* w_s, void* z,
+                          int64_t n, int32_t d_src, int32_t r) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    KVX_REQUIRE_PTR(x_src, "x_src");
+    KVX_REQUIRE_PTR(w_s, "w_s");
+    KVX_REQUIRE_PTR(z, "z");
+    KVX_REQUIRE(n >= 0 && n <= INT32_MAX, "n (%lld) must be in [0, 2^31)", (long long)n);
+    KVX_REQUIRE(d_src > 0 && r > 0, "d_src (%d) and r (%d) must be positive", d_src, r);
+    if (dtype == KVX_BF16) {
+        KVX_REQUIRE(d_src % 64 == 0, "bf16 needs d_src %% 64 == 0 (got %d)", d_src);
+        KVX_REQUIRE(r % 8 == 0, "bf16 needs r %% 8 == 0 (got %d)", r);
+    }
+    if (n == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == KVX_BF16) {
+        GemmArgs a{};
+        a.A = (const bf16*)x_src; a.lda = d_src; a.K_a = d_src;
+        a.B = (const bf16*)w_s; a.ldb = d_src; a.b_group_stride = 0;
+        a.M = (int)n; a.N = r; a.K = d_src; a.groups = 1;
+        a.rows.mode = 0;
+        a.epi = EPI_STORE; a.C = (bf16*)z; a.ldc = r;
+        return hip_status(launch_gemm_bf16(a, s), "map_latent");
+    }
+    GemmF32Args a{};
+    a.A = (const float*)x_src; a.lda = d_src; a.K_a = d_src;
+    a.B = (const float*)w_s; a.ldb = d_src;
+    a.M = (int)n; a.N = r; a.K = d_src; a.groups = 1;
+    a.rows.mode = 0;
+    a.epi = EPI_STORE; a.C = (float*)z; a.ldc = r;
+    return hip_status(launch_gemm_f32(a, s), "map_latent");
+}
+
+kvx_status kvx_score_prepare_workspace(int32_t r, int32_t d_t, int32_t c, size_t* bytes) {
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(r > 0 && d_t > 0 && c >= 0 && c <= d_t, "need r > 0, d_t > 0, 0 <= c <= d_t");
+    *bytes = round256((size_t)c * r * 8) + round256((size_t)d_t * r * 8) + round256((size_t)r * r * 8);
+    return ok();
+}
+
+kvx_status kvx_score_prepare(void* stream, int32_t dtype, const void* w_l, const float* u, int32_t L_t,
+                             int32_t r, int32_t d_t, int32_t c, void* op, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    KVX_REQUIRE_PTR(w_l, "w_l");
+    KVX_REQUIRE_PTR(op, "op");
+    KVX_REQUIRE(L_t > 0 && r > 0 && d_t > 0, "L_t, r and d_t must be positive");
+    KVX_REQUIRE(c >= 0 && c <= d_t, "calibration rank c (%d) must be in [0, d_t]", c);
+    if (c > 0) KVX_REQUIRE_PTR(u, "u");
+    size_t need = 0;
+    kvx_score_prepare_workspace(r, d_t, c, &need);
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "score_prepare needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char* p = (char*)ws;
+    double* G = (double*)p; p += round256((size_t)c * r * 8);
+    double* R = (double*)p; p += round256((size_t)d_t * r * 8);
+    double* A = (double*)p;
+    const int tw = dtype == KVX_BF16 ? ET_BF16 : ET_F32;
+    const size_t es = elem_size(dtype);
+    KVX_TRY_HIP(launch_zero_f64(A, (int64_t)r * r, s), "score_prepare");
+    for (int l = 0; l < L_t; ++l) {
+        const void* W = (const char*)w_l + (size_t)l * d_t * r * es;     // [d_t][r]
+        const float* U = u ? u + (size_t)l * d_t * c : nullptr;          // [d_t][c]
+        KVX_TRY_HIP(launch_to_f64(W, tw, R, (int64_t)d_t * r, s), "score_prepare");
+        if (c > 0) {
+            // G = U^T W  [c][r]
+            KVX_TRY_HIP(launch_gemm_f64(c, r, d_t, 1.0, U, ET_F32, 1, c, W, tw, r, 1, G, r, false, s),
+                        "score_prepare");
+            // R = W - U G  [d_t][r]: the part of every column of W outside span(U)
+            KVX_TRY_HIP(launch_gemm_f64(d_t, r, c, -1.0, U, ET_F32, c, 1, G, ET_F64, r, 1, R, r, true, s),
+                        "score_prepare");
+        }
+        // A += R^T R  [r][r]
+        KVX_TRY_HIP(launch_gemm_f64(r, r, d_t, 1.0, R, ET_F64, 1, r, R, ET_F64, r, 1, A, r, true, s),
+                    "score_prepare");
+    }
+    return hip_status(launch_pack_operator(A, r, dtype, op, s), "score_prepare");
+}
+
+kvx_status kvx_select_topk(void* stream, const float* scores, const kvx_batch* batch, int32_t* sel,
+                           int32_t* rest) {
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(scores, "scores");
+    if (bi.n_sel > 0) KVX_REQUIRE_PTR(sel, "sel");
+    if (bi.n_rest > 0) KVX_REQUIRE_PTR(rest, "rest");
+    return hip_status(launch_select(nullptr, 0, bi.n_tokens, (float*)scores, batch->cu_tokens_d,
+                                    batch->cu_sel_d, bi.n_req, sel, rest, (hipStream_t)stream),
+                      "select_topk");
+}
+
+kvx_status kvx_score_select_workspace(int32_t dtype, int32_t r, int64_t n, size_t* bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(r > 0 && n >= 0, "need r > 0 and n >= 0");
+    if (dtype == KVX_BF16) {
+        const int nt = cdiv(r, gemm_bf16_block_n());
+        *bytes = round256((size_t)nt * n * 4);
+    } else {
+        *bytes = round256((size_t)n * r * 4) + round256((size_t)n * 4);
+    }
+    return ok();
+}
+
+kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, const void* op, int32_t r,
+                            const kvx_batch* batch, const int32_t* budget_pct, float* scores,
+                            int32_t* sel, int32_t* rest, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(z, "z");
+    KVX_REQUIRE_PTR(op, "op");
+    KVX_REQUIRE_PTR(scores, "scores");
+    KVX_REQUIRE(budget_pct, "budget_pct must not be null");
+    KVX_REQUIRE(r > 0, "r must be positive");
+    if (dtype == KVX_BF16) KVX_REQUIRE(r % 64 == 0, "bf16 needs r %% 64 == 0 (got %d)", r);
+    if (bi.n_sel > 0) KVX_REQUIRE_PTR(sel, "sel");
+    if (bi.n_rest > 0) KVX_REQUIRE_PTR(rest, "rest");
+    for (int b = 0; b < bi.n_req; ++b) {
+        const int T = batch->cu_tokens_h[b + 1] - batch->cu_tokens_h[b];
+        const int k = batch->cu_sel_h[b + 1] - batch->cu_sel_h[b];
+        KVX_REQUIRE(budget_pct[b] >= 0 && budget_pct[b] <= 100, "budget_pct[%d] = %d outside [0, 100]", b,
+                    budget_pct[b]);
+        KVX_REQUIRE(k == budget_of(T, budget_pct[b]), "request %d: cu_sel gives %d positions but the "
+                    "budget of %d%% of %d is %d", b, k, budget_pct[b], T, budget_of(T, budget_pct[b]));
+    }
+    size_t need = 0;
+    kvx_score_select_workspace(dtype, r, bi.n_tokens, &need);
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "score_select needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    KVX_REQUIRE(bi.n_tokens <= INT32_MAX, "too many rows");
+    if (bi.n_tokens == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == KVX_BF16) {
+        GemmArgs a{};
+        a.A = (const bf16*)z; a.lda = r; a.K_a = r;
+        a.B = (const bf16*)op; a.ldb = 2 * r; a.b_group_stride = 0;
+        a.M = (int)bi.n_tokens; a.N = r; a.K = 2 * r; a.groups = 1;
+        a.rows.mode = 0;
+        a.epi = EPI_SCORE; a.partial = (float*)ws; a.Z = (const bf16*)z; a.ldz = r;
+        KVX_TRY_HIP(launch_gemm_bf16(a, s), "score");
+        const int nt = cdiv(r, gemm_bf16_block_n());
+        return hip_status(launch_select((const float*)ws, nt, bi.n_tokens, scores, batch->cu_tokens_d,
+                                        batch->cu_sel_d, bi.n_req, sel, rest, s),
+                          "select");
+    }
+    float* P = (float*)ws;
+    float* partial = (float*)((char*)ws + round256((size_t)bi.n_tokens * r * 4));
+    GemmF32Args a{};
+    a.A = (const float*)z; a.lda = r; a.K_a = r;
+    a.B = (const float*)op; a.ldb = r;
+    a.M = (int)bi.n_tokens; a.N = r; a.K = r; a.groups = 1;
+    a.rows.mode = 0;
+    a.epi = EPI_STORE; a.C = P; a.ldc = r;
+    KVX_TRY_HIP(launch_gemm_f32(a, s), "score");
+    KVX_TRY_HIP(launch_rowdot_f32(P, (const float*)z, bi.n_tokens, r, partial, s), "score");
+    return hip_status(launch_select(partial, 1, bi.n_tokens, scores, batch->cu_tokens_d, batch->cu_sel_d,
+                                    bi.n_req, sel, rest, s),
+                      "select");
+}
+
+kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t L_t,
+                           int32_t r, int32_t H_kv, int32_t d_h, const kvx_batch* batch,
+                           const int32_t* rows, const kvx_cache* cache) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(z, "z");
+    KVX_REQUIRE_PTR(w_l, "w_l");
+    KVX_REQUIRE(L_t > 0 && r > 0 && H_kv > 0 && d_h > 0, "L_t, r, H_kv and d_h must be positive");
+    KVX_REQUIRE(d_h % 8 == 0, "d_h must be a multiple of 8 (got %d)", d_h);
+    if (dtype == KVX_BF16) KVX_REQUIRE(r % 64 == 0, "bf16 needs r %% 64 == 0 (got %d)", r);
+    if (kvx_status st = check_cache(cache, bi, dtype, H_kv, d_h, L_t)) return st;
+    if (kvx_status st = check_page_table_debug(cache, batch)) return st;
+    if (rows) KVX_REQUIRE(aligned16(rows), "rows must be 16-byte aligned");
+    const int64_t M = rows ? bi.n_rest : bi.n_tokens;
+    if (M == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const int hd = H_kv * d_h, d_t = 2 * hd;
+    RowMap rm{};
+    rm.mode = rows ? 2 : 1;
+    rm.list = rows;
+    rm.list_is_rest = 1;
+    rm.cu_tok = batch->cu_tokens_d;
+    rm.cu_sel = batch->cu_sel_d;
+    rm.n_req = bi.n_req;
+    if (dtype == KVX_BF16) {
+        GemmArgs a{};
+        a.A = (const bf16*)z; a.lda = r; a.K_a = r;
+        a.B = (const bf16*)w_l; a.ldb = r; a.b_group_stride = (int64_t)d_t * r;
+        a.M = (int)M; a.N = d_t; a.K = r; a.groups = L_t;
+        a.rows = rm;
+        a.epi = EPI_CACHE;
+        a.kc = (bf16*)cache->k; a.vc = (bf16*)cache->v;
+        a.layer_elems = cache->n_slots * hd; a.hd = hd; a.slots = slot_map(cache, batch);
+        return hip_status(launch_gemm_bf16(a, s), "reconstruct");
+    }
+    GemmF32Args a{};
+    a.A = (const float*)z; a.lda = r; a.K_a = r;
+    a.B = (const float*)w_l; a.ldb = r; a.b_group_stride = (int64_t)d_t * r;
+    a.M = (int)M; a.N = d_t; a.K = r; a.groups = L_t;
+    a.rows = rm;
+    a.epi = EPI_CACHE;
+    a.kc = (float*)cache->k; a.vc = (float*)cache->v;
+    a.layer_elems = cache->n_slots * hd; a.hd = hd; a.slots = slot_map(cache, batch);
+    return hip_status(launch_gemm_f32(a, s), "reconstruct");
+}
+
+kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_t max_pos, float* table) {
+    KVX_REQUIRE_PTR(table, "table");
+    KVX_REQUIRE(d_h >= 2 && d_h % 2 == 0, "d_h must be even and >= 2 (got %d)", d_h);
+    KVX_REQUIRE(max_pos >= 1, "max_pos must be >= 1");
+    KVX_REQUIRE(base > 0.0, "base must be positive");
+    return hip_status(launch_rope_table(base, d_h, max_pos, table, (hipStream_t)stream), "rope_table");
+}
+
+kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, int32_t H_q, int32_t H_kv,
+                                        int32_t d_h, size_t* bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(H_q > 0 && H_kv > 0 && d_h > 0, "H_q, H_kv and d_h must be positive");
+    *bytes = round256((size_t)bi.n_sel * (H_q + 2 * H_kv) * d_h * elem_size(dtype));
+    return ok();
+}
+
+kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const void* x_l,
+                              const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h,
+                              const float* rope, int32_t max_pos, const kvx_batch* batch,
+                              const int32_t* sel, const kvx_cache* cache, void* out, float* lse,
+                              void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(x_l, "x_l");
+    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
+    KVX_REQUIRE_PTR(rope, "rope");
+    KVX_REQUIRE(D > 0 && H_q > 0 && H_kv > 0, "D, H_q and H_kv must be positive");
+    if (d_h != 64 && d_h != 128) return fail(KVX_ERR_UNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+    KVX_REQUIRE(H_q % H_kv == 0, "H_q (%d) must be a multiple of H_kv (%d)", H_q, H_kv);
+    const int g = H_q / H_kv;
+    if (g > 16) return fail(KVX_ERR_UNSUPPORTED, "H_q / H_kv = %d > 16", g);
+    if (dtype == KVX_BF16) {
+        KVX_REQUIRE(D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+        if (attn_bf16_block_queries(g) == 0)
+            return fail(KVX_ERR_UNSUPPORTED, "bf16 attention supports H_q / H_kv in {1..8, 16} (got %d)", g);
+    }
+    if (bi.n_req > MAX_ATTN_REQ)
+        return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
+    KVX_REQUIRE(max_pos >= bi.max_T, "rope table has %d positions, the longest request %d", max_pos, bi.max_T);
+    if (kvx_status st = check_cache(cache, bi, dtype, H_kv, d_h, 1)) return st;
+    KVX_REQUIRE(layer >= 0 && layer < cache->n_layers, "layer %d outside [0, %d)", layer, cache->n_layers);
+    if (kvx_status st = check_page_table_debug(cache, batch)) return st;
+    if (bi.n_sel > 0) {
+        KVX_REQUIRE_PTR(sel, "sel");
+        KVX_REQUIRE_PTR(out, "out");
+        if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+    }
+    size_t need = 0;
+    kvx_recompute_attn_workspace(dtype, batch, H_q, H_kv, d_h, &need);
+    if (bi.n_sel > 0 && (!ws || ws_bytes < need))
+        return fail(KVX_ERR_WORKSPACE, "recompute_attn needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (bi.n_sel > 0) KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+
+    hipStream_t s = (hipStream_t)stream;
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    const int hd = H_kv * d_h;
+    const size_t es = elem_size(dtype);
+    const int64_t layer_off = (int64_t)layer * cache->n_slots * hd;
+    RowMap rm{};
+    rm.mode = 2;
+    rm.list = sel;
+    rm.list_is_rest = 0;
+    rm.cu_tok = batch->cu_tokens_d;
+    rm.cu_sel = batch->cu_sel_d;
+    rm.n_req = bi.n_req;
+    const SlotMap sm = slot_map(cache, batch);
+
+    // 1. [q | k | v] of the selected rows
+    if (dtype == KVX_BF16) {
+        GemmArgs a{};
+        a.A = (const bf16*)x_l; a.lda = D; a.K_a = D;
+        a.B = (const bf16*)w_qkv; a.ldb = D;
+        a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
+        a.rows = rm;
+        a.epi = EPI_STORE; a.C = (bf16*)ws; a.ldc = n_qkv;
+        KVX_TRY_HIP(launch_gemm_bf16(a, s), "recompute qkv");
+    } else {
+        GemmF32Args a{};
+        a.A = (const float*)x_l; a.lda = D; a.K_a = D;
+        a.B = (const float*)w_qkv; a.ldb = D;
+        a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
+        a.rows = rm;
+        a.epi = EPI_STORE; a.C = (float*)ws; a.ldc = n_qkv;
+        KVX_TRY_HIP(launch_gemm_f32(a, s), "recompute qkv");
+    }
+    // 2-3. rotate k at the true positions and write k, v into the layer's cache slots
+    ScatterArgs sc{};
+    sc.qkv = ws; sc.ld = n_qkv;
+    sc.H_q = H_q; sc.H_kv = H_kv; sc.d_h = d_h;
+    sc.rope = rope;
+    sc.sel = sel; sc.cu_sel = batch->cu_sel_d; sc.n_req = bi.n_req; sc.n_sel = bi.n_sel;
+    sc.slots = sm;
+    sc.kc = (char*)cache->k + layer_off * es;
+    sc.vc = (char*)cache->v + layer_off * es;
+    KVX_TRY_HIP(launch_rope_scatter(sc, dtype, s), "rope_scatter");
+    // 4. causal attention of the selected queries over the mixed cache
+    AttnArgs at{};
+    at.qkv = ws; at.ld = n_qkv;
+    at.H_q = H_q; at.H_kv = H_kv; at.d_h = d_h;
+    at.rope = rope;
+    at.sel = sel; at.cu_sel = batch->cu_sel_d; at.n_req = bi.n_req;
+    at.slots = sm;
+    at.kc = sc.kc; at.vc = sc.vc;
+    at.out = out; at.lse = lse;
+    if (dtype == KVX_BF16) {
+        at.bq = attn_bf16_block_queries(g);
+        at.blk_cu[0] = 0;
+        for (int b = 0; b < bi.n_req; ++b) {
+            const int k = batch->cu_sel_h[b + 1] - batch->cu_sel_h[b];
+            at.blk_cu[b + 1] = at.blk_cu[b] + (k + at.bq - 1) / at.bq;
+        }
+        at.n_blocks = at.blk_cu[bi.n_req];
+        return hip_status(launch_attn_bf16(at, s), "attention");
+    }
+    at.bq = 1;
+    at.n_blocks = (int)bi.n_sel;
+    return hip_status(launch_attn_f32(at, s), "attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Internal definitions shared by the kvx HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvx.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+namespace kvx {
+
+// ----------------------------------------------------------------------------- rows
+// A row of a flattened [N, ...] activation belongs to request b with cu[b] <= m < cu[b+1].
+__device__ __forceinline__ int find_request(const int32_t* cu, int n_req, int m) {
+    int lo = 0, hi = n_req - 1;            // largest b in [0, n_req) with cu[b] <= m
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Complement lists start at cu_tokens[b] - cu_sel[b].
+__device__ __forceinline__ int find_request_rest(const int32_t* cu_tok, const int32_t* cu_sel,
+                                                 int n_req, int m) {
+    int lo = 0, hi = n_req - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cu_tok[mid] - cu_sel[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Cache slot of position p of request b.
+struct SlotMap {
+    const int32_t* cu_tok;      // device [n_req+1]
+    const int32_t* page_table;  // device [n_req][max_pages] (paged) or null
+    int32_t max_pages;
+    int32_t page_size;
+    int32_t paged;
+    __device__ __forceinline__ int64_t slot(int b, int p) const {
+        if (paged) {
+            int pg = page_table[(int64_t)b * max_pages + p / page_size];
+            return (int64_t)pg * page_size + p % page_size;
+        }
+        return (int64_t)cu_tok[b] + p;
+    }
+};
+
+// ----------------------------------------------------------------------------- misc
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+__device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }
+
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) { return *p; }
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Chunk swizzle for [rows][8 chunks of 16 B] LDS tiles: chunk c of row key n lives at
+// c ^ sw(n).  Any 8 consecutive keys, and any 16 consecutive keys taken with their parity,
+// land on distinct chunk positions, so 16-lane reads of consecutive keys are conflict-free
+// for 32- and 64-bank LDS.
+__device__ __forceinline__ int swz(int key) { return (key ^ (key >> 3)) & 7; }
+
+}  // namespace kvx
+
+// ----------------------------------------------------------------------------- launchers
+// Host-side launch helpers implemented in the .hip files; the C ABI in kvx_api.hip validates
+// arguments before calling them.  Each returns hipSuccess or the launch error.
+namespace kvx {
+
+struct RowMap {
+    int32_t mode;           // 0: row m is source row m; 1: all rows of a batch; 2: listed rows
+    const int32_t* list;    // mode 2: request-local positions
+    int32_t list_is_rest;   // mode 2: list is a complement list (else a selected list)
+    const int32_t* cu_tok;  // device [n_req+1]
+    const int32_t* cu_sel;  // device [n_req+1]
+    int32_t n_req;
+};
+
+// Source row, request and request-local position of GEMM row m.
+struct RowInfo { int src, b, pos; };
+__device__ __forceinline__ RowInfo row_info(const RowMap& rm, int m) {
+    RowInfo r{m, 0, m};
+    if (rm.mode == 1) {
+        r.b = find_request(rm.cu_tok, rm.n_req, m);
+        r.pos = m - rm.cu_tok[r.b];
+    } else if (rm.mode == 2) {
+        r.b = rm.list_is_rest ? find_request_rest(rm.cu_tok, rm.cu_sel, rm.n_req, m)
+                              : find_request(rm.cu_sel, rm.n_req, m);
+        r.pos = rm.list[m];
+        r.src = rm.cu_tok[r.b] + r.pos;
+    }
+    return r;
+}
+
+enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2 };
+
+struct GemmArgs {
+    // C[m][n] = sum_k A[src(m)][k mod K_a] * B[n][k]
+    const bf16* A; int64_t lda; int32_t K_a;
+    const bf16* B; int64_t ldb; int64_t b_group_stride;
+    int32_t M, N, K, groups;
+    RowMap rows;
+    int32_t epi;
+    // EPI_STORE
+    bf16* C; int64_t ldc;
+    // EPI_CACHE (group = layer)
+    bf16* kc; bf16* vc; int64_t layer_elems; int32_t hd; SlotMap slots;
+    // EPI_SCORE: partial[n_block][m] = sum_{n in block} C[m][n] * Z[m][n]
+    float* partial; const bf16* Z; int64_t ldz;
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+int gemm_bf16_block_n();
+
+}  // namespace kvx

@@ -1,0 +1,75 @@
+// Launchers of the kvx kernels (internal; the C ABI validates arguments before calling).
+#pragma once
+
+#include "kvx_common.h"
+
+namespace kvx {
+
+// ---- fp64 strided GEMM used once per model pair by the score-operator preparation:
+//      C[m][n] = (accumulate ? C[m][n] : 0) + alpha * sum_k A(m,k) B(k,n)
+//      A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn], C row-major with ldc.
+enum ElemType { ET_F32 = 0, ET_BF16 = 1, ET_F64 = 2 };
+hipError_t launch_gemm_f64(int M, int N, int K, double alpha, const void* A, int ta, int64_t sam,
+                           int64_t sak, const void* B, int tb, int64_t sbk, int64_t sbn, double* C,
+                           int64_t ldc, bool accumulate, hipStream_t s);
+hipError_t launch_to_f64(const void* src, int t, double* dst, int64_t n, hipStream_t s);
+hipError_t launch_zero_f64(double* dst, int64_t n, hipStream_t s);
+// op = hi/lo bf16 [r][2r] or fp32 [r][r] from the fp64 operator
+hipError_t launch_pack_operator(const double* A, int r, int dtype, void* op, hipStream_t s);
+
+// ---- selection: scores[t] = sum_p partial[p][t] (when n_part > 0), then the k_b largest per
+//      request (ties to the lower position) written ascending to sel, the rest to rest.
+hipError_t launch_select(const float* partial, int n_part, int64_t n_rows, float* scores,
+                         const int32_t* cu_tok, const int32_t* cu_sel, int n_req, int32_t* sel,
+                         int32_t* rest, hipStream_t s);
+
+// ---- rotary table [max_pos][d_h/2][2] (cos, sin), angles in fp64
+hipError_t launch_rope_table(double base, int d_h, int max_pos, float* table, hipStream_t s);
+
+// ---- rotate recomputed k and write k, v of every selected row into the layer's cache
+struct ScatterArgs {
+    const void* qkv; int64_t ld;      // [k][n_qkv]
+    int H_q, H_kv, d_h;
+    const float* rope;
+    const int32_t* sel; const int32_t* cu_sel; int n_req; int64_t n_sel;
+    SlotMap slots;
+    void* kc; void* vc;               // layer base pointers
+};
+hipError_t launch_rope_scatter(const ScatterArgs& a, int dtype, hipStream_t s);
+
+// Requests per recompute_attn call: the query-block plan travels in the kernel arguments.
+constexpr int MAX_ATTN_REQ = 256;
+
+struct AttnArgs {
+    const void* qkv; int64_t ld;      // Q heads are the first H_q*d_h columns
+    int H_q, H_kv, d_h;
+    const float* rope;
+    const int32_t* sel; const int32_t* cu_sel; int n_req;
+    int n_blocks;                     // total query blocks over all requests
+    int bq;                           // selected queries per block
+    SlotMap slots;
+    const void* kc; const void* vc;   // layer base pointers
+    void* out; float* lse;
+    int32_t blk_cu[MAX_ATTN_REQ + 1];  // blk_cu[b] = sum_{b' < b} ceil(k_b' / bq)
+};
+// bf16 matrix-core path (d_h 64 or 128); returns the number of queries per block it uses
+int attn_bf16_block_queries(int g);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+// fp32 path: one wave per (query, head)
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+// ---- fp32 GEMM with the same row maps and epilogues as the bf16 matrix-core GEMM
+struct GemmF32Args {
+    const float* A; int64_t lda; int32_t K_a;
+    const float* B; int64_t ldb; int64_t b_group_stride;
+    int32_t M, N, K, groups;
+    RowMap rows;
+    int32_t epi;                      // EPI_STORE or EPI_CACHE
+    float* C; int64_t ldc;
+    float* kc; float* vc; int64_t layer_elems; int32_t hd; SlotMap slots;
+};
+hipError_t launch_gemm_f32(const GemmF32Args& a, hipStream_t s);
+// partial[t] = sum_n P[t][n] * Z[t][n]
+hipError_t launch_rowdot_f32(const float* P, const float* Z, int64_t n, int r, float* out, hipStream_t s);
+
+}  // namespace kvx

@@ -1,0 +1,85 @@
+"""One cross-model KV handoff on the GPU: buffers and the call order of the C ABI.
+
+map_latent -> score_select -> reconstruct(complement rows) -> per target layer
+recompute_attn.  Selection runs before reconstruction because the score needs only the
+latent; the selected rows are then left for recompute_attn to write, so reconstruction
+computes the complement only (the translated values it would write there are overwritten
+before anything reads them).  No arithmetic happens here.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import kvx
+from .synth import Inputs
+
+
+class Handoff:
+    def __init__(self, inp: Inputs, device="cuda", keep_all_outputs: bool = True):
+        wl = inp.wl
+        self.inp = inp
+        self.wl = wl
+        self.device = torch.device(device)
+        dt = inp.x_src.dtype
+        self.batch = kvx.Batch.for_budgets(inp.lengths, inp.pcts, self.device)
+        N = self.batch.n_tokens
+        # one-time preparations per model pair (not part of a handoff)
+        self.op = kvx.score_prepare(inp.w_l, inp.u)
+        self.rope = kvx.rope_table(wl.rope_base, wl.d_h, max(inp.lengths), self.device)
+        # buffers
+        self.z = torch.empty((N, wl.r), dtype=dt, device=self.device)
+        self.scores = torch.empty(N, dtype=torch.float32, device=self.device)
+        self.sel = torch.empty(max(self.batch.total_sel, 1), dtype=torch.int32, device=self.device)
+        self.rest = torch.empty(max(self.batch.total_rest, 1), dtype=torch.int32, device=self.device)
+        self.ws_score = torch.empty(max(kvx.score_select_workspace(kvx._dtype(self.z), wl.r, N), 16),
+                                    dtype=torch.uint8, device=self.device)
+        self.ws_attn = torch.empty(max(kvx.recompute_attn_workspace(kvx._dtype(self.z), self.batch, wl.H_q,
+                                                                    wl.H_kv, wl.d_h), 16),
+                                   dtype=torch.uint8, device=self.device)
+        if wl.paged:
+            n_slots = inp.n_pages * wl.page_size
+            self.cache = kvx.Cache.empty(wl.L_t, n_slots, wl.H_kv, wl.d_h, dt, self.device,
+                                         page_table=inp.page_table, page_size=wl.page_size)
+        else:
+            self.cache = kvx.Cache.empty(wl.L_t, N, wl.H_kv, wl.d_h, dt, self.device)
+        n_out = wl.L_t if keep_all_outputs else 1
+        k = max(self.batch.total_sel, 1)
+        self.out = torch.empty((n_out, k, wl.H_q, wl.d_h), dtype=dt, device=self.device)
+        self.lse = torch.empty((n_out, k, wl.H_q), dtype=torch.float32, device=self.device)
+
+    # the four stages ------------------------------------------------------------------
+    def map(self):
+        kvx.map_latent(self.inp.x_src, self.inp.w_s, self.z)
+
+    def select(self):
+        kvx.score_select(self.z, self.op, self.batch, self.inp.pcts, ws=self.ws_score,
+                         out=(self.scores, self.sel, self.rest))
+
+    def reconstruct(self, all_rows: bool = False):
+        rows = None if all_rows else self.rest[:self.batch.total_rest]
+        kvx.reconstruct(self.z, self.inp.w_l, self.wl.H_kv, self.wl.d_h, self.batch, self.cache, rows=rows)
+
+    def recompute(self, layer: int):
+        wl = self.wl
+        slot = layer if self.out.shape[0] > 1 else 0
+        kvx.recompute_attn(layer, self.inp.x_l[layer], self.inp.w_qkv[layer], wl.H_q, wl.H_kv, wl.d_h,
+                           self.rope, self.batch, self.sel[:self.batch.total_sel], self.cache,
+                           out=self.out[slot], lse=self.lse[slot], ws=self.ws_attn)
+
+    def run(self, all_rows: bool = False):
+        self.map()
+        self.select()
+        self.reconstruct(all_rows)
+        for l in range(self.wl.L_t):
+            self.recompute(l)
+
+    # views --------------------------------------------------------------------------
+    @property
+    def S(self) -> torch.Tensor:
+        return self.sel[:self.batch.total_sel]
+
+    @property
+    def C(self) -> torch.Tensor:
+        return self.rest[:self.batch.total_rest]

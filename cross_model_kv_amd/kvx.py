@@ -1,0 +1,299 @@
+"""Thin Python binding of libkvx (ctypes).
+
+Argument marshalling only: every step of the handoff runs in the HIP kernels behind the C
+ABI in include/kvx.h.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if libkvx.so is missing or was built for another GPU, calls fail loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvx.so")
+
+F32, BF16 = 0, 1
+CONTIGUOUS, PAGED = 0, 1
+STATUS = {0: "KVX_OK", -1: "KVX_ERR_INVALID", -2: "KVX_ERR_UNSUPPORTED", -3: "KVX_ERR_HIP",
+          -4: "KVX_ERR_WORKSPACE"}
+
+
+class KvxError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _Batch(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32),
+                ("cu_tokens_h", ctypes.POINTER(ctypes.c_int32)),
+                ("cu_sel_h", ctypes.POINTER(ctypes.c_int32)),
+                ("cu_tokens_d", ctypes.c_void_p),
+                ("cu_sel_d", ctypes.c_void_p)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32),
+                ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p),
+                ("n_layers", ctypes.c_int32),
+                ("n_slots", ctypes.c_int64),
+                ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32),
+                ("page_table", ctypes.c_void_p)]
+
+
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "kvx_last_error": ([], ctypes.c_char_p),
+    "kvx_version": ([], ctypes.c_char_p),
+    "kvx_budget": ([_I32, _I32], _I32),
+    "kvx_map_latent": ([_P, _I32, _P, _P, _P, _I64, _I32, _I32], _I32),
+    "kvx_score_prepare_workspace": ([_I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "kvx_score_prepare": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ], _I32),
+    "kvx_select_topk": ([_P, _P, ctypes.POINTER(_Batch), _P, _P], _I32),
+    "kvx_score_select_workspace": ([_I32, _I32, _I64, ctypes.POINTER(_SZ)], _I32),
+    "kvx_score_select": ([_P, _I32, _P, _P, _I32, ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P, _P,
+                          _P, _P, _SZ], _I32),
+    "kvx_reconstruct": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P,
+                         ctypes.POINTER(_Cache)], _I32),
+    "kvx_rope_table": ([_P, ctypes.c_double, _I32, _I32, _P], _I32),
+    "kvx_recompute_attn_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, ctypes.POINTER(_SZ)],
+                                     _I32),
+    "kvx_recompute_attn": ([_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
+                            ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P, _P, _P, _SZ], _I32),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvx.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() first")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise KvxError(fn, code, lib().kvx_last_error().decode())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def version() -> str:
+    return lib().kvx_version().decode()
+
+
+def budget(T: int, pct: int) -> int:
+    k = lib().kvx_budget(T, pct)
+    if k < 0:
+        raise KvxError("kvx_budget", -1, lib().kvx_last_error().decode())
+    return k
+
+
+class Batch:
+    """Ragged batch descriptor: request lengths and selected counts, host and device copies."""
+
+    def __init__(self, lengths: Sequence[int], n_sel: Sequence[int], device):
+        self.lengths = [int(t) for t in lengths]
+        self.n_sel = [int(k) for k in n_sel]
+        self.cu_tokens = [0]
+        self.cu_sel = [0]
+        for t, k in zip(self.lengths, self.n_sel):
+            self.cu_tokens.append(self.cu_tokens[-1] + t)
+            self.cu_sel.append(self.cu_sel[-1] + k)
+        n = len(self.lengths)
+        self._h_tok = (ctypes.c_int32 * (n + 1))(*self.cu_tokens)
+        self._h_sel = (ctypes.c_int32 * (n + 1))(*self.cu_sel)
+        self.d_tok = torch.tensor(self.cu_tokens, dtype=torch.int32, device=device)
+        self.d_sel = torch.tensor(self.cu_sel, dtype=torch.int32, device=device)
+        self.c = _Batch(n, self._h_tok, self._h_sel, self.d_tok.data_ptr(), self.d_sel.data_ptr())
+
+    @classmethod
+    def for_budgets(cls, lengths: Sequence[int], pcts: Sequence[int], device) -> "Batch":
+        return cls(lengths, [budget(t, p) for t, p in zip(lengths, pcts)], device)
+
+    @property
+    def n_req(self) -> int:
+        return len(self.lengths)
+
+    @property
+    def n_tokens(self) -> int:
+        return self.cu_tokens[-1]
+
+    @property
+    def total_sel(self) -> int:
+        return self.cu_sel[-1]
+
+    @property
+    def total_rest(self) -> int:
+        return self.n_tokens - self.total_sel
+
+
+class Cache:
+    """Target K/V cache of all layers, contiguous [L][slots][H_kv][d_h] or paged."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, n_layers: int, n_slots: int,
+                 page_table: Optional[torch.Tensor] = None, page_size: int = 16):
+        self.k, self.v, self.page_table = k, v, page_table
+        paged = page_table is not None
+        self.c = _Cache(PAGED if paged else CONTIGUOUS, k.data_ptr(), v.data_ptr(), n_layers, n_slots,
+                        page_size if paged else 0, page_table.shape[1] if paged else 0,
+                        page_table.data_ptr() if paged else None)
+
+    @classmethod
+    def empty(cls, n_layers: int, n_slots: int, H_kv: int, d_h: int, dtype, device,
+              page_table: Optional[torch.Tensor] = None, page_size: int = 16) -> "Cache":
+        shape = (n_layers, n_slots, H_kv, d_h)
+        k = torch.empty(shape, dtype=dtype, device=device)
+        v = torch.empty(shape, dtype=dtype, device=device)
+        return cls(k, v, n_layers, n_slots, page_table, page_size)
+
+
+def map_latent(x_src: torch.Tensor, w_s: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:
+    n, d_src = x_src.shape
+    r = w_s.shape[0]
+    if z is None:
+        z = torch.empty((n, r), dtype=x_src.dtype, device=x_src.device)
+    _check("kvx_map_latent", lib().kvx_map_latent(_stream(x_src.device), _dtype(x_src), _ptr(x_src),
+                                                  _ptr(w_s), _ptr(z), n, d_src, r))
+    return z
+
+
+def score_prepare(w_l: torch.Tensor, u: torch.Tensor) -> torch.Tensor:
+    L_t, d_t, r = w_l.shape
+    c = u.shape[2]
+    dt = _dtype(w_l)
+    ws_bytes = _SZ()
+    _check("kvx_score_prepare_workspace", lib().kvx_score_prepare_workspace(r, d_t, c, ctypes.byref(ws_bytes)))
+    ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=w_l.device)
+    op = (torch.empty((r, 2 * r), dtype=torch.bfloat16, device=w_l.device) if dt == BF16
+          else torch.empty((r, r), dtype=torch.float32, device=w_l.device))
+    _check("kvx_score_prepare", lib().kvx_score_prepare(_stream(w_l.device), dt, _ptr(w_l),
+                                                        _ptr(u) if c > 0 else None, L_t, r, d_t, c,
+                                                        _ptr(op), _ptr(ws), ws_bytes.value))
+    return op
+
+
+def select_topk(scores: torch.Tensor, batch: Batch):
+    dev = scores.device
+    sel = torch.empty(max(batch.total_sel, 1), dtype=torch.int32, device=dev)
+    rest = torch.empty(max(batch.total_rest, 1), dtype=torch.int32, device=dev)
+    _check("kvx_select_topk", lib().kvx_select_topk(_stream(dev), _ptr(scores), ctypes.byref(batch.c),
+                                                    _ptr(sel), _ptr(rest)))
+    return sel[:batch.total_sel], rest[:batch.total_rest]
+
+
+def score_select_workspace(dtype: int, r: int, n: int) -> int:
+    b = _SZ()
+    _check("kvx_score_select_workspace", lib().kvx_score_select_workspace(dtype, r, n, ctypes.byref(b)))
+    return b.value
+
+
+def score_select(z: torch.Tensor, op: torch.Tensor, batch: Batch, pcts: Sequence[int],
+                 ws: Optional[torch.Tensor] = None, out=None):
+    dev = z.device
+    r = z.shape[1]
+    dt = _dtype(z)
+    need = score_select_workspace(dt, r, batch.n_tokens)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        scores = torch.empty(batch.n_tokens, dtype=torch.float32, device=dev)
+        sel = torch.empty(max(batch.total_sel, 1), dtype=torch.int32, device=dev)
+        rest = torch.empty(max(batch.total_rest, 1), dtype=torch.int32, device=dev)
+    else:
+        scores, sel, rest = out
+    pct = (ctypes.c_int32 * batch.n_req)(*[int(p) for p in pcts])
+    _check("kvx_score_select", lib().kvx_score_select(_stream(dev), dt, _ptr(z), _ptr(op), r,
+                                                      ctypes.byref(batch.c), pct, _ptr(scores), _ptr(sel),
+                                                      _ptr(rest), _ptr(ws), need))
+    return scores, sel[:batch.total_sel], rest[:batch.total_rest]
+
+
+def reconstruct(z: torch.Tensor, w_l: torch.Tensor, H_kv: int, d_h: int, batch: Batch, cache: Cache,
+                rows: Optional[torch.Tensor] = None):
+    L_t, _, r = w_l.shape
+    if rows is None:
+        rp = None                                   # every position
+    elif rows.numel() == 0:
+        rp = _ptr(_placeholder(z.device))           # an empty list: nothing to reconstruct
+    else:
+        rp = _ptr(rows)
+    _check("kvx_reconstruct", lib().kvx_reconstruct(_stream(z.device), _dtype(z), _ptr(z), _ptr(w_l), L_t, r,
+                                                    H_kv, d_h, ctypes.byref(batch.c), rp,
+                                                    ctypes.byref(cache.c)))
+
+
+_placeholders = {}
+
+
+def _placeholder(device) -> torch.Tensor:
+    key = str(device)
+    if key not in _placeholders:
+        _placeholders[key] = torch.zeros(4, dtype=torch.int32, device=device)
+    return _placeholders[key]
+
+
+def rope_table(base: float, d_h: int, max_pos: int, device) -> torch.Tensor:
+    t = torch.empty((max_pos, d_h // 2, 2), dtype=torch.float32, device=device)
+    _check("kvx_rope_table", lib().kvx_rope_table(_stream(device), float(base), d_h, max_pos, _ptr(t)))
+    return t
+
+
+def recompute_attn_workspace(dtype: int, batch: Batch, H_q: int, H_kv: int, d_h: int) -> int:
+    b = _SZ()
+    _check("kvx_recompute_attn_workspace",
+           lib().kvx_recompute_attn_workspace(dtype, ctypes.byref(batch.c), H_q, H_kv, d_h, ctypes.byref(b)))
+    return b.value
+
+
+def recompute_attn(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int,
+                   rope: torch.Tensor, batch: Batch, sel: torch.Tensor, cache: Cache,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None):
+    dev = x_l.device
+    dt = _dtype(x_l)
+    D = x_l.shape[1]
+    need = recompute_attn_workspace(dt, batch, H_q, H_kv, d_h)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((max(batch.total_sel, 1), H_q, d_h), dtype=x_l.dtype, device=dev)
+    _check("kvx_recompute_attn", lib().kvx_recompute_attn(
+        _stream(dev), dt, layer, _ptr(x_l), _ptr(w_qkv), D, H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
+        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c),
+        _ptr(out), _ptr(lse), _ptr(ws), ws.numel()))
+    return out[:batch.total_sel]

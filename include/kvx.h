@@ -1,0 +1,200 @@
+/*
+ * kvx.h - C ABI of the MI355X (gfx950) cross-model KV handoff library, libkvx.so.
+ *
+ * The handoff (PANORAMA: Cross-Model KV Sharing via Contextual Recomputation, abstract;
+ * RaReCache abstract on the CacheReforge card) runs in four calls:
+ *
+ *   kvx_map_latent      shared source projection: source KV -> compact latent per position
+ *   kvx_score_select    rank-disagreement score of every position, then the top-budget set
+ *   kvx_reconstruct     layer-specific reconstruction of the target K/V from the latent
+ *   kvx_recompute_attn  per layer: recompute Q/K/V of the selected positions, rotate,
+ *                       write K/V into the mixed cache, attend causally over that cache
+ *
+ * plus two one-time preparations per model pair (kvx_score_prepare, kvx_rope_table)
+ * and a standalone top-k (kvx_select_topk).
+ *
+ * Conventions
+ *  - Every call returns a kvx_status (0 = KVX_OK).  On failure nothing is enqueued and
+ *    kvx_last_error() returns a message (thread-local; valid until the next call on the
+ *    same thread).  No C++ exception crosses this ABI.
+ *  - All arguments are validated on the host before any GPU work is enqueued.
+ *  - Work is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  Faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - The caller allocates and owns every buffer.  Pointers marked (device) are device
+ *    memory, (host) are host memory.  The library never allocates device memory and
+ *    keeps no state between calls; calls on distinct streams with distinct buffers may
+ *    run concurrently.  Scratch memory is passed explicitly as a workspace whose size
+ *    the matching *_workspace() call returns.
+ *  - Storage dtype KVX_BF16 or KVX_F32 applies to activations, weights, the latent,
+ *    the cache, Q and the attention output; accumulation, softmax and scores are fp32.
+ *    Device pointers must be 16-byte aligned; all arrays are dense row-major, the last
+ *    index fastest.
+ *  - Weights are stored output-major: row j holds the weights that produce output j
+ *    (y = W x is computed as y_j = sum_c W[j][c] x[c]).
+ *
+ * Shapes (one request of T positions, or a ragged batch of n_req requests flattened
+ * into N = sum T_b rows; positions restart at 0 in every request)
+ *   d_src = 2 * L_s * H_s * d_hs     source K and V of all source layers per position,
+ *                                    channel order (layer, K/V, head, dim)
+ *   r                                latent rank
+ *   d_t   = 2 * H_kv * d_h           one target layer's [K heads | V heads], head-major
+ *   n_qkv = (H_q + 2 H_kv) * d_h     rows [Q heads | K heads | V heads] of W_qkv
+ */
+#ifndef KVX_H
+#define KVX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KVX_API __attribute__((visibility("default")))
+#else
+#define KVX_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvx_status;
+#define KVX_OK 0
+#define KVX_ERR_INVALID (-1)     /* bad argument: null pointer, size, alignment, shape */
+#define KVX_ERR_UNSUPPORTED (-2) /* valid request this library does not implement */
+#define KVX_ERR_HIP (-3)         /* a HIP runtime call or kernel launch failed */
+#define KVX_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required */
+
+#define KVX_F32 0
+#define KVX_BF16 1
+
+#define KVX_CONTIGUOUS 0
+#define KVX_PAGED 1
+
+/* Ragged batch.  Request b owns rows [cu_tokens[b], cu_tokens[b+1]) of every [N, ...]
+ * activation and selects k_b = cu_sel[b+1] - cu_sel[b] positions.  The host and device
+ * copies must hold the same values; cu_*[0] = 0 and both are non-decreasing.  The
+ * complement list of request b starts at cu_tokens[b] - cu_sel[b]. */
+typedef struct kvx_batch {
+    int32_t n_req;
+    const int32_t* cu_tokens_h; /* (host)   [n_req + 1] */
+    const int32_t* cu_sel_h;    /* (host)   [n_req + 1] */
+    const int32_t* cu_tokens_d; /* (device) [n_req + 1] */
+    const int32_t* cu_sel_d;    /* (device) [n_req + 1] */
+} kvx_batch;
+
+/* Target KV cache of all layers, K and V in separate arrays of the storage dtype.
+ *  KVX_CONTIGUOUS: k, v are [n_layers][n_slots][H_kv][d_h]; position p of request b is
+ *                  slot cu_tokens[b] + p (n_slots >= N).
+ *  KVX_PAGED:      k, v are [n_layers][n_pages][page_size][H_kv][d_h] (n_slots =
+ *                  n_pages * page_size); position p of request b is slot
+ *                  page_table[b][p / page_size] * page_size + p % page_size.
+ * Distinct (request, position) pairs must map to distinct slots. */
+typedef struct kvx_cache {
+    int32_t layout;
+    void* k;                      /* (device) */
+    void* v;                      /* (device) */
+    int32_t n_layers;
+    int64_t n_slots;
+    int32_t page_size;            /* KVX_PAGED only, > 0 */
+    int32_t max_pages;            /* KVX_PAGED only: row length of page_table */
+    const int32_t* page_table;    /* (device) [n_req][max_pages] int32, KVX_PAGED only */
+} kvx_cache;
+
+/* Message of the last failed call on this thread ("" if none). */
+KVX_API const char* kvx_last_error(void);
+
+/* Library version string. */
+KVX_API const char* kvx_version(void);
+
+/* Recompute budget: k = ceil(pct * T / 100) in integer arithmetic (RaReCache abstract:
+ * 30% and 40% of positions are recomputed; rounded up so the budget is never
+ * under-spent).  Returns -1 if T < 0 or pct is outside [0, 100]. */
+KVX_API int32_t kvx_budget(int32_t T, int32_t pct);
+
+/* Shared source projection (PANORAMA abstract: "shared source projection", "compact
+ * latent per prompt position"):  z[t][i] = sum_c w_s[i][c] * x_src[t][c].
+ *   x_src (device) [n][d_src], w_s (device) [r][d_src], z (device, out) [n][r].
+ *   bf16 needs d_src % 64 == 0 and r % 8 == 0.  No workspace. */
+KVX_API kvx_status kvx_map_latent(void* stream, int32_t dtype, const void* x_src, const void* w_s,
+                          void* z, int64_t n, int32_t d_src, int32_t r);
+
+/* Score operator of the rank-disagreement metric (RaReCache abstract: energy of the
+ * mapped KV in output directions weakly supported by the calibration data).  With
+ * R_l = (I - U_l U_l^T) W_l the score of a latent z is
+ *   s(z) = sum_l |(I - U_l U_l^T) W_l z|^2 = z^T A z,   A = sum_l R_l^T R_l  (r x r),
+ * exact for the linear bias-free mapper.  Computed in fp64 on the device, once per
+ * (mapper, calibration) pair.
+ *   w_l (device) [L_t][d_t][r] storage dtype; u (device) [L_t][d_t][c] fp32 with
+ *   orthonormal columns (c may be 0); op (device, out):
+ *     bf16: [r][2r] bf16, row i = [hi(A[i][:]) | lo(A[i][:])] with hi = bf16(A),
+ *           lo = bf16(A - hi);
+ *     f32:  [r][r] fp32.
+ *   ws (device) of kvx_score_prepare_workspace() bytes. */
+KVX_API kvx_status kvx_score_prepare_workspace(int32_t r, int32_t d_t, int32_t c, size_t* bytes);
+KVX_API kvx_status kvx_score_prepare(void* stream, int32_t dtype, const void* w_l, const float* u,
+                             int32_t L_t, int32_t r, int32_t d_t, int32_t c, void* op,
+                             void* ws, size_t ws_bytes);
+
+/* Top-k of given scores per request: the k_b largest scores of request b, ties to the
+ * lower position, -0.0 equal to +0.0.  scores (device) [N] fp32, finite.
+ * sel (device, out) [cu_sel[n_req]] request-local positions, ascending per request;
+ * rest (device, out) [N - cu_sel[n_req]] the complement, ascending per request. */
+KVX_API kvx_status kvx_select_topk(void* stream, const float* scores, const kvx_batch* batch,
+                           int32_t* sel, int32_t* rest);
+
+/* Rank-disagreement score of every position and the top-budget selection.
+ *   z (device) [N][r] latent; op (device) from kvx_score_prepare for the same dtype;
+ *   budget_pct (host) [n_req]: must satisfy cu_sel[b+1]-cu_sel[b] = kvx_budget(T_b, pct_b);
+ *   scores (device, out) [N] fp32 = z^T A z per position;
+ *   sel, rest as in kvx_select_topk; ws (device) of kvx_score_select_workspace() bytes. */
+KVX_API kvx_status kvx_score_select_workspace(int32_t dtype, int32_t r, int64_t n, size_t* bytes);
+KVX_API kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, const void* op,
+                            int32_t r, const kvx_batch* batch, const int32_t* budget_pct,
+                            float* scores, int32_t* sel, int32_t* rest, void* ws,
+                            size_t ws_bytes);
+
+/* Layer-specific target reconstruction (PANORAMA abstract) into the translated cache:
+ * for every layer l and listed position p of request b,
+ *   y = W_l z[cu_tokens[b] + p];  K_l[slot(b,p)] = y[0 : H_kv d_h],
+ *                                 V_l[slot(b,p)] = y[H_kv d_h : 2 H_kv d_h].
+ *   rows (device) NULL = every position; else the complement list from
+ *   kvx_score_select (positions about to be recomputed are skipped: kvx_recompute_attn
+ *   overwrites them).  w_l (device) [L_t][d_t][r].  bf16 needs r % 64 == 0.
+ *   cache->n_layers must be >= L_t.  No workspace. */
+KVX_API kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const void* w_l,
+                           int32_t L_t, int32_t r, int32_t H_kv, int32_t d_h,
+                           const kvx_batch* batch, const int32_t* rows,
+                           const kvx_cache* cache);
+
+/* Rotary table for positions [0, max_pos): table[p][j] = (cos, sin)(p * base^(-2j/d_h)),
+ * j < d_h/2, angles formed in fp64, stored fp32.  table (device, out) [max_pos][d_h/2][2]. */
+KVX_API kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_t max_pos,
+                          float* table);
+
+/* Contextual recomputation of one target layer (PANORAMA abstract: the selected positions
+ * are recomputed over the full KV cache the mapper produced):
+ *   1. [q | k | v]_i = W_qkv x_l[cu_tokens[b] + p_i] for every selected position p_i;
+ *   2. q and k rotated (rotate-half: pair (j, j + d_h/2) by angle p_i * base^(-2j/d_h));
+ *   3. K[layer][slot(b,p_i)] = k_i, V[layer][slot(b,p_i)] = v_i for all i;
+ *   4. after all of step 3, for every i and query head h:
+ *      out[i][h] = sum_{j <= p_i} softmax_j(q_ih . K_j / sqrt(d_h)) V_j over KV head
+ *      h / (H_q / H_kv) of request b's cache;  lse[i][h] = natural log-sum-exp of the
+ *      scaled logits.
+ *   x_l (device) [N][D]; w_qkv (device) [n_qkv][D]; rope (device) from kvx_rope_table
+ *   with max_pos > every T_b; sel (device) [cu_sel[n_req]]; out (device, out)
+ *   [cu_sel[n_req]][H_q][d_h]; lse (device, out, nullable) [cu_sel[n_req]][H_q] fp32.
+ *   d_h must be 64 or 128, H_q % H_kv == 0, H_q / H_kv <= 16; bf16 needs D % 64 == 0.
+ *   ws (device) of kvx_recompute_attn_workspace() bytes. */
+KVX_API kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, int32_t H_q,
+                                        int32_t H_kv, int32_t d_h, size_t* bytes);
+KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const void* x_l,
+                              const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv,
+                              int32_t d_h, const float* rope, int32_t max_pos,
+                              const kvx_batch* batch, const int32_t* sel,
+                              const kvx_cache* cache, void* out, float* lse, void* ws,
+                              size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVX_H */

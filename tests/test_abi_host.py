@@ -1,0 +1,174 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports every symbol
+include/kvx.h declares, computes the budget, and rejects bad arguments on the host before
+any GPU work (every call below fails validation, so nothing reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cross_model_kv_amd import kvx
+from oracle import kvx_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -4
+A16 = ctypes.c_void_p(0x10000)           # aligned fake device address (never dereferenced)
+A16B = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)           # misaligned fake address
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "kvx.h")) as f:
+        return sorted(set(re.findall(r"^KVX_API[^(]*?\b(kvx_\w+)\s*\(", f.read(), flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 13
+    lib = kvx.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert kvx.version().startswith("kvx")
+
+
+def test_budget_matches_oracle():
+    for T in range(0, 2000, 7):
+        for pct in (0, 1, 20, 30, 33, 40, 99, 100):
+            assert kvx.budget(T, pct) == O.budget(T, pct)
+    assert kvx.lib().kvx_budget(10, 101) == -1
+    assert kvx.lib().kvx_budget(-1, 30) == -1
+    assert b"pct" in kvx.lib().kvx_last_error()
+
+
+class FakeBatch:
+    def __init__(self, lengths, ks, dev_ptrs=True):
+        n = len(lengths)
+        self.cu_t = [0]
+        self.cu_s = [0]
+        for t, k in zip(lengths, ks):
+            self.cu_t.append(self.cu_t[-1] + t)
+            self.cu_s.append(self.cu_s[-1] + k)
+        self.h_t = (ctypes.c_int32 * (n + 1))(*self.cu_t)
+        self.h_s = (ctypes.c_int32 * (n + 1))(*self.cu_s)
+        self.c = kvx._Batch(n, self.h_t, self.h_s, 0x30000 if dev_ptrs else None, 0x40000 if dev_ptrs else None)
+
+
+def cache(layout=0, n_layers=2, n_slots=1000, page_size=16, max_pages=8, k=A16, v=A16B, page_table=0x50000):
+    return kvx._Cache(layout, k.value if k is not None else None, v.value if v is not None else None, n_layers,
+                      n_slots, page_size, max_pages, page_table)
+
+
+def status(code, expect, needle=None):
+    assert code == expect, (code, kvx.lib().kvx_last_error())
+    if needle:
+        assert needle.encode() in kvx.lib().kvx_last_error(), kvx.lib().kvx_last_error()
+
+
+def test_map_latent_validation():
+    L = kvx.lib()
+    status(L.kvx_map_latent(None, 7, A16, A16, A16, 10, 64, 8), UNSUPPORTED, "dtype")
+    status(L.kvx_map_latent(None, 1, None, A16, A16, 10, 64, 8), INVALID, "x_src")
+    status(L.kvx_map_latent(None, 1, MIS, A16, A16, 10, 64, 8), INVALID, "aligned")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, -1, 64, 8), INVALID, "n")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 0, 8), INVALID, "positive")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 100, 8), INVALID, "d_src % 64")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 64, 12), INVALID, "r % 8")
+
+
+def test_score_prepare_validation():
+    L = kvx.lib()
+    b = ctypes.c_size_t()
+    status(L.kvx_score_prepare_workspace(8, 16, 17, ctypes.byref(b)), INVALID)
+    assert L.kvx_score_prepare_workspace(8, 16, 4, ctypes.byref(b)) == 0 and b.value > 0
+    status(L.kvx_score_prepare(None, 1, A16, A16, 2, 8, 16, 4, A16, None, 0), WORKSPACE)
+    status(L.kvx_score_prepare(None, 1, A16, A16, 2, 8, 16, 4, A16, A16, 1), WORKSPACE)
+    status(L.kvx_score_prepare(None, 1, A16, None, 2, 8, 16, 4, A16, A16, 1 << 20), INVALID, "u")
+    status(L.kvx_score_prepare(None, 1, A16, A16, 0, 8, 16, 4, A16, A16, 1 << 20), INVALID)
+    status(L.kvx_score_prepare(None, 1, A16, A16, 2, 8, 16, 20, A16, A16, 1 << 20), INVALID, "calibration")
+
+
+def test_batch_validation():
+    L = kvx.lib()
+    bad = FakeBatch([10, 5], [3, 6])                      # k > T
+    status(L.kvx_select_topk(None, A16, ctypes.byref(bad.c), A16, A16), INVALID, "selects")
+    nodev = FakeBatch([10], [3], dev_ptrs=False)
+    status(L.kvx_select_topk(None, A16, ctypes.byref(nodev.c), A16, A16), INVALID, "device")
+    empty = kvx._Batch(0, None, None, None, None)
+    status(L.kvx_select_topk(None, A16, ctypes.byref(empty), A16, A16), INVALID, "n_req")
+    ok = FakeBatch([10], [3])
+    status(L.kvx_select_topk(None, None, ctypes.byref(ok.c), A16, A16), INVALID, "scores")
+    status(L.kvx_select_topk(None, A16, ctypes.byref(ok.c), None, A16), INVALID, "sel")
+    status(L.kvx_select_topk(None, A16, None, A16, A16), INVALID, "batch")
+
+
+def test_score_select_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    pct = (ctypes.c_int32 * 2)(30, 30)
+    need = ctypes.c_size_t()
+    assert L.kvx_score_select_workspace(1, 128, 150, ctypes.byref(need)) == 0
+    args = lambda p, r=128, ws=A16, wsb=need.value: (None, 1, A16, A16, r, ctypes.byref(bt.c), p, A16, A16,
+                                                     A16, ws, wsb)
+    status(L.kvx_score_select(*args(pct, r=96)), INVALID, "r % 64")
+    status(L.kvx_score_select(*args(None)), INVALID, "budget_pct")
+    status(L.kvx_score_select(*args((ctypes.c_int32 * 2)(30, 40))), INVALID, "budget")
+    status(L.kvx_score_select(*args((ctypes.c_int32 * 2)(30, 130))), INVALID, "outside")
+    status(L.kvx_score_select(*args(pct, ws=None)), WORKSPACE)
+    status(L.kvx_score_select(*args(pct, wsb=need.value - 1)), WORKSPACE)
+
+
+def test_reconstruct_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    c = cache()
+    status(L.kvx_reconstruct(None, 1, A16, A16, 2, 96, 2, 64, ctypes.byref(bt.c), None, ctypes.byref(c)),
+           INVALID, "r % 64")
+    small = cache(n_slots=100)
+    status(L.kvx_reconstruct(None, 1, A16, A16, 2, 128, 2, 64, ctypes.byref(bt.c), None, ctypes.byref(small)),
+           INVALID, "n_slots")
+    few = cache(n_layers=1)
+    status(L.kvx_reconstruct(None, 1, A16, A16, 2, 128, 2, 64, ctypes.byref(bt.c), None, ctypes.byref(few)),
+           INVALID, "n_layers")
+    paged = cache(layout=1, n_slots=16 * 20, max_pages=3)   # 100 positions need 7 pages
+    status(L.kvx_reconstruct(None, 1, A16, A16, 2, 128, 2, 64, ctypes.byref(bt.c), None, ctypes.byref(paged)),
+           INVALID, "max_pages")
+    nopt = cache(layout=1, n_slots=16 * 20, page_table=None)
+    status(L.kvx_reconstruct(None, 1, A16, A16, 2, 128, 2, 64, ctypes.byref(bt.c), None, ctypes.byref(nopt)),
+           INVALID, "page_table")
+    badlayout = cache(layout=5)
+    status(L.kvx_reconstruct(None, 1, A16, A16, 2, 128, 2, 64, ctypes.byref(bt.c), None,
+                             ctypes.byref(badlayout)), INVALID, "layout")
+    status(L.kvx_reconstruct(None, 1, A16, A16, 2, 128, 2, 64, ctypes.byref(bt.c), MIS, ctypes.byref(c)),
+           INVALID, "rows")
+
+
+def test_rope_table_validation():
+    L = kvx.lib()
+    status(L.kvx_rope_table(None, 10000.0, 7, 10, A16), INVALID, "even")
+    status(L.kvx_rope_table(None, 10000.0, 64, 0, A16), INVALID, "max_pos")
+    status(L.kvx_rope_table(None, -1.0, 64, 10, A16), INVALID, "base")
+    status(L.kvx_rope_table(None, 10000.0, 64, 10, None), INVALID, "table")
+
+
+def test_recompute_attn_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    c = cache()
+    need = ctypes.c_size_t()
+    assert L.kvx_recompute_attn_workspace(1, ctypes.byref(bt.c), 8, 2, 64, ctypes.byref(need)) == 0
+    assert need.value >= 45 * 12 * 64 * 2
+
+    def call(dtype=1, layer=0, D=256, H_q=8, H_kv=2, d_h=64, max_pos=100, cc=c, ws=A16, wsb=None):
+        return L.kvx_recompute_attn(None, dtype, layer, A16, A16, D, H_q, H_kv, d_h, A16, max_pos,
+                                    ctypes.byref(bt.c), A16, ctypes.byref(cc), A16, None, ws,
+                                    need.value if wsb is None else wsb)
+    status(call(d_h=96), UNSUPPORTED, "d_h")
+    status(call(H_q=9), INVALID, "multiple")
+    status(call(H_q=34, H_kv=2), UNSUPPORTED, "> 16")
+    status(call(H_q=18, H_kv=2), UNSUPPORTED, "H_q / H_kv")
+    status(call(D=100), INVALID, "D % 64")
+    status(call(max_pos=99), INVALID, "rope")
+    status(call(layer=2), INVALID, "layer")
+    status(call(ws=None), WORKSPACE)
+    status(call(wsb=need.value - 1), WORKSPACE)
+    status(call(dtype=3), UNSUPPORTED, "dtype")

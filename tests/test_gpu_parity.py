@@ -1,0 +1,350 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle, small sizes.
+
+Sizes span several GEMM tiles with ragged tails and several attention blocks with a
+partial last block; the oracle finishes each case in seconds.  Tolerances (relative,
+normwise and max-abs per tensor): fp32 storage 1e-4, bf16 storage 2e-2; attention
+outputs need a minimum row cosine of 0.999.  Selection is bit-exact where it is decided
+by exact scores (fp32 path, select-only cases) and exact outside the band of near-ties
+that bf16 rounding of the latent can swap otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+from cross_model_kv_amd import kvx, synth
+from cross_model_kv_amd.handoff import Handoff
+from cross_model_kv_amd.workloads import TINY_F32, Workload
+from helpers import (assert_close, band_check, f64, logical, min_row_cosine, rel_max, rel_norm)
+from oracle import kvx_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def small(name, **kw) -> Workload:
+    base = dict(name=name, dtype="bf16", T=384, L_s=2, H_s=2, d_hs=64, r=128, L_t=2, H_q=8, H_kv=2,
+                d_h=128, D=256, c=64, pct=30)
+    base.update(kw)
+    return TINY_F32.shrink(**base)
+
+
+SMALL = {
+    "bf16-g4-d128": small("bf16-g4-d128"),
+    "bf16-g5-d128": small("bf16-g5-d128", H_q=10, T=450, pct=40),
+    "bf16-g4-d64": small("bf16-g4-d64", d_h=64, H_q=8, H_kv=2, r=192, T=300),
+    "bf16-g8-batched-paged": small("bf16-g8-batched-paged", H_q=16, H_kv=2, n_req=3, t_min=60, t_max=600,
+                                   pct_choices=(20, 30, 40), paged=True, page_size=16),
+    "f32-batched-paged": TINY_F32.shrink(name="f32-batched-paged", n_req=3, t_min=40, t_max=300,
+                                         pct_choices=(20, 30, 40), paged=True, page_size=16),
+}
+
+
+def oracle_request(inp, b):
+    wl = inp.wl
+    cu = inp.cu_tokens
+    rows = slice(cu[b], cu[b + 1])
+    return O.handoff_request(f64(inp.x_src[rows]), f64(inp.w_s), f64(inp.w_l), f64(inp.u),
+                             f64(inp.x_l[:, rows]), f64(inp.w_qkv), inp.pcts[b], wl.H_q, wl.H_kv, wl.d_h,
+                             wl.rope_base)
+
+
+def cache_views(h, b, T):
+    pt = h.inp.page_table.cpu().numpy() if h.wl.paged else None
+    cu = h.inp.cu_tokens
+    K = np.stack([logical(h.cache.k, l, b, T, cu, pt, h.wl.page_size) for l in range(h.wl.L_t)])
+    V = np.stack([logical(h.cache.v, l, b, T, cu, pt, h.wl.page_size) for l in range(h.wl.L_t)])
+    return K, V
+
+
+# --------------------------------------------------------------------------- end to end
+
+def test_end_to_end_tiny_fp32():
+    wl = TINY_F32
+    say(f"[e2e] {wl.name} seed 1")
+    inp = synth.generate(wl, 1, DEV)
+    h = Handoff(inp, DEV)
+    h.run()
+    torch.cuda.synchronize()
+    ref = oracle_request(inp, 0)
+    assert_close(f64(h.z), ref["z"], 1e-4, "Z")
+    s = f64(h.scores)
+    assert np.max(np.abs(s - ref["s"]) / ref["s"]) <= 1e-5
+    k = O.budget(wl.T, wl.pct)
+    gap = O.score_gap(ref["s"], k)
+    assert gap > 2e-5, f"seed gives a boundary gap of {gap:.2e}: too small for an exact comparison"
+    S = h.S.cpu().numpy()
+    assert np.array_equal(S, ref["S"]) and np.array_equal(h.C.cpu().numpy(), ref["C"])
+    K, V = cache_views(h, 0, wl.T)
+    assert_close(K, ref["K"], 1e-4, "K cache")
+    assert_close(V, ref["V"], 1e-4, "V cache")
+    o = f64(h.out[:, :k])
+    assert_close(o, ref["O"], 1e-4, "attention output")
+    assert min_row_cosine(o, ref["O"]) >= 0.999
+    assert np.abs(f64(h.lse[:, :k]) - ref["LSE"]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_end_to_end_small(name):
+    wl = SMALL[name]
+    say(f"[e2e] {name}")
+    inp = synth.generate(wl, 11, DEV)
+    h = Handoff(inp, DEV)
+    h.run()
+    torch.cuda.synchronize()
+    tol = 1e-4 if wl.dtype == "f32" else 2e-2
+    eps = 1e-5 if wl.dtype == "f32" else 2e-3
+    z = f64(h.z)
+    scores = f64(h.scores)
+    S_all = h.S.cpu().numpy()
+    cu, cs = inp.cu_tokens, h.batch.cu_sel
+    for b in range(len(inp.lengths)):
+        T = inp.lengths[b]
+        ref = oracle_request(inp, b)
+        assert_close(z[cu[b]:cu[b + 1]], ref["z"], tol, f"Z[{b}]")
+        assert rel_max(scores[cu[b]:cu[b + 1]], ref["s"]) <= (1e-5 if wl.dtype == "f32" else 1e-2)
+        S = S_all[cs[b]:cs[b + 1]]
+        assert np.all(np.diff(S) > 0) and len(S) == O.budget(T, inp.pcts[b])
+        nb, nd, gap = band_check(S, ref["s"], len(S), eps)
+        say(f"  request {b}: T={T} k={len(S)} band={nb} swapped={nd} gap={gap:.2e}")
+        K, V = cache_views(h, b, T)
+        same_S = set(S.tolist()) == set(ref["S"].tolist())
+        C_both = sorted(set(range(T)) - set(S.tolist()) - set(ref["S"].tolist()))
+        S_both = sorted(set(S.tolist()) & set(ref["S"].tolist()))
+        assert_close(K[:, C_both], ref["K"][:, C_both], tol, "translated K")
+        assert_close(V[:, C_both], ref["V"][:, C_both], tol, "translated V")
+        assert_close(K[:, S_both], ref["K"][:, S_both], tol, "recomputed K")
+        assert_close(V[:, S_both], ref["V"][:, S_both], tol, "recomputed V")
+        if same_S:
+            o = f64(h.out[:, cs[b]:cs[b + 1]])
+            assert min_row_cosine(o, ref["O"]) >= 0.999
+            assert_close(o, ref["O"], tol, "attention output")
+
+
+def test_full_budget_equals_causal_prefill():
+    """A 100% budget recomputes every position: the outputs are plain causal attention of
+    the target's own Q/K/V, whatever the translated cache held."""
+    wl = small("full-budget", pct=100, T=200)
+    say(f"[e2e] {wl.name}")
+    inp = synth.generate(wl, 5, DEV)
+    h = Handoff(inp, DEV)
+    h.run()
+    torch.cuda.synchronize()
+    ref = oracle_request(inp, 0)
+    assert np.array_equal(h.S.cpu().numpy(), np.arange(wl.T))
+    o = f64(h.out)
+    assert min_row_cosine(o, ref["O"]) >= 0.999
+    assert_close(o, ref["O"], 2e-2, "attention output")
+
+
+def test_zero_budget_keeps_translated_cache():
+    wl = small("zero-budget", pct=0, T=200)
+    say(f"[e2e] {wl.name}")
+    inp = synth.generate(wl, 6, DEV)
+    h = Handoff(inp, DEV)
+    h.run()
+    torch.cuda.synchronize()
+    ref = oracle_request(inp, 0)
+    assert h.batch.total_sel == 0 and np.array_equal(h.C.cpu().numpy(), np.arange(wl.T))
+    K, V = cache_views(h, 0, wl.T)
+    assert_close(K, ref["K_tr"], 2e-2, "K")
+    assert_close(V, ref["V_tr"], 2e-2, "V")
+
+
+def test_determinism_bitwise():
+    wl = SMALL["bf16-g8-batched-paged"]
+    say(f"[determinism] {wl.name}")
+    inp = synth.generate(wl, 12, DEV)
+    h1, h2 = Handoff(inp, DEV), Handoff(inp, DEV)
+    h1.run()
+    h2.run()
+    torch.cuda.synchronize()
+    for a, b in ((h1.z, h2.z), (h1.scores, h2.scores), (h1.S, h2.S), (h1.C, h2.C), (h1.cache.k, h2.cache.k),
+                 (h1.cache.v, h2.cache.v), (h1.out, h2.out), (h1.lse, h2.lse)):
+        assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------- stage-wise
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identity_mapper_bitexact(dtype):
+    say(f"[map] identity {dtype}")
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    n, d = 300, 512
+    x = synth.latent(n, d, 21, dtype=dt, device=DEV)
+    eye = torch.eye(d, dtype=dt, device=DEV)
+    z = kvx.map_latent(x, eye)
+    torch.cuda.synchronize()
+    assert torch.equal(z, x)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_score_select_stagewise(dtype):
+    """Scores from a given latent: per-position relative error against the oracle's
+    explicit residual energy, the selected set exactly the top-k of the returned scores,
+    and equal to the oracle's set outside a 1e-5 band."""
+    wl = small(f"score-{dtype}", dtype=dtype, T=700, L_t=3, r=128, c=64)
+    say(f"[score] {wl.name}")
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    inp = synth.generate(wl, 31, DEV)
+    z = synth.latent(wl.T, wl.r, 31, dtype=dt, device=DEV)
+    op = kvx.score_prepare(inp.w_l, inp.u)
+    batch = kvx.Batch.for_budgets([wl.T], [wl.pct], DEV)
+    scores, sel, rest = kvx.score_select(z, op, batch, [wl.pct])
+    torch.cuda.synchronize()
+    _, _, Y = O.reconstruct(f64(z), f64(inp.w_l), wl.H_kv, wl.d_h)
+    s_ref = O.rank_disagreement(Y, f64(inp.u))
+    s = f64(scores)
+    err = np.max(np.abs(s - s_ref) / s_ref)
+    say(f"  max relative score error {err:.2e}")
+    assert err <= 1e-5
+    k = O.budget(wl.T, wl.pct)
+    S_own, C_own = O.select(s.astype(np.float32).astype(np.float64), k)
+    assert np.array_equal(sel.cpu().numpy(), S_own) and np.array_equal(rest.cpu().numpy(), C_own)
+    band_check(sel.cpu().numpy(), s_ref, k, 1e-5)
+
+
+def test_in_span_scores_zero():
+    """A mapper whose every output lies in the calibration span scores zero (fp32)."""
+    wl = small("in-span", dtype="f32", T=256, L_t=2, r=64, c=64, H_kv=1, d_h=64)
+    say(f"[score] {wl.name}")
+    inp = synth.generate(wl, 32, DEV)
+    rng = np.random.default_rng(32)
+    u = f64(inp.u)
+    w = np.stack([u[l] @ rng.standard_normal((wl.c, wl.r)) for l in range(wl.L_t)])
+    w_l = torch.from_numpy(w.astype(np.float32)).to(DEV)
+    z = synth.latent(wl.T, wl.r, 32, dtype=torch.float32, device=DEV)
+    op = kvx.score_prepare(w_l, inp.u)
+    batch = kvx.Batch.for_budgets([wl.T], [wl.pct], DEV)
+    scores, _, _ = kvx.score_select(z, op, batch, [wl.pct])
+    torch.cuda.synchronize()
+    _, _, Y = O.reconstruct(f64(z), f64(w_l), wl.H_kv, wl.d_h)
+    energy = np.sum(Y * Y, axis=(0, 2))
+    assert np.all(np.abs(f64(scores)) <= 1e-5 * energy)
+
+
+@pytest.mark.parametrize("kind", ["equal", "few_values", "signed_zeros", "ulp", "normal", "positive"])
+def test_select_topk_adversarial(kind):
+    lengths = [1, 2, 63, 1000, 4097]
+    rng = np.random.default_rng(41)
+    ks = [int(rng.integers(0, t + 1)) for t in lengths]
+    ks[3], ks[4] = 0, 4097            # empty and full selections
+    say(f"[select] {kind} lengths {lengths} k {ks}")
+    s = np.concatenate([synth.adversarial_scores(kind, t, 41 + i) for i, t in enumerate(lengths)])
+    batch = kvx.Batch(lengths, ks, DEV)
+    sel, rest = kvx.select_topk(torch.from_numpy(s).to(DEV), batch)
+    torch.cuda.synchronize()
+    sel, rest = sel.cpu().numpy(), rest.cpu().numpy()
+    cu, cs = batch.cu_tokens, batch.cu_sel
+    for b, (t, k) in enumerate(zip(lengths, ks)):
+        S, C = O.select(s[cu[b]:cu[b + 1]].astype(np.float64), k)
+        assert np.array_equal(sel[cs[b]:cs[b + 1]], S), (kind, b)
+        assert np.array_equal(rest[cu[b] - cs[b]:cu[b + 1] - cs[b + 1]], C), (kind, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reconstruct_layouts(dtype):
+    """Complement rows written through a contiguous and a paged cache agree bit for bit and
+    with the oracle; rows of the selected set are left untouched."""
+    wl = small(f"reconstruct-{dtype}", dtype=dtype, n_req=3, t_min=50, t_max=700, pct_choices=(20, 40),
+               paged=True, L_t=3)
+    say(f"[reconstruct] {wl.name}")
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    inp = synth.generate(wl, 51, DEV)
+    batch = kvx.Batch.for_budgets(inp.lengths, inp.pcts, DEV)
+    N = batch.n_tokens
+    z = synth.latent(N, wl.r, 51, dtype=dt, device=DEV)
+    S_list = [synth.random_subset(t, k, 51 + b) for b, (t, k) in enumerate(zip(inp.lengths, batch.n_sel))]
+    C_list = [np.setdiff1d(np.arange(t), S) for t, S in zip(inp.lengths, S_list)]
+    rest = torch.from_numpy(np.concatenate(C_list).astype(np.int32)).to(DEV)
+    cont = kvx.Cache(torch.full((wl.L_t, N, wl.H_kv, wl.d_h), 7.0, dtype=dt, device=DEV),
+                     torch.full((wl.L_t, N, wl.H_kv, wl.d_h), 7.0, dtype=dt, device=DEV), wl.L_t, N)
+    n_slots = inp.n_pages * wl.page_size
+    paged = kvx.Cache(torch.full((wl.L_t, n_slots, wl.H_kv, wl.d_h), 7.0, dtype=dt, device=DEV),
+                      torch.full((wl.L_t, n_slots, wl.H_kv, wl.d_h), 7.0, dtype=dt, device=DEV), wl.L_t,
+                      n_slots, page_table=inp.page_table, page_size=wl.page_size)
+    kvx.reconstruct(z, inp.w_l, wl.H_kv, wl.d_h, batch, cont, rows=rest)
+    kvx.reconstruct(z, inp.w_l, wl.H_kv, wl.d_h, batch, paged, rows=rest)
+    full = kvx.Cache.empty(wl.L_t, N, wl.H_kv, wl.d_h, dt, DEV)
+    kvx.reconstruct(z, inp.w_l, wl.H_kv, wl.d_h, batch, full, rows=None)
+    torch.cuda.synchronize()
+    pt = inp.page_table.cpu().numpy()
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for b, T in enumerate(inp.lengths):
+        for cache_t in ("k", "v"):
+            a = np.stack([logical(getattr(cont, cache_t), l, b, T, batch.cu_tokens) for l in range(wl.L_t)])
+            p = np.stack([logical(getattr(paged, cache_t), l, b, T, batch.cu_tokens, pt, wl.page_size)
+                          for l in range(wl.L_t)])
+            f = np.stack([logical(getattr(full, cache_t), l, b, T, batch.cu_tokens) for l in range(wl.L_t)])
+            assert np.array_equal(a, p), "paged and contiguous layouts differ"
+            C, S = C_list[b], S_list[b]
+            assert np.array_equal(a[:, C], f[:, C]), "complement rows differ from all rows"
+            assert np.all(a[:, S] == 7.0), "selected rows were written"
+            K, V, _ = O.reconstruct(f64(z[batch.cu_tokens[b]:batch.cu_tokens[b + 1]]), f64(inp.w_l), wl.H_kv,
+                                    wl.d_h)
+            assert_close(f, K if cache_t == "k" else V, tol, f"reconstructed {cache_t}")
+
+
+RECOMPUTE_CASES = {
+    "bf16-g8": small("rc-bf16-g8", H_q=16, H_kv=2, T=700, pct=30),
+    "bf16-g5": small("rc-bf16-g5", H_q=10, H_kv=2, T=517, pct=40),
+    "bf16-g1-d64": small("rc-bf16-g1-d64", H_q=2, H_kv=2, d_h=64, T=333, pct=20),
+    "bf16-g8-batched-paged": small("rc-bf16-batched", H_q=16, H_kv=2, n_req=4, t_min=20, t_max=900,
+                                   pct_choices=(20, 30, 40), paged=True),
+    "f32-g4": small("rc-f32-g4", dtype="f32", H_q=8, H_kv=2, d_h=64, T=300, pct=30),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RECOMPUTE_CASES))
+def test_recompute_attn_stagewise(name):
+    """Given a translated cache and a selected set: recomputed K/V land at the selected
+    slots (rotated k), other slots stay bit-identical, and the selected queries' causal
+    attention over the mixed cache matches the oracle."""
+    wl = RECOMPUTE_CASES[name]
+    say(f"[recompute] {name}")
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    inp = synth.generate(wl, 61, DEV)
+    batch = kvx.Batch.for_budgets(inp.lengths, inp.pcts, DEV)
+    S_list = [synth.random_subset(t, k, 61 + b) for b, (t, k) in enumerate(zip(inp.lengths, batch.n_sel))]
+    sel = torch.from_numpy(np.concatenate(S_list).astype(np.int32)).to(DEV)
+    n_slots = inp.n_pages * wl.page_size if wl.paged else batch.n_tokens
+    shape = (wl.L_t, n_slots, wl.H_kv, wl.d_h)
+    k0 = synth.cache_fill(shape, 61, dtype=dt, device=DEV)
+    v0 = synth.cache_fill(shape, 62, dtype=dt, device=DEV)
+    cache = kvx.Cache(k0.clone(), v0.clone(), wl.L_t, n_slots,
+                      page_table=inp.page_table if wl.paged else None, page_size=wl.page_size)
+    rope = kvx.rope_table(wl.rope_base, wl.d_h, max(inp.lengths), DEV)
+    layer = wl.L_t - 1
+    lse = torch.empty((max(batch.total_sel, 1), wl.H_q), dtype=torch.float32, device=DEV)
+    out = kvx.recompute_attn(layer, inp.x_l[layer], inp.w_qkv[layer], wl.H_q, wl.H_kv, wl.d_h, rope, batch,
+                             sel, cache, lse=lse)
+    torch.cuda.synchronize()
+    tol = 1e-4 if wl.dtype == "f32" else 2e-2
+    pt = inp.page_table.cpu().numpy() if wl.paged else None
+    cu, cs = batch.cu_tokens, batch.cu_sel
+    o_all, lse_all = f64(out), f64(lse)
+    for b, T in enumerate(inp.lengths):
+        S = S_list[b]
+        Kg = logical(cache.k, layer, b, T, cu, pt, wl.page_size)
+        Vg = logical(cache.v, layer, b, T, cu, pt, wl.page_size)
+        K0 = logical(k0, layer, b, T, cu, pt, wl.page_size)
+        V0 = logical(v0, layer, b, T, cu, pt, wl.page_size)
+        C = np.setdiff1d(np.arange(T), S)
+        assert np.array_equal(Kg[C], K0[C]) and np.array_equal(Vg[C], V0[C]), "translated slots changed"
+        x_rows = f64(inp.x_l[layer, cu[b]:cu[b + 1]])[S]
+        q, kk, vv = O.recompute_qkv(x_rows, f64(inp.w_qkv[layer]), S, wl.H_q, wl.H_kv, wl.d_h, wl.rope_base)
+        if len(S):
+            assert_close(Kg[S], kk, tol, "recomputed k")
+            assert_close(Vg[S], vv, tol, "recomputed v")
+        Km, Vm = O.scatter(K0, V0, S, kk, vv)
+        o_ref, lse_ref = O.sparse_causal_attention(q, Km, Vm, S)
+        o = o_all[cs[b]:cs[b + 1]]
+        if len(S):
+            cos = min_row_cosine(o, o_ref)
+            say(f"  request {b}: T={T} k={len(S)} min cosine {cos:.6f} normwise {rel_norm(o, o_ref):.2e}")
+            assert cos >= 0.999
+            assert_close(o, o_ref, tol, "attention output")
+            assert np.abs(lse_all[cs[b]:cs[b + 1]] - lse_ref).max() <= (1e-4 if wl.dtype == "f32" else 2e-2)
