@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Handoff throughput of the cross-model KV handoff on one MI355X.
+
+One step = one whole handoff of the 16K-token 8B-to-32B-shaped workload: map the source KV
+to the latent, score and select the top-30% positions, reconstruct the translated cache of
+the complement, then for each of the 64 target layers project Q/K/V of the selected
+positions, rotate and scatter K/V into the mixed cache and run the sparse causal attention.
+All inputs are synthetic (seeded) and resident in HBM before timing.
+
+Prints one JSON line: handoff tokens/s (positions handed off per second), the roofline of
+the dominant kernel (the sparse attention, timed with HIP events on its launch stream
+over the timed steps), per-stage times, and the fp64 CPU oracle timed on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+METRIC = "handoff tokens/s (map+select+recompute-attn) at 16K; % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_8B-to-32B-T16384.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def f64(t):
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def stage_work(wl, T, k, pos_sum):
+    """Algorithmic flops / bytes of every stage of one handoff (per launch for per-layer stages)."""
+    d_t, n_qkv = wl.d_t, wl.n_qkv
+    return {
+        "map_latent": dict(flops=2.0 * T * wl.d_src * wl.r, bytes=2.0 * (T * wl.d_src + wl.d_src * wl.r + T * wl.r)),
+        "score_select": dict(flops=2.0 * T * wl.r * wl.r, bytes=2.0 * T * wl.r + 4.0 * wl.r * wl.r + 4.0 * T),
+        "reconstruct": dict(flops=2.0 * (T - k) * wl.r * d_t * wl.L_t,
+                            bytes=2.0 * ((T - k) * d_t * wl.L_t + wl.L_t * wl.r * d_t + T * wl.r)),
+        "qkv_project": dict(flops=2.0 * k * wl.D * n_qkv, bytes=2.0 * (k * wl.D + wl.D * n_qkv + k * n_qkv)),
+        "rope_scatter": dict(flops=0.0, bytes=2.0 * 2.0 * k * d_t),
+        "sparse_attention": dict(flops=4.0 * wl.H_q * wl.d_h * pos_sum,
+                                 bytes=2.0 * (T * d_t + 2.0 * k * wl.H_q * wl.d_h)),
+    }
+
+
+def cpu_baseline(inp, wl, S, T, k, pos_sum):
+    """The fp64 oracle as it is, timed on a bounded sample of the workload and scaled to one
+    handoff: 512 source rows of the map, 256 rows of reconstruct + score (all layers), the
+    full-length select, one layer's Q/K/V projection of 512 selected rows, one layer's scatter,
+    and one layer's attention of 24 selected queries spread over the positions."""
+    from oracle import kvx_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    parts = {}
+
+    rows = np.sort(rng.choice(T, 512, replace=False))
+    x = f64(inp.x_src[rows])
+    w_s = f64(inp.w_s)
+    t0 = time.perf_counter()
+    z = O.map_latent(x, w_s)
+    parts["map_latent"] = (time.perf_counter() - t0) * T / len(rows)
+    del w_s, x
+
+    w_l, u = f64(inp.w_l), f64(inp.u)
+    zr = z[:256]
+    t0 = time.perf_counter()
+    _, _, Y = O.reconstruct(zr, w_l, wl.H_kv, wl.d_h)
+    parts["reconstruct"] = (time.perf_counter() - t0) * T / len(zr)
+    t0 = time.perf_counter()
+    s = O.rank_disagreement(Y, u)
+    parts["score"] = (time.perf_counter() - t0) * T / len(zr)
+    del Y, w_l, u
+    s_full = np.tile(s, T // len(s) + 1)[:T] * (1.0 + 1e-9 * np.arange(T))
+    t0 = time.perf_counter()
+    O.select(s_full, k)
+    parts["select"] = time.perf_counter() - t0
+
+    sel_rows = np.sort(rng.choice(S, min(512, len(S)), replace=False))
+    xq = f64(inp.x_l[0][torch.as_tensor(sel_rows, device=inp.x_l.device)])
+    wq = f64(inp.w_qkv[0])
+    t0 = time.perf_counter()
+    q, kk, vv = O.recompute_qkv(xq, wq, sel_rows, wl.H_q, wl.H_kv, wl.d_h, wl.rope_base)
+    parts["qkv_project"] = (time.perf_counter() - t0) * k / len(sel_rows) * wl.L_t
+    del xq, wq
+    Kc = rng.standard_normal((T, wl.H_kv, wl.d_h))
+    Vc = rng.standard_normal((T, wl.H_kv, wl.d_h))
+    t0 = time.perf_counter()
+    O.scatter(Kc, Vc, sel_rows, kk, vv)
+    parts["rope_scatter"] = (time.perf_counter() - t0) * k / len(sel_rows) * wl.L_t
+    qi = np.linspace(0, len(sel_rows) - 1, 24).astype(int)
+    t0 = time.perf_counter()
+    O.sparse_causal_attention(q[qi], Kc, Vc, sel_rows[qi])
+    dt = time.perf_counter() - t0
+    parts["sparse_attention"] = dt * pos_sum / float(np.sum(sel_rows[qi] + 1)) * wl.L_t
+    total = sum(parts.values())
+    return {"value": T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": ("fp64 numpy oracle on the 16K workload: map 512 rows, reconstruct+score 256 rows x 64 "
+                       "layers, full select, 1 layer of qkv (512 rows), scatter, attention (24 queries); "
+                       "each part scaled to one handoff (rows, layers, sum of causal lengths)"),
+            "seconds_per_handoff": total, "parts_s": {k2: round(v2, 4) for k2, v2 in parts.items()}}
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB, for scaling HBM byte counters (FETCH_SIZE / WRITE_SIZE)."""
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 2 * n, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="8B-to-32B-shape-T16384")
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the handoff path here is single-GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from cross_model_kv_amd import kvx, synth, workloads
+    from cross_model_kv_amd.handoff import Handoff
+
+    wl = workloads.ALL[args.workload]
+    if wl.batched:
+        raise SystemExit("bench.py times single-request workloads")
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = synth.generate(wl, args.seed, dev)
+    h = Handoff(inp, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: inputs and one-time preparation {time.perf_counter() - t_gen:.1f}s")
+    T = wl.T
+    k = h.batch.total_sel
+    qkv = h.ws_attn[: k * wl.n_qkv * 2].view(torch.bfloat16).view(k, wl.n_qkv)
+    stream = torch.cuda.current_stream(dev)
+
+    names = ["map_latent", "score_select", "reconstruct", "qkv_project", "rope_scatter", "sparse_attention"]
+
+    def step(ev=None):
+        def mark(key):
+            if ev is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev.setdefault(key, []).append(e)
+        mark("t0")
+        h.map()
+        mark("map_latent")
+        h.select()
+        mark("score_select")
+        h.reconstruct()
+        mark("reconstruct")
+        for l in range(wl.L_t):
+            kvx.qkv_project(inp.x_l[l], inp.w_qkv[l], wl.H_q, wl.H_kv, wl.d_h, h.batch, h.S, qkv)
+            mark("qkv_project")
+            kvx.rope_scatter(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache)
+            mark("rope_scatter")
+            kvx.sparse_attention(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache, h.out[l], h.lse[l])
+            mark("sparse_attention")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = {}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # per-stage GPU times from the events (each stage ends where the next begins)
+    seq = []
+    per_step = 3 + 3 * wl.L_t
+    order = ["map_latent", "score_select", "reconstruct"] + ["qkv_project", "rope_scatter", "sparse_attention"] * wl.L_t
+    idx = {n: 0 for n in names}
+    starts = events["t0"]
+    stage_ms = {n: 0.0 for n in names}
+    launches = {n: 0 for n in names}
+    for s in range(args.steps):
+        prev = starts[s]
+        for n in order:
+            e = events[n][idx[n]]
+            idx[n] += 1
+            stage_ms[n] += prev.elapsed_time(e)
+            launches[n] += 1
+            prev = e
+    avg_launch_ms = {n: stage_ms[n] / launches[n] for n in names}
+    step_stage_ms = {n: stage_ms[n] / args.steps for n in names}
+
+    S = h.S.cpu().numpy()
+    pos_sum = float(np.sum(S.astype(np.float64) + 1.0))
+    work = stage_work(wl, T, k, pos_sum)
+    stages = {}
+    for n in names:
+        t = avg_launch_ms[n] * 1e-3
+        w = work[n]
+        stages[n] = {"ms_per_step": round(step_stage_ms[n], 4), "ms_per_launch": round(avg_launch_ms[n], 5),
+                     "tflops": round(w["flops"] / t / 1e12, 2) if w["flops"] else None,
+                     "gbs": round(w["bytes"] / t / 1e9, 1)}
+    att_t = avg_launch_ms["sparse_attention"] * 1e-3
+    achieved = work["sparse_attention"]["flops"] / att_t / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            traffic = json.load(f).get("hbm_bytes_per_launch")
+    line = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "source_layers": wl.L_s, "d_src": wl.d_src, "latent_rank": wl.r,
+                   "target_layers": wl.L_t, "H_q": wl.H_q, "H_kv": wl.H_kv, "d_h": wl.d_h, "D": wl.D,
+                   "calibration_rank": wl.c, "budget_pct": wl.pct, "selected": k, "parallelism": "none"},
+        "roofline": {"kernel": "sparse_attention", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_flops_per_launch": work["sparse_attention"]["flops"],
+                     "avg_launch_ms": round(avg_launch_ms["sparse_attention"], 5)},
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        line["cpu_baseline"] = cpu_baseline(inp, wl, S, T, k, pos_sum)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -406,110 +406,196 @@ kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, i
     return ok();
 }
 
-kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const void* x_l,
-                              const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h,
-                              const float* rope, int32_t max_pos, const kvx_batch* batch,
-                              const int32_t* sel, const kvx_cache* cache, void* out, float* lse,
-                              void* ws, size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Head shape and batch checks shared by the recompute steps.
+kvx_status check_heads(int32_t dtype, int32_t H_q, int32_t H_kv, int32_t d_h) {
     if (kvx_status st = check_dtype(dtype)) return st;
-    BatchInfo bi;
-    if (kvx_status st = check_batch(batch, &bi)) return st;
-    KVX_REQUIRE_PTR(x_l, "x_l");
-    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
-    KVX_REQUIRE_PTR(rope, "rope");
-    KVX_REQUIRE(D > 0 && H_q > 0 && H_kv > 0, "D, H_q and H_kv must be positive");
+    KVX_REQUIRE(H_q > 0 && H_kv > 0, "H_q and H_kv must be positive");
     if (d_h != 64 && d_h != 128) return fail(KVX_ERR_UNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
     KVX_REQUIRE(H_q % H_kv == 0, "H_q (%d) must be a multiple of H_kv (%d)", H_q, H_kv);
     const int g = H_q / H_kv;
     if (g > 16) return fail(KVX_ERR_UNSUPPORTED, "H_q / H_kv = %d > 16", g);
-    if (dtype == KVX_BF16) {
-        KVX_REQUIRE(D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
-        if (attn_bf16_block_queries(g) == 0)
-            return fail(KVX_ERR_UNSUPPORTED, "bf16 attention supports H_q / H_kv in {1..8, 16} (got %d)", g);
-    }
-    if (bi.n_req > MAX_ATTN_REQ)
-        return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
+    if (dtype == KVX_BF16 && attn_bf16_block_queries(g) == 0)
+        return fail(KVX_ERR_UNSUPPORTED, "bf16 attention supports H_q / H_kv in {1..8, 16} (got %d)", g);
+    return KVX_OK;
+}
+
+kvx_status check_layer_cache(const kvx_cache* cache, const kvx_batch* batch, const BatchInfo& bi, int32_t dtype,
+                             int32_t H_kv, int32_t d_h, int32_t layer, const float* rope, int32_t max_pos) {
+    KVX_REQUIRE_PTR(rope, "rope");
     KVX_REQUIRE(max_pos >= bi.max_T, "rope table has %d positions, the longest request %d", max_pos, bi.max_T);
     if (kvx_status st = check_cache(cache, bi, dtype, H_kv, d_h, 1)) return st;
     KVX_REQUIRE(layer >= 0 && layer < cache->n_layers, "layer %d outside [0, %d)", layer, cache->n_layers);
-    if (kvx_status st = check_page_table_debug(cache, batch)) return st;
-    if (bi.n_sel > 0) {
-        KVX_REQUIRE_PTR(sel, "sel");
-        KVX_REQUIRE_PTR(out, "out");
-        if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
-    }
-    size_t need = 0;
-    kvx_recompute_attn_workspace(dtype, batch, H_q, H_kv, d_h, &need);
-    if (bi.n_sel > 0 && (!ws || ws_bytes < need))
-        return fail(KVX_ERR_WORKSPACE, "recompute_attn needs %zu workspace bytes (got %zu)", need, ws_bytes);
-    if (bi.n_sel > 0) KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
-    if (bi.n_sel == 0) return ok();
-    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    return check_page_table_debug(cache, batch);
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    const int n_qkv = (H_q + 2 * H_kv) * d_h;
-    const int hd = H_kv * d_h;
-    const size_t es = elem_size(dtype);
-    const int64_t layer_off = (int64_t)layer * cache->n_slots * hd;
+RowMap sel_rows(const kvx_batch* batch, const int32_t* sel, int n_req) {
     RowMap rm{};
     rm.mode = 2;
     rm.list = sel;
     rm.list_is_rest = 0;
     rm.cu_tok = batch->cu_tokens_d;
     rm.cu_sel = batch->cu_sel_d;
-    rm.n_req = bi.n_req;
-    const SlotMap sm = slot_map(cache, batch);
+    rm.n_req = n_req;
+    return rm;
+}
 
-    // 1. [q | k | v] of the selected rows
+hipError_t run_qkv(hipStream_t s, int32_t dtype, const void* x_l, const void* w_qkv, int32_t D, int n_qkv,
+                   const kvx_batch* batch, const BatchInfo& bi, const int32_t* sel, void* qkv) {
+    const RowMap rm = sel_rows(batch, sel, bi.n_req);
     if (dtype == KVX_BF16) {
         GemmArgs a{};
         a.A = (const bf16*)x_l; a.lda = D; a.K_a = D;
         a.B = (const bf16*)w_qkv; a.ldb = D;
         a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
         a.rows = rm;
-        a.epi = EPI_STORE; a.C = (bf16*)ws; a.ldc = n_qkv;
-        KVX_TRY_HIP(launch_gemm_bf16(a, s), "recompute qkv");
-    } else {
-        GemmF32Args a{};
-        a.A = (const float*)x_l; a.lda = D; a.K_a = D;
-        a.B = (const float*)w_qkv; a.ldb = D;
-        a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
-        a.rows = rm;
-        a.epi = EPI_STORE; a.C = (float*)ws; a.ldc = n_qkv;
-        KVX_TRY_HIP(launch_gemm_f32(a, s), "recompute qkv");
+        a.epi = EPI_STORE; a.C = (bf16*)qkv; a.ldc = n_qkv;
+        return launch_gemm_bf16(a, s);
     }
-    // 2-3. rotate k at the true positions and write k, v into the layer's cache slots
+    GemmF32Args a{};
+    a.A = (const float*)x_l; a.lda = D; a.K_a = D;
+    a.B = (const float*)w_qkv; a.ldb = D;
+    a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
+    a.rows = rm;
+    a.epi = EPI_STORE; a.C = (float*)qkv; a.ldc = n_qkv;
+    return launch_gemm_f32(a, s);
+}
+
+void* layer_base(void* base, const kvx_cache* cache, int layer, int hd, int32_t dtype) {
+    return (char*)base + (int64_t)layer * cache->n_slots * hd * (int64_t)elem_size(dtype);
+}
+
+hipError_t run_scatter(hipStream_t s, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q, int32_t H_kv,
+                       int32_t d_h, const float* rope, const kvx_batch* batch, const BatchInfo& bi,
+                       const int32_t* sel, const kvx_cache* cache) {
+    const int hd = H_kv * d_h;
     ScatterArgs sc{};
-    sc.qkv = ws; sc.ld = n_qkv;
+    sc.qkv = qkv; sc.ld = (H_q + 2 * H_kv) * d_h;
     sc.H_q = H_q; sc.H_kv = H_kv; sc.d_h = d_h;
     sc.rope = rope;
     sc.sel = sel; sc.cu_sel = batch->cu_sel_d; sc.n_req = bi.n_req; sc.n_sel = bi.n_sel;
-    sc.slots = sm;
-    sc.kc = (char*)cache->k + layer_off * es;
-    sc.vc = (char*)cache->v + layer_off * es;
-    KVX_TRY_HIP(launch_rope_scatter(sc, dtype, s), "rope_scatter");
-    // 4. causal attention of the selected queries over the mixed cache
+    sc.slots = slot_map(cache, batch);
+    sc.kc = layer_base(cache->k, cache, layer, hd, dtype);
+    sc.vc = layer_base(cache->v, cache, layer, hd, dtype);
+    return launch_rope_scatter(sc, dtype, s);
+}
+
+hipError_t run_attention(hipStream_t s, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
+                         int32_t H_kv, int32_t d_h, const float* rope, const kvx_batch* batch,
+                         const BatchInfo& bi, const int32_t* sel, const kvx_cache* cache, void* out,
+                         float* lse) {
+    const int hd = H_kv * d_h;
     AttnArgs at{};
-    at.qkv = ws; at.ld = n_qkv;
+    at.qkv = qkv; at.ld = (H_q + 2 * H_kv) * d_h;
     at.H_q = H_q; at.H_kv = H_kv; at.d_h = d_h;
     at.rope = rope;
     at.sel = sel; at.cu_sel = batch->cu_sel_d; at.n_req = bi.n_req;
-    at.slots = sm;
-    at.kc = sc.kc; at.vc = sc.vc;
+    at.slots = slot_map(cache, batch);
+    at.kc = layer_base(cache->k, cache, layer, hd, dtype);
+    at.vc = layer_base(cache->v, cache, layer, hd, dtype);
     at.out = out; at.lse = lse;
     if (dtype == KVX_BF16) {
-        at.bq = attn_bf16_block_queries(g);
+        at.bq = attn_bf16_block_queries(H_q / H_kv);
         at.blk_cu[0] = 0;
         for (int b = 0; b < bi.n_req; ++b) {
             const int k = batch->cu_sel_h[b + 1] - batch->cu_sel_h[b];
             at.blk_cu[b + 1] = at.blk_cu[b] + (k + at.bq - 1) / at.bq;
         }
         at.n_blocks = at.blk_cu[bi.n_req];
-        return hip_status(launch_attn_bf16(at, s), "attention");
+        return launch_attn_bf16(at, s);
     }
     at.bq = 1;
-    at.n_blocks = (int)bi.n_sel;
-    return hip_status(launch_attn_f32(at, s), "attention");
+    at.n_blocks = (int)bi.n_sel;     // one wave per (selected row, head)
+    return launch_attn_f32(at, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvx_status kvx_qkv_project(void* stream, int32_t dtype, const void* x_l, const void* w_qkv, int32_t D,
+                           int32_t H_q, int32_t H_kv, int32_t d_h, const kvx_batch* batch, const int32_t* sel,
+                           void* qkv) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(x_l, "x_l");
+    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
+    KVX_REQUIRE(D > 0, "D must be positive");
+    if (dtype == KVX_BF16) KVX_REQUIRE(D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(sel, "sel");
+    KVX_REQUIRE_PTR(qkv, "qkv");
+    return hip_status(run_qkv((hipStream_t)stream, dtype, x_l, w_qkv, D, (H_q + 2 * H_kv) * d_h, batch, bi, sel,
+                              qkv), "qkv_project");
+}
+
+kvx_status kvx_rope_scatter(void* stream, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
+                            int32_t H_kv, int32_t d_h, const float* rope, int32_t max_pos, const kvx_batch* batch,
+                            const int32_t* sel, const kvx_cache* cache) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE_PTR(sel, "sel");
+    KVX_REQUIRE_PTR(qkv, "qkv");
+    return hip_status(run_scatter((hipStream_t)stream, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel,
+                                  cache), "rope_scatter");
+}
+
+kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
+                                int32_t H_kv, int32_t d_h, const float* rope, int32_t max_pos,
+                                const kvx_batch* batch, const int32_t* sel, const kvx_cache* cache, void* out,
+                                float* lse) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    if (bi.n_req > MAX_ATTN_REQ)
+        return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
+    if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE_PTR(sel, "sel");
+    KVX_REQUIRE_PTR(qkv, "qkv");
+    KVX_REQUIRE_PTR(out, "out");
+    if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+    return hip_status(run_attention((hipStream_t)stream, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel,
+                                    cache, out, lse), "sparse_attention");
+}
+
+kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const void* x_l, const void* w_qkv,
+                              int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
+                              int32_t max_pos, const kvx_batch* batch, const int32_t* sel,
+                              const kvx_cache* cache, void* out, float* lse, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(x_l, "x_l");
+    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
+    KVX_REQUIRE(D > 0, "D must be positive");
+    if (dtype == KVX_BF16) KVX_REQUIRE(D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    if (bi.n_req > MAX_ATTN_REQ)
+        return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
+    if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
+    size_t need = 0;
+    kvx_recompute_attn_workspace(dtype, batch, H_q, H_kv, d_h, &need);
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(sel, "sel");
+    KVX_REQUIRE_PTR(out, "out");
+    if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "recompute_attn needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    KVX_TRY_HIP(run_qkv(s, dtype, x_l, w_qkv, D, (H_q + 2 * H_kv) * d_h, batch, bi, sel, ws), "recompute qkv");
+    KVX_TRY_HIP(run_scatter(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache), "rope_scatter");
+    return hip_status(run_attention(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse),
+                      "attention");
 }
 
 }  // extern "C"

@@ -65,6 +65,11 @@ _SIGS = {
                                      _I32),
     "kvx_recompute_attn": ([_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
                             ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P, _P, _P, _SZ], _I32),
+    "kvx_qkv_project": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P, _P], _I32),
+    "kvx_rope_scatter": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
+                          ctypes.POINTER(_Cache)], _I32),
+    "kvx_sparse_attention": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
+                              ctypes.POINTER(_Cache), _P, _P], _I32),
 }
 
 _lib = None
@@ -297,3 +302,31 @@ def recompute_attn(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int,
         ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c),
         _ptr(out), _ptr(lse), _ptr(ws), ws.numel()))
     return out[:batch.total_sel]
+
+
+def qkv_project(x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, batch: Batch,
+                sel: torch.Tensor, qkv: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dev = x_l.device
+    n_qkv = (H_q + 2 * H_kv) * d_h
+    if qkv is None:
+        qkv = torch.empty((max(batch.total_sel, 1), n_qkv), dtype=x_l.dtype, device=dev)
+    _check("kvx_qkv_project", lib().kvx_qkv_project(_stream(dev), _dtype(x_l), _ptr(x_l), _ptr(w_qkv), x_l.shape[1],
+                                                    H_q, H_kv, d_h, ctypes.byref(batch.c),
+                                                    _ptr(sel) if sel.numel() else None, _ptr(qkv)))
+    return qkv
+
+
+def rope_scatter(layer: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, rope: torch.Tensor, batch: Batch,
+                 sel: torch.Tensor, cache: Cache):
+    _check("kvx_rope_scatter", lib().kvx_rope_scatter(_stream(qkv.device), _dtype(qkv), layer, _ptr(qkv), H_q, H_kv,
+                                                      d_h, _ptr(rope), rope.shape[0], ctypes.byref(batch.c),
+                                                      _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c)))
+
+
+def sparse_attention(layer: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, rope: torch.Tensor,
+                     batch: Batch, sel: torch.Tensor, cache: Cache, out: torch.Tensor,
+                     lse: Optional[torch.Tensor] = None):
+    _check("kvx_sparse_attention", lib().kvx_sparse_attention(
+        _stream(qkv.device), _dtype(qkv), layer, _ptr(qkv), H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
+        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(out), _ptr(lse)))
+    return out

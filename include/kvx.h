@@ -193,6 +193,31 @@ KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer
                               const kvx_cache* cache, void* out, float* lse, void* ws,
                               size_t ws_bytes);
 
+/* The three steps of kvx_recompute_attn as separate calls (same kernels, same work), for
+ * callers that schedule or time them individually.
+ *
+ * kvx_qkv_project: step 1, qkv (device, out) [cu_sel[n_req]][n_qkv] in the storage dtype,
+ *   row i = W_qkv x_l[cu_tokens[b] + sel[i]] (not rotated).  bf16 needs D % 64 == 0. */
+KVX_API kvx_status kvx_qkv_project(void* stream, int32_t dtype, const void* x_l, const void* w_qkv,
+                                   int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h,
+                                   const kvx_batch* batch, const int32_t* sel, void* qkv);
+
+/* kvx_rope_scatter: steps 2-3, rotate the k part of every qkv row at its true position and
+ * write k and v into layer `layer` of the cache (slots of the selected positions). */
+KVX_API kvx_status kvx_rope_scatter(void* stream, int32_t dtype, int32_t layer, const void* qkv,
+                                    int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
+                                    int32_t max_pos, const kvx_batch* batch, const int32_t* sel,
+                                    const kvx_cache* cache);
+
+/* kvx_sparse_attention: step 4, causal attention of the selected queries (the q part of
+ * the qkv rows, rotated at their true positions inside the kernel) over layer `layer` of
+ * the cache; out and lse as in kvx_recompute_attn.  d_h must be 64 or 128. */
+KVX_API kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, const void* qkv,
+                                        int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
+                                        int32_t max_pos, const kvx_batch* batch,
+                                        const int32_t* sel, const kvx_cache* cache, void* out,
+                                        float* lse);
+
 #ifdef __cplusplus
 }
 #endif
