@@ -12,10 +12,17 @@
 //  * O^T = V^T P^T: P comes straight from the S^T registers (bf16), V^T fragments are read
 //    from the row-major V tile with ds_read_b64_tr_b16, and the output rows stay lane-local,
 //    so the rescale by exp2(m_old - m_new) needs no cross-lane traffic.
-//  * K and V tiles are double-buffered in LDS with per-row XOR-swizzled 16-byte chunks; the
-//    next tile is loaded into registers while the current one is consumed.
-//  * q is rotated (rotate-half, table angles at the query's true position) while it is
-//    loaded; k was rotated when it was scattered into the cache.
+//  * K and V tiles are double-buffered in LDS with per-row XOR-swizzled 16-byte chunks and
+//    arrive by direct global -> LDS loads (global_load_lds_dwordx4): each wave fills whole
+//    1 KB blocks, every lane fetching the chunk that belongs at its slot; the next tile's
+//    loads are in flight while the current tile is consumed.  Keys past the request's end
+//    load key 0 instead (finite data; such keys are always masked).
+//  * q is rotated (rotate-half, table angles at the query's true position) and scaled by
+//    log2(e)/sqrt(d_h) while it is loaded; k was rotated when it was scattered into the cache.
+//  * VALU work per tile is kept small: the causal mask is applied only on tiles that reach
+//    past the smallest query position of the wave, and the running max is updated lazily:
+//    O and the row sum are rescaled only when some row's max grows by more than 2^8 (the
+//    ratio O / l does not depend on which max is used; p stays below 2^8).
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
 //    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
 #include "kvx_internal.h"
@@ -39,9 +46,10 @@ void attn_bf16_kernel(AttnArgs a) {
     constexpr int QC = D_H / 16;               // 16-deep k-steps of S^T = K Q^T
     constexpr int DB = D_H / 32;               // 32-wide output blocks
     constexpr int TILE = KT * D_H;             // elements of one K (or V) tile
-    constexpr int CHUNKS = 2 * KT * NCH;       // K and V chunks per tile
-    constexpr int CPT = (CHUNKS + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) bf16 lds[2][2 * TILE];
+    constexpr int KPB = 1024 / (2 * D_H);      // keys per 1 KB block
+    constexpr int NBLK = 2 * TILE * 2 / 1024;  // 1 KB blocks of a K+V tile
+    __shared__ __attribute__((aligned(1024))) bf16 lds0[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 lds1[2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hf = lane >> 5, lr = lane & 31;
@@ -73,7 +81,8 @@ void attn_bf16_kernel(AttnArgs a) {
     const int h = hk * g + hh;
     const int p_row = valid ? a.sel[i0 + qi] : p_max;
 
-    // ---- rotated Q fragments (B operand: row lr, dims 16c + 8hf + e)
+    // ---- rotated, scaled Q fragments (B operand: row lr, dims 16c + 8hf + e)
+    const float sl2 = 1.4426950408889634f / sqrtf((float)D_H);
     bf16x8 qf[QC];
     {
         const bf16* qrow = (const bf16*)a.qkv + (int64_t)(i0 + (valid ? qi : 0)) * a.ld + (int64_t)h * D_H;
@@ -98,43 +107,51 @@ void attn_bf16_kernel(AttnArgs a) {
                     const int e = 2 * e2 + u;
                     const float co = u ? t.z : t.x, si = u ? t.w : t.y;
                     const float x1 = (float)qf[c][e], x2 = (float)qf[c + HC][e];
-                    qf[c][e] = (bf16)(x1 * co - x2 * si);
-                    qf[c + HC][e] = (bf16)(x2 * co + x1 * si);
+                    qf[c][e] = (bf16)((x1 * co - x2 * si) * sl2);
+                    qf[c + HC][e] = (bf16)((x2 * co + x1 * si) * sl2);
                 }
             }
         }
     }
 
-    // ---- K/V tile staging
+    // ---- K/V tile staging: block q of a tile holds KPB consecutive keys of K (q < NBLK/2) or V
     const bf16* kbase = (const bf16*)a.kc;
-    const bf16* vbase = (const bf16*)a.vc;
-    uint4 pre[CPT];
-    auto gload = [&](int kt) {
+    const int64_t vdelta = (const bf16*)a.vc - kbase;   // V addressed relative to K
+    // slots of the keys first (page-table loads complete before any of the tile's direct
+    // loads is issued), then the direct loads themselves
+    constexpr int NBW = (NBLK + W - 1) / W;   // blocks per wave
+    const int tok0 = a.slots.cu_tok[b];
+    const int32_t* ptab = a.slots.page_table + (int64_t)b * a.slots.max_pages;
+    const int psz = a.slots.page_size, psh = a.slots.page_shift;
+    const bool paged = a.slots.paged != 0;
+    auto issue = [&](bf16* st, int kt) {
+        int64_t off[NBW];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int idx = tid + c * NT;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (idx < CHUNKS) {
-                const int kv = idx / (KT * NCH);
-                const int kk = (idx / NCH) % KT, ch = idx % NCH;
-                const int j = kt * KT + kk;
-                if (j < T_b) {
-                    const int64_t slot = a.slots.slot(b, j);
-                    const bf16* src = (kv ? vbase : kbase) + (slot * H_kv + hk) * D_H + ch * 8;
-                    v = *(const uint4*)src;
-                }
+        for (int c = 0; c < NBW; ++c) {
+            const int q = w + c * W;
+            const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+            const int key = ql * KPB + lane / NCH;
+            const int ch = (lane % NCH) ^ kv_swz<D_H>(key);
+            int j = kt * KT + key;
+            if (j >= T_b) j = 0;
+            int64_t slot;
+            if (paged) {
+                const int pi = psh >= 0 ? j >> psh : j / psz;
+                const int po = psh >= 0 ? j & (psz - 1) : j % psz;
+                slot = (int64_t)ptab[pi] * psz + po;
+            } else {
+                slot = tok0 + j;
             }
-            pre[c] = v;
+            off[c] = (slot * H_kv + hk) * D_H + ch * 8 + (kv ? vdelta : 0);
         }
-    };
-    auto lstore = [&](int stage) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int idx = tid + c * NT;
-            if (idx < CHUNKS) {
-                const int kv = idx / (KT * NCH);
-                const int kk = (idx / NCH) % KT, ch = idx % NCH;
-                *(uint4*)(&lds[stage][kv * TILE + kk * D_H + ((ch ^ kv_swz<D_H>(kk)) << 3)]) = pre[c];
+        for (int c = 0; c < NBW; ++c) {
+            const int q = w + c * W;
+            if (NBLK % W == 0 || q < NBLK) {
+                const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                __builtin_amdgcn_global_load_lds((const void*)(kbase + off[c]),
+                                                 (__attribute__((address_space(3))) void*)(st + kv * TILE + ql * 512),
+                                                 16, 0, 0);
             }
         }
     };
@@ -145,19 +162,14 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = 1.4426950408889634f / sqrtf((float)D_H);
+    // smallest query position of this wave: tiles ending at or below it need no mask
+    int p_min = p_row;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) p_min = min(p_min, __shfl_xor(p_min, o));
 
     const int n_tiles = p_max / KT + 1;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        const int stage = kt & 1;
-        if (kt + 1 < n_tiles) gload(kt + 1);
-        const bf16* lk = &lds[stage][0];
-        const bf16* lv = &lds[stage][TILE];
-
+    auto compute = [&](const bf16* lk, int kt) {
+        const bf16* lv = lk + TILE;
         // S^T for the two 32-key halves of the tile
         f32x16 sacc[2];
 #pragma unroll
@@ -172,38 +184,48 @@ void attn_bf16_kernel(AttnArgs a) {
             }
         }
 
-        // online softmax in the log2 domain
-        float mx = -INFINITY;
-        const int jbase = kt * KT + 4 * hf;
+        // online softmax in the log2 domain (q carries the scale)
+        if (kt * KT + KT - 1 > p_min) {          // tile crosses a row's position (rare)
+            asm volatile("");                     // keep this a branch, not per-element selects
+            const int jbase = kt * KT + 4 * hf;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = jbase + kb * 32 + 8 * (i >> 2) + (i & 3);
+                    if (j > p_row) sacc[kb][i] = -INFINITY;
+                }
+        }
+        float mx = sacc[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = jbase + kb * 32 + 8 * (i >> 2) + (i & 3);
-                const float x = j <= p_row ? sacc[kb][i] * sl2 : -INFINITY;
-                sacc[kb][i] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        const bool grow = mx > m_run + 8.f;
+        if (__any(grow)) {                        // some row's max grew by > 2^8 (rare)
+            asm volatile("");
+            const float m_new = grow ? mx : m_run;
+            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= corr;
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
+        }
         float rs = 0.f;
         bf16x8 pf[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float pv = __builtin_amdgcn_exp2f(sacc[kb][i] - m_new);
+                const float pv = __builtin_amdgcn_exp2f(sacc[kb][i] - m_run);
                 rs += pv;
                 pf[kb][i >> 3][i & 7] = (bf16)pv;
             }
         rs += __shfl_xor(rs, 32);
-        l_run = l_run * corr + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int d = 0; d < DB; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
+        l_run += rs;
 
         // O^T += V^T P^T
         const int G = lane >> 4, gi = lane & 15;
@@ -229,9 +251,22 @@ void attn_bf16_kernel(AttnArgs a) {
                 }
             }
         }
+    };
 
-        if (kt + 1 < n_tiles) lstore(stage ^ 1);
+    issue(lds0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < n_tiles; kt += 2) {
+        if (kt + 1 < n_tiles) issue(lds1, kt + 1);
+        compute(lds0, kt);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (kt + 1 < n_tiles) {
+            if (kt + 2 < n_tiles) issue(lds0, kt + 2);
+            compute(lds1, kt + 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     }
 
     if (!valid) return;
@@ -255,10 +290,10 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)a.n_blocks * a.H_kv));
     switch (W) {
         case 3: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 3>), grid, dim3(3 * 64), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 4>), grid, dim3(4 * 64), 0, s, a); break;
         case 5: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 5>), grid, dim3(5 * 64), 0, s, a); break;
         case 6: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 6>), grid, dim3(6 * 64), 0, s, a); break;
         case 7: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 7>), grid, dim3(7 * 64), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8>), grid, dim3(8 * 64), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -266,10 +301,10 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
 
 }  // namespace
 
-// Rows per workgroup are 32 per wave: 4 waves when g divides 128, else g waves of 32 queries.
+// Rows per workgroup are 32 per wave: 8 waves when g divides 256, else g waves of 32 queries.
 int attn_bf16_block_queries(int g) {
     if (g <= 0) return 0;
-    if (128 % g == 0 && g <= 16) return 128 / g;
+    if (256 % g == 0 && g <= 16) return 256 / g;
     if (g <= 7) return 32;
     return 0;
 }

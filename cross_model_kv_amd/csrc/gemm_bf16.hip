@@ -3,14 +3,18 @@
 // Both operands are K-contiguous (weights are stored output-major), so every 16-byte global
 // load feeds one LDS chunk and every MFMA operand is one 16-byte LDS read.
 //
-//  * 256x256x64 block tile, 4 waves in 2x2, each wave a 128x128 tile of 8x8
-//    v_mfma_f32_16x16x32_bf16 blocks (256 fp32 accumulators per lane).
-//  * LDS holds two stages of A and B ([256 rows][8 chunks of 16 B] each, 128 KB in total);
-//    chunks are XOR-swizzled per row so the 16-lane fragment reads hit distinct banks.
-//    The next K tile is loaded into registers while the current one feeds the MFMAs.
-//  * B fragment j of lane l reads tile row (l%16)*8 + j, so after the K loop each lane
-//    holds 8 consecutive output columns of every row it owns: the epilogue writes 16-byte
-//    chunks with no LDS staging.
+//  * Block tiles of 256 x 256 x 64 with 8 waves (two per SIMD, so one wave's LDS waits hide
+//    behind the other's MFMAs), each wave a 64 x 128 grid of v_mfma_f32_16x16x32_bf16 blocks.
+//  * Tiles travel global -> LDS with direct loads (global_load_lds_dwordx4): every wave
+//    fills whole 1 KB blocks of the stage, each lane fetching the chunk that belongs at its
+//    slot of the XOR-swizzled layout.  No VGPRs hold the next tile; the two LDS stages are
+//    separate objects so the next tile's loads stay in flight while the current one is read.
+//  * Row pointers of the gathered A rows and of the B rows are computed once per block;
+//    rows past M or N are clamped to row 0 (their outputs are never stored), so the K loop
+//    has no branches.
+//  * B fragment j of lane l reads tile row (l%16)*FN + j, so after the K loop each lane
+//    holds FN consecutive output columns of every row it owns: the epilogue writes 8- or
+//    16-byte chunks with no LDS staging.
 //  * Rows of A can be gathered (selected or complement positions of a ragged batch), and
 //    the epilogue can write a plain matrix, the K/V cache of a layer (contiguous or paged
 //    slots), or per-row partial sums of C[m][n] * Z[m][n] (the score quadratic form).
@@ -21,16 +25,7 @@
 namespace kvx {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WM = 2, WN = 2;
-constexpr int NTH = WM * WN * 64;
-constexpr int WTM = BM / WM, WTN = BN / WN;
-constexpr int FM = WTM / 16, FN = WTN / 16;
-constexpr int A_CH = BM * 8 / NTH;   // 16-byte chunks per thread per A tile
-constexpr int B_CH = BN * 8 / NTH;
-constexpr int TILE_ELEMS = (BM + BN) * BK;
-
-static_assert(FN == 8, "the epilogue writes 8 consecutive bf16 columns per lane");
+constexpr int BK = 64;
 
 struct Tile { int group, tm, tn; };
 
@@ -48,9 +43,21 @@ __device__ __forceinline__ Tile tile_of(int bid, int mt, int nt, int groups, boo
     return t;
 }
 
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
-    __shared__ __attribute__((aligned(16))) bf16 lds[2 * TILE_ELEMS];
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int A_I = BM / 8 / NW;     // 1 KB direct loads per wave per A tile
+    constexpr int B_I = BN / 8 / NW;
+    static_assert(A_I * NW * 8 == BM && B_I * NW * 8 == BN, "tiles split into whole 1 KB blocks per wave");
+    static_assert(FN == 4 || FN == 8, "lanes own 4 or 8 consecutive output columns");
+    constexpr int STAGE = (BM + BN) * BK;
+    __shared__ __attribute__((aligned(1024))) bf16 lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) bf16 lds1[STAGE];
     __shared__ int s_src[BM];
     __shared__ int64_t s_slot[BM];
     __shared__ float s_red[WN][BM];
@@ -62,8 +69,8 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
     const int m0 = t.tm * BM, n0 = t.tn * BN;
 
     // ---- row map: source row of every tile row, and its cache slot
-    if (tid < BM) {
-        const int m = m0 + tid;
+    for (int r = tid; r < BM; r += NW * 64) {
+        const int m = m0 + r;
         int src = -1;
         int64_t slot = 0;
         if (m < a.M) {
@@ -71,45 +78,39 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
             src = ri.src;
             if (a.epi == EPI_CACHE) slot = a.slots.slot(ri.b, ri.pos);
         }
-        s_src[tid] = src;
-        s_slot[tid] = slot;
+        s_src[r] = src;
+        s_slot[r] = slot;
     }
     __syncthreads();
 
+    // ---- per-lane sources of the direct loads: lane owns LDS chunk P = (c*NW + wave)*64 + lane
     const bf16* Bg = a.B + (int64_t)t.group * a.b_group_stride;
-    const int nk = a.K / BK;
-
-    uint4 ra[A_CH], rb[B_CH];
-    auto gload = [&](int kt) {
+    const bf16* asrc[A_I];
+    const bf16* bsrc[B_I];
+#pragma unroll
+    for (int c = 0; c < A_I; ++c) {
+        const int P = (c * NW + wave) * 64 + lane;
+        const int row = P >> 3, ch = (P & 7) ^ swz(row);
+        const int src = max(s_src[row], 0);
+        asrc[c] = a.A + (int64_t)src * a.lda + ch * 8;
+    }
+#pragma unroll
+    for (int c = 0; c < B_I; ++c) {
+        const int P = (c * NW + wave) * 64 + lane;
+        const int row = P >> 3, ch = (P & 7) ^ swz(row / FN);
+        const int n = n0 + row < a.N ? n0 + row : 0;
+        bsrc[c] = Bg + (int64_t)n * a.ldb + ch * 8;
+    }
+    auto issue = [&](bf16* st, int kt) {
         const int ka = (kt * BK) % a.K_a;
 #pragma unroll
-        for (int c = 0; c < A_CH; ++c) {
-            const int idx = tid + c * NTH, row = idx >> 3, ch = idx & 7;
-            const int src = s_src[row];
-            ra[c] = src >= 0 ? *(const uint4*)(a.A + (int64_t)src * a.lda + ka + ch * 8)
-                             : make_uint4(0, 0, 0, 0);
-        }
+        for (int c = 0; c < A_I; ++c)
+            __builtin_amdgcn_global_load_lds((const void*)(asrc[c] + ka),
+                                             (lds_ptr_t)(st + (c * NW + wave) * 512), 16, 0, 0);
 #pragma unroll
-        for (int c = 0; c < B_CH; ++c) {
-            const int idx = tid + c * NTH, row = idx >> 3, ch = idx & 7;
-            const int n = n0 + row;
-            rb[c] = n < a.N ? *(const uint4*)(Bg + (int64_t)n * a.ldb + kt * BK + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto lstore = [&](int stage) {
-        bf16* la = lds + stage * TILE_ELEMS;
-        bf16* lb = la + BM * BK;
-#pragma unroll
-        for (int c = 0; c < A_CH; ++c) {
-            const int idx = tid + c * NTH, row = idx >> 3, ch = idx & 7;
-            *(uint4*)(la + row * BK + ((ch ^ swz(row)) << 3)) = ra[c];
-        }
-#pragma unroll
-        for (int c = 0; c < B_CH; ++c) {
-            const int idx = tid + c * NTH, row = idx >> 3, ch = idx & 7;
-            *(uint4*)(lb + row * BK + ((ch ^ swz(row / FN)) << 3)) = rb[c];
-        }
+        for (int c = 0; c < B_I; ++c)
+            __builtin_amdgcn_global_load_lds((const void*)(bsrc[c] + kt * BK),
+                                             (lds_ptr_t)(st + BM * BK + (c * NW + wave) * 512), 16, 0, 0);
     };
 
     f32x4 acc[FM][FN];
@@ -118,16 +119,10 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
     const int lr = lane & 15, lq = lane >> 4;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int stage = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const bf16* la = lds + stage * TILE_ELEMS;
-        const bf16* lb = la + BM * BK;
+    auto compute = [&](const bf16* st) {
+        const bf16* la = st;
+        const bf16* lb = st + BM * BK;
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
             const int ch = ks * 4 + lq;
@@ -137,20 +132,42 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
                 const int nl = wn * WTN + lr * FN + j;
                 bfr[j] = *(const bf16x8*)(lb + nl * BK + ((ch ^ swz(nl / FN)) << 3));
             }
+            bf16x8 afr[2];
+            {
+                const int ml = wm * WTM + lr;
+                afr[0] = *(const bf16x8*)(la + ml * BK + ((ch ^ swz(ml)) << 3));
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int ml = wm * WTM + i * 16 + lr;
-                const bf16x8 afr = *(const bf16x8*)(la + ml * BK + ((ch ^ swz(ml)) << 3));
+                if (i + 1 < FM) {
+                    const int ml = wm * WTM + (i + 1) * 16 + lr;
+                    afr[(i + 1) & 1] = *(const bf16x8*)(la + ml * BK + ((ch ^ swz(ml)) << 3));
+                }
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i & 1], bfr[j], acc[i][j], 0, 0, 0);
             }
         }
-        if (kt + 1 < nk) lstore(stage ^ 1);
+    };
+
+    const int nk = a.K / BK;
+    issue(lds0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        if (kt + 1 < nk) issue(lds1, kt + 1);
+        compute(lds0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (kt + 1 < nk) {
+            if (kt + 2 < nk) issue(lds0, kt + 2);
+            compute(lds1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     }
 
-    // ---- epilogue: lane owns rows wm*WTM + i*16 + 4*lq + v and columns nl0 .. nl0+7
+    // ---- epilogue: lane owns rows wm*WTM + i*16 + 4*lq + v and columns nl0 .. nl0+FN-1
     const int nl0 = wn * WTN + lr * FN;
     const int ng = n0 + nl0;
     if (a.epi == EPI_SCORE) {
@@ -162,9 +179,9 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
                 const int src = s_src[ml];
                 float p = 0.f;
                 if (src >= 0 && ng < a.N) {
-                    const bf16x8 z = *(const bf16x8*)(a.Z + (int64_t)src * a.ldz + ng);
+                    const bf16* zr = a.Z + (int64_t)src * a.ldz + ng;
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) p += acc[i][j][v] * (float)z[j];
+                    for (int j = 0; j < FN; ++j) p += acc[i][j][v] * (float)zr[j];
                 }
                 p += __shfl_xor(p, 1);
                 p += __shfl_xor(p, 2);
@@ -174,22 +191,24 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
             }
         }
         __syncthreads();
-        if (tid < BM && m0 + tid < a.M) {
+        for (int r = tid; r < BM; r += NW * 64) {
+            if (m0 + r >= a.M) continue;
             float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < WN; ++w) s += s_red[w][tid];
-            a.partial[(int64_t)t.tn * a.M + m0 + tid] = s;
+            for (int w = 0; w < WN; ++w) s += s_red[w][r];
+            a.partial[(int64_t)t.tn * a.M + m0 + r] = s;
         }
         return;
     }
     if (ng >= a.N) return;
+    typedef __bf16 vecN __attribute__((ext_vector_type(FN)));
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int ml = wm * WTM + i * 16 + 4 * lq + v;
             if (s_src[ml] < 0) continue;
-            bf16x8 o;
+            vecN o;
 #pragma unroll
             for (int j = 0; j < FN; ++j) o[j] = (bf16)acc[i][j][v];
             bf16* dst;
@@ -200,23 +219,25 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
                 dst = (is_k ? a.kc : a.vc) + (int64_t)t.group * a.layer_elems +
                       s_slot[ml] * a.hd + (is_k ? ng : ng - a.hd);
             }
-            *(bf16x8*)dst = o;
+            *(vecN*)dst = o;
         }
     }
 }
 
 }  // namespace
 
-int gemm_bf16_block_n() { return BN; }
+// Score partial sums are written per 256-column block of the output.
+int gemm_bf16_block_n() { return 256; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
-    const int mt = cdiv(a.M, BM), nt = cdiv(a.N, BN);
-    const int64_t total = (int64_t)mt * nt * a.groups;
-    if (total == 0) return hipSuccess;
+    const int mt = cdiv(a.M, 256);
+    if ((int64_t)mt * a.groups == 0 || a.N == 0) return hipSuccess;
     // read the larger operand once: keep tiles that share its panel on one XCD
     const double a_bytes = (double)a.M * a.K_a, b_bytes = (double)a.N * a.K * a.groups;
     const int n_major = b_bytes > a_bytes ? 1 : 0;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)total), dim3(NTH), 0, s, a, mt, nt, n_major);
+    const int64_t tiles = (int64_t)mt * cdiv(a.N, 256) * a.groups;
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)tiles), dim3(512), 0, s, a, mt,
+                       cdiv(a.N, 256), n_major);
     return hipGetLastError();
 }
 

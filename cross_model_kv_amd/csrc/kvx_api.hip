@@ -157,6 +157,9 @@ SlotMap slot_map(const kvx_cache* c, const kvx_batch* bt) {
     s.page_table = s.paged ? c->page_table : nullptr;
     s.max_pages = s.paged ? c->max_pages : 0;
     s.page_size = s.paged ? c->page_size : 1;
+    s.page_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == s.page_size) s.page_shift = sh;
     return s;
 }
 

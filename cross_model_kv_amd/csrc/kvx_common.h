@@ -43,11 +43,14 @@ struct SlotMap {
     const int32_t* page_table;  // device [n_req][max_pages] (paged) or null
     int32_t max_pages;
     int32_t page_size;
+    int32_t page_shift;         // log2(page_size) when it is a power of two, else -1
     int32_t paged;
     __device__ __forceinline__ int64_t slot(int b, int p) const {
         if (paged) {
-            int pg = page_table[(int64_t)b * max_pages + p / page_size];
-            return (int64_t)pg * page_size + p % page_size;
+            const int pi = page_shift >= 0 ? p >> page_shift : p / page_size;
+            const int po = page_shift >= 0 ? p & (page_size - 1) : p % page_size;
+            const int pg = page_table[(int64_t)b * max_pages + pi];
+            return (int64_t)pg * page_size + po;
         }
         return (int64_t)cu_tok[b] + p;
     }
