@@ -32,9 +32,12 @@ namespace {
 
 constexpr int KT = 64;   // keys per tile
 
+// Chunk swizzle of the K/V tiles, chosen by measuring gfx950 LDS throughput for both reads
+// of a tile: ds_read_b128 of 32 consecutive keys (K) and ds_read_b64_tr_b16 of 8 keys x 64 B
+// (V).  For 8-chunk rows (d_h = 64) the 16-row pattern swizzle is used.
 template <int D_H>
 __device__ __forceinline__ int kv_swz(int key) {
-    if constexpr (D_H == 128) return key & 15;
+    if constexpr (D_H == 128) return (key & 15) ^ ((key & 3) << 2);
     else return swz(key);
 }
 

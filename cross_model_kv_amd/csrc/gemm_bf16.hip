@@ -12,9 +12,10 @@
 //  * Row pointers of the gathered A rows and of the B rows are computed once per block;
 //    rows past M or N are clamped to row 0 (their outputs are never stored), so the K loop
 //    has no branches.
-//  * B fragment j of lane l reads tile row (l%16)*FN + j, so after the K loop each lane
-//    holds FN consecutive output columns of every row it owns: the epilogue writes 8- or
-//    16-byte chunks with no LDS staging.
+//  * B fragment j of lane l is tile row (l%16)*FN + j, so after the K loop each lane holds
+//    FN consecutive output columns of every row it owns: the epilogue writes 8- or 16-byte
+//    chunks with no LDS staging.  In LDS that row is stored at row j*16 + l%16 of the wave's
+//    slab, so a fragment read touches 16 consecutive LDS rows (the conflict-free pattern).
 //  * Rows of A can be gathered (selected or complement positions of a ragged batch), and
 //    the epilogue can write a plain matrix, the K/V cache of a layer (contiguous or paged
 //    slots), or per-row partial sums of C[m][n] * Z[m][n] (the score quadratic form).
@@ -97,7 +98,9 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
 #pragma unroll
     for (int c = 0; c < B_I; ++c) {
         const int P = (c * NW + wave) * 64 + lane;
-        const int row = P >> 3, ch = (P & 7) ^ swz(row / FN);
+        const int R = P >> 3, ch = (P & 7) ^ swz(R);          // LDS row R of the B stage
+        const int slab = R / WTN, rl = R % WTN;               // rl = j*16 + s  <->  tile row s*FN + j
+        const int row = slab * WTN + (rl % 16) * FN + rl / 16;
         const int n = n0 + row < a.N ? n0 + row : 0;
         bsrc[c] = Bg + (int64_t)n * a.ldb + ch * 8;
     }
@@ -129,8 +132,8 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
             bf16x8 bfr[FN];
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int nl = wn * WTN + lr * FN + j;
-                bfr[j] = *(const bf16x8*)(lb + nl * BK + ((ch ^ swz(nl / FN)) << 3));
+                const int R = wn * WTN + j * 16 + lr;
+                bfr[j] = *(const bf16x8*)(lb + R * BK + ((ch ^ swz(R)) << 3));
             }
             bf16x8 afr[2];
             {
