@@ -15,6 +15,7 @@ of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,6 +32,7 @@ METRIC = "handoff tokens/s (map+select+recompute-attn) at 16K; % of MFMA/HBM roo
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_8B-to-32B-T16384.json")
+ATTN_SOURCE = os.path.join(ROOT, "cross_model_kv_amd", "csrc", "attn_bf16.hip")
 
 
 def log(msg):
@@ -230,9 +232,14 @@ def main():
     att_t = avg_launch_ms["sparse_attention"] * 1e-3
     achieved = work["sparse_attention"]["flops"] / att_t / 1e12
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(TRAFFIC_FILE) and wl.name == "8B-to-32B-shape-T16384":
+        # HBM bytes counted by rocprofv3 (FETCH_SIZE, WRITE_SIZE scaled by a 1 GiB copy); valid only for
+        # the kernel source they were counted on
         with open(TRAFFIC_FILE) as f:
-            traffic = json.load(f).get("hbm_bytes_per_launch")
+            rec = json.load(f)
+        with open(ATTN_SOURCE, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() == rec.get("kernel_source_sha256"):
+                traffic = rec.get("hbm_bytes_per_launch")
     line = {
         "metric": METRIC,
         "value": T * args.steps / elapsed,
