@@ -127,7 +127,26 @@ void attn_bf16_kernel(AttnArgs a) {
     const int32_t* ptab = a.slots.page_table + (int64_t)b * a.slots.max_pages;
     const int psz = a.slots.page_size, psh = a.slots.page_shift;
     const bool paged = a.slots.paged != 0;
+    // when W divides 16 every block of the wave sits a lane-independent distance from the
+    // wave's first block (same swizzle, keys a multiple of 16 apart): one lane address serves all
+    constexpr bool UNIFORM = 16 % W == 0;
+    const int key0 = (w % (NBLK / 2)) * KPB + lane / NCH;
+    const bf16* src0 = kbase + ((int64_t)(tok0 + key0) * H_kv + hk) * D_H + (((lane % NCH) ^ kv_swz<D_H>(key0)) << 3);
+    const int64_t tile_stride = (int64_t)KT * H_kv * D_H;
     auto issue = [&](bf16* st, int kt) {
+        if (UNIFORM && !paged && (kt + 1) * KT <= T_b) {
+            const bf16* base = src0 + kt * tile_stride;
+#pragma unroll
+            for (int c = 0; c < NBW; ++c) {
+                const int q = w + c * W;
+                const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                const int64_t d = (int64_t)(ql - w % (NBLK / 2)) * KPB * H_kv * D_H + (kv ? vdelta : 0);
+                __builtin_amdgcn_global_load_lds((const void*)(base + d),
+                                                 (__attribute__((address_space(3))) void*)(st + kv * TILE + ql * 512),
+                                                 16, 0, 0);
+            }
+            return;
+        }
         int64_t off[NBW];
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
@@ -171,6 +190,11 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int o = 32; o > 0; o >>= 1) p_min = min(p_min, __shfl_xor(p_min, o));
 
     const int n_tiles = p_max / KT + 1;
+    // value held by lane ^ 32 (the other 16 keys of each row's 32-key half tile)
+    auto other_half = [&](float x) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return hf ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+    };
     auto compute = [&](const bf16* lk, int kt) {
         const bf16* lv = lk + TILE;
         // S^T for the two 32-key halves of the tile
@@ -204,7 +228,7 @@ void attn_bf16_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, other_half(mx));
         const bool grow = mx > m_run + 8.f;
         if (__any(grow)) {                        // some row's max grew by > 2^8 (rare)
             asm volatile("");
@@ -227,7 +251,7 @@ void attn_bf16_kernel(AttnArgs a) {
                 rs += pv;
                 pf[kb][i >> 3][i & 7] = (bf16)pv;
             }
-        rs += __shfl_xor(rs, 32);
+        rs += other_half(rs);
         l_run += rs;
 
         // O^T += V^T P^T
