@@ -19,8 +19,10 @@
 //  * Rows of A can be gathered (selected or complement positions of a ragged batch), and
 //    the epilogue can write a plain matrix, the K/V cache of a layer (contiguous or paged
 //    slots), or per-row partial sums of C[m][n] * Z[m][n] (the score quadratic form).
-//  * Tiles are numbered so that every XCD (workgroup i runs on XCD i % 8) owns one
-//    contiguous range of tiles; tiles that share the larger operand's panel share an L2.
+//  * Tiles are numbered so that every XCD owns one contiguous range of tiles, walked in
+//    groups of row panels sized so the tiles in flight on an XCD share operand panels in L2.
+#include <algorithm>
+
 #include "kvx_common.h"
 
 namespace kvx {
@@ -30,17 +32,26 @@ constexpr int BK = 64;
 
 struct Tile { int group, tm, tn; };
 
-__device__ __forceinline__ Tile tile_of(int bid, int mt, int nt, int groups, bool n_major) {
-    const int per_group = mt * nt;
-    const int total = per_group * groups;
+// Tile order.  Every XCD (workgroup i runs on XCD i % 8) owns one contiguous range of the linear
+// tile index, and its 32 CUs run consecutive indices together.  The linear index walks groups
+// of gm row panels: inside a group the row panel varies fastest, then the column panel (the
+// columns of all groups side by side), so the 32 tiles in flight on an XCD share gm row panels
+// and 32/gm column panels of their operands in that XCD's L2.
+__device__ __forceinline__ Tile tile_of(int bid, int mt, int nt, int groups, int gm) {
+    const int cols = nt * groups;
+    const int total = mt * cols;
     const int xcd = bid & 7, j = bid >> 3;
     const int per = total >> 3, rem = total & 7;
     const int lin = xcd * per + min(xcd, rem) + j;
+    const int band = lin / (gm * cols);
+    const int m0 = band * gm;
+    const int g = min(mt - m0, gm);
+    const int r = lin - band * gm * cols;
+    const int cp = r / g;
     Tile t;
-    t.group = lin / per_group;
-    const int r = lin - t.group * per_group;
-    if (n_major) { t.tn = r / mt; t.tm = r - t.tn * mt; }
-    else         { t.tm = r / nt; t.tn = r - t.tm * nt; }
+    t.tm = m0 + (r - cp * g);
+    t.group = cp / nt;
+    t.tn = cp - t.group * nt;
     return t;
 }
 
@@ -48,7 +59,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
-void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
+void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -66,7 +77,7 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const Tile t = tile_of(blockIdx.x, mt, nt, a.groups, n_major != 0);
+    const Tile t = tile_of(blockIdx.x, mt, nt, a.groups, gm);
     const int m0 = t.tm * BM, n0 = t.tn * BN;
 
     // ---- row map: source row of every tile row, and its cache slot
@@ -232,15 +243,31 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int n_major) {
 // Score partial sums are written per 256-column block of the output.
 int gemm_bf16_block_n() { return 256; }
 
+// Row-panel group size of the tile order: the one that fetches the fewest operand panel bytes
+// per window of 32 concurrent tiles (an XCD's share of one round).
+static int pick_group_rows(int mt, int cols, double a_panel, double b_panel) {
+    int best = 1;
+    double best_bytes = 0.0;
+    for (int gm = 1; gm <= 32; gm *= 2) {
+        const int rows_w = std::min(gm, mt);
+        const int cols_w = std::min(cols, std::max(1, 32 / rows_w));
+        const int rows_eff = std::min(mt, std::max(rows_w, 32 / cols_w));
+        const double bytes = rows_eff * a_panel + cols_w * b_panel;
+        if (gm == 1 || bytes < best_bytes) { best = gm; best_bytes = bytes; }
+    }
+    return best;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     const int mt = cdiv(a.M, 256);
     if ((int64_t)mt * a.groups == 0 || a.N == 0) return hipSuccess;
-    // read the larger operand once: keep tiles that share its panel on one XCD
-    const double a_bytes = (double)a.M * a.K_a, b_bytes = (double)a.N * a.K * a.groups;
-    const int n_major = b_bytes > a_bytes ? 1 : 0;
-    const int64_t tiles = (int64_t)mt * cdiv(a.N, 256) * a.groups;
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)tiles), dim3(512), 0, s, a, mt,
-                       cdiv(a.N, 256), n_major);
+    const int nt = cdiv(a.N, 256);
+    // A row operand shared by several groups (the per-layer reconstruction) is small next to the
+    // groups' weights: walking all row panels first streams each weight panel through an XCD
+    // once while the row operand stays resident in the last-level cache (measured fastest).
+    const int gm = a.groups > 1 ? mt : pick_group_rows(mt, nt * a.groups, 256.0 * a.K_a, 256.0 * a.K);
+    const int64_t tiles = (int64_t)mt * nt * a.groups;
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)tiles), dim3(512), 0, s, a, mt, nt, gm);
     return hipGetLastError();
 }
 
