@@ -164,6 +164,7 @@ def main():
     T = wl.T
     k = h.batch.total_sel
     qkv = h.ws_attn[: k * wl.n_qkv * 2].view(torch.bfloat16).view(k, wl.n_qkv)
+    ws_qkv = h.ws_attn[(k * wl.n_qkv * 2 + 255) // 256 * 256:]     # the projection's split-tail workspace
     stream = torch.cuda.current_stream(dev)
 
     names = ["map_latent", "score_select", "reconstruct", "qkv_project", "rope_scatter", "sparse_attention"]
@@ -182,7 +183,7 @@ def main():
         h.reconstruct()
         mark("reconstruct")
         for l in range(wl.L_t):
-            kvx.qkv_project(inp.x_l[l], inp.w_qkv[l], wl.H_q, wl.H_kv, wl.d_h, h.batch, h.S, qkv)
+            kvx.qkv_project(inp.x_l[l], inp.w_qkv[l], wl.H_q, wl.H_kv, wl.d_h, h.batch, h.S, qkv, ws_qkv)
             mark("qkv_project")
             kvx.rope_scatter(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache)
             mark("rope_scatter")

@@ -22,6 +22,7 @@
 //  * Tiles are numbered so that every XCD owns one contiguous range of tiles, walked in
 //    groups of row panels sized so the tiles in flight on an XCD share operand panels in L2.
 #include <algorithm>
+#include <climits>
 
 #include "kvx_common.h"
 
@@ -37,12 +38,8 @@ struct Tile { int group, tm, tn; };
 // of gm row panels: inside a group the row panel varies fastest, then the column panel (the
 // columns of all groups side by side), so the 32 tiles in flight on an XCD share gm row panels
 // and 32/gm column panels of their operands in that XCD's L2.
-__device__ __forceinline__ Tile tile_of(int bid, int mt, int nt, int groups, int gm) {
+__device__ __forceinline__ Tile tile_at(int lin, int mt, int nt, int groups, int gm) {
     const int cols = nt * groups;
-    const int total = mt * cols;
-    const int xcd = bid & 7, j = bid >> 3;
-    const int per = total >> 3, rem = total & 7;
-    const int lin = xcd * per + min(xcd, rem) + j;
     const int band = lin / (gm * cols);
     const int m0 = band * gm;
     const int g = min(mt - m0, gm);
@@ -55,11 +52,24 @@ __device__ __forceinline__ Tile tile_of(int bid, int mt, int nt, int groups, int
     return t;
 }
 
+// linear tile index of workgroup bid among `total` tiles: XCD x owns one contiguous range
+__device__ __forceinline__ int xcd_linear(int bid, int total) {
+    const int xcd = bid & 7, j = bid >> 3;
+    const int per = total >> 3, rem = total & 7;
+    return xcd * per + min(xcd, rem) + j;
+}
+
+// Split tail.  When the last round of tiles would leave most CUs idle, the workgroups past
+// the whole rounds each take one K slice of a tail tile and write its fp32 partial tile; a
+// second kernel adds the slices in order and stores the result (deterministic).
+constexpr int CU_COUNT = 256;             // MI355X compute units
+struct SplitPlan { int full, rem, split; };
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
-void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm) {
+void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -77,7 +87,14 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const Tile t = tile_of(blockIdx.x, mt, nt, a.groups, gm);
+    const int nk_all = a.K / BK;
+    const int bid = blockIdx.x;
+    const bool tail = bid >= sp.full;                 // a K slice of a tail tile
+    const int unit = bid - sp.full;
+    const Tile t = tail ? tile_at(sp.full + unit / sp.split, mt, nt, a.groups, gm)
+                        : tile_at(xcd_linear(bid, sp.full), mt, nt, a.groups, gm);
+    const int k_first = tail ? (unit % sp.split) * (nk_all / sp.split) : 0;
+    const int nk = tail ? nk_all / sp.split : nk_all;
     const int m0 = t.tm * BM, n0 = t.tn * BN;
 
     // ---- row map: source row of every tile row, and its cache slot
@@ -164,17 +181,16 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm) {
         }
     };
 
-    const int nk = a.K / BK;
-    issue(lds0, 0);
+    issue(lds0, k_first);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nk; kt += 2) {
-        if (kt + 1 < nk) issue(lds1, kt + 1);
+        if (kt + 1 < nk) issue(lds1, k_first + kt + 1);
         compute(lds0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (kt + 1 < nk) {
-            if (kt + 2 < nk) issue(lds0, kt + 2);
+            if (kt + 2 < nk) issue(lds0, k_first + kt + 2);
             compute(lds1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -184,6 +200,20 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm) {
     // ---- epilogue: lane owns rows wm*WTM + i*16 + 4*lq + v and columns nl0 .. nl0+FN-1
     const int nl0 = wn * WTN + lr * FN;
     const int ng = n0 + nl0;
+    if (tail) {                               // fp32 partial tile [BM][BN] of this K slice
+        float* pt = a.split_ws + (int64_t)unit * BM * BN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ml = wm * WTM + i * 16 + 4 * lq + v;
+#pragma unroll
+                for (int j = 0; j < FN; j += 4)
+                    *(f32x4*)(pt + ml * BN + nl0 + j) =
+                        f32x4{acc[i][j][v], acc[i][j + 1][v], acc[i][j + 2][v], acc[i][j + 3][v]};
+            }
+        return;
+    }
     if (a.epi == EPI_SCORE) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -238,10 +268,63 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm) {
     }
 }
 
+// C rows of the tail tiles: out = sum over the K slices, in slice order.  One thread per 8
+// consecutive columns of one tile row.
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
+    const int tile = blockIdx.y;
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 8;      // element of the 256 x 256 tile
+    const int ml = e >> 8, nl = e & 255;
+    const Tile t = tile_at(sp.full + tile, mt, nt, a.groups, gm);
+    const int m = t.tm * 256 + ml, n = t.tn * 256 + nl;
+    if (m >= a.M || n >= a.N) return;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float* p = a.split_ws + (int64_t)tile * sp.split * 65536 + e;
+    for (int k = 0; k < sp.split; ++k) {
+        const f32x4 x0 = *(const f32x4*)(p + (int64_t)k * 65536);
+        const f32x4 x1 = *(const f32x4*)(p + (int64_t)k * 65536 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { s[i] += x0[i]; s[4 + i] += x1[i]; }
+    }
+    bf16* dst = a.C + (int64_t)m * a.ldc + n;
+    if (n + 8 <= a.N) {
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (bf16)s[i];
+        *(bf16x8*)dst = o;
+    } else {
+        for (int i = 0; i < a.N - n; ++i) dst[i] = (bf16)s[i];
+    }
+}
+
+// Split of the last round: only for a plain store, and only when that round is at most half
+// full; K slices of at least 4 k-tiles each, so that the tail units fill (nearly) one round.
+SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
+    const int64_t tiles = (int64_t)cdiv(M, 256) * cdiv(N, 256) * groups;
+    SplitPlan sp{(int)tiles, 0, 1};
+    if (epi != EPI_STORE || groups != 1 || tiles > INT32_MAX) return sp;
+    const int rem = (int)(tiles % CU_COUNT);
+    const int nk = K / BK;
+    if (rem == 0 || rem > CU_COUNT / 2) return sp;
+    for (int split = 8; split >= 2; split /= 2) {
+        if (split * rem <= CU_COUNT && nk % split == 0 && nk / split >= 4) {
+            sp.full = (int)tiles - rem;
+            sp.rem = rem;
+            sp.split = split;
+            return sp;
+        }
+    }
+    return sp;
+}
+
 }  // namespace
 
 // Score partial sums are written per 256-column block of the output.
 int gemm_bf16_block_n() { return 256; }
+
+size_t gemm_bf16_split_bytes(int M, int N, int K, int groups, int epi) {
+    const SplitPlan sp = plan_split(M, N, K, groups, epi);
+    return sp.rem ? (size_t)sp.rem * sp.split * 65536 * sizeof(float) : 0;
+}
 
 // Row-panel group size of the tile order: the one that fetches the fewest operand panel bytes
 // per window of 32 concurrent tiles (an XCD's share of one round).
@@ -266,8 +349,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     // groups' weights: walking all row panels first streams each weight panel through an XCD
     // once while the row operand stays resident in the last-level cache (measured fastest).
     const int gm = a.groups > 1 ? mt : pick_group_rows(mt, nt * a.groups, 256.0 * a.K_a, 256.0 * a.K);
-    const int64_t tiles = (int64_t)mt * nt * a.groups;
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)tiles), dim3(512), 0, s, a, mt, nt, gm);
+    SplitPlan sp = plan_split(a.M, a.N, a.K, a.groups, a.epi);
+    if (sp.rem && !a.split_ws) sp = SplitPlan{sp.full + sp.rem, 0, 1};   // no workspace: whole tiles
+    const int64_t grid = (int64_t)sp.full + (int64_t)sp.rem * sp.split;
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)grid), dim3(512), 0, s, a, mt, nt, gm, sp);
+    if (sp.rem) {
+        if (hipError_t e = hipGetLastError()) return e;
+        hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3(65536 / (256 * 8), sp.rem), dim3(256), 0, s, a, mt, nt, gm, sp);
+    }
     return hipGetLastError();
 }
 

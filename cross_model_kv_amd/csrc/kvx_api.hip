@@ -45,6 +45,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace of the gathered QKV projection: the K-slice partials of its split tail (bf16 only).
+size_t qkv_split_bytes(int32_t dtype, int64_t n_sel, int32_t D, int n_qkv) {
+    if (dtype != KVX_BF16 || n_sel == 0 || n_sel > INT32_MAX) return 0;
+    return round256(gemm_bf16_split_bytes((int)n_sel, n_qkv, D, 1, EPI_STORE));
+}
+
+
 bool debug_checks() {
     static const int on = [] {
         const char* v = getenv("KVX_DEBUG");
@@ -398,14 +405,28 @@ kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_t max_po
     return hip_status(launch_rope_table(base, d_h, max_pos, table, (hipStream_t)stream), "rope_table");
 }
 
-kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, int32_t H_q, int32_t H_kv,
-                                        int32_t d_h, size_t* bytes) {
+kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, int32_t D, int32_t H_q,
+                                        int32_t H_kv, int32_t d_h, size_t* bytes) {
     if (kvx_status st = check_dtype(dtype)) return st;
     BatchInfo bi;
     if (kvx_status st = check_batch(batch, &bi)) return st;
     KVX_REQUIRE(bytes, "bytes must not be null");
     KVX_REQUIRE(H_q > 0 && H_kv > 0 && d_h > 0, "H_q, H_kv and d_h must be positive");
-    *bytes = round256((size_t)bi.n_sel * (H_q + 2 * H_kv) * d_h * elem_size(dtype));
+    KVX_REQUIRE(D > 0, "D must be positive");
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    *bytes = round256((size_t)bi.n_sel * n_qkv * elem_size(dtype)) + qkv_split_bytes(dtype, bi.n_sel, D, n_qkv);
+    return ok();
+}
+
+kvx_status kvx_qkv_project_workspace(int32_t dtype, const kvx_batch* batch, int32_t D, int32_t H_q, int32_t H_kv,
+                                     int32_t d_h, size_t* bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(H_q > 0 && H_kv > 0 && d_h > 0, "H_q, H_kv and d_h must be positive");
+    KVX_REQUIRE(D > 0, "D must be positive");
+    *bytes = qkv_split_bytes(dtype, bi.n_sel, D, (H_q + 2 * H_kv) * d_h);
     return ok();
 }
 
@@ -447,7 +468,7 @@ RowMap sel_rows(const kvx_batch* batch, const int32_t* sel, int n_req) {
 }
 
 hipError_t run_qkv(hipStream_t s, int32_t dtype, const void* x_l, const void* w_qkv, int32_t D, int n_qkv,
-                   const kvx_batch* batch, const BatchInfo& bi, const int32_t* sel, void* qkv) {
+                   const kvx_batch* batch, const BatchInfo& bi, const int32_t* sel, void* qkv, void* split_ws) {
     const RowMap rm = sel_rows(batch, sel, bi.n_req);
     if (dtype == KVX_BF16) {
         GemmArgs a{};
@@ -456,6 +477,7 @@ hipError_t run_qkv(hipStream_t s, int32_t dtype, const void* x_l, const void* w_
         a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
         a.rows = rm;
         a.epi = EPI_STORE; a.C = (bf16*)qkv; a.ldc = n_qkv;
+        a.split_ws = (float*)split_ws;
         return launch_gemm_bf16(a, s);
     }
     GemmF32Args a{};
@@ -521,7 +543,7 @@ extern "C" {
 
 kvx_status kvx_qkv_project(void* stream, int32_t dtype, const void* x_l, const void* w_qkv, int32_t D,
                            int32_t H_q, int32_t H_kv, int32_t d_h, const kvx_batch* batch, const int32_t* sel,
-                           void* qkv) {
+                           void* qkv, void* ws, size_t ws_bytes) {
     if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
     BatchInfo bi;
     if (kvx_status st = check_batch(batch, &bi)) return st;
@@ -533,8 +555,13 @@ kvx_status kvx_qkv_project(void* stream, int32_t dtype, const void* x_l, const v
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
     KVX_REQUIRE_PTR(sel, "sel");
     KVX_REQUIRE_PTR(qkv, "qkv");
-    return hip_status(run_qkv((hipStream_t)stream, dtype, x_l, w_qkv, D, (H_q + 2 * H_kv) * d_h, batch, bi, sel,
-                              qkv), "qkv_project");
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    const size_t need = qkv_split_bytes(dtype, bi.n_sel, D, n_qkv);
+    if (need && (!ws || ws_bytes < need))
+        return fail(KVX_ERR_WORKSPACE, "qkv_project needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (need) KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    return hip_status(run_qkv((hipStream_t)stream, dtype, x_l, w_qkv, D, n_qkv, batch, bi, sel, qkv, need ? ws : nullptr),
+                      "qkv_project");
 }
 
 kvx_status kvx_rope_scatter(void* stream, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
@@ -585,7 +612,7 @@ kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const 
         return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
     if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
     size_t need = 0;
-    kvx_recompute_attn_workspace(dtype, batch, H_q, H_kv, d_h, &need);
+    kvx_recompute_attn_workspace(dtype, batch, D, H_q, H_kv, d_h, &need);
     if (bi.n_sel == 0) return ok();
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
     KVX_REQUIRE_PTR(sel, "sel");
@@ -595,7 +622,10 @@ kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const 
         return fail(KVX_ERR_WORKSPACE, "recompute_attn needs %zu workspace bytes (got %zu)", need, ws_bytes);
     KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
-    KVX_TRY_HIP(run_qkv(s, dtype, x_l, w_qkv, D, (H_q + 2 * H_kv) * d_h, batch, bi, sel, ws), "recompute qkv");
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    const size_t qkv_bytes = round256((size_t)bi.n_sel * n_qkv * elem_size(dtype));
+    void* split_ws = qkv_split_bytes(dtype, bi.n_sel, D, n_qkv) ? (char*)ws + qkv_bytes : nullptr;
+    KVX_TRY_HIP(run_qkv(s, dtype, x_l, w_qkv, D, n_qkv, batch, bi, sel, ws, split_ws), "recompute qkv");
     KVX_TRY_HIP(run_scatter(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache), "rope_scatter");
     return hip_status(run_attention(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse),
                       "attention");

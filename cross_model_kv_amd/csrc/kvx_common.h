@@ -117,9 +117,14 @@ struct GemmArgs {
     bf16* kc; bf16* vc; int64_t layer_elems; int32_t hd; SlotMap slots;
     // EPI_SCORE: partial[n_block][m] = sum_{n in block} C[m][n] * Z[m][n]
     float* partial; const bf16* Z; int64_t ldz;
+    // EPI_STORE with a split tail (see gemm_bf16_split_bytes): fp32 workspace of the K slices
+    float* split_ws;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 int gemm_bf16_block_n();
+// Workspace bytes the bf16 GEMM needs to split its last, partly filled round of tiles along K
+// (EPI_STORE, one group); 0 when it runs without a split.
+size_t gemm_bf16_split_bytes(int M, int N, int K, int groups, int epi);
 
 }  // namespace kvx

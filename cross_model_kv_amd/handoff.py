@@ -35,7 +35,7 @@ class Handoff:
         self.rest = torch.empty(max(self.batch.total_rest, 1), dtype=torch.int32, device=self.device)
         self.ws_score = torch.empty(max(kvx.score_select_workspace(kvx._dtype(self.z), wl.r, N), 16),
                                     dtype=torch.uint8, device=self.device)
-        self.ws_attn = torch.empty(max(kvx.recompute_attn_workspace(kvx._dtype(self.z), self.batch, wl.H_q,
+        self.ws_attn = torch.empty(max(kvx.recompute_attn_workspace(kvx._dtype(self.z), self.batch, wl.D, wl.H_q,
                                                                     wl.H_kv, wl.d_h), 16),
                                    dtype=torch.uint8, device=self.device)
         if wl.paged:

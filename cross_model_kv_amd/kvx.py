@@ -61,11 +61,14 @@ _SIGS = {
     "kvx_reconstruct": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P,
                          ctypes.POINTER(_Cache)], _I32),
     "kvx_rope_table": ([_P, ctypes.c_double, _I32, _I32, _P], _I32),
-    "kvx_recompute_attn_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, ctypes.POINTER(_SZ)],
+    "kvx_recompute_attn_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
                                      _I32),
+    "kvx_qkv_project_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
+                                  _I32),
     "kvx_recompute_attn": ([_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
                             ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P, _P, _P, _SZ], _I32),
-    "kvx_qkv_project": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P, _P], _I32),
+    "kvx_qkv_project": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P, _P, _P, _SZ],
+                        _I32),
     "kvx_rope_scatter": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
                           ctypes.POINTER(_Cache)], _I32),
     "kvx_sparse_attention": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
@@ -278,10 +281,17 @@ def rope_table(base: float, d_h: int, max_pos: int, device) -> torch.Tensor:
     return t
 
 
-def recompute_attn_workspace(dtype: int, batch: Batch, H_q: int, H_kv: int, d_h: int) -> int:
+def recompute_attn_workspace(dtype: int, batch: Batch, D: int, H_q: int, H_kv: int, d_h: int) -> int:
     b = _SZ()
     _check("kvx_recompute_attn_workspace",
-           lib().kvx_recompute_attn_workspace(dtype, ctypes.byref(batch.c), H_q, H_kv, d_h, ctypes.byref(b)))
+           lib().kvx_recompute_attn_workspace(dtype, ctypes.byref(batch.c), D, H_q, H_kv, d_h, ctypes.byref(b)))
+    return b.value
+
+
+def qkv_project_workspace(dtype: int, batch: Batch, D: int, H_q: int, H_kv: int, d_h: int) -> int:
+    b = _SZ()
+    _check("kvx_qkv_project_workspace",
+           lib().kvx_qkv_project_workspace(dtype, ctypes.byref(batch.c), D, H_q, H_kv, d_h, ctypes.byref(b)))
     return b.value
 
 
@@ -292,7 +302,7 @@ def recompute_attn(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int,
     dev = x_l.device
     dt = _dtype(x_l)
     D = x_l.shape[1]
-    need = recompute_attn_workspace(dt, batch, H_q, H_kv, d_h)
+    need = recompute_attn_workspace(dt, batch, D, H_q, H_kv, d_h)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if out is None:
@@ -305,14 +315,21 @@ def recompute_attn(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int,
 
 
 def qkv_project(x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, batch: Batch,
-                sel: torch.Tensor, qkv: Optional[torch.Tensor] = None) -> torch.Tensor:
+                sel: torch.Tensor, qkv: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     dev = x_l.device
+    dt = _dtype(x_l)
+    D = x_l.shape[1]
     n_qkv = (H_q + 2 * H_kv) * d_h
     if qkv is None:
         qkv = torch.empty((max(batch.total_sel, 1), n_qkv), dtype=x_l.dtype, device=dev)
-    _check("kvx_qkv_project", lib().kvx_qkv_project(_stream(dev), _dtype(x_l), _ptr(x_l), _ptr(w_qkv), x_l.shape[1],
+    need = qkv_project_workspace(dt, batch, D, H_q, H_kv, d_h)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("kvx_qkv_project", lib().kvx_qkv_project(_stream(dev), dt, _ptr(x_l), _ptr(w_qkv), D,
                                                     H_q, H_kv, d_h, ctypes.byref(batch.c),
-                                                    _ptr(sel) if sel.numel() else None, _ptr(qkv)))
+                                                    _ptr(sel) if sel.numel() else None, _ptr(qkv),
+                                                    _ptr(ws) if need else None, ws.numel() if need else 0))
     return qkv
 
 

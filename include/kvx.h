@@ -183,9 +183,10 @@ KVX_API kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_
  *   with max_pos > every T_b; sel (device) [cu_sel[n_req]]; out (device, out)
  *   [cu_sel[n_req]][H_q][d_h]; lse (device, out, nullable) [cu_sel[n_req]][H_q] fp32.
  *   d_h must be 64 or 128, H_q % H_kv == 0, H_q / H_kv <= 16; bf16 needs D % 64 == 0.
- *   ws (device) of kvx_recompute_attn_workspace() bytes. */
-KVX_API kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, int32_t H_q,
-                                        int32_t H_kv, int32_t d_h, size_t* bytes);
+ *   ws (device) of kvx_recompute_attn_workspace() bytes (the qkv rows, then the
+ *   workspace of kvx_qkv_project). */
+KVX_API kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, int32_t D,
+                                        int32_t H_q, int32_t H_kv, int32_t d_h, size_t* bytes);
 KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const void* x_l,
                               const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv,
                               int32_t d_h, const float* rope, int32_t max_pos,
@@ -197,10 +198,18 @@ KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer
  * callers that schedule or time them individually.
  *
  * kvx_qkv_project: step 1, qkv (device, out) [cu_sel[n_req]][n_qkv] in the storage dtype,
- *   row i = W_qkv x_l[cu_tokens[b] + sel[i]] (not rotated).  bf16 needs D % 64 == 0. */
+ *   row i = W_qkv x_l[cu_tokens[b] + sel[i]] (not rotated).  bf16 needs D % 64 == 0.
+ *   ws (device): kvx_qkv_project_workspace() bytes, fp32 partial sums of the K slices of
+ *   the projection's last, partly filled round of tiles (the GPU's compute units split
+ *   those tiles along D and the slices are added in a fixed order, so results do not
+ *   depend on timing).  When the size is 0, ws may be NULL; a smaller non-zero ws_bytes
+ *   is KVX_ERR_WORKSPACE. */
+KVX_API kvx_status kvx_qkv_project_workspace(int32_t dtype, const kvx_batch* batch, int32_t D,
+                                             int32_t H_q, int32_t H_kv, int32_t d_h, size_t* bytes);
 KVX_API kvx_status kvx_qkv_project(void* stream, int32_t dtype, const void* x_l, const void* w_qkv,
                                    int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h,
-                                   const kvx_batch* batch, const int32_t* sel, void* qkv);
+                                   const kvx_batch* batch, const int32_t* sel, void* qkv,
+                                   void* ws, size_t ws_bytes);
 
 /* kvx_rope_scatter: steps 2-3, rotate the k part of every qkv row at its true position and
  * write k and v into layer `layer` of the cache (slots of the selected positions). */

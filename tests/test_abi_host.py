@@ -155,7 +155,7 @@ def test_recompute_attn_validation():
     bt = FakeBatch([100, 50], [30, 15])
     c = cache()
     need = ctypes.c_size_t()
-    assert L.kvx_recompute_attn_workspace(1, ctypes.byref(bt.c), 8, 2, 64, ctypes.byref(need)) == 0
+    assert L.kvx_recompute_attn_workspace(1, ctypes.byref(bt.c), 256, 8, 2, 64, ctypes.byref(need)) == 0
     assert need.value >= 45 * 12 * 64 * 2
 
     def call(dtype=1, layer=0, D=256, H_q=8, H_kv=2, d_h=64, max_pos=100, cc=c, ws=A16, wsb=None):

@@ -7,6 +7,8 @@ outputs need a minimum row cosine of 0.999.  Selection is bit-exact where it is 
 by exact scores (fp32 path, select-only cases) and exact outside the band of near-ties
 that bf16 rounding of the latent can swap otherwise.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -326,6 +328,8 @@ RECOMPUTE_CASES = {
     "bf16-g8-batched-paged": small("rc-bf16-batched", H_q=16, H_kv=2, n_req=4, t_min=20, t_max=900,
                                    pct_choices=(20, 30, 40), paged=True),
     "f32-g4": small("rc-f32-g4", dtype="f32", H_q=8, H_kv=2, d_h=64, T=300, pct=30),
+    # D = 2048: the projection's tiles fill under half a round, so they are split along D
+    "bf16-g4-wide-D": small("rc-bf16-wide-D", H_q=8, H_kv=2, d_h=64, D=2048, T=600, pct=40),
 }
 
 
@@ -379,3 +383,31 @@ def test_recompute_attn_stagewise(name):
             assert cos >= 0.999
             assert_close(o, o_ref, tol, "attention output")
             assert np.abs(lse_all[cs[b]:cs[b + 1]] - lse_ref).max() <= (1e-4 if wl.dtype == "f32" else 2e-2)
+
+
+def test_qkv_split_tail():
+    """The gathered projection with its last round split along D (fp32 K-slice partials added
+    in a fixed order): matches the oracle's projection (positions 0: no rotation), repeats
+    bit for bit, and refuses a too-small workspace."""
+    wl = RECOMPUTE_CASES["bf16-g4-wide-D"]
+    say(f"[qkv split] {wl.name}")
+    inp = synth.generate(wl, 71, DEV)
+    batch = kvx.Batch.for_budgets(inp.lengths, inp.pcts, DEV)
+    S = synth.random_subset(inp.lengths[0], batch.n_sel[0], 71)
+    sel = torch.from_numpy(S.astype(np.int32)).to(DEV)
+    need = kvx.qkv_project_workspace(kvx.BF16, batch, wl.D, wl.H_q, wl.H_kv, wl.d_h)
+    assert need > 0, "this shape should take the split path"
+    q1 = kvx.qkv_project(inp.x_l[0], inp.w_qkv[0], wl.H_q, wl.H_kv, wl.d_h, batch, sel)
+    q2 = kvx.qkv_project(inp.x_l[0], inp.w_qkv[0], wl.H_q, wl.H_kv, wl.d_h, batch, sel)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2)
+    x_rows = f64(inp.x_l[0])[S]
+    q, k, v = O.recompute_qkv(x_rows, f64(inp.w_qkv[0]), np.zeros_like(S), wl.H_q, wl.H_kv, wl.d_h, wl.rope_base)
+    ref = np.concatenate([q.reshape(len(S), -1), k.reshape(len(S), -1), v.reshape(len(S), -1)], axis=1)
+    assert_close(f64(q1[:len(S)]), ref, 2e-2, "split projection")
+    small_ws = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    qkv = torch.empty_like(q1)
+    with pytest.raises(kvx.KvxError):
+        kvx._check("kvx_qkv_project", kvx.lib().kvx_qkv_project(
+            kvx._stream(DEV), kvx.BF16, kvx._ptr(inp.x_l[0]), kvx._ptr(inp.w_qkv[0]), wl.D, wl.H_q, wl.H_kv, wl.d_h,
+            ctypes.byref(batch.c), kvx._ptr(sel), kvx._ptr(qkv), kvx._ptr(small_ws), small_ws.numel()))
