@@ -113,8 +113,8 @@ def cpu_baseline(inp, wl, S, T, k, pos_sum):
     parts["sparse_attention"] = dt * pos_sum / float(np.sum(sel_rows[qi] + 1)) * wl.L_t
     total = sum(parts.values())
     return {"value": T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": ("fp64 numpy oracle on the 16K workload: map 512 rows, reconstruct+score 256 rows x 64 "
-                       "layers, full select, 1 layer of qkv (512 rows), scatter, attention (24 queries); "
+            "sample": (f"fp64 numpy oracle on the {wl.name} workload: map 512 rows, reconstruct+score 256 rows "
+                       f"x {wl.L_t} layers, full select, 1 layer of qkv (512 rows), scatter, attention (24 queries); "
                        "each part scaled to one handoff (rows, layers, sum of causal lengths)"),
             "seconds_per_handoff": total, "parts_s": {k2: round(v2, 4) for k2, v2 in parts.items()}}
 
@@ -153,15 +153,13 @@ def main():
     from cross_model_kv_amd.handoff import Handoff
 
     wl = workloads.ALL[args.workload]
-    if wl.batched:
-        raise SystemExit("bench.py times single-request workloads")
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     inp = synth.generate(wl, args.seed, dev)
     h = Handoff(inp, dev)
     torch.cuda.synchronize()
     log(f"[bench] {wl.name}: inputs and one-time preparation {time.perf_counter() - t_gen:.1f}s")
-    T = wl.T
+    T = h.batch.n_tokens           # all positions of the batch (one request: T)
     k = h.batch.total_sel
     qkv = h.ws_attn[: k * wl.n_qkv * 2].view(torch.bfloat16).view(k, wl.n_qkv)
     ws_qkv = h.ws_attn[(k * wl.n_qkv * 2 + 255) // 256 * 256:]     # the projection's split-tail workspace
@@ -254,9 +252,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": T, "source_layers": wl.L_s, "d_src": wl.d_src, "latent_rank": wl.r,
+        "config": {"workload": wl.name, "T": T, "requests": h.batch.n_req, "source_layers": wl.L_s,
+                   "d_src": wl.d_src, "latent_rank": wl.r,
                    "target_layers": wl.L_t, "H_q": wl.H_q, "H_kv": wl.H_kv, "d_h": wl.d_h, "D": wl.D,
-                   "calibration_rank": wl.c, "budget_pct": wl.pct, "selected": k, "parallelism": "none"},
+                   "calibration_rank": wl.c, "budget_pct": list(h.inp.pcts) if wl.batched else wl.pct,
+                   "selected": k, "cache": "paged" if wl.paged else "contiguous", "parallelism": "none"},
         "roofline": {"kernel": "sparse_attention", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "algorithmic_flops_per_launch": work["sparse_attention"]["flops"],

@@ -31,6 +31,7 @@ namespace kvx {
 namespace {
 
 constexpr int KT = 64;   // keys per tile
+constexpr int PT_MAX = 2048;   // page-table entries staged in LDS (longer requests read it from HBM)
 
 // Chunk swizzle of the K/V tiles, chosen by measuring gfx950 LDS throughput for both reads
 // of a tile: ds_read_b128 of 32 consecutive keys (K) and ds_read_b64_tr_b16 of 8 keys x 64 B
@@ -53,6 +54,7 @@ void attn_bf16_kernel(AttnArgs a) {
     constexpr int NBLK = 2 * TILE * 2 / 1024;  // 1 KB blocks of a K+V tile
     __shared__ __attribute__((aligned(1024))) bf16 lds0[2 * TILE];
     __shared__ __attribute__((aligned(1024))) bf16 lds1[2 * TILE];
+    __shared__ int32_t s_pt[PT_MAX];           // the request's page table (paged caches)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hf = lane >> 5, lr = lane & 31;
@@ -127,6 +129,13 @@ void attn_bf16_kernel(AttnArgs a) {
     const int32_t* ptab = a.slots.page_table + (int64_t)b * a.slots.max_pages;
     const int psz = a.slots.page_size, psh = a.slots.page_shift;
     const bool paged = a.slots.paged != 0;
+    // the pages this block's tiles touch, staged in LDS once (made visible by the first barrier)
+    const int n_tiles_pt = p_max / KT + 1;
+    const int n_pages = !paged ? 0 : psh >= 0 ? ((min(n_tiles_pt * KT, T_b) - 1) >> psh) + 1
+                                               : (min(n_tiles_pt * KT, T_b) - 1) / psz + 1;
+    const bool pt_lds = n_pages <= PT_MAX;
+    if (paged && pt_lds)
+        for (int i = tid; i < n_pages; i += NT) s_pt[i] = ptab[i];
     // when W divides 16 every block of the wave sits a lane-independent distance from the
     // wave's first block (same swizzle, keys a multiple of 16 apart): one lane address serves all
     constexpr bool UNIFORM = 16 % W == 0;
@@ -160,7 +169,7 @@ void attn_bf16_kernel(AttnArgs a) {
             if (paged) {
                 const int pi = psh >= 0 ? j >> psh : j / psz;
                 const int po = psh >= 0 ? j & (psz - 1) : j % psz;
-                slot = (int64_t)ptab[pi] * psz + po;
+                slot = (int64_t)(pt_lds ? s_pt[pi] : ptab[pi]) * psz + po;
             } else {
                 slot = tok0 + j;
             }
@@ -280,6 +289,7 @@ void attn_bf16_kernel(AttnArgs a) {
         }
     };
 
+    if (paged && pt_lds) __syncthreads();      // the staged page table, before the first loads
     issue(lds0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -296,24 +296,39 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
     }
 }
 
-// Split of the last round: only for a plain store, and only when that round is at most half
-// full; K slices of at least 4 k-tiles each, so that the tail units fill (nearly) one round.
+// K splits of a plain store (one group).  Time is counted in tile-times on CU_COUNT CUs:
+//   whole tiles:            ceil(tiles / CUs)
+//   split tail (split s):   floor(tiles / CUs) + ceil(rem * s / CUs) / s, rem = tiles % CUs
+//   every tile split (s):   ceil(tiles * s / CUs) / s
+// plus, for split plans, the HBM time of writing and re-reading the fp32 partial tiles
+// (512 KB per partial at ~5 TB/s) in units of one tile's compute (2*256*256*K flops at
+// ~4.7 TFLOP/s per CU, the rate these tiles reach).  The cheapest wins (ties keep fewer
+// partials); every K slice spans at least 4 k-tiles.
 SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
     const int64_t tiles = (int64_t)cdiv(M, 256) * cdiv(N, 256) * groups;
-    SplitPlan sp{(int)tiles, 0, 1};
-    if (epi != EPI_STORE || groups != 1 || tiles > INT32_MAX) return sp;
-    const int rem = (int)(tiles % CU_COUNT);
+    SplitPlan best{(int)tiles, 0, 1};
+    if (epi != EPI_STORE || groups != 1 || tiles == 0 || tiles > INT32_MAX / 8) return best;
     const int nk = K / BK;
-    if (rem == 0 || rem > CU_COUNT / 2) return sp;
-    for (int split = 8; split >= 2; split /= 2) {
-        if (split * rem <= CU_COUNT && nk % split == 0 && nk / split >= 4) {
-            sp.full = (int)tiles - rem;
-            sp.rem = rem;
-            sp.split = split;
-            return sp;
+    const int64_t cu = CU_COUNT;
+    double best_t = (double)((tiles + cu - 1) / cu);
+    int64_t best_parts = 0;
+    auto consider = [&](int full, int rem, int split) {
+        const int64_t parts = (int64_t)rem * split;
+        const double partial_s = parts * 524288.0 / 5e12;
+        const double tile_s = 2.0 * 65536.0 * K / 4.7e12;
+        const double t = (double)(full / cu) + (double)((rem * (int64_t)split + cu - 1) / cu) / split +
+                         partial_s / tile_s;
+        if (t < best_t - 1e-9 || (t < best_t + 1e-9 && best_parts && parts < best_parts)) {
+            best_t = t; best_parts = parts; best = SplitPlan{full, rem, split};
         }
+    };
+    for (int split = 2; split <= 8; split *= 2) {
+        if (nk % split != 0 || nk / split < 4) continue;
+        const int rem = (int)(tiles % cu);
+        if (rem) consider((int)(tiles - rem), rem, split);      // split the last round only
+        consider(0, (int)tiles, split);                         // split every tile
     }
-    return sp;
+    return best;
 }
 
 }  // namespace

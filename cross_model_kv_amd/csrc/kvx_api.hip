@@ -188,8 +188,17 @@ int32_t kvx_budget(int32_t T, int32_t pct) {
     return budget_of(T, pct);
 }
 
+kvx_status kvx_map_latent_workspace(int32_t dtype, int64_t n, int32_t d_src, int32_t r, size_t* bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(n >= 0 && n <= INT32_MAX, "n (%lld) must be in [0, 2^31)", (long long)n);
+    KVX_REQUIRE(d_src > 0 && r > 0, "d_src (%d) and r (%d) must be positive", d_src, r);
+    *bytes = (dtype == KVX_BF16 && n > 0) ? round256(gemm_bf16_split_bytes((int)n, r, d_src, 1, EPI_STORE)) : 0;
+    return ok();
+}
+
 kvx_status kvx_map_latent(void* stream, int32_t dtype, const void* x_src, const void* w_s, void* z,
-                          int64_t n, int32_t d_src, int32_t r) {
+                          int64_t n, int32_t d_src, int32_t r, void* ws, size_t ws_bytes) {
     if (kvx_status st = check_dtype(dtype)) return st;
     KVX_REQUIRE_PTR(x_src, "x_src");
     KVX_REQUIRE_PTR(w_s, "w_s");
@@ -201,6 +210,11 @@ kvx_status kvx_map_latent(void* stream, int32_t dtype, const void* x_src, const 
         KVX_REQUIRE(r % 8 == 0, "bf16 needs r %% 8 == 0 (got %d)", r);
     }
     if (n == 0) return ok();
+    size_t need = 0;
+    kvx_map_latent_workspace(dtype, n, d_src, r, &need);
+    if (need && (!ws || ws_bytes < need))
+        return fail(KVX_ERR_WORKSPACE, "map_latent needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (need) KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     if (dtype == KVX_BF16) {
         GemmArgs a{};
@@ -209,6 +223,7 @@ kvx_status kvx_map_latent(void* stream, int32_t dtype, const void* x_src, const 
         a.M = (int)n; a.N = r; a.K = d_src; a.groups = 1;
         a.rows.mode = 0;
         a.epi = EPI_STORE; a.C = (bf16*)z; a.ldc = r;
+        a.split_ws = need ? (float*)ws : nullptr;
         return hip_status(launch_gemm_bf16(a, s), "map_latent");
     }
     GemmF32Args a{};

@@ -33,6 +33,8 @@ class Handoff:
         self.scores = torch.empty(N, dtype=torch.float32, device=self.device)
         self.sel = torch.empty(max(self.batch.total_sel, 1), dtype=torch.int32, device=self.device)
         self.rest = torch.empty(max(self.batch.total_rest, 1), dtype=torch.int32, device=self.device)
+        self.ws_map = torch.empty(max(kvx.map_latent_workspace(kvx._dtype(self.z), N, wl.d_src, wl.r), 16),
+                                  dtype=torch.uint8, device=self.device)
         self.ws_score = torch.empty(max(kvx.score_select_workspace(kvx._dtype(self.z), wl.r, N), 16),
                                     dtype=torch.uint8, device=self.device)
         self.ws_attn = torch.empty(max(kvx.recompute_attn_workspace(kvx._dtype(self.z), self.batch, wl.D, wl.H_q,
@@ -51,7 +53,7 @@ class Handoff:
 
     # the four stages ------------------------------------------------------------------
     def map(self):
-        kvx.map_latent(self.inp.x_src, self.inp.w_s, self.z)
+        kvx.map_latent(self.inp.x_src, self.inp.w_s, self.z, self.ws_map)
 
     def select(self):
         kvx.score_select(self.z, self.op, self.batch, self.inp.pcts, ws=self.ws_score,

@@ -51,7 +51,8 @@ _SIGS = {
     "kvx_last_error": ([], ctypes.c_char_p),
     "kvx_version": ([], ctypes.c_char_p),
     "kvx_budget": ([_I32, _I32], _I32),
-    "kvx_map_latent": ([_P, _I32, _P, _P, _P, _I64, _I32, _I32], _I32),
+    "kvx_map_latent_workspace": ([_I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "kvx_map_latent": ([_P, _I32, _P, _P, _P, _I64, _I32, _I32, _P, _SZ], _I32),
     "kvx_score_prepare_workspace": ([_I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_score_prepare": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ], _I32),
     "kvx_select_topk": ([_P, _P, ctypes.POINTER(_Batch), _P, _P], _I32),
@@ -190,13 +191,24 @@ class Cache:
         return cls(k, v, n_layers, n_slots, page_table, page_size)
 
 
-def map_latent(x_src: torch.Tensor, w_s: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:
+def map_latent_workspace(dtype: int, n: int, d_src: int, r: int) -> int:
+    b = _SZ()
+    _check("kvx_map_latent_workspace", lib().kvx_map_latent_workspace(dtype, n, d_src, r, ctypes.byref(b)))
+    return b.value
+
+
+def map_latent(x_src: torch.Tensor, w_s: torch.Tensor, z: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     n, d_src = x_src.shape
     r = w_s.shape[0]
+    dt = _dtype(x_src)
     if z is None:
         z = torch.empty((n, r), dtype=x_src.dtype, device=x_src.device)
-    _check("kvx_map_latent", lib().kvx_map_latent(_stream(x_src.device), _dtype(x_src), _ptr(x_src),
-                                                  _ptr(w_s), _ptr(z), n, d_src, r))
+    need = map_latent_workspace(dt, n, d_src, r)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=x_src.device)
+    _check("kvx_map_latent", lib().kvx_map_latent(_stream(x_src.device), dt, _ptr(x_src), _ptr(w_s), _ptr(z), n,
+                                                  d_src, r, _ptr(ws) if need else None, ws.numel() if need else 0))
     return z
 
 

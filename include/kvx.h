@@ -110,12 +110,19 @@ KVX_API const char* kvx_version(void);
  * under-spent).  Returns -1 if T < 0 or pct is outside [0, 100]. */
 KVX_API int32_t kvx_budget(int32_t T, int32_t pct);
 
-/* Shared source projection (PANORAMA abstract: "shared source projection", "compact
- * latent per prompt position"):  z[t][i] = sum_c w_s[i][c] * x_src[t][c].
+/* Source side of the factorized mapper (PANORAMA abstract: one projection shared by all
+ * target layers turns each position's source KV into a short latent vector):
+ *   z[t][i] = sum_c w_s[i][c] * x_src[t][c].
  *   x_src (device) [n][d_src], w_s (device) [r][d_src], z (device, out) [n][r].
- *   bf16 needs d_src % 64 == 0 and r % 8 == 0.  No workspace. */
+ *   bf16 needs d_src % 64 == 0 and r % 8 == 0.
+ *   ws (device): kvx_map_latent_workspace() bytes.  When the product has too few output
+ *   tiles to fill the GPU, tiles are split along d_src into fp32 partial sums that a second
+ *   kernel adds in a fixed order (results do not depend on timing).  A size of 0 allows
+ *   ws = NULL; a smaller non-zero ws_bytes is KVX_ERR_WORKSPACE. */
+KVX_API kvx_status kvx_map_latent_workspace(int32_t dtype, int64_t n, int32_t d_src, int32_t r,
+                                            size_t* bytes);
 KVX_API kvx_status kvx_map_latent(void* stream, int32_t dtype, const void* x_src, const void* w_s,
-                          void* z, int64_t n, int32_t d_src, int32_t r);
+                          void* z, int64_t n, int32_t d_src, int32_t r, void* ws, size_t ws_bytes);
 
 /* Score operator of the rank-disagreement metric (RaReCache abstract: energy of the
  * mapped KV in output directions weakly supported by the calibration data).  With
@@ -199,11 +206,11 @@ KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer
  *
  * kvx_qkv_project: step 1, qkv (device, out) [cu_sel[n_req]][n_qkv] in the storage dtype,
  *   row i = W_qkv x_l[cu_tokens[b] + sel[i]] (not rotated).  bf16 needs D % 64 == 0.
- *   ws (device): kvx_qkv_project_workspace() bytes, fp32 partial sums of the K slices of
- *   the projection's last, partly filled round of tiles (the GPU's compute units split
- *   those tiles along D and the slices are added in a fixed order, so results do not
- *   depend on timing).  When the size is 0, ws may be NULL; a smaller non-zero ws_bytes
- *   is KVX_ERR_WORKSPACE. */
+ *   ws (device): kvx_qkv_project_workspace() bytes, fp32 partial sums of output tiles split
+ *   along D (the last, partly filled round of tiles, or every tile when there are too few
+ *   to fill the GPU); a second kernel adds the slices in a fixed order, so results do not
+ *   depend on timing.  When the size is 0, ws may be NULL; a smaller non-zero ws_bytes is
+ *   KVX_ERR_WORKSPACE. */
 KVX_API kvx_status kvx_qkv_project_workspace(int32_t dtype, const kvx_batch* batch, int32_t D,
                                              int32_t H_q, int32_t H_kv, int32_t d_h, size_t* bytes);
 KVX_API kvx_status kvx_qkv_project(void* stream, int32_t dtype, const void* x_l, const void* w_qkv,

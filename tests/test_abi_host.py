@@ -66,13 +66,19 @@ def status(code, expect, needle=None):
 
 def test_map_latent_validation():
     L = kvx.lib()
-    status(L.kvx_map_latent(None, 7, A16, A16, A16, 10, 64, 8), UNSUPPORTED, "dtype")
-    status(L.kvx_map_latent(None, 1, None, A16, A16, 10, 64, 8), INVALID, "x_src")
-    status(L.kvx_map_latent(None, 1, MIS, A16, A16, 10, 64, 8), INVALID, "aligned")
-    status(L.kvx_map_latent(None, 1, A16, A16, A16, -1, 64, 8), INVALID, "n")
-    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 0, 8), INVALID, "positive")
-    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 100, 8), INVALID, "d_src % 64")
-    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 64, 12), INVALID, "r % 8")
+    status(L.kvx_map_latent(None, 7, A16, A16, A16, 10, 64, 8, None, 0), UNSUPPORTED, "dtype")
+    status(L.kvx_map_latent(None, 1, None, A16, A16, 10, 64, 8, None, 0), INVALID, "x_src")
+    status(L.kvx_map_latent(None, 1, MIS, A16, A16, 10, 64, 8, None, 0), INVALID, "aligned")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, -1, 64, 8, None, 0), INVALID, "n")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 0, 8, None, 0), INVALID, "positive")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 100, 8, None, 0), INVALID, "d_src % 64")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 10, 64, 12, None, 0), INVALID, "r % 8")
+    # too few output tiles to fill the GPU: the product is split along d_src and needs a workspace
+    need = ctypes.c_size_t()
+    assert L.kvx_map_latent_workspace(1, 4096, 57344, 1024, ctypes.byref(need)) == 0 and need.value > 0
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 4096, 57344, 1024, None, 0), WORKSPACE, "workspace")
+    status(L.kvx_map_latent(None, 1, A16, A16, A16, 4096, 57344, 1024, A16, need.value - 1), WORKSPACE, "workspace")
+    assert L.kvx_map_latent_workspace(0, 4096, 57344, 1024, ctypes.byref(need)) == 0 and need.value == 0
 
 
 def test_score_prepare_validation():

@@ -411,3 +411,19 @@ def test_qkv_split_tail():
         kvx._check("kvx_qkv_project", kvx.lib().kvx_qkv_project(
             kvx._stream(DEV), kvx.BF16, kvx._ptr(inp.x_l[0]), kvx._ptr(inp.w_qkv[0]), wl.D, wl.H_q, wl.H_kv, wl.d_h,
             ctypes.byref(batch.c), kvx._ptr(sel), kvx._ptr(qkv), kvx._ptr(small_ws), small_ws.numel()))
+
+
+def test_map_split_all_tiles():
+    """A projection with far fewer output tiles than compute units splits every tile along
+    d_src (fp32 slices added in a fixed order): matches the oracle, repeats bit for bit."""
+    n, d_src, r = 1000, 4096, 512
+    say(f"[map split] n={n} d_src={d_src} r={r}")
+    need = kvx.map_latent_workspace(kvx.BF16, n, d_src, r)
+    assert need > 0, "this shape should take the split path"
+    x = synth.latent(n, d_src, 81, dtype=torch.bfloat16, device=DEV)
+    w = (synth.latent(r, d_src, 82, dtype=torch.float32, device=DEV) / np.sqrt(d_src)).to(torch.bfloat16)
+    z1 = kvx.map_latent(x, w)
+    z2 = kvx.map_latent(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(z1, z2)
+    assert_close(f64(z1), O.map_latent(f64(x), f64(w)), 2e-2, "split map")
