@@ -19,10 +19,14 @@
 //    load key 0 instead (finite data; such keys are always masked).
 //  * q is rotated (rotate-half, table angles at the query's true position) and scaled by
 //    log2(e)/sqrt(d_h) while it is loaded; k was rotated when it was scattered into the cache.
-//  * VALU work per tile is kept small: the causal mask is applied only on tiles that reach
-//    past the smallest query position of the wave, and the running max is updated lazily:
-//    O and the row sum are rescaled only when some row's max grows by more than 2^8 (the
-//    ratio O / l does not depend on which max is used; p stays below 2^8).
+//  * VALU work per tile is kept small, because on gfx950 a wave's VALU instructions do not
+//    overlap its own MFMAs: the causal mask runs only on tiles that reach past the smallest
+//    query position of the wave; the scores leave the MFMAs already shifted by a reference
+//    maximum (the accumulators start at -m_ref); the row sum is a packed bf16 dot product of
+//    the rounded P that the MFMA consumes (so O and l use the same weights), kept per lane
+//    until the end.  The common tile is exp2, bf16 packing and 16 dot products; only when a
+//    lane sum exceeds 2^16 (a score far above m_ref) does a slow path take the true maximum
+//    and rescale O and l (the ratio O / l does not depend on the reference used).
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
 //    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
 #include "kvx_internal.h"
@@ -192,7 +196,17 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    // Online softmax with a reference maximum m_ref (log2 domain; q carries the scale).  The
+    // scores come out of the MFMAs already shifted by -m_ref (the accumulators start at
+    // -m_ref), so the common tile costs only exp2, the bf16 packing and a packed-dot row sum.
+    // m_ref is always a maximum some earlier tile reached, and a tile is accepted only if its
+    // lane sums stay <= 2^16 (so every p <= 2^16 and the row's mass stays >= 1); otherwise the
+    // rare slow path takes the tile's true maximum and rescales O and l.
+    float m_ref = 0.f, l_lane = 0.f;           // l_lane: this lane's half of the row sum
+    bool have_ref = false;
+    f32x16 negm;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = 0.f;
     // smallest query position of this wave: tiles ending at or below it need no mask
     int p_min = p_row;
 #pragma unroll
@@ -204,23 +218,22 @@ void attn_bf16_kernel(AttnArgs a) {
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
         return hf ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
     };
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
     auto compute = [&](const bf16* lk, int kt) {
         const bf16* lv = lk + TILE;
-        // S^T for the two 32-key halves of the tile
+        // S^T - m_ref for the two 32-key halves of the tile
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
             const int key = kb * 32 + lr;
+            sacc[kb] = negm;
 #pragma unroll
             for (int c = 0; c < QC; ++c) {
                 const bf16x8 kf = *(const bf16x8*)(lk + key * D_H + (((2 * c + hf) ^ kv_swz<D_H>(key)) << 3));
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
             }
         }
-
-        // online softmax in the log2 domain (q carries the scale)
         if (kt * KT + KT - 1 > p_min) {          // tile crosses a row's position (rare)
             asm volatile("");                     // keep this a branch, not per-element selects
             const int jbase = kt * KT + 4 * hf;
@@ -232,36 +245,46 @@ void attn_bf16_kernel(AttnArgs a) {
                     if (j > p_row) sacc[kb][i] = -INFINITY;
                 }
         }
-        float mx = sacc[0][0];
+        bf16x8 pf[2][2];
+        // P = bf16(exp2(sacc + shift)) (no shift on the common path); returns the lane sum
+        auto exp_pack = [&](bool shifted, float shift) -> float {
+            float rs = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        mx = fmaxf(mx, other_half(mx));
-        const bool grow = mx > m_run + 8.f;
-        if (__any(grow)) {                        // some row's max grew by > 2^8 (rare)
+                for (int i = 0; i < 16; i += 2) {
+                    bf16x2 pp;
+                    pp[0] = (bf16)__builtin_amdgcn_exp2f(shifted ? sacc[kb][i] + shift : sacc[kb][i]);
+                    pp[1] = (bf16)__builtin_amdgcn_exp2f(shifted ? sacc[kb][i + 1] + shift : sacc[kb][i + 1]);
+                    pf[kb][i >> 3][i & 7] = pp[0];
+                    pf[kb][i >> 3][(i & 7) + 1] = pp[1];
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs, false);
+                }
+            return rs;
+        };
+        float rs = exp_pack(false, 0.f);
+        if (__any(!have_ref || !(rs <= 65536.f))) {   // no reference yet, or a score far above it (rare)
             asm volatile("");
-            const float m_new = grow ? mx : m_run;
-            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= corr;
+            float mx = sacc[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+            mx = fmaxf(mx, other_half(mx)) + m_ref;   // the row's true tile maximum
+            const float m_new = have_ref ? fmaxf(m_ref, mx) : mx;
+            const float corr = have_ref ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
+            l_lane *= corr;
 #pragma unroll
             for (int d = 0; d < DB; ++d)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
+            rs = exp_pack(true, m_ref - m_new);
+            m_ref = m_new;
+            have_ref = true;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) negm[i] = -m_new;
         }
-        float rs = 0.f;
-        bf16x8 pf[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = __builtin_amdgcn_exp2f(sacc[kb][i] - m_run);
-                rs += pv;
-                pf[kb][i >> 3][i & 7] = (bf16)pv;
-            }
-        rs += other_half(rs);
-        l_run += rs;
+        l_lane += rs;
 
         // O^T += V^T P^T
         const int G = lane >> 4, gi = lane & 15;
@@ -306,6 +329,7 @@ void attn_bf16_kernel(AttnArgs a) {
         }
     }
 
+    const float l_run = l_lane + other_half(l_lane);
     if (!valid) return;
     const float inv = 1.f / l_run;
     bf16* orow = (bf16*)a.out + ((int64_t)(i0 + qi) * a.H_q + h) * D_H;
@@ -319,7 +343,7 @@ void attn_bf16_kernel(AttnArgs a) {
             *(bf16x4*)(orow + d * 32 + 8 * q4 + 4 * hf) = o;
         }
     if (a.lse && hf == 0)
-        a.lse[(int64_t)(i0 + qi) * a.H_q + h] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
+        a.lse[(int64_t)(i0 + qi) * a.H_q + h] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
 }
 
 template <int D_H>
