@@ -35,6 +35,9 @@ namespace kvx {
 namespace {
 
 constexpr int KT = 64;   // keys per tile
+// LDS fragment reads kept in flight ahead of the MFMAs that consume them (measured best)
+constexpr int PF_K = 4;   // K fragments (one per MFMA)
+constexpr int PF_V = 8;   // transposed V reads (two per MFMA)
 constexpr int PT_MAX = 2048;   // page-table entries staged in LDS (longer requests read it from HBM)
 
 // Chunk swizzle of the K/V tiles, chosen by measuring gfx950 LDS throughput for both reads
@@ -234,6 +237,14 @@ void attn_bf16_kernel(AttnArgs a) {
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
             }
         }
+        // K fragment reads PF_K ahead of the MFMAs that use them
+        __builtin_amdgcn_sched_group_barrier(0x100, PF_K, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * QC - PF_K; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF_K, 0);
         if (kt * KT + KT - 1 > p_min) {          // tile crosses a row's position (rare)
             asm volatile("");                     // keep this a branch, not per-element selects
             const int jbase = kt * KT + 4 * hf;
@@ -310,6 +321,14 @@ void attn_bf16_kernel(AttnArgs a) {
                 }
             }
         }
+        // V^T fragment reads (two per MFMA: 8 * DB reads, 4 * DB MFMAs) PF_V ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, PF_V, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * DB - PF_V / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF_V / 2, 0);
     };
 
     if (paged && pt_lds) __syncthreads();      // the staged page table, before the first loads
