@@ -18,7 +18,7 @@ What it follows, step by step (page titles as printed on the pages):
 
 Readings taken where the pages are silent (each stated where it is used):
 linear bias-free mapper; calibration subspace given as an orthonormal basis per
-layer and "weakly supported" read as "outside its span"; score = sum over target
+layer, with weak support by the calibration data read as lying outside its span; score = sum over target
 layers of the squared residual of the concatenated [K | V] vector; budget
 k = ceil(pct * T / 100); ties go to the lower position; rotate-half RoPE with base
 10000 applied only to recomputed q and k at their true positions; all selected K/V
@@ -43,8 +43,8 @@ import numpy as np
 def budget(T: int, pct: int) -> int:
     """Number of positions to recompute: ceil(pct * T / 100) in integer arithmetic.
 
-    RaReCache abstract: "recomputing just 30% of positions" (and 40%).  The count is
-    rounded up so the budget is never under-spent.
+    RaReCache abstract: a fixed share of the positions (30%, also 40%) is recomputed.
+    The count is rounded up so the budget is never under-spent.
     """
     if not (0 <= pct <= 100) or T < 0:
         raise ValueError("budget: need 0 <= pct <= 100 and T >= 0")
@@ -84,7 +84,7 @@ def reconstruct(z: np.ndarray, w_l: np.ndarray, H_kv: int, d_h: int):
 # ------------------------------------------------------------------------------------
 
 def rank_disagreement(Y: np.ndarray, u: np.ndarray) -> np.ndarray:
-    """Score of every position (RaReCache abstract, "rank disagreement").
+    """Score of every position (RaReCache abstract: the rank-disagreement score).
 
     The energy of a token's mapped KV in directions the calibration data supports
     weakly, read as: the squared norm of the part of y_{t,l} outside span(U_l), summed
