@@ -367,32 +367,25 @@ void attn_bf16_kernel(AttnArgs a) {
 
 template <int D_H>
 hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
+    if (W != 8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((int64_t)a.n_blocks * a.H_kv));
-    switch (W) {
-        case 3: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 3>), grid, dim3(3 * 64), 0, s, a); break;
-        case 5: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 5>), grid, dim3(5 * 64), 0, s, a); break;
-        case 6: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 6>), grid, dim3(6 * 64), 0, s, a); break;
-        case 7: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 7>), grid, dim3(7 * 64), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8>), grid, dim3(8 * 64), 0, s, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8>), grid, dim3(8 * 64), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Rows per workgroup are 32 per wave: 8 waves when g divides 256, else g waves of 32 queries.
+// Blocks of 8 waves (256 rows): floor(256 / g) queries, so a g that does not divide 256 leaves
+// fewer than g rows of the last wave idle (measured faster than g-wave blocks of 32 queries).
 int attn_bf16_block_queries(int g) {
-    if (g <= 0) return 0;
-    if (256 % g == 0 && g <= 16) return 256 / g;
-    if (g <= 7) return 32;
-    return 0;
+    if (g <= 0 || g > 16) return 0;
+    return 256 / g;            // 8 waves of 32 rows; g that do not divide 256 leave < g rows idle
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
     if (a.n_blocks == 0) return hipSuccess;
     const int g = a.H_q / a.H_kv;
-    const int W = a.bq * g / 32;
+    const int W = (a.bq * g + 31) / 32;
     if (a.d_h == 128) return launch_dh<128>(a, W, s);
     if (a.d_h == 64) return launch_dh<64>(a, W, s);
     return hipErrorInvalidValue;

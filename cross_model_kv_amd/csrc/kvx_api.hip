@@ -458,7 +458,7 @@ kvx_status check_heads(int32_t dtype, int32_t H_q, int32_t H_kv, int32_t d_h) {
     const int g = H_q / H_kv;
     if (g > 16) return fail(KVX_ERR_UNSUPPORTED, "H_q / H_kv = %d > 16", g);
     if (dtype == KVX_BF16 && attn_bf16_block_queries(g) == 0)
-        return fail(KVX_ERR_UNSUPPORTED, "bf16 attention supports H_q / H_kv in {1..8, 16} (got %d)", g);
+        return fail(KVX_ERR_UNSUPPORTED, "bf16 attention supports H_q / H_kv <= 16 (got %d)", g);
     return KVX_OK;
 }
 

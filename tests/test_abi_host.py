@@ -171,7 +171,7 @@ def test_recompute_attn_validation():
     status(call(d_h=96), UNSUPPORTED, "d_h")
     status(call(H_q=9), INVALID, "multiple")
     status(call(H_q=34, H_kv=2), UNSUPPORTED, "> 16")
-    status(call(H_q=18, H_kv=2), UNSUPPORTED, "H_q / H_kv")
+    status(call(H_q=18, H_kv=2, wsb=0), WORKSPACE)      # g = 9 is supported (padded 8-wave blocks)
     status(call(D=100), INVALID, "D % 64")
     status(call(max_pos=99), INVALID, "rope")
     status(call(layer=2), INVALID, "layer")

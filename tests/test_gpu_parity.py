@@ -325,6 +325,11 @@ RECOMPUTE_CASES = {
     "bf16-g8": small("rc-bf16-g8", H_q=16, H_kv=2, T=700, pct=30),
     "bf16-g5": small("rc-bf16-g5", H_q=10, H_kv=2, T=517, pct=40),
     "bf16-g1-d64": small("rc-bf16-g1-d64", H_q=2, H_kv=2, d_h=64, T=333, pct=20),
+    # group sizes that do not divide 256 (blocks of floor(256/g) queries leave rows idle), and g = 16
+    "bf16-g3": small("rc-bf16-g3", H_q=6, H_kv=2, T=640, pct=30),
+    "bf16-g7-d64": small("rc-bf16-g7-d64", H_q=14, H_kv=2, d_h=64, T=500, pct=40),
+    "bf16-g9": small("rc-bf16-g9", H_q=18, H_kv=2, T=421, pct=30),
+    "bf16-g16": small("rc-bf16-g16", H_q=32, H_kv=2, T=300, pct=40),
     "bf16-g8-batched-paged": small("rc-bf16-batched", H_q=16, H_kv=2, n_req=4, t_min=20, t_max=900,
                                    pct_choices=(20, 30, 40), paged=True),
     "f32-g4": small("rc-f32-g4", dtype="f32", H_q=8, H_kv=2, d_h=64, T=300, pct=30),
