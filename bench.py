@@ -4,7 +4,8 @@
 One step = one whole handoff of the 16K-token 8B-to-32B-shaped workload: map the source KV
 to the latent, score and select the top-30% positions, reconstruct the translated cache of
 the complement, then for each of the 64 target layers project Q/K/V of the selected
-positions, rotate and scatter K/V into the mixed cache and run the sparse causal attention.
+positions, rotate and scatter K/V into the mixed cache (one kernel) and run the sparse causal
+attention.
 All inputs are synthetic (seeded) and resident in HBM before timing.
 
 Prints one JSON line: handoff tokens/s (positions handed off per second), the roofline of
@@ -51,8 +52,9 @@ def stage_work(wl, T, k, pos_sum):
         "score_select": dict(flops=2.0 * T * wl.r * wl.r, bytes=2.0 * T * wl.r + 4.0 * wl.r * wl.r + 4.0 * T),
         "reconstruct": dict(flops=2.0 * (T - k) * wl.r * d_t * wl.L_t,
                             bytes=2.0 * ((T - k) * d_t * wl.L_t + wl.L_t * wl.r * d_t + T * wl.r)),
-        "qkv_project": dict(flops=2.0 * k * wl.D * n_qkv, bytes=2.0 * (k * wl.D + wl.D * n_qkv + k * n_qkv)),
-        "rope_scatter": dict(flops=0.0, bytes=2.0 * 2.0 * k * d_t),
+        # one kernel: gathered rows and W_qkv in, q rows and the rotated k / v cache rows out
+        "qkv_rope_scatter": dict(flops=2.0 * k * wl.D * n_qkv,
+                                 bytes=2.0 * (k * wl.D + wl.D * n_qkv + k * wl.H_q * wl.d_h + 2.0 * k * d_t)),
         "sparse_attention": dict(flops=4.0 * wl.H_q * wl.d_h * pos_sum,
                                  bytes=2.0 * (T * d_t + 2.0 * k * wl.H_q * wl.d_h)),
     }
@@ -165,7 +167,7 @@ def main():
     ws_qkv = h.ws_attn[(k * wl.n_qkv * 2 + 255) // 256 * 256:]     # the projection's split-tail workspace
     stream = torch.cuda.current_stream(dev)
 
-    names = ["map_latent", "score_select", "reconstruct", "qkv_project", "rope_scatter", "sparse_attention"]
+    names = ["map_latent", "score_select", "reconstruct", "qkv_rope_scatter", "sparse_attention"]
 
     def step(ev=None):
         def mark(key):
@@ -181,10 +183,9 @@ def main():
         h.reconstruct()
         mark("reconstruct")
         for l in range(wl.L_t):
-            kvx.qkv_project(inp.x_l[l], inp.w_qkv[l], wl.H_q, wl.H_kv, wl.d_h, h.batch, h.S, qkv, ws_qkv)
-            mark("qkv_project")
-            kvx.rope_scatter(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache)
-            mark("rope_scatter")
+            kvx.qkv_rope_scatter(l, inp.x_l[l], inp.w_qkv[l], wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S,
+                                 h.cache, qkv, ws_qkv)
+            mark("qkv_rope_scatter")
             kvx.sparse_attention(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache, h.out[l], h.lse[l])
             mark("sparse_attention")
 
@@ -201,8 +202,7 @@ def main():
 
     # per-stage GPU times from the events (each stage ends where the next begins)
     seq = []
-    per_step = 3 + 3 * wl.L_t
-    order = ["map_latent", "score_select", "reconstruct"] + ["qkv_project", "rope_scatter", "sparse_attention"] * wl.L_t
+    order = ["map_latent", "score_select", "reconstruct"] + ["qkv_rope_scatter", "sparse_attention"] * wl.L_t
     idx = {n: 0 for n in names}
     starts = events["t0"]
     stage_ms = {n: 0.0 for n in names}

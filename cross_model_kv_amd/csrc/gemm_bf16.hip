@@ -82,6 +82,7 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     __shared__ __attribute__((aligned(1024))) bf16 lds1[STAGE];
     __shared__ int s_src[BM];
     __shared__ int64_t s_slot[BM];
+    __shared__ int s_pos[BM];
     __shared__ float s_red[WN][BM];
 
     const int tid = threadIdx.x;
@@ -100,15 +101,17 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     // ---- row map: source row of every tile row, and its cache slot
     for (int r = tid; r < BM; r += NW * 64) {
         const int m = m0 + r;
-        int src = -1;
+        int src = -1, pos = 0;
         int64_t slot = 0;
         if (m < a.M) {
             const RowInfo ri = row_info(a.rows, m);
             src = ri.src;
-            if (a.epi == EPI_CACHE) slot = a.slots.slot(ri.b, ri.pos);
+            if (a.epi == EPI_CACHE || a.epi == EPI_QKV) slot = a.slots.slot(ri.b, ri.pos);
+            pos = ri.pos;
         }
         s_src[r] = src;
         s_slot[r] = slot;
+        s_pos[r] = pos;
     }
     __syncthreads();
 
@@ -244,6 +247,61 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
         }
         return;
     }
+    if (a.epi == EPI_QKV) {
+        // columns nl0 .. nl0+7 of one head (heads are 64 or 128 columns, aligned to 8)
+        static_assert(FN == 8, "the fused QKV epilogue expects 8 columns per lane");
+        const int half = a.d_h / 2;
+        // a wave whose 128-column slab touches the K columns exchanges rotation partners:
+        // column j of a head pairs with j +- d_h/2, held by lane ^ (d_h/16)
+        const int slab0 = n0 + wn * WTN;
+        const bool k_slab = slab0 < a.q_cols + a.hd && slab0 + WTN > a.q_cols;
+        const int cc = ng - a.q_cols;                 // column in [K | V]
+        const bool is_k = ng >= a.q_cols && cc < a.hd;
+        const int j0 = (cc % a.d_h) % half;           // rotation index of the first column
+        const bool lo = (cc % a.d_h) < half;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ml = wm * WTM + i * 16 + 4 * lq + v;
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = (float)(bf16)acc[i][j][v];
+                float y[8];
+                if (k_slab) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int xi = __float_as_int(x[j]);
+                        const int pi = a.d_h == 128 ? __builtin_amdgcn_update_dpp(0, xi, 0x128, 0xF, 0xF, false)
+                                                    : __shfl_xor(xi, 4);
+                        y[j] = __int_as_float(pi);           // the partner column's value
+                    }
+                }
+                if (ng >= a.N || s_src[ml] < 0) continue;
+                bf16x8 o;
+                if (is_k) {
+                    const float4* cs = (const float4*)(a.rope + ((int64_t)s_pos[ml] * half + j0) * 2);
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) {
+                        const float4 t2 = cs[j2];
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int j = 2 * j2 + u;
+                            const float c = u ? t2.z : t2.x, sn = u ? t2.w : t2.y;
+                            o[j] = (bf16)(lo ? rope_lo(x[j], y[j], c, sn) : rope_hi(y[j], x[j], c, sn));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) o[j] = (bf16)x[j];
+                }
+                bf16* dst = ng < a.q_cols ? a.C + (int64_t)(m0 + ml) * a.ldc + ng
+                                          : (is_k ? a.kc : a.vc) + s_slot[ml] * a.hd + (is_k ? cc : cc - a.hd);
+                *(bf16x8*)dst = o;
+            }
+        }
+        return;
+    }
     if (ng >= a.N) return;
     typedef __bf16 vecN __attribute__((ext_vector_type(FN)));
 #pragma unroll
@@ -285,6 +343,45 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) { s[i] += x0[i]; s[4 + i] += x1[i]; }
     }
+    if (a.epi == EPI_QKV) {               // same column handling as the tile epilogue
+        const RowInfo ri = row_info(a.rows, m);
+        const int64_t slot = a.slots.slot(ri.b, ri.pos);
+        const int half = a.d_h / 2;
+        const int cc = n - a.q_cols;
+        const bool is_k = n >= a.q_cols && cc < a.hd;
+        bf16x8 o;
+        if (is_k) {
+            const bool lo = (cc % a.d_h) < half;
+            const int j0 = (cc % a.d_h) % half;
+            float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            const float* pp = p + (lo ? half : -half);
+            for (int k = 0; k < sp.split; ++k) {
+                const f32x4 x0 = *(const f32x4*)(pp + (int64_t)k * 65536);
+                const f32x4 x1 = *(const f32x4*)(pp + (int64_t)k * 65536 + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { y[i] += x0[i]; y[4 + i] += x1[i]; }
+            }
+            const float4* cs = (const float4*)(a.rope + ((int64_t)ri.pos * half + j0) * 2);
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2) {
+                const float4 t2 = cs[j2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int j = 2 * j2 + u;
+                    const float c = u ? t2.z : t2.x, sn = u ? t2.w : t2.y;
+                    const float xm = (float)(bf16)s[j], xp = (float)(bf16)y[j];
+                    o[j] = (bf16)(lo ? rope_lo(xm, xp, c, sn) : rope_hi(xp, xm, c, sn));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (bf16)s[i];
+        }
+        bf16* dst = n < a.q_cols ? a.C + (int64_t)m * a.ldc + n
+                                 : (is_k ? a.kc : a.vc) + slot * a.hd + (is_k ? cc : cc - a.hd);
+        *(bf16x8*)dst = o;
+        return;
+    }
     bf16* dst = a.C + (int64_t)m * a.ldc + n;
     if (n + 8 <= a.N) {
         bf16x8 o;
@@ -307,7 +404,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
 SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
     const int64_t tiles = (int64_t)cdiv(M, 256) * cdiv(N, 256) * groups;
     SplitPlan best{(int)tiles, 0, 1};
-    if (epi != EPI_STORE || groups != 1 || tiles == 0 || tiles > INT32_MAX / 8) return best;
+    if ((epi != EPI_STORE && epi != EPI_QKV) || groups != 1 || tiles == 0 || tiles > INT32_MAX / 8) return best;
     const int nk = K / BK;
     const int64_t cu = CU_COUNT;
     double best_t = (double)((tiles + cu - 1) / cu);

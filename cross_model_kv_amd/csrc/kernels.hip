@@ -297,8 +297,8 @@ __global__ void rope_scatter_kernel(ScatterArgs a) {
     const float x1 = to_f(kr[j]), x2 = to_f(kr[j + half]);
     TE* kd = (TE*)a.kc + (slot * a.H_kv + h) * a.d_h;
     TE* vd = (TE*)a.vc + (slot * a.H_kv + h) * a.d_h;
-    kd[j] = (TE)(x1 * c - x2 * s);
-    kd[j + half] = (TE)(x2 * c + x1 * s);
+    kd[j] = (TE)rope_lo(x1, x2, c, s);
+    kd[j + half] = (TE)rope_hi(x1, x2, c, s);
     vd[j] = vr[j];
     vd[j + half] = vr[j + half];
 }

@@ -523,6 +523,33 @@ hipError_t run_scatter(hipStream_t s, int32_t dtype, int32_t layer, const void* 
     return launch_rope_scatter(sc, dtype, s);
 }
 
+// Steps 1-3 of one layer.  bf16: one GEMM whose epilogue rounds every output to bf16, keeps
+// the q columns in qkv and writes rotated k and v to the cache slots, with the arithmetic of
+// the separate steps (bit-identical to run_qkv + run_scatter).  fp32: the two separate kernels.
+hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, const void* x_l, const void* w_qkv,
+                                int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
+                                const kvx_batch* batch, const BatchInfo& bi, const int32_t* sel,
+                                const kvx_cache* cache, void* qkv, void* split_ws) {
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    if (dtype != KVX_BF16) {
+        if (hipError_t e = run_qkv(s, dtype, x_l, w_qkv, D, n_qkv, batch, bi, sel, qkv, split_ws)) return e;
+        return run_scatter(s, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel, cache);
+    }
+    const int hd = H_kv * d_h;
+    GemmArgs a{};
+    a.A = (const bf16*)x_l; a.lda = D; a.K_a = D;
+    a.B = (const bf16*)w_qkv; a.ldb = D;
+    a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
+    a.rows = sel_rows(batch, sel, bi.n_req);
+    a.epi = EPI_QKV; a.C = (bf16*)qkv; a.ldc = n_qkv;
+    a.kc = (bf16*)layer_base(cache->k, cache, layer, hd, dtype);
+    a.vc = (bf16*)layer_base(cache->v, cache, layer, hd, dtype);
+    a.hd = hd; a.slots = slot_map(cache, batch);
+    a.rope = rope; a.q_cols = H_q * d_h; a.d_h = d_h;
+    a.split_ws = (float*)split_ws;
+    return launch_gemm_bf16(a, s);
+}
+
 hipError_t run_attention(hipStream_t s, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
                          int32_t H_kv, int32_t d_h, const float* rope, const kvx_batch* batch,
                          const BatchInfo& bi, const int32_t* sel, const kvx_cache* cache, void* out,
@@ -593,6 +620,32 @@ kvx_status kvx_rope_scatter(void* stream, int32_t dtype, int32_t layer, const vo
                                   cache), "rope_scatter");
 }
 
+kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t layer, const void* x_l, const void* w_qkv,
+                                int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
+                                int32_t max_pos, const kvx_batch* batch, const int32_t* sel,
+                                const kvx_cache* cache, void* qkv, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(x_l, "x_l");
+    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
+    KVX_REQUIRE(D > 0, "D must be positive");
+    if (dtype == KVX_BF16) KVX_REQUIRE(D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(sel, "sel");
+    KVX_REQUIRE_PTR(qkv, "qkv");
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    const size_t need = qkv_split_bytes(dtype, bi.n_sel, D, n_qkv);
+    if (need && (!ws || ws_bytes < need))
+        return fail(KVX_ERR_WORKSPACE, "qkv_rope_scatter needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (need) KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    return hip_status(run_qkv_rope_scatter((hipStream_t)stream, dtype, layer, x_l, w_qkv, D, H_q, H_kv, d_h, rope,
+                                           batch, bi, sel, cache, qkv, need ? ws : nullptr),
+                      "qkv_rope_scatter");
+}
+
 kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
                                 int32_t H_kv, int32_t d_h, const float* rope, int32_t max_pos,
                                 const kvx_batch* batch, const int32_t* sel, const kvx_cache* cache, void* out,
@@ -640,8 +693,8 @@ kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const 
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     const size_t qkv_bytes = round256((size_t)bi.n_sel * n_qkv * elem_size(dtype));
     void* split_ws = qkv_split_bytes(dtype, bi.n_sel, D, n_qkv) ? (char*)ws + qkv_bytes : nullptr;
-    KVX_TRY_HIP(run_qkv(s, dtype, x_l, w_qkv, D, n_qkv, batch, bi, sel, ws, split_ws), "recompute qkv");
-    KVX_TRY_HIP(run_scatter(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache), "rope_scatter");
+    KVX_TRY_HIP(run_qkv_rope_scatter(s, dtype, layer, x_l, w_qkv, D, H_q, H_kv, d_h, rope, batch, bi, sel, cache,
+                                     ws, split_ws), "recompute qkv/rope/scatter");
     return hip_status(run_attention(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse),
                       "attention");
 }

@@ -102,7 +102,7 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& rm, int m) {
     return r;
 }
 
-enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2 };
+enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2, EPI_QKV = 3 };
 
 struct GemmArgs {
     // C[m][n] = sum_k A[src(m)][k mod K_a] * B[n][k]
@@ -117,9 +117,18 @@ struct GemmArgs {
     bf16* kc; bf16* vc; int64_t layer_elems; int32_t hd; SlotMap slots;
     // EPI_SCORE: partial[n_block][m] = sum_{n in block} C[m][n] * Z[m][n]
     float* partial; const bf16* Z; int64_t ldz;
-    // EPI_STORE with a split tail (see gemm_bf16_split_bytes): fp32 workspace of the K slices
+    // EPI_STORE / EPI_QKV with a split tail (see gemm_bf16_split_bytes): fp32 K-slice partials
     float* split_ws;
+    // EPI_QKV (the gathered QKV projection of one layer): columns [0, q_cols) go to C like a
+    // store; the K columns are rounded to bf16, rotated (rotate-half, table rope at the row's
+    // position) and written with the V columns to the layer's cache slots (kc, vc, hd, slots)
+    const float* rope; int32_t q_cols; int32_t d_h;
 };
+
+// Rotate-half of one pair, in the order every kernel uses (results are bit-identical):
+//   first half:  x1 * c - x2 * s        second half:  x2 * c + x1 * s
+__device__ __forceinline__ float rope_lo(float x1, float x2, float c, float s) { return __builtin_fmaf(x1, c, -(x2 * s)); }
+__device__ __forceinline__ float rope_hi(float x1, float x2, float c, float s) { return __builtin_fmaf(x2, c, x1 * s); }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 int gemm_bf16_block_n();

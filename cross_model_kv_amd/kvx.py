@@ -72,6 +72,8 @@ _SIGS = {
                         _I32),
     "kvx_rope_scatter": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
                           ctypes.POINTER(_Cache)], _I32),
+    "kvx_qkv_rope_scatter": ([_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch),
+                              _P, ctypes.POINTER(_Cache), _P, _P, _SZ], _I32),
     "kvx_sparse_attention": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
                               ctypes.POINTER(_Cache), _P, _P], _I32),
 }
@@ -350,6 +352,27 @@ def rope_scatter(layer: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, r
     _check("kvx_rope_scatter", lib().kvx_rope_scatter(_stream(qkv.device), _dtype(qkv), layer, _ptr(qkv), H_q, H_kv,
                                                       d_h, _ptr(rope), rope.shape[0], ctypes.byref(batch.c),
                                                       _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c)))
+
+
+def qkv_rope_scatter(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int,
+                     rope: torch.Tensor, batch: Batch, sel: torch.Tensor, cache: Cache,
+                     qkv: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Steps 1-3 in one call: q rows into qkv (its k/v columns stay unwritten), rotated k and v
+    into the cache.  Returns qkv."""
+    dev = x_l.device
+    dt = _dtype(x_l)
+    D = x_l.shape[1]
+    n_qkv = (H_q + 2 * H_kv) * d_h
+    if qkv is None:
+        qkv = torch.empty((max(batch.total_sel, 1), n_qkv), dtype=x_l.dtype, device=dev)
+    need = qkv_project_workspace(dt, batch, D, H_q, H_kv, d_h)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("kvx_qkv_rope_scatter", lib().kvx_qkv_rope_scatter(
+        _stream(dev), dt, layer, _ptr(x_l), _ptr(w_qkv), D, H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
+        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(qkv),
+        _ptr(ws) if need else None, ws.numel() if need else 0))
+    return qkv
 
 
 def sparse_attention(layer: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, rope: torch.Tensor,

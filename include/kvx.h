@@ -201,8 +201,10 @@ KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer
                               const kvx_cache* cache, void* out, float* lse, void* ws,
                               size_t ws_bytes);
 
-/* The three steps of kvx_recompute_attn as separate calls (same kernels, same work), for
- * callers that schedule or time them individually.
+/* The steps of kvx_recompute_attn as separate calls, for callers that schedule or time them
+ * individually.  kvx_recompute_attn is kvx_qkv_rope_scatter followed by kvx_sparse_attention;
+ * kvx_qkv_project followed by kvx_rope_scatter gives the same cache and q rows (and also the
+ * unrotated k and v columns of qkv).
  *
  * kvx_qkv_project: step 1, qkv (device, out) [cu_sel[n_req]][n_qkv] in the storage dtype,
  *   row i = W_qkv x_l[cu_tokens[b] + sel[i]] (not rotated).  bf16 needs D % 64 == 0.
@@ -224,6 +226,19 @@ KVX_API kvx_status kvx_rope_scatter(void* stream, int32_t dtype, int32_t layer, 
                                     int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
                                     int32_t max_pos, const kvx_batch* batch, const int32_t* sel,
                                     const kvx_cache* cache);
+
+/* kvx_qkv_rope_scatter: steps 1-3 in one call.  Writes the q part of every qkv row (the k and
+ * v columns of qkv are left unwritten) and the rotated k and the v rows into layer `layer` of
+ * the cache, with results identical to kvx_qkv_project followed by kvx_rope_scatter (bf16:
+ * one kernel, whose epilogue rounds to bf16 and rotates as the separate kernel does; fp32:
+ * the two kernels).  Arguments as in kvx_qkv_project and kvx_rope_scatter; ws and its size
+ * as in kvx_qkv_project (kvx_qkv_project_workspace). */
+KVX_API kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t layer, const void* x_l,
+                                        const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv,
+                                        int32_t d_h, const float* rope, int32_t max_pos,
+                                        const kvx_batch* batch, const int32_t* sel,
+                                        const kvx_cache* cache, void* qkv, void* ws,
+                                        size_t ws_bytes);
 
 /* kvx_sparse_attention: step 4, causal attention of the selected queries (the q part of
  * the qkv rows, rotated at their true positions inside the kernel) over layer `layer` of

@@ -178,3 +178,26 @@ def test_recompute_attn_validation():
     status(call(ws=None), WORKSPACE)
     status(call(wsb=need.value - 1), WORKSPACE)
     status(call(dtype=3), UNSUPPORTED, "dtype")
+
+
+def test_qkv_rope_scatter_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    c = cache()
+    need = ctypes.c_size_t()
+    assert L.kvx_qkv_project_workspace(1, ctypes.byref(bt.c), 4096, 8, 2, 64, ctypes.byref(need)) == 0
+    assert need.value > 0, "a few rows over a wide D split along D"
+
+    def call(dtype=1, layer=0, D=4096, H_q=8, H_kv=2, d_h=64, max_pos=100, cc=c, ws=A16, wsb=None, qkv=A16):
+        return L.kvx_qkv_rope_scatter(None, dtype, layer, A16, A16, D, H_q, H_kv, d_h, A16, max_pos,
+                                      ctypes.byref(bt.c), A16, ctypes.byref(cc), qkv, ws,
+                                      need.value if wsb is None else wsb)
+    status(call(d_h=96), UNSUPPORTED, "d_h")
+    status(call(H_q=9), INVALID, "multiple")
+    status(call(D=100), INVALID, "D % 64")
+    status(call(max_pos=99), INVALID, "rope")
+    status(call(layer=2), INVALID, "layer")
+    status(call(qkv=None), INVALID, "qkv")
+    status(call(ws=None), WORKSPACE)
+    status(call(wsb=need.value - 1), WORKSPACE)
+    status(call(dtype=3), UNSUPPORTED, "dtype")

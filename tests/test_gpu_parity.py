@@ -175,29 +175,44 @@ def test_determinism_bitwise():
             assert np.array_equal(x, y)
 
 
-def test_split_steps_equal_composite():
+@pytest.mark.parametrize("name", ["bf16-g8-batched-paged", "bf16-g8-wide-D", "bf16-g4-wide-D", "bf16-g7-d64",
+                                  "f32-g4"])
+def test_split_steps_equal_composite(name):
     """kvx_qkv_project + kvx_rope_scatter + kvx_sparse_attention give bit for bit what
-    kvx_recompute_attn gives."""
-    wl = RECOMPUTE_CASES["bf16-g8-batched-paged"]
+    kvx_recompute_attn gives, and what kvx_qkv_rope_scatter (projection, rotation and cache
+    write in one kernel for bf16) + kvx_sparse_attention give: the same cache, the same q
+    columns, the same outputs.  Cases: paged batch, d_h 128 and 64, tiles split along D."""
+    wl = RECOMPUTE_CASES[name]
     say(f"[split] {wl.name}")
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     inp = synth.generate(wl, 13, DEV)
     batch = kvx.Batch.for_budgets(inp.lengths, inp.pcts, DEV)
     sel = torch.from_numpy(np.concatenate([synth.random_subset(t, k, 13 + b) for b, (t, k) in
                                            enumerate(zip(inp.lengths, batch.n_sel))]).astype(np.int32)).to(DEV)
-    n_slots = inp.n_pages * wl.page_size
+    n_slots = inp.n_pages * wl.page_size if wl.paged else batch.n_tokens
+    pt = inp.page_table if wl.paged else None
     shape = (wl.L_t, n_slots, wl.H_kv, wl.d_h)
-    k0 = synth.cache_fill(shape, 13, device=DEV)
-    v0 = synth.cache_fill(shape, 14, device=DEV)
+    k0 = synth.cache_fill(shape, 13, dtype=dt, device=DEV)
+    v0 = synth.cache_fill(shape, 14, dtype=dt, device=DEV)
     rope = kvx.rope_table(wl.rope_base, wl.d_h, max(inp.lengths), DEV)
-    c1 = kvx.Cache(k0.clone(), v0.clone(), wl.L_t, n_slots, inp.page_table, wl.page_size)
-    c2 = kvx.Cache(k0.clone(), v0.clone(), wl.L_t, n_slots, inp.page_table, wl.page_size)
-    o1 = kvx.recompute_attn(0, inp.x_l[0], inp.w_qkv[0], wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, c1)
-    qkv = kvx.qkv_project(inp.x_l[0], inp.w_qkv[0], wl.H_q, wl.H_kv, wl.d_h, batch, sel)
-    kvx.rope_scatter(0, qkv, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, c2)
+    caches = [kvx.Cache(k0.clone(), v0.clone(), wl.L_t, n_slots, pt, wl.page_size) for _ in range(3)]
+    layer = wl.L_t - 1
+    args = (inp.x_l[layer], inp.w_qkv[layer], wl.H_q, wl.H_kv, wl.d_h)
+    o1 = kvx.recompute_attn(layer, *args, rope, batch, sel, caches[0])
+    qkv2 = kvx.qkv_project(*args, batch, sel)
+    kvx.rope_scatter(layer, qkv2, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, caches[1])
     o2 = torch.empty_like(o1)
-    kvx.sparse_attention(0, qkv, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, c2, o2)
+    kvx.sparse_attention(layer, qkv2, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, caches[1], o2)
+    qkv3 = kvx.qkv_rope_scatter(layer, *args, rope, batch, sel, caches[2])
+    o3 = torch.empty_like(o1)
+    kvx.sparse_attention(layer, qkv3, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, caches[2], o3)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(c1.k, c2.k) and torch.equal(c1.v, c2.v)
+    k = batch.total_sel
+    qc = wl.H_q * wl.d_h
+    assert torch.equal(qkv2[:k, :qc], qkv3[:k, :qc]), "q columns differ"
+    for c in caches[1:]:
+        assert torch.equal(caches[0].k, c.k) and torch.equal(caches[0].v, c.v), "caches differ"
+    assert torch.equal(o1, o2) and torch.equal(o1, o3), "attention outputs differ"
 
 
 # --------------------------------------------------------------------------- stage-wise
@@ -335,6 +350,7 @@ RECOMPUTE_CASES = {
     "f32-g4": small("rc-f32-g4", dtype="f32", H_q=8, H_kv=2, d_h=64, T=300, pct=30),
     # D = 2048: the projection's tiles fill under half a round, so they are split along D
     "bf16-g4-wide-D": small("rc-bf16-wide-D", H_q=8, H_kv=2, d_h=64, D=2048, T=600, pct=40),
+    "bf16-g8-wide-D": small("rc-bf16-g8-wide-D", H_q=16, H_kv=2, D=2048, T=600, pct=40),
 }
 
 
