@@ -25,6 +25,13 @@ k = ceil(pct * T / 100); ties go to the lower position; rotate-half RoPE with ba
 of a layer are written before any selected query attends; inclusive causal mask,
 scale 1/sqrt(d_h), KV head = h // (H_q / H_kv).
 
+Target layer chaining (the selected rows continuing through the rest of each target
+layer, so that layer l+1's recomputed rows come from layer l's output): the pages name
+the model pairs (Qwen3 and Llama targets) but not their blocks; the reading here is the
+plain pre-norm decoder layer those families share - RMS normalisation with a per-channel
+gain, the recomputed attention, an output projection and a residual add, a second RMS
+normalisation, a SiLU-gated MLP and a second residual add - with no norm on q or k.
+
 Every function takes float64 numpy arrays (exact upcasts of the stored values) and
 computes its result by its plain definition.
 """
@@ -226,6 +233,72 @@ def handoff_request(x_src: np.ndarray, w_s: np.ndarray, w_l: np.ndarray, u: np.n
         K[l], V[l] = scatter(K[l], V[l], S, kk, vv)
         O[l], LSE[l] = sparse_causal_attention(q, K[l], V[l], S)
     return dict(z=z, K_tr=K_tr, V_tr=V_tr, s=s, S=S, C=C, K=K, V=V, O=O, LSE=LSE)
+
+
+# ------------------------------------------------------------------------------------
+# target layer chaining: the rest of the target layer on the selected rows
+# ------------------------------------------------------------------------------------
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """Root-mean-square normalisation of every row, then a per-channel gain:
+    y = x / sqrt(mean_j(x_j^2) + eps) * gamma."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gamma
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x)."""
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu_mlp(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """SiLU-gated MLP: W_down (silu(W_gate x) * (W_up x)).  w_gate, w_up [F, D] and
+    w_down [D, F], stored output-major."""
+    return (silu(x @ w_gate.T) * (x @ w_up.T)) @ w_down.T
+
+
+def target_layer(x_rows: np.ndarray, S: np.ndarray, K: np.ndarray, V: np.ndarray, w: Dict[str, np.ndarray],
+                 H_q: int, H_kv: int, d_h: int, base: float, eps: float):
+    """One pre-norm decoder layer of the target, run on the selected rows only.
+
+    x_rows [k, D] is the residual stream at the selected positions S (ascending), K, V
+    [T, H_kv, d_h] the layer's translated cache.  w holds gamma_in [D], w_qkv, w_o
+    [D, H_q d_h], gamma_post [D], w_gate, w_up [F, D], w_down [D, F].  Steps:
+    h = rmsnorm(x); q, k, v from h (rotated at the true positions); all k, v written
+    into the cache; attention of the selected queries over the mixed cache;
+    x1 = x + O W_o^T; x2 = x1 + mlp(rmsnorm(x1)).  Returns x2, the mixed cache K, V,
+    the attention output O [k, H_q, d_h] and its LSE.
+    """
+    n = x_rows.shape[0]
+    h = rmsnorm(x_rows, w["gamma_in"], eps)
+    q, kk, vv = recompute_qkv(h, w["w_qkv"], S, H_q, H_kv, d_h, base)
+    K, V = scatter(K, V, S, kk, vv)
+    O, lse = sparse_causal_attention(q, K, V, S)
+    x1 = x_rows + O.reshape(n, H_q * d_h) @ w["w_o"].T
+    x2 = x1 + swiglu_mlp(rmsnorm(x1, w["gamma_post"], eps), w["w_gate"], w["w_up"], w["w_down"])
+    return x2, K, V, O, lse
+
+
+def chained_layers(x0_rows: np.ndarray, S: np.ndarray, K_tr: np.ndarray, V_tr: np.ndarray,
+                   layers: Sequence[Dict[str, np.ndarray]], H_q: int, H_kv: int, d_h: int,
+                   base: float = 10000.0, eps: float = 1e-6) -> Dict[str, np.ndarray]:
+    """The selected rows through every target layer in turn: layer l+1 takes layer l's
+    output rows.  x0_rows [k, D] are the target's input rows at the selected positions,
+    K_tr, V_tr [L_t, T, H_kv, d_h] the translated cache.  Returns the final rows X, the
+    mixed cache K, V, and O, LSE per layer."""
+    L = len(layers)
+    x = x0_rows
+    K = K_tr.copy()
+    V = V_tr.copy()
+    n = x0_rows.shape[0]
+    O = np.zeros((L, n, H_q, d_h))
+    LSE = np.zeros((L, n, H_q))
+    X = np.zeros((L + 1,) + x0_rows.shape)
+    X[0] = x
+    for l in range(L):
+        x, K[l], V[l], O[l], LSE[l] = target_layer(x, S, K[l], V[l], layers[l], H_q, H_kv, d_h, base, eps)
+        X[l + 1] = x
+    return dict(X=X, K=K, V=V, O=O, LSE=LSE)
 
 
 def score_gap(s: np.ndarray, k: int) -> float:

@@ -424,6 +424,156 @@ def pin_handoff_partial_budget_mixed_cache():
     assert np.abs(o2[0] - out["O"][l, i]).max() > 1e-6
 
 
+# ------------------------------------------------------------------------- layer chaining
+
+def pin_rmsnorm_hand():
+    """[3, 4, 0, 0]: mean square 25/4, rms 2.5; with gain [1, 2, 3, 4] -> [1.2, 3.2, 0, 0]."""
+    y = O.rmsnorm(np.array([[3.0, 4.0, 0.0, 0.0]]), np.array([1.0, 2.0, 3.0, 4.0]), 0.0)
+    assert np.abs(y - np.array([[1.2, 3.2, 0.0, 0.0]])).max() < 1e-15
+    # eps enters under the root: [1, 1] with eps 3 -> 1 / sqrt(1 + 3) = 0.5
+    assert np.abs(O.rmsnorm(np.ones((1, 2)), np.ones(2), 3.0) - 0.5).max() < 1e-15
+
+
+def pin_rmsnorm_invariants():
+    rng = _rng(41)
+    x = rng.standard_normal((5, 12))
+    g = rng.uniform(0.5, 2.0, 12)
+    y = O.rmsnorm(x, g, 0.0)
+    assert np.abs(O.rmsnorm(7.5 * x, g, 0.0) - y).max() < 1e-13      # scale invariant
+    assert np.abs(np.mean((y / g) ** 2, axis=1) - 1.0).max() < 1e-13  # unit rms before the gain
+
+
+def pin_silu_closed_form():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    # sigmoid(ln 3) = 3/4
+    assert abs(O.silu(np.array([math.log(3.0)]))[0] - 0.75 * math.log(3.0)) < 1e-15
+    x = _rng(42).standard_normal(50) * 4
+    assert np.abs(O.silu(x) - O.silu(-x) - x).max() < 1e-13          # x s(x) + x s(-x) = x
+
+
+def _layer_loops(x, S, K, V, w, H_q, H_kv, d_h, base, eps):
+    """One decoder layer written element by element (independent of the vectorised oracle)."""
+    n, D = x.shape
+    F = w["w_gate"].shape[0]
+    g = H_q // H_kv
+    def norm(row, gain):
+        ms = sum(v * v for v in row) / len(row)
+        return [row[j] / math.sqrt(ms + eps) * gain[j] for j in range(len(row))]
+    def rot(vec, p):
+        out = list(vec)
+        for j in range(d_h // 2):
+            a = p * base ** (-2.0 * j / d_h)
+            x1, x2 = vec[j], vec[j + d_h // 2]
+            out[j] = x1 * math.cos(a) - x2 * math.sin(a)
+            out[j + d_h // 2] = x2 * math.cos(a) + x1 * math.sin(a)
+        return out
+    Km, Vm = K.copy(), V.copy()
+    qs = []
+    for i in range(n):
+        h = norm(list(x[i]), w["gamma_in"])
+        row = [sum(w["w_qkv"][c][j] * h[j] for j in range(D)) for c in range((H_q + 2 * H_kv) * d_h)]
+        p = int(S[i])
+        qs.append([rot(row[hh * d_h:(hh + 1) * d_h], p) for hh in range(H_q)])
+        for hk in range(H_kv):
+            Km[p, hk] = rot(row[(H_q + hk) * d_h:(H_q + hk + 1) * d_h], p)
+            Vm[p, hk] = row[(H_q + H_kv + hk) * d_h:(H_q + H_kv + hk + 1) * d_h]
+    out = np.zeros_like(x)
+    for i in range(n):
+        p = int(S[i])
+        o = []
+        for hh in range(H_q):
+            kv = hh // g
+            lg = [sum(qs[i][hh][d] * Km[j, kv, d] for d in range(d_h)) / math.sqrt(d_h) for j in range(p + 1)]
+            m = max(lg)
+            e = [math.exp(v - m) for v in lg]
+            tot = sum(e)
+            o += [sum(e[j] / tot * Vm[j, kv, d] for j in range(p + 1)) for d in range(d_h)]
+        x1 = [x[i][c] + sum(w["w_o"][c][j] * o[j] for j in range(H_q * d_h)) for c in range(D)]
+        h2 = norm(x1, w["gamma_post"])
+        a = []
+        for f in range(F):
+            gt = sum(w["w_gate"][f][j] * h2[j] for j in range(D))
+            up = sum(w["w_up"][f][j] * h2[j] for j in range(D))
+            a.append(gt / (1.0 + math.exp(-gt)) * up)
+        out[i] = [x1[c] + sum(w["w_down"][c][f] * a[f] for f in range(F)) for c in range(D)]
+    return out, Km, Vm
+
+
+def _tiny_layers(seed, L, D, F, H_q, H_kv, d_h):
+    rng = _rng(seed)
+    return [dict(gamma_in=rng.uniform(0.5, 1.5, D), w_qkv=rng.standard_normal(((H_q + 2 * H_kv) * d_h, D)) / 2,
+                 w_o=rng.standard_normal((D, H_q * d_h)) / 2, gamma_post=rng.uniform(0.5, 1.5, D),
+                 w_gate=rng.standard_normal((F, D)) / 2, w_up=rng.standard_normal((F, D)) / 2,
+                 w_down=rng.standard_normal((D, F)) / 2) for _ in range(L)]
+
+
+def pin_target_layer_brute_force():
+    rng = _rng(43)
+    T, D, F, H_q, H_kv, d_h = 7, 6, 5, 4, 2, 4
+    S = np.array([1, 3, 4, 6])
+    x = rng.standard_normal((len(S), D))
+    K, V = rng.standard_normal((T, H_kv, d_h)), rng.standard_normal((T, H_kv, d_h))
+    w = _tiny_layers(44, 1, D, F, H_q, H_kv, d_h)[0]
+    got, Kg, Vg, _, _ = O.target_layer(x, S, K, V, w, H_q, H_kv, d_h, 10000.0, 1e-6)
+    want, Kw, Vw = _layer_loops(x, S, K, V, w, H_q, H_kv, d_h, 10000.0, 1e-6)
+    assert np.abs(got - want).max() < 1e-11
+    assert np.abs(Kg - Kw).max() < 1e-12 and np.abs(Vg - Vw).max() < 1e-12
+
+
+def pin_target_layer_zero_weights_pass_through():
+    """With W_o = 0 and W_down = 0 both residual branches vanish: the rows pass unchanged,
+    and the cache and outputs are those of the plain recompute of rmsnorm(x)."""
+    rng = _rng(45)
+    T, D, F, H_q, H_kv, d_h = 9, 8, 6, 4, 2, 4
+    S = np.array([0, 2, 5, 8])
+    x = rng.standard_normal((len(S), D))
+    K, V = rng.standard_normal((T, H_kv, d_h)), rng.standard_normal((T, H_kv, d_h))
+    w = _tiny_layers(46, 1, D, F, H_q, H_kv, d_h)[0]
+    w["w_o"][:] = 0.0
+    w["w_down"][:] = 0.0
+    out, Km, Vm, Oo, _ = O.target_layer(x, S, K, V, w, H_q, H_kv, d_h, 10000.0, 1e-6)
+    assert np.array_equal(out, x)
+    h = O.rmsnorm(x, w["gamma_in"], 1e-6)
+    q, kk, vv = O.recompute_qkv(h, w["w_qkv"], S, H_q, H_kv, d_h, 10000.0)
+    K2, V2 = O.scatter(K, V, S, kk, vv)
+    assert np.array_equal(Km, K2) and np.array_equal(Vm, V2)
+    assert np.abs(Oo - O.sparse_causal_attention(q, K2, V2, S)[0]).max() == 0.0
+
+
+def pin_chained_full_budget_is_dense_forward():
+    """Selecting every position turns the chained layers into the target's own forward pass:
+    each layer's cache is its own rotated K/V and each layer's rows follow from dense
+    causal attention (compared with torch's scaled-dot-product attention)."""
+    rng = _rng(47)
+    T, D, F, H_q, H_kv, d_h, L = 6, 8, 10, 4, 2, 4, 2
+    layers = _tiny_layers(48, L, D, F, H_q, H_kv, d_h)
+    x0 = rng.standard_normal((T, D))
+    S = np.arange(T)
+    K_tr = rng.standard_normal((L, T, H_kv, d_h))
+    V_tr = rng.standard_normal((L, T, H_kv, d_h))
+    out = O.chained_layers(x0, S, K_tr, V_tr, layers, H_q, H_kv, d_h)
+    x = x0
+    for l, w in enumerate(layers):
+        ms = np.mean(x * x, axis=1, keepdims=True)
+        h = x / np.sqrt(ms + 1e-6) * w["gamma_in"]
+        qkv = h @ w["w_qkv"].T
+        q = qkv[:, :H_q * d_h].reshape(T, H_q, d_h)
+        k = qkv[:, H_q * d_h:(H_q + H_kv) * d_h].reshape(T, H_kv, d_h)
+        v = qkv[:, (H_q + H_kv) * d_h:].reshape(T, H_kv, d_h)
+        ang = np.arange(T)[:, None, None] * 10000.0 ** (-2.0 * np.arange(d_h // 2) / d_h)
+        c, s_ = np.cos(ang), np.sin(ang)
+        rot = lambda a: np.concatenate([a[..., :d_h // 2] * c - a[..., d_h // 2:] * s_,
+                                        a[..., d_h // 2:] * c + a[..., :d_h // 2] * s_], -1)
+        q, k = rot(q), rot(k)
+        assert np.abs(out["K"][l] - k).max() < 1e-12 and np.abs(out["V"][l] - v).max() < 1e-12
+        o = _sdpa_causal(q, k, v)
+        x1 = x + o.reshape(T, -1) @ w["w_o"].T
+        h2 = x1 / np.sqrt(np.mean(x1 * x1, axis=1, keepdims=True) + 1e-6) * w["gamma_post"]
+        gt = h2 @ w["w_gate"].T
+        x = x1 + ((gt * torch.sigmoid(torch.from_numpy(gt)).numpy()) * (h2 @ w["w_up"].T)) @ w["w_down"].T
+        assert np.abs(out["X"][l + 1] - x).max() < 1e-10, l
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 
@@ -506,6 +656,31 @@ def _mut_budget_floor(T, pct):
 
 RECONSTRUCT = O.reconstruct
 
+
+def _mut_rmsnorm_no_root(x, gamma, eps):
+    return x / (np.mean(x * x, axis=-1, keepdims=True) + eps) * gamma
+
+
+def _mut_rmsnorm_sum(x, gamma, eps):
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * gamma
+
+
+def _mut_silu_sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _mut_mlp_gate_up_swapped(x, w_gate, w_up, w_down):
+    return (O_SILU(x @ w_up.T) * (x @ w_gate.T)) @ w_down.T
+
+
+def _mut_layer_no_residual(x_rows, S, K, V, w, H_q, H_kv, d_h, base, eps):
+    x2, K2, V2, Oo, lse = TARGET_LAYER(x_rows, S, K, V, w, H_q, H_kv, d_h, base, eps)
+    return x2 - x_rows, K2, V2, Oo, lse
+
+
+O_SILU = O.silu
+TARGET_LAYER = O.target_layer
+
 MUTANTS = {
     "rope_sign": ("rope", _mut_rope_sign),
     "rope_interleaved": ("rope", _mut_rope_interleaved),
@@ -518,6 +693,11 @@ MUTANTS = {
     "map_untransposed": ("map_latent", _mut_map_no_transpose),
     "reconstruct_kv_swapped": ("reconstruct", _mut_reconstruct_kv_swapped),
     "budget_floor": ("budget", _mut_budget_floor),
+    "rmsnorm_no_root": ("rmsnorm", _mut_rmsnorm_no_root),
+    "rmsnorm_sum_not_mean": ("rmsnorm", _mut_rmsnorm_sum),
+    "silu_is_sigmoid": ("silu", _mut_silu_sigmoid),
+    "mlp_gate_up_swapped": ("swiglu_mlp", _mut_mlp_gate_up_swapped),
+    "layer_no_residual": ("target_layer", _mut_layer_no_residual),
 }
 
 
