@@ -133,7 +133,10 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
         const int slab = R / WTN, rl = R % WTN;               // rl = j*16 + s  <->  tile row s*FN + j
         const int row = slab * WTN + (rl % 16) * FN + rl / 16;
         const int n = n0 + row < a.N ? n0 + row : 0;
-        bsrc[c] = Bg + (int64_t)n * a.ldb + ch * 8;
+        const bf16* brow = a.epi == EPI_SWIGLU
+                               ? ((n >> 3) & 1 ? a.B2 : a.B) + (int64_t)((n >> 4) * 8 + (n & 7)) * a.ldb
+                               : Bg + (int64_t)n * a.ldb;
+        bsrc[c] = brow + ch * 8;
     }
     auto issue = [&](bf16* st, int kt) {
         const int ka = (kt * BK) % a.K_a;
@@ -302,7 +305,48 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
         }
         return;
     }
+    if (a.epi == EPI_SWIGLU) {
+        // lane pairs (lr even, lr odd) hold the gate and the up columns of the same 8 features
+        const bool gate_lane = (lr & 1) == 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ml = wm * WTM + i * 16 + 4 * lq + v;
+                float up[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    up[j] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[i][j][v]), 0xB1, 0xF, 0xF,
+                                                                       false));
+                if (!gate_lane || ng >= a.N || s_src[ml] < 0) continue;
+                bf16x8 o;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float g = acc[i][j][v];
+                    o[j] = (bf16)(g / (1.f + __expf(-g)) * up[j]);
+                }
+                *(bf16x8*)(a.C + (int64_t)(m0 + ml) * a.ldc + (ng >> 4) * 8) = o;
+            }
+        }
+        return;
+    }
     if (ng >= a.N) return;
+    if (a.epi == EPI_RESID) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ml = wm * WTM + i * 16 + 4 * lq + v;
+                if (s_src[ml] < 0) continue;
+                const bf16x8 r = *(const bf16x8*)(a.R + (int64_t)(m0 + ml) * a.ldr + ng);
+                bf16x8 o;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = (bf16)((float)r[j] + acc[i][j][v]);
+                *(bf16x8*)(a.C + (int64_t)(m0 + ml) * a.ldc + ng) = o;
+            }
+        }
+        return;
+    }
     typedef __bf16 vecN __attribute__((ext_vector_type(FN)));
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -342,6 +386,29 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
         const f32x4 x1 = *(const f32x4*)(p + (int64_t)k * 65536 + 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) { s[i] += x0[i]; s[4 + i] += x1[i]; }
+    }
+    if (a.epi == EPI_SWIGLU) {            // the gate thread of each 16-column group
+        if ((n >> 3) & 1) return;
+        float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < sp.split; ++k) {
+            const f32x4 x0 = *(const f32x4*)(p + 8 + (int64_t)k * 65536);
+            const f32x4 x1 = *(const f32x4*)(p + 12 + (int64_t)k * 65536);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { u[i] += x0[i]; u[4 + i] += x1[i]; }
+        }
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (bf16)(s[i] / (1.f + __expf(-s[i])) * u[i]);
+        *(bf16x8*)(a.C + (int64_t)m * a.ldc + (n >> 4) * 8) = o;
+        return;
+    }
+    if (a.epi == EPI_RESID) {
+        const bf16x8 r = *(const bf16x8*)(a.R + (int64_t)m * a.ldr + n);
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (bf16)((float)r[i] + s[i]);
+        *(bf16x8*)(a.C + (int64_t)m * a.ldc + n) = o;
+        return;
     }
     if (a.epi == EPI_QKV) {               // same column handling as the tile epilogue
         const RowInfo ri = row_info(a.rows, m);
@@ -404,7 +471,9 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
 SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
     const int64_t tiles = (int64_t)cdiv(M, 256) * cdiv(N, 256) * groups;
     SplitPlan best{(int)tiles, 0, 1};
-    if ((epi != EPI_STORE && epi != EPI_QKV) || groups != 1 || tiles == 0 || tiles > INT32_MAX / 8) return best;
+    if ((epi != EPI_STORE && epi != EPI_QKV && epi != EPI_RESID && epi != EPI_SWIGLU) || groups != 1 || tiles == 0 ||
+        tiles > INT32_MAX / 8)
+        return best;
     const int nk = K / BK;
     const int64_t cu = CU_COUNT;
     double best_t = (double)((tiles + cu - 1) / cu);

@@ -451,7 +451,86 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
+// =========================================================================== target layer rows
+namespace {
+constexpr int NORM_THREADS = 256;
+constexpr int NORM_MAXC = 8;   // 16-byte chunks per thread: D <= 256 * 8 * 8
+
+// y[i] = x[i] / sqrt(mean_j(x[i][j]^2) + eps) * gamma: one row per block, fp32 arithmetic, the
+// sum of squares in a fixed order (per-thread chunks, then the wave and block trees)
+__global__ __launch_bounds__(NORM_THREADS) void rmsnorm_bf16_kernel(const bf16* x, const bf16* gamma, float eps,
+                                                                     int D, bf16* y) {
+    __shared__ float red[NORM_THREADS / 64];
+    const int64_t row = blockIdx.x;
+    const int nch = D / 8;
+    const bf16x8* xr = (const bf16x8*)(x + row * D);
+    bf16x8 v[NORM_MAXC];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NORM_MAXC; ++c) {
+        const int idx = threadIdx.x + c * NORM_THREADS;
+        if (idx < nch) {
+            v[c] = xr[idx];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss = __builtin_fmaf((float)v[c][j], (float)v[c][j], ss);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NORM_THREADS / 64; ++w) tot += red[w];
+    const float inv = 1.f / sqrtf(tot / (float)D + eps);
+    const bf16x8* gr = (const bf16x8*)gamma;
+    bf16x8* yr = (bf16x8*)(y + row * D);
+#pragma unroll
+    for (int c = 0; c < NORM_MAXC; ++c) {
+        const int idx = threadIdx.x + c * NORM_THREADS;
+        if (idx < nch) {
+            const bf16x8 g = gr[idx];
+            bf16x8 o;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = (bf16)((float)v[c][j] * inv * (float)g[j]);
+            yr[idx] = o;
+        }
+    }
+}
+
+// dst[i] = src[cu_tok[b] + sel[i]] (the selected rows of a batch, compact)
+__global__ __launch_bounds__(256) void gather_rows_bf16_kernel(const bf16* src, int D, const int32_t* sel,
+                                                                const int32_t* cu_tok, const int32_t* cu_sel,
+                                                                int n_req, bf16* dst) {
+    const int i = blockIdx.x;
+    const int b = find_request(cu_sel, n_req, i);
+    const bf16x8* sr = (const bf16x8*)(src + (int64_t)(cu_tok[b] + sel[i]) * D);
+    bf16x8* dr = (bf16x8*)(dst + (int64_t)i * D);
+    for (int c = threadIdx.x; c < D / 8; c += 256) dr[c] = sr[c];
+}
+
+}  // namespace
+
 // =========================================================================== launchers
+int rmsnorm_max_dim() { return NORM_THREADS * NORM_MAXC * 8; }
+
+hipError_t launch_rmsnorm_bf16(const bf16* x, const bf16* gamma, float eps, int64_t n, int D, bf16* y,
+                               hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    if (D % 8 || D > rmsnorm_max_dim() || n > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3((unsigned)n), dim3(NORM_THREADS), 0, s, x, gamma, eps, D, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows_bf16(const bf16* src, int D, const int32_t* sel, const int32_t* cu_tok,
+                                   const int32_t* cu_sel, int n_req, int64_t n_sel, bf16* dst, hipStream_t s) {
+    if (n_sel == 0) return hipSuccess;
+    if (D % 8 || n_sel > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gather_rows_bf16_kernel, dim3((unsigned)n_sel), dim3(256), 0, s, src, D, sel, cu_tok, cu_sel,
+                       n_req, dst);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_f64(int M, int N, int K, double alpha, const void* A, int ta, int64_t sam,
                            int64_t sak, const void* B, int tb, int64_t sbk, int64_t sbn, double* C,
                            int64_t ldc, bool accumulate, hipStream_t s) {

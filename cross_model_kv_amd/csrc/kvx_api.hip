@@ -1,9 +1,11 @@
 // C ABI of libkvx: argument validation (host only, before any GPU work is enqueued), workspace
 // sizing and the launch sequence of every entry point declared in include/kvx.h.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -526,10 +528,12 @@ hipError_t run_scatter(hipStream_t s, int32_t dtype, int32_t layer, const void* 
 // Steps 1-3 of one layer.  bf16: one GEMM whose epilogue rounds every output to bf16, keeps
 // the q columns in qkv and writes rotated k and v to the cache slots, with the arithmetic of
 // the separate steps (bit-identical to run_qkv + run_scatter).  fp32: the two separate kernels.
+// compact_rows: row i of x_l is the i-th selected row itself (the chained layer's rows), not
+// row cu_tokens[b] + sel[i] of the batch.
 hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, const void* x_l, const void* w_qkv,
                                 int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
                                 const kvx_batch* batch, const BatchInfo& bi, const int32_t* sel,
-                                const kvx_cache* cache, void* qkv, void* split_ws) {
+                                const kvx_cache* cache, void* qkv, void* split_ws, bool compact_rows = false) {
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     if (dtype != KVX_BF16) {
         if (hipError_t e = run_qkv(s, dtype, x_l, w_qkv, D, n_qkv, batch, bi, sel, qkv, split_ws)) return e;
@@ -541,6 +545,7 @@ hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, con
     a.B = (const bf16*)w_qkv; a.ldb = D;
     a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = 1;
     a.rows = sel_rows(batch, sel, bi.n_req);
+    if (compact_rows) a.rows.mode = 3;
     a.epi = EPI_QKV; a.C = (bf16*)qkv; a.ldc = n_qkv;
     a.kc = (bf16*)layer_base(cache->k, cache, layer, hd, dtype);
     a.vc = (bf16*)layer_base(cache->v, cache, layer, hd, dtype);
@@ -577,6 +582,67 @@ hipError_t run_attention(hipStream_t s, int32_t dtype, int32_t layer, const void
     at.bq = 1;
     at.n_blocks = (int)bi.n_sel;     // one wave per (selected row, head)
     return launch_attn_f32(at, s);
+}
+
+// ---- chained target layer (bf16)
+
+size_t gemm_split_ws(int64_t M, int N, int K, int epi) {
+    if (M <= 0 || M > INT32_MAX || N <= 0 || K <= 0) return 0;
+    return round256(gemm_bf16_split_bytes((int)M, N, K, 1, epi));
+}
+
+// out = resid + a w^T (compact rows)
+hipError_t run_linear_residual(hipStream_t s, const void* a, const void* w, const void* resid, void* out, int64_t M,
+                               int N, int K, void* split_ws) {
+    GemmArgs g{};
+    g.A = (const bf16*)a; g.lda = K; g.K_a = K;
+    g.B = (const bf16*)w; g.ldb = K;
+    g.M = (int)M; g.N = N; g.K = K; g.groups = 1;
+    g.epi = EPI_RESID; g.C = (bf16*)out; g.ldc = N; g.R = (const bf16*)resid; g.ldr = N;
+    g.split_ws = (float*)split_ws;
+    return launch_gemm_bf16(g, s);
+}
+
+// h = silu(x w_gate^T) * (x w_up^T)
+hipError_t run_swiglu(hipStream_t s, const void* x, const void* w_gate, const void* w_up, void* h, int64_t M, int D,
+                      int F, void* split_ws) {
+    GemmArgs g{};
+    g.A = (const bf16*)x; g.lda = D; g.K_a = D;
+    g.B = (const bf16*)w_gate; g.B2 = (const bf16*)w_up; g.ldb = D;
+    g.M = (int)M; g.N = 2 * F; g.K = D; g.groups = 1;
+    g.epi = EPI_SWIGLU; g.C = (bf16*)h; g.ldc = F;
+    g.split_ws = (float*)split_ws;
+    return launch_gemm_bf16(g, s);
+}
+
+struct LayerWs {
+    size_t xn, qkv, attn, mlp, split, total;
+};
+
+LayerWs layer_ws(int64_t k, int D, int F, int H_q, int H_kv, int d_h) {
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    LayerWs w{};
+    w.xn = round256((size_t)k * D * 2);
+    w.qkv = round256((size_t)k * n_qkv * 2);
+    w.attn = round256((size_t)k * H_q * d_h * 2);
+    w.mlp = round256((size_t)k * F * 2);
+    w.split = std::max(std::max(gemm_split_ws(k, n_qkv, D, EPI_QKV), gemm_split_ws(k, D, H_q * d_h, EPI_RESID)),
+                       std::max(gemm_split_ws(k, 2 * F, D, EPI_SWIGLU), gemm_split_ws(k, D, F, EPI_RESID)));
+    w.total = w.xn + w.qkv + w.attn + w.mlp + w.split;
+    return w;
+}
+
+kvx_status check_bf16_only(int32_t dtype, const char* what) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    if (dtype != KVX_BF16) return fail(KVX_ERR_UNSUPPORTED, "%s supports KVX_BF16 only", what);
+    return KVX_OK;
+}
+
+kvx_status check_ws(size_t need, const void* ws, size_t ws_bytes, const char* what) {
+    if (need && (!ws || ws_bytes < need))
+        return fail(KVX_ERR_WORKSPACE, "%s needs %zu workspace bytes (got %zu)", what, need, ws_bytes);
+    if (need && !aligned16(ws)) return fail(KVX_ERR_INVALID, "ws must be 16-byte aligned");
+    return KVX_OK;
 }
 
 }  // namespace
@@ -697,6 +763,152 @@ kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const 
                                      ws, split_ws), "recompute qkv/rope/scatter");
     return hip_status(run_attention(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse),
                       "attention");
+}
+
+kvx_status kvx_gather_rows(void* stream, int32_t dtype, const void* src, int32_t D, const kvx_batch* batch,
+                           const int32_t* sel, void* dst) {
+    if (kvx_status st = check_bf16_only(dtype, "gather_rows")) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(D > 0 && D % 8 == 0, "D must be a positive multiple of 8 (got %d)", D);
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(src, "src");
+    KVX_REQUIRE_PTR(sel, "sel");
+    KVX_REQUIRE_PTR(dst, "dst");
+    return hip_status(launch_gather_rows_bf16((const bf16*)src, D, sel, batch->cu_tokens_d, batch->cu_sel_d, bi.n_req,
+                                              bi.n_sel, (bf16*)dst, (hipStream_t)stream),
+                      "gather_rows");
+}
+
+kvx_status kvx_rmsnorm(void* stream, int32_t dtype, const void* x, const void* gamma, float eps, int64_t n,
+                       int32_t D, void* y) {
+    if (kvx_status st = check_bf16_only(dtype, "rmsnorm")) return st;
+    KVX_REQUIRE(n >= 0 && n <= INT32_MAX, "n must be in [0, 2^31) (got %lld)", (long long)n);
+    KVX_REQUIRE(D > 0 && D % 8 == 0 && D <= rmsnorm_max_dim(), "D must be a multiple of 8 in [8, %d] (got %d)",
+                rmsnorm_max_dim(), D);
+    KVX_REQUIRE(eps >= 0.f && eps < INFINITY, "eps must be finite and >= 0");
+    if (n == 0) return ok();
+    KVX_REQUIRE_PTR(x, "x");
+    KVX_REQUIRE_PTR(gamma, "gamma");
+    KVX_REQUIRE_PTR(y, "y");
+    return hip_status(launch_rmsnorm_bf16((const bf16*)x, (const bf16*)gamma, eps, n, D, (bf16*)y, (hipStream_t)stream),
+                      "rmsnorm");
+}
+
+kvx_status kvx_linear_residual_workspace(int32_t dtype, int64_t M, int32_t N, int32_t K, size_t* bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "linear_residual")) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(M >= 0 && M <= INT32_MAX && N > 0 && K > 0, "M must be in [0, 2^31), N and K positive");
+    *bytes = gemm_split_ws(M, N, K, EPI_RESID);
+    return ok();
+}
+
+kvx_status kvx_linear_residual(void* stream, int32_t dtype, const void* a, const void* w, const void* resid, void* out,
+                               int64_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "linear_residual")) return st;
+    KVX_REQUIRE(M >= 0 && M <= INT32_MAX, "M must be in [0, 2^31)");
+    KVX_REQUIRE(N > 0 && N % 8 == 0, "N must be a positive multiple of 8 (got %d)", N);
+    KVX_REQUIRE(K > 0 && K % 64 == 0, "K must be a positive multiple of 64 (got %d)", K);
+    if (M == 0) return ok();
+    KVX_REQUIRE_PTR(a, "a");
+    KVX_REQUIRE_PTR(w, "w");
+    KVX_REQUIRE_PTR(resid, "resid");
+    KVX_REQUIRE_PTR(out, "out");
+    const size_t need = gemm_split_ws(M, N, K, EPI_RESID);
+    if (kvx_status st = check_ws(need, ws, ws_bytes, "linear_residual")) return st;
+    return hip_status(run_linear_residual((hipStream_t)stream, a, w, resid, out, M, N, K, need ? ws : nullptr),
+                      "linear_residual");
+}
+
+kvx_status kvx_swiglu_workspace(int32_t dtype, int64_t M, int32_t D, int32_t F, size_t* bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "swiglu")) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(M >= 0 && M <= INT32_MAX && D > 0 && F > 0 && F <= INT32_MAX / 2,
+                "M must be in [0, 2^31), D and F positive");
+    *bytes = gemm_split_ws(M, 2 * F, D, EPI_SWIGLU);
+    return ok();
+}
+
+kvx_status kvx_swiglu(void* stream, int32_t dtype, const void* x, const void* w_gate, const void* w_up, void* h,
+                      int64_t M, int32_t D, int32_t F, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "swiglu")) return st;
+    KVX_REQUIRE(M >= 0 && M <= INT32_MAX, "M must be in [0, 2^31)");
+    KVX_REQUIRE(D > 0 && D % 64 == 0, "D must be a positive multiple of 64 (got %d)", D);
+    KVX_REQUIRE(F > 0 && F % 8 == 0 && F <= INT32_MAX / 2, "F must be a positive multiple of 8 (got %d)", F);
+    if (M == 0) return ok();
+    KVX_REQUIRE_PTR(x, "x");
+    KVX_REQUIRE_PTR(w_gate, "w_gate");
+    KVX_REQUIRE_PTR(w_up, "w_up");
+    KVX_REQUIRE_PTR(h, "h");
+    const size_t need = gemm_split_ws(M, 2 * F, D, EPI_SWIGLU);
+    if (kvx_status st = check_ws(need, ws, ws_bytes, "swiglu")) return st;
+    return hip_status(run_swiglu((hipStream_t)stream, x, w_gate, w_up, h, M, D, F, need ? ws : nullptr), "swiglu");
+}
+
+kvx_status kvx_target_layer_workspace(int32_t dtype, const kvx_batch* batch, int32_t D, int32_t F, int32_t H_q,
+                                      int32_t H_kv, int32_t d_h, size_t* bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "target_layer")) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(D > 0 && F > 0 && H_q > 0 && H_kv > 0 && d_h > 0 && F <= INT32_MAX / 2,
+                "D, F, H_q, H_kv and d_h must be positive");
+    *bytes = layer_ws(bi.n_sel, D, F, H_q, H_kv, d_h).total;
+    return ok();
+}
+
+kvx_status kvx_target_layer(void* stream, int32_t dtype, int32_t layer, void* x, const kvx_layer_weights* w,
+                            int32_t D, int32_t F, int32_t H_q, int32_t H_kv, int32_t d_h, float eps,
+                            const float* rope, int32_t max_pos, const kvx_batch* batch, const int32_t* sel,
+                            const kvx_cache* cache, void* attn_out, float* lse, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "target_layer")) return st;
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    if (bi.n_req > MAX_ATTN_REQ)
+        return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
+    KVX_REQUIRE(D > 0 && D % 64 == 0 && D <= rmsnorm_max_dim(), "D must be a multiple of 64 in [64, %d] (got %d)",
+                rmsnorm_max_dim(), D);
+    KVX_REQUIRE(F > 0 && F % 64 == 0 && F <= INT32_MAX / 2, "F must be a positive multiple of 64 (got %d)", F);
+    KVX_REQUIRE(eps >= 0.f && eps < INFINITY, "eps must be finite and >= 0");
+    KVX_REQUIRE(w, "w must not be null");
+    KVX_REQUIRE_PTR(w->gamma_in, "w.gamma_in");
+    KVX_REQUIRE_PTR(w->w_qkv, "w.w_qkv");
+    KVX_REQUIRE_PTR(w->w_o, "w.w_o");
+    KVX_REQUIRE_PTR(w->gamma_post, "w.gamma_post");
+    KVX_REQUIRE_PTR(w->w_gate, "w.w_gate");
+    KVX_REQUIRE_PTR(w->w_up, "w.w_up");
+    KVX_REQUIRE_PTR(w->w_down, "w.w_down");
+    if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(x, "x");
+    KVX_REQUIRE_PTR(sel, "sel");
+    if (attn_out) KVX_REQUIRE(aligned16(attn_out), "attn_out must be 16-byte aligned");
+    if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+    const int64_t k = bi.n_sel;
+    const LayerWs L = layer_ws(k, D, F, H_q, H_kv, d_h);
+    if (!ws || ws_bytes < L.total)
+        return fail(KVX_ERR_WORKSPACE, "target_layer needs %zu workspace bytes (got %zu)", L.total, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    bf16* xn = (bf16*)base;
+    void* qkv = base + L.xn;
+    void* attn = attn_out ? attn_out : (void*)(base + L.xn + L.qkv);
+    bf16* mlp = (bf16*)(base + L.xn + L.qkv + L.attn);
+    void* split = L.split ? (void*)(base + L.xn + L.qkv + L.attn + L.mlp) : nullptr;
+    bf16* xr = (bf16*)x;
+    KVX_TRY_HIP(launch_rmsnorm_bf16(xr, (const bf16*)w->gamma_in, eps, k, D, xn, s), "input norm");
+    KVX_TRY_HIP(run_qkv_rope_scatter(s, dtype, layer, xn, w->w_qkv, D, H_q, H_kv, d_h, rope, batch, bi, sel, cache,
+                                     qkv, split, true), "qkv/rope/scatter");
+    KVX_TRY_HIP(run_attention(s, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel, cache, attn, lse),
+                "attention");
+    KVX_TRY_HIP(run_linear_residual(s, attn, w->w_o, xr, xr, k, D, H_q * d_h, split), "output projection");
+    KVX_TRY_HIP(launch_rmsnorm_bf16(xr, (const bf16*)w->gamma_post, eps, k, D, xn, s), "post-attention norm");
+    KVX_TRY_HIP(run_swiglu(s, xn, w->w_gate, w->w_up, mlp, k, D, F, split), "gate/up");
+    return hip_status(run_linear_residual(s, mlp, w->w_down, xr, xr, k, D, F, split), "down projection");
 }
 
 }  // extern "C"

@@ -78,7 +78,9 @@ __device__ __forceinline__ int swz(int key) { return (key ^ (key >> 1)) & 7; }
 namespace kvx {
 
 struct RowMap {
-    int32_t mode;           // 0: row m is source row m; 1: all rows of a batch; 2: listed rows
+    int32_t mode;           // 0: row m is source row m; 1: all rows of a batch; 2: listed rows;
+                            // 3: row m is source row m, at the position list[m] (selected rows
+                            //    already gathered into a compact matrix)
     const int32_t* list;    // mode 2: request-local positions
     int32_t list_is_rest;   // mode 2: list is a complement list (else a selected list)
     const int32_t* cu_tok;  // device [n_req+1]
@@ -98,11 +100,14 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& rm, int m) {
                               : find_request(rm.cu_sel, rm.n_req, m);
         r.pos = rm.list[m];
         r.src = rm.cu_tok[r.b] + r.pos;
+    } else if (rm.mode == 3) {
+        r.b = find_request(rm.cu_sel, rm.n_req, m);
+        r.pos = rm.list[m];
     }
     return r;
 }
 
-enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2, EPI_QKV = 3 };
+enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2, EPI_QKV = 3, EPI_RESID = 4, EPI_SWIGLU = 5 };
 
 struct GemmArgs {
     // C[m][n] = sum_k A[src(m)][k mod K_a] * B[n][k]
@@ -123,6 +128,12 @@ struct GemmArgs {
     // store; the K columns are rounded to bf16, rotated (rotate-half, table rope at the row's
     // position) and written with the V columns to the layer's cache slots (kc, vc, hd, slots)
     const float* rope; int32_t q_cols; int32_t d_h;
+    // EPI_RESID: C[m][n] = R[m][n] + acc (C may be R: every element is read, then written, by
+    // one thread)
+    const bf16* R; int64_t ldr;
+    // EPI_SWIGLU: B row n is row (n/16)*8 + n%8 of the gate weight B (n/8 even) or of the up
+    // weight B2 (n/8 odd); C[m][f] = silu(gate_f) * up_f for f = (n/16)*8 + n%8, N = 2F
+    const bf16* B2;
 };
 
 // Rotate-half of one pair, in the order every kernel uses (results are bit-identical):

@@ -72,4 +72,12 @@ hipError_t launch_gemm_f32(const GemmF32Args& a, hipStream_t s);
 // partial[t] = sum_n P[t][n] * Z[t][n]
 hipError_t launch_rowdot_f32(const float* P, const float* Z, int64_t n, int r, float* out, hipStream_t s);
 
+// ---- rows of the chained target layer (bf16): RMS normalisation and the gather of the
+//      selected rows of a batch into a compact matrix
+int rmsnorm_max_dim();
+hipError_t launch_rmsnorm_bf16(const bf16* x, const bf16* gamma, float eps, int64_t n, int D, bf16* y,
+                               hipStream_t s);
+hipError_t launch_gather_rows_bf16(const bf16* src, int D, const int32_t* sel, const int32_t* cu_tok,
+                                   const int32_t* cu_sel, int n_req, int64_t n_sel, bf16* dst, hipStream_t s);
+
 }  // namespace kvx

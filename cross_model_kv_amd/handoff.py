@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from . import kvx
-from .synth import Inputs
+from .synth import ChainWeights, Inputs
 
 
 class Handoff:
@@ -85,3 +85,39 @@ class Handoff:
     @property
     def C(self) -> torch.Tensor:
         return self.rest[:self.batch.total_rest]
+
+
+class ChainedHandoff(Handoff):
+    """The handoff with the selected rows continuing through every target layer: after each
+    layer's recomputed attention, its output projection, norms and gated MLP run on the same
+    rows, and layer l+1 recomputes its Q/K/V from layer l's output rows (kvx_target_layer).
+    Layer 0 starts from the target's input rows at the selected positions."""
+
+    def __init__(self, inp: Inputs, cw: ChainWeights, device="cuda", keep_all_outputs: bool = True):
+        super().__init__(inp, device, keep_all_outputs)
+        wl = self.wl
+        self.cw = cw
+        k = max(self.batch.total_sel, 1)
+        self.x = torch.empty((k, wl.D), dtype=inp.x_l.dtype, device=self.device)
+        self.layers = [kvx.LayerWeights(cw.gamma_in[l], inp.w_qkv[l], cw.w_o[l], cw.gamma_post[l], cw.w_gate[l],
+                                        cw.w_up[l], cw.w_down[l]) for l in range(wl.L_t)]
+        need = kvx.target_layer_workspace(kvx._dtype(self.x), self.batch, wl.D, wl.F, wl.H_q, wl.H_kv, wl.d_h)
+        self.ws_layer = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+
+    def start_rows(self):
+        kvx.gather_rows(self.inp.x_l[0], self.batch, self.S, self.x)
+
+    def chain_layer(self, layer: int):
+        wl = self.wl
+        slot = layer if self.out.shape[0] > 1 else 0
+        kvx.target_layer(layer, self.x, self.layers[layer], wl.F, wl.H_q, wl.H_kv, wl.d_h, wl.norm_eps, self.rope,
+                         self.batch, self.S, self.cache, attn_out=self.out[slot], lse=self.lse[slot],
+                         ws=self.ws_layer)
+
+    def run(self, all_rows: bool = False):
+        self.map()
+        self.select()
+        self.reconstruct(all_rows)
+        self.start_rows()
+        for l in range(self.wl.L_t):
+            self.chain_layer(l)

@@ -46,6 +46,10 @@ class _Cache(ctypes.Structure):
                 ("page_table", ctypes.c_void_p)]
 
 
+class _LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("gamma_in", "w_qkv", "w_o", "gamma_post", "w_gate", "w_up", "w_down")]
+
+
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "kvx_last_error": ([], ctypes.c_char_p),
@@ -76,6 +80,17 @@ _SIGS = {
                               _P, ctypes.POINTER(_Cache), _P, _P, _SZ], _I32),
     "kvx_sparse_attention": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
                               ctypes.POINTER(_Cache), _P, _P], _I32),
+    "kvx_gather_rows": ([_P, _I32, _P, _I32, ctypes.POINTER(_Batch), _P, _P], _I32),
+    "kvx_rmsnorm": ([_P, _I32, _P, _P, ctypes.c_float, _I64, _I32, _P], _I32),
+    "kvx_linear_residual_workspace": ([_I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "kvx_linear_residual": ([_P, _I32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _SZ], _I32),
+    "kvx_swiglu_workspace": ([_I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "kvx_swiglu": ([_P, _I32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _SZ], _I32),
+    "kvx_target_layer_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
+                                   _I32),
+    "kvx_target_layer": ([_P, _I32, _I32, _P, ctypes.POINTER(_LayerWeights), _I32, _I32, _I32, _I32, _I32,
+                          ctypes.c_float, _P, _I32, ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P, _P, _P,
+                          _SZ], _I32),
 }
 
 _lib = None
@@ -382,3 +397,92 @@ def sparse_attention(layer: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: in
         _stream(qkv.device), _dtype(qkv), layer, _ptr(qkv), H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
         ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(out), _ptr(lse)))
     return out
+
+
+# ------------------------------------------------------------------------------ layer chaining
+
+def gather_rows(src: torch.Tensor, batch: Batch, sel: torch.Tensor, dst: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dst[i] = src[cu_tokens[b] + sel[i]]: the compact selected rows of a batch."""
+    D = src.shape[1]
+    if dst is None:
+        dst = torch.empty((max(batch.total_sel, 1), D), dtype=src.dtype, device=src.device)
+    _check("kvx_gather_rows", lib().kvx_gather_rows(_stream(src.device), _dtype(src), _ptr(src), D,
+                                                    ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None,
+                                                    _ptr(dst)))
+    return dst
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    n, D = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    _check("kvx_rmsnorm", lib().kvx_rmsnorm(_stream(x.device), _dtype(x), _ptr(x), _ptr(gamma), eps, n, D, _ptr(y)))
+    return y
+
+
+def _ws(need: int, ws: Optional[torch.Tensor], device):
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return (_ptr(ws), ws.numel()) if need else (None, 0)
+
+
+def linear_residual(a: torch.Tensor, w: torch.Tensor, resid: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = resid + a w^T (out may be resid)."""
+    M, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty_like(resid)
+    b = _SZ()
+    _check("kvx_linear_residual_workspace", lib().kvx_linear_residual_workspace(_dtype(a), M, N, K, ctypes.byref(b)))
+    wp, wn = _ws(b.value, ws, a.device)
+    _check("kvx_linear_residual", lib().kvx_linear_residual(_stream(a.device), _dtype(a), _ptr(a), _ptr(w),
+                                                            _ptr(resid), _ptr(out), M, N, K, wp, wn))
+    return out
+
+
+def swiglu(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, h: Optional[torch.Tensor] = None,
+           ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h = silu(x w_gate^T) * (x w_up^T)."""
+    M, D = x.shape
+    F = w_gate.shape[0]
+    if h is None:
+        h = torch.empty((M, F), dtype=x.dtype, device=x.device)
+    b = _SZ()
+    _check("kvx_swiglu_workspace", lib().kvx_swiglu_workspace(_dtype(x), M, D, F, ctypes.byref(b)))
+    wp, wn = _ws(b.value, ws, x.device)
+    _check("kvx_swiglu", lib().kvx_swiglu(_stream(x.device), _dtype(x), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(h),
+                                          M, D, F, wp, wn))
+    return h
+
+
+class LayerWeights:
+    """Device weights of one chained target layer (bf16, output-major)."""
+
+    def __init__(self, gamma_in, w_qkv, w_o, gamma_post, w_gate, w_up, w_down):
+        self.tensors = (gamma_in, w_qkv, w_o, gamma_post, w_gate, w_up, w_down)
+        self.c = _LayerWeights(*[t.data_ptr() for t in self.tensors])
+
+
+def target_layer_workspace(dtype: int, batch: Batch, D: int, F: int, H_q: int, H_kv: int, d_h: int) -> int:
+    b = _SZ()
+    _check("kvx_target_layer_workspace",
+           lib().kvx_target_layer_workspace(dtype, ctypes.byref(batch.c), D, F, H_q, H_kv, d_h, ctypes.byref(b)))
+    return b.value
+
+
+def target_layer(layer: int, x: torch.Tensor, w: LayerWeights, F: int, H_q: int, H_kv: int, d_h: int, eps: float,
+                 rope: torch.Tensor, batch: Batch, sel: torch.Tensor, cache: Cache,
+                 attn_out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One chained target layer on the compact selected rows x (updated in place)."""
+    D = x.shape[1]
+    dt = _dtype(x)
+    need = target_layer_workspace(dt, batch, D, F, H_q, H_kv, d_h)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check("kvx_target_layer", lib().kvx_target_layer(
+        _stream(x.device), dt, layer, _ptr(x), ctypes.byref(w.c), D, F, H_q, H_kv, d_h, eps, _ptr(rope),
+        rope.shape[0], ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c),
+        _ptr(attn_out), _ptr(lse), _ptr(ws), ws.numel()))
+    return x

@@ -175,6 +175,57 @@ def generate(wl: Workload, seed: int, device="cpu", where: str = "auto") -> Inpu
 
 
 # ---------------------------------------------------------------------------------
+# chained target layers: the weights of the rest of each target layer
+# ---------------------------------------------------------------------------------
+
+@dataclass
+class ChainWeights:
+    gamma_in: torch.Tensor      # [L_t, D]       U(0.5, 1.5)
+    w_o: torch.Tensor           # [L_t, D, H_q d_h] ~ N(0, 1/(H_q d_h))
+    gamma_post: torch.Tensor    # [L_t, D]       U(0.5, 1.5)
+    w_gate: torch.Tensor        # [L_t, F, D]    ~ N(0, 1/D)
+    w_up: torch.Tensor          # [L_t, F, D]    ~ N(0, 1/D)
+    w_down: torch.Tensor        # [L_t, D, F]    ~ N(0, 1/F)
+
+
+_CHAIN_SUBSEEDS = ("gamma_in", "w_o", "gamma_post", "w_gate", "w_up", "w_down")
+
+
+def chain_weights(wl: Workload, seed: int, device="cpu", where: str = "auto") -> ChainWeights:
+    """Weights of the chained layers of workload ``wl`` (bf16).  Sub-seeds come from
+    ``SeedSequence([seed, 404]).spawn(6)`` so the handoff's own inputs are unchanged."""
+    if wl.F <= 0:
+        raise ValueError(f"workload {wl.name} has no MLP width")
+    ss = dict(zip(_CHAIN_SUBSEEDS, np.random.SeedSequence([seed, 404]).spawn(len(_CHAIN_SUBSEEDS))))
+    dev = torch.device(device)
+    L, D, F, HD = wl.L_t, wl.D, wl.F, wl.H_q * wl.d_h
+    total = L * (D * HD + 3 * F * D)
+    on_host = where == "host" or (where == "auto" and (total <= HOST_LIMIT or dev.type == "cpu"))
+
+    def gains(name):
+        rng = np.random.Generator(np.random.PCG64(ss[name]))
+        return torch.from_numpy(rng.uniform(0.5, 1.5, size=(L, D)).astype(np.float32)).to(torch.bfloat16).to(dev)
+
+    def normal(name, shape, std):
+        if on_host:
+            return torch.from_numpy((_host_normal(ss[name], shape) * std).astype(np.float32)).to(torch.bfloat16).to(dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(_torch_seed(ss[name]))
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        rows = out.view(-1, shape[-1])
+        chunk = max(1, (1 << 26) // shape[-1])
+        for i in range(0, rows.shape[0], chunk):
+            blk = torch.randn((min(chunk, rows.shape[0] - i), shape[-1]), generator=g, device=dev,
+                              dtype=torch.float32)
+            rows[i:i + blk.shape[0]].copy_(blk.mul_(std))
+        return out
+
+    return ChainWeights(gains("gamma_in"), normal("w_o", (L, D, HD), 1.0 / math.sqrt(HD)), gains("gamma_post"),
+                        normal("w_gate", (L, F, D), 1.0 / math.sqrt(D)), normal("w_up", (L, F, D), 1.0 / math.sqrt(D)),
+                        normal("w_down", (L, D, F), 1.0 / math.sqrt(F)))
+
+
+# ---------------------------------------------------------------------------------
 # stage inputs: seeded stand-ins for the upstream results of a single stage
 # ---------------------------------------------------------------------------------
 

@@ -249,6 +249,78 @@ KVX_API kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t lay
                                         const int32_t* sel, const kvx_cache* cache, void* out,
                                         float* lse);
 
+/* ---------------------------------------------------------------------------------------
+ * Target layer chaining (bf16 only; KVX_ERR_UNSUPPORTED for KVX_F32).  PANORAMA abstract:
+ * the recomputed positions let the target model's own computation use the translated
+ * context.  The selected rows continue through the rest of each target layer, so layer l+1
+ * recomputes its Q/K/V from layer l's output rows instead of from a given input.  The block
+ * is the plain pre-norm decoder layer of the pages' target families (the pages name the
+ * model pairs, not their blocks):
+ *   h  = rmsnorm(x, gamma_in);  q, k, v = W_qkv h (k rotated, k and v written into the
+ *   cache, q rotated inside the attention);  o = attention over the mixed cache;
+ *   x1 = x + W_o o;  x2 = x1 + W_down (silu(W_gate h2) * (W_up h2)), h2 = rmsnorm(x1, gamma_post)
+ * with rmsnorm(x, g)_j = x_j / sqrt(mean(x^2) + eps) * g_j and silu(a) = a / (1 + e^-a).
+ * Rows are the compact selected rows of the batch (row i = the i-th entry of sel). */
+
+/* Per-layer weights of the chained block, all (device) bf16, output-major.
+ *   gamma_in, gamma_post [D];  w_qkv [n_qkv][D];  w_o [D][H_q * d_h];
+ *   w_gate, w_up [F][D];  w_down [D][F]. */
+typedef struct kvx_layer_weights {
+    const void* gamma_in;
+    const void* w_qkv;
+    const void* w_o;
+    const void* gamma_post;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+} kvx_layer_weights;
+
+/* dst[i] = src[cu_tokens[b] + sel[i]] for every selected row i (request b owning row i):
+ * the compact input rows of the chain.  src (device) [N][D], dst (device, out)
+ * [cu_sel[n_req]][D]; D % 8 == 0. */
+KVX_API kvx_status kvx_gather_rows(void* stream, int32_t dtype, const void* src, int32_t D,
+                                   const kvx_batch* batch, const int32_t* sel, void* dst);
+
+/* y[i] = rmsnorm(x[i], gamma) for n rows of width D (fp32 arithmetic, eps under the root).
+ * x, y (device) [n][D] (y may be x), gamma (device) [D]; D % 8 == 0, D <= 16384, eps >= 0. */
+KVX_API kvx_status kvx_rmsnorm(void* stream, int32_t dtype, const void* x, const void* gamma,
+                               float eps, int64_t n, int32_t D, void* y);
+
+/* out = resid + a W^T: a (device) [M][K], w (device) [N][K], resid and out (device) [M][N]
+ * (out may be resid: every element is read before it is written, by the same thread).
+ * One bf16 rounding of the fp32 sum.  K % 64 == 0, N % 8 == 0.  ws as in kvx_qkv_project
+ * (fp32 K-slice partials of a split last round, added in a fixed order). */
+KVX_API kvx_status kvx_linear_residual_workspace(int32_t dtype, int64_t M, int32_t N, int32_t K,
+                                                 size_t* bytes);
+KVX_API kvx_status kvx_linear_residual(void* stream, int32_t dtype, const void* a, const void* w,
+                                       const void* resid, void* out, int64_t M, int32_t N,
+                                       int32_t K, void* ws, size_t ws_bytes);
+
+/* h = silu(x W_gate^T) * (x W_up^T): x (device) [M][D], w_gate, w_up (device) [F][D],
+ * h (device, out) [M][F]; gate and up accumulate in fp32, one bf16 rounding of the product.
+ * D % 64 == 0, F % 8 == 0.  ws as in kvx_linear_residual. */
+KVX_API kvx_status kvx_swiglu_workspace(int32_t dtype, int64_t M, int32_t D, int32_t F, size_t* bytes);
+KVX_API kvx_status kvx_swiglu(void* stream, int32_t dtype, const void* x, const void* w_gate,
+                              const void* w_up, void* h, int64_t M, int32_t D, int32_t F,
+                              void* ws, size_t ws_bytes);
+
+/* One chained target layer on the selected rows.  x (device, in/out) [cu_sel[n_req]][D]:
+ * layer l's input rows on entry, its output rows on return.  Cache, rope, batch and sel as
+ * in kvx_recompute_attn (layer `layer` of the cache gets the recomputed k and v).
+ * attn_out (device, out, nullable) [cu_sel[n_req]][H_q][d_h] and lse (nullable) as in
+ * kvx_recompute_attn.  F % 64 == 0, D % 64 == 0, D <= 16384, eps >= 0.  ws (device) of
+ * kvx_target_layer_workspace() bytes: normalised rows, qkv rows, attention rows (when
+ * attn_out is NULL), MLP rows, then the largest split workspace of the four projections. */
+KVX_API kvx_status kvx_target_layer_workspace(int32_t dtype, const kvx_batch* batch, int32_t D,
+                                              int32_t F, int32_t H_q, int32_t H_kv, int32_t d_h,
+                                              size_t* bytes);
+KVX_API kvx_status kvx_target_layer(void* stream, int32_t dtype, int32_t layer, void* x,
+                                    const kvx_layer_weights* w, int32_t D, int32_t F,
+                                    int32_t H_q, int32_t H_kv, int32_t d_h, float eps,
+                                    const float* rope, int32_t max_pos, const kvx_batch* batch,
+                                    const int32_t* sel, const kvx_cache* cache, void* attn_out,
+                                    float* lse, void* ws, size_t ws_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -201,3 +201,46 @@ def test_qkv_rope_scatter_validation():
     status(call(ws=None), WORKSPACE)
     status(call(wsb=need.value - 1), WORKSPACE)
     status(call(dtype=3), UNSUPPORTED, "dtype")
+
+
+def test_chaining_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    c = cache()
+    # gather / rmsnorm
+    status(L.kvx_gather_rows(None, 0, A16, 64, ctypes.byref(bt.c), A16, A16B), UNSUPPORTED, "BF16 only")
+    status(L.kvx_gather_rows(None, 1, A16, 60, ctypes.byref(bt.c), A16, A16B), INVALID, "multiple of 8")
+    status(L.kvx_gather_rows(None, 1, A16, 64, ctypes.byref(bt.c), None, A16B), INVALID, "sel")
+    status(L.kvx_rmsnorm(None, 1, A16, A16B, 1e-6, 4, 20000, A16), INVALID, "D")
+    status(L.kvx_rmsnorm(None, 1, A16, A16B, -1.0, 4, 64, A16), INVALID, "eps")
+    status(L.kvx_rmsnorm(None, 1, A16, MIS, 1e-6, 4, 64, A16), INVALID, "gamma")
+    # linear + residual, gated MLP
+    need = ctypes.c_size_t()
+    assert L.kvx_linear_residual_workspace(1, 64, 4096, 4096, ctypes.byref(need)) == 0
+    assert need.value > 0, "a few rows over a wide K split along K"
+    status(L.kvx_linear_residual(None, 1, A16, A16, A16, A16, 64, 4096, 100, A16, need.value), INVALID, "K")
+    status(L.kvx_linear_residual(None, 1, A16, A16, A16, A16, 64, 4096, 4096, None, 0), WORKSPACE)
+    status(L.kvx_linear_residual(None, 1, A16, A16, A16, A16, 64, 4096, 4096, A16, need.value - 1), WORKSPACE)
+    status(L.kvx_swiglu(None, 1, A16, A16, A16, A16, 64, 100, 256, None, 0), INVALID, "D")
+    status(L.kvx_swiglu(None, 1, A16, A16, A16, A16, 64, 256, 12, None, 0), INVALID, "F")
+    status(L.kvx_swiglu(None, 1, A16, None, A16, A16, 64, 256, 256, None, 0), INVALID, "w_gate")
+    # the whole layer
+    assert L.kvx_target_layer_workspace(1, ctypes.byref(bt.c), 256, 512, 8, 2, 64, ctypes.byref(need)) == 0
+    assert need.value >= 45 * (256 + 12 * 64 + 8 * 64 + 512) * 2
+    W = kvx._LayerWeights(*([A16.value] * 7))
+    Wbad = kvx._LayerWeights(*([A16.value] * 5 + [None, A16.value]))
+
+    def call(dtype=1, layer=0, D=256, F=512, H_q=8, H_kv=2, d_h=64, eps=1e-6, w=W, ws=A16, wsb=None, max_pos=100):
+        return L.kvx_target_layer(None, dtype, layer, A16, ctypes.byref(w), D, F, H_q, H_kv, d_h, eps, A16, max_pos,
+                                  ctypes.byref(bt.c), A16, ctypes.byref(c), None, None, ws,
+                                  need.value if wsb is None else wsb)
+    status(call(dtype=0), UNSUPPORTED, "BF16 only")
+    status(call(d_h=96), UNSUPPORTED, "d_h")
+    status(call(D=100), INVALID, "D")
+    status(call(F=100), INVALID, "F")
+    status(call(eps=-1.0), INVALID, "eps")
+    status(call(w=Wbad), INVALID, "w_up")
+    status(call(max_pos=99), INVALID, "rope")
+    status(call(layer=2), INVALID, "layer")
+    status(call(ws=None), WORKSPACE)
+    status(call(wsb=need.value - 16), WORKSPACE)
