@@ -132,6 +132,153 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": 2 * n, "launches": 5}))
 
 
+def chain_layer_work(wl, k, pos_sum):
+    """Algorithmic flops / bytes of one chained target layer (bf16 storage)."""
+    HD, D, F, n_qkv, d_t = wl.H_q * wl.d_h, wl.D, wl.F, wl.n_qkv, wl.d_t
+    parts = {
+        "rmsnorm x2": (0.0, 2.0 * 2 * 2.0 * k * D),
+        "qkv_rope_scatter": (2.0 * k * D * n_qkv, 2.0 * (k * D + D * n_qkv + k * HD + k * d_t)),
+        "sparse_attention": (4.0 * wl.H_q * wl.d_h * pos_sum, 2.0 * (k * d_t + 2.0 * k * HD)),
+        "o_proj+residual": (2.0 * k * HD * D, 2.0 * (k * HD + D * HD + 2.0 * k * D)),
+        "swiglu": (2.0 * k * D * 2 * F, 2.0 * (k * D + 2.0 * F * D + k * F)),
+        "down+residual": (2.0 * k * F * D, 2.0 * (k * F + D * F + 2.0 * k * D)),
+    }
+    return parts
+
+
+def chain_cpu_baseline(inp, cw, wl, S, T, k, pos_sum):
+    """The fp64 oracle's chained layer on a bounded sample, scaled to one chained handoff: the
+    handoff's own stages as in cpu_baseline, plus one layer's norms, projections and MLP on
+    128 selected rows (the attention part is already in the handoff's sample)."""
+    from oracle import kvx_oracle as O
+    base = cpu_baseline(inp, wl, S, T, k, pos_sum)
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(S, min(128, len(S)), replace=False))
+    x = f64(inp.x_l[0][torch.as_tensor(rows, device=inp.x_l.device)])
+    o = rng.standard_normal((len(rows), wl.H_q * wl.d_h))
+    w_o, g1, g2 = f64(cw.w_o[0]), f64(cw.gamma_in[0]), f64(cw.gamma_post[0])
+    wg, wu, wd = f64(cw.w_gate[0]), f64(cw.w_up[0]), f64(cw.w_down[0])
+    t0 = time.perf_counter()
+    O.rmsnorm(x, g1, wl.norm_eps)
+    x1 = x + o @ w_o.T
+    x2 = x1 + O.swiglu_mlp(O.rmsnorm(x1, g2, wl.norm_eps), wg, wu, wd)
+    dt = (time.perf_counter() - t0) * k / len(rows) * wl.L_t
+    total = base["seconds_per_handoff"] + dt
+    base["parts_s"]["norms+o_proj+mlp"] = round(dt, 4)
+    base.update(value=T / total, seconds_per_handoff=total,
+                sample=base["sample"] + "; plus 1 layer of norms, output projection and gated MLP on 128 rows, "
+                                        "scaled by selected rows and layers")
+    return base
+
+
+def main_chain(args, wl):
+    """The handoff with the selected rows chained through every target layer."""
+    from cross_model_kv_amd import kvx, synth
+    from cross_model_kv_amd.handoff import ChainedHandoff
+
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = synth.generate(wl, args.seed, dev)
+    cw = synth.chain_weights(wl, args.seed, dev)
+    h = ChainedHandoff(inp, cw, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name} chained: inputs and one-time preparation {time.perf_counter() - t_gen:.1f}s")
+    T, k = h.batch.n_tokens, h.batch.total_sel
+    stream = torch.cuda.current_stream(dev)
+    names = ["map_latent", "score_select", "reconstruct", "gather_rows", "target_layer"]
+
+    def step(ev=None):
+        def mark(key):
+            if ev is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev.setdefault(key, []).append(e)
+        mark("t0")
+        h.map()
+        mark("map_latent")
+        h.select()
+        mark("score_select")
+        h.reconstruct()
+        mark("reconstruct")
+        h.start_rows()
+        mark("gather_rows")
+        for l in range(wl.L_t):
+            h.chain_layer(l)
+            mark("target_layer")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = {}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    order = ["map_latent", "score_select", "reconstruct", "gather_rows"] + ["target_layer"] * wl.L_t
+    stage_ms = {n: 0.0 for n in names}
+    launches = {n: 0 for n in names}
+    idx = {n: 0 for n in names}
+    for st in range(args.steps):
+        prev = events["t0"][st]
+        for n in order:
+            e = events[n][idx[n]]
+            idx[n] += 1
+            stage_ms[n] += prev.elapsed_time(e)
+            launches[n] += 1
+            prev = e
+
+    # the dominant kernel of a chained layer, the gated MLP's gate/up GEMM, timed live on its
+    # launch stream with the layer-0 weights and the chain's own rows
+    xn = torch.empty_like(h.x)
+    hmid = torch.empty((max(k, 1), wl.F), dtype=torch.bfloat16, device=dev)
+    kvx.rmsnorm(h.x, cw.gamma_post[0], wl.norm_eps, y=xn)
+    ws = torch.empty(max(kvx.target_layer_workspace(kvx.BF16, h.batch, wl.D, wl.F, wl.H_q, wl.H_kv, wl.d_h), 16),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        kvx.swiglu(xn[:k], cw.w_gate[0], cw.w_up[0], hmid[:k], ws)
+    n_rep = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_rep):
+        kvx.swiglu(xn[:k], cw.w_gate[0], cw.w_up[0], hmid[:k], ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    swiglu_ms = e0.elapsed_time(e1) / n_rep
+
+    S = h.S.cpu().numpy()
+    pos_sum = float(np.sum(S.astype(np.float64) + 1.0))
+    parts = chain_layer_work(wl, k, pos_sum)
+    layer_flops = sum(f for f, _ in parts.values())
+    layer_ms = stage_ms["target_layer"] / launches["target_layer"]
+    hand = stage_work(wl, T, k, pos_sum)
+    stages = {n: {"ms_per_step": round(stage_ms[n] / args.steps, 4),
+                  "ms_per_launch": round(stage_ms[n] / launches[n], 5)} for n in names}
+    for n in ("map_latent", "score_select", "reconstruct"):
+        stages[n]["tflops"] = round(hand[n]["flops"] / (stages[n]["ms_per_launch"] * 1e-3) / 1e12, 2)
+    stages["target_layer"]["tflops"] = round(layer_flops / (layer_ms * 1e-3) / 1e12, 2)
+    stages["target_layer"]["algorithmic_flops_per_launch"] = layer_flops
+    sw_flops = parts["swiglu"][0]
+    achieved = sw_flops / (swiglu_ms * 1e-3) / 1e12
+    line = {
+        "metric": "chained handoff tokens/s (map+select+recompute through every target layer) at 16K",
+        "value": T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "-chained", "T": T, "requests": h.batch.n_req, "target_layers": wl.L_t,
+                   "H_q": wl.H_q, "H_kv": wl.H_kv, "d_h": wl.d_h, "D": wl.D, "F": wl.F, "selected": k,
+                   "cache": "paged" if wl.paged else "contiguous", "parallelism": "none"},
+        "roofline": {"kernel": "swiglu (gate/up GEMM)", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": sw_flops, "avg_launch_ms": round(swiglu_ms, 5)},
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        line["cpu_baseline"] = chain_cpu_baseline(inp, cw, wl, S, T, k, pos_sum)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +288,8 @@ def main():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--chain", action="store_true",
+                    help="chain the selected rows through every target layer (norms, output projection, MLP)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -155,6 +304,9 @@ def main():
     from cross_model_kv_amd.handoff import Handoff
 
     wl = workloads.ALL[args.workload]
+    if args.chain:
+        main_chain(args, wl)
+        return
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     inp = synth.generate(wl, args.seed, dev)
