@@ -338,7 +338,8 @@ def main():
             kvx.qkv_rope_scatter(l, inp.x_l[l], inp.w_qkv[l], wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S,
                                  h.cache, qkv, ws_qkv)
             mark("qkv_rope_scatter")
-            kvx.sparse_attention(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache, h.out[l], h.lse[l])
+            kvx.sparse_attention(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache, h.out[l], h.lse[l],
+                                 ws_qkv)
             mark("sparse_attention")
 
     for _ in range(args.warmup):

@@ -29,12 +29,15 @@
 //    and rescale O and l (the ratio O / l does not depend on the reference used).
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
 //    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
+#include <algorithm>
+#include <climits>
+
 #include "kvx_internal.h"
 
 namespace kvx {
 namespace {
 
-constexpr int KT = 64;   // keys per tile
+constexpr int KT = ATTN_KEY_TILE;
 // LDS fragment reads kept in flight ahead of the MFMAs that consume them (measured best)
 constexpr int PF_K = 4;   // K fragments (one per MFMA)
 constexpr int PF_V = 8;   // transposed V reads (two per MFMA)
@@ -67,7 +70,9 @@ void attn_bf16_kernel(AttnArgs a) {
     const int hf = lane >> 5, lr = lane & 31;
     const int H_kv = a.H_kv, g = a.H_q / H_kv;
     const int hk = blockIdx.x % H_kv;
-    const int qb = a.n_blocks - 1 - (int)(blockIdx.x / H_kv);   // longest first
+    const int item = (int)(blockIdx.x / H_kv);
+    const int qb = a.n_blocks - 1 - item / a.n_split;   // longest first
+    const int chunk = item % a.n_split;
 
     // request of this query block
     int b = 0;
@@ -92,6 +97,15 @@ void attn_bf16_kernel(AttnArgs a) {
     const bool valid = qi < nq;
     const int h = hk * g + hh;
     const int p_row = valid ? a.sel[i0 + qi] : p_max;
+    // key tiles of this workgroup: all of the block's tiles, or one chunk of them
+    const int n_tiles_all = p_max / KT + 1;
+    int t_lo = 0, t_hi = n_tiles_all;
+    if (a.n_split > 1) {           // chunk c: the c-th run of split_len tiles from the block's end
+        t_hi = max(n_tiles_all - chunk * a.split_len, 0);
+        t_lo = max(t_hi - a.split_len, 0);
+    }
+    // a row whose position lies before the chunk has no key in it: its work is discarded
+    const bool active = p_row >= t_lo * KT;
 
     // ---- rotated, scaled Q fragments (B operand: row lr, dims 16c + 8hf + e)
     const float sl2 = 1.4426950408889634f / sqrtf((float)D_H);
@@ -211,11 +225,10 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) negm[i] = 0.f;
     // smallest query position of this wave: tiles ending at or below it need no mask
-    int p_min = p_row;
+    int p_min = active ? p_row : INT_MAX;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) p_min = min(p_min, __shfl_xor(p_min, o));
 
-    const int n_tiles = p_max / KT + 1;
     // value held by lane ^ 32 (the other 16 keys of each row's 32-key half tile)
     auto other_half = [&](float x) {
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -282,7 +295,10 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
             mx = fmaxf(mx, other_half(mx)) + m_ref;   // the row's true tile maximum
-            const float m_new = have_ref ? fmaxf(m_ref, mx) : mx;
+            // a row with every key of the tile masked (possible only in a chunk that starts
+            // past the row's position) keeps its reference: its P is 0
+            const bool none = !(mx > -INFINITY);
+            const float m_new = none ? m_ref : have_ref ? fmaxf(m_ref, mx) : mx;
             const float corr = have_ref ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
             l_lane *= corr;
 #pragma unroll
@@ -291,7 +307,7 @@ void attn_bf16_kernel(AttnArgs a) {
                 for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
             rs = exp_pack(true, m_ref - m_new);
             m_ref = m_new;
-            have_ref = true;
+            have_ref = have_ref || !none;
 #pragma unroll
             for (int i = 0; i < 16; ++i) negm[i] = -m_new;
         }
@@ -332,16 +348,18 @@ void attn_bf16_kernel(AttnArgs a) {
     };
 
     if (paged && pt_lds) __syncthreads();      // the staged page table, before the first loads
-    issue(lds0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < n_tiles; kt += 2) {
-        if (kt + 1 < n_tiles) issue(lds1, kt + 1);
+    if (t_lo < t_hi) {
+        issue(lds0, t_lo);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    for (int kt = t_lo; kt < t_hi; kt += 2) {
+        if (kt + 1 < t_hi) issue(lds1, kt + 1);
         compute(lds0, kt);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (kt + 1 < n_tiles) {
-            if (kt + 2 < n_tiles) issue(lds0, kt + 2);
+        if (kt + 1 < t_hi) {
+            if (kt + 2 < t_hi) issue(lds0, kt + 2);
             compute(lds1, kt + 1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -350,6 +368,27 @@ void attn_bf16_kernel(AttnArgs a) {
 
     const float l_run = l_lane + other_half(l_lane);
     if (!valid) return;
+    if (a.n_split > 1) {           // partial rows of this chunk: unnormalised O, m (log2), l
+        // rows without keys in the chunk leave only l = 0 (the merge skips their output)
+        const bool has = active && t_lo < t_hi;
+        const int64_t prow = ((int64_t)(i0 + qi) * a.H_q + h) * a.n_split + chunk;
+        float* po = a.part + prow * D_H;
+        if (has)
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 o;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[v] = oacc[d][4 * q4 + v];
+                    *(f32x4*)(po + d * 32 + 8 * q4 + 4 * hf) = o;
+                }
+        if (hf == 0) {
+            a.part_ml[prow * 2] = m_ref;
+            a.part_ml[prow * 2 + 1] = has ? l_run : 0.f;
+        }
+        return;
+    }
     const float inv = 1.f / l_run;
     bf16* orow = (bf16*)a.out + ((int64_t)(i0 + qi) * a.H_q + h) * D_H;
 #pragma unroll
@@ -365,11 +404,55 @@ void attn_bf16_kernel(AttnArgs a) {
         a.lse[(int64_t)(i0 + qi) * a.H_q + h] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
 }
 
+// Merge of a split attention: out = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over the
+// chunks with l_c > 0 (m their largest m_c), in chunk order; one thread per 8 output columns.
+template <int D_H>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, const float* ml, int n_split,
+                                                            int64_t rows, bf16* out, float* lse) {
+    constexpr int G = D_H / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * G) return;
+    const int64_t row = idx / G;
+    const int d0 = (int)(idx % G) * 8;
+    const float* mlr = ml + row * n_split * 2;
+    float m = -INFINITY;
+    for (int c = 0; c < n_split; ++c)
+        if (mlr[2 * c + 1] > 0.f) m = fmaxf(m, mlr[2 * c]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    for (int c = 0; c < n_split; ++c) {
+        const float lc = mlr[2 * c + 1];
+        if (!(lc > 0.f)) continue;
+        const float wgt = __builtin_amdgcn_exp2f(mlr[2 * c] - m);
+        L += wgt * lc;
+        const f32x4* pc = (const f32x4*)(part + (row * n_split + c) * D_H + d0);
+        const f32x4 x0 = pc[0], x1 = pc[1];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            acc[v] += wgt * x0[v];
+            acc[4 + v] += wgt * x1[v];
+        }
+    }
+    const float inv = 1.f / L;
+    bf16x8 o;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) o[v] = (bf16)(acc[v] * inv);
+    *(bf16x8*)(out + row * D_H + d0) = o;
+    if (lse && d0 == 0) lse[row] = (m + __log2f(L)) * 0.6931471805599453f;
+}
+
 template <int D_H>
 hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
     if (W != 8) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((int64_t)a.n_blocks * a.H_kv));
+    if (a.n_split < 1 || (a.n_split > 1 && (!a.part || !a.part_ml))) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((int64_t)a.n_blocks * a.n_split * a.H_kv));
     hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8>), grid, dim3(8 * 64), 0, s, a);
+    if (a.n_split == 1) return hipGetLastError();
+    if (hipError_t e = hipGetLastError()) return e;
+    const int64_t rows = a.n_rows_total * a.H_q;   // (selected row, query head) rows
+    const int64_t threads = rows * (D_H / 8);
+    hipLaunchKernelGGL((attn_combine_kernel<D_H>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       (const float*)a.part, (const float*)a.part_ml, a.n_split, rows, (bf16*)a.out, a.lse);
     return hipGetLastError();
 }
 
@@ -377,6 +460,22 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
 
 // Blocks of 8 waves (256 rows): floor(256 / g) queries, so a g that does not divide 256 leaves
 // fewer than g rows of the last wave idle (measured faster than g-wave blocks of 32 queries).
+int attn_bf16_split(int n_blocks, int H_kv, int max_T) {
+    constexpr int CUS = 256;
+    const int64_t items = (int64_t)n_blocks * H_kv;
+    if (items <= 0 || items >= 2 * CUS) return 1;
+    const int max_tiles = (max_T + KT - 1) / KT;
+    int c = (int)((2 * CUS + items - 1) / items);
+    c = std::min(c, std::min(max_tiles / 4, 64));
+    return std::max(c, 1);
+}
+
+size_t attn_bf16_split_bytes(int64_t n_sel, int H_q, int d_h, int n_split) {
+    if (n_split <= 1) return 0;
+    const size_t rows = (size_t)n_sel * H_q * n_split;
+    return ((rows * d_h * 4 + 255) & ~(size_t)255) + ((rows * 2 * 4 + 255) & ~(size_t)255);
+}
+
 int attn_bf16_block_queries(int g) {
     if (g <= 0 || g > 16) return 0;
     return 256 / g;            // 8 waves of 32 rows; g that do not divide 256 leave < g rows idle

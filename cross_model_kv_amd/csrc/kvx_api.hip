@@ -174,6 +174,17 @@ SlotMap slot_map(const kvx_cache* c, const kvx_batch* bt) {
 
 int32_t budget_of(int32_t T, int32_t pct) { return (int32_t)(((int64_t)pct * T + 99) / 100); }
 
+// Workspace of the attention's key-range split (bf16; 0 when the batch fills the GPU without it).
+size_t attn_split_bytes(int32_t dtype, const kvx_batch* batch, const BatchInfo& bi, int H_q, int H_kv, int d_h) {
+    if (dtype != KVX_BF16 || H_kv <= 0 || H_q % H_kv != 0 || bi.n_sel == 0) return 0;
+    const int bq = attn_bf16_block_queries(H_q / H_kv);
+    if (bq == 0) return 0;
+    int64_t n_blocks = 0;
+    for (int b = 0; b < bi.n_req; ++b) n_blocks += (batch->cu_sel_h[b + 1] - batch->cu_sel_h[b] + bq - 1) / bq;
+    if (n_blocks > INT32_MAX) return 0;
+    return attn_bf16_split_bytes(bi.n_sel, H_q, d_h, attn_bf16_split((int)n_blocks, H_kv, bi.max_T));
+}
+
 }  // namespace
 
 extern "C" {
@@ -431,7 +442,19 @@ kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, i
     KVX_REQUIRE(H_q > 0 && H_kv > 0 && d_h > 0, "H_q, H_kv and d_h must be positive");
     KVX_REQUIRE(D > 0, "D must be positive");
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
-    *bytes = round256((size_t)bi.n_sel * n_qkv * elem_size(dtype)) + qkv_split_bytes(dtype, bi.n_sel, D, n_qkv);
+    *bytes = round256((size_t)bi.n_sel * n_qkv * elem_size(dtype)) +
+             std::max(qkv_split_bytes(dtype, bi.n_sel, D, n_qkv), attn_split_bytes(dtype, batch, bi, H_q, H_kv, d_h));
+    return ok();
+}
+
+kvx_status kvx_sparse_attention_workspace(int32_t dtype, const kvx_batch* batch, int32_t H_q, int32_t H_kv,
+                                          int32_t d_h, size_t* bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(H_q > 0 && H_kv > 0 && d_h > 0, "H_q, H_kv and d_h must be positive");
+    *bytes = attn_split_bytes(dtype, batch, bi, H_q, H_kv, d_h);
     return ok();
 }
 
@@ -558,9 +581,10 @@ hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, con
 hipError_t run_attention(hipStream_t s, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
                          int32_t H_kv, int32_t d_h, const float* rope, const kvx_batch* batch,
                          const BatchInfo& bi, const int32_t* sel, const kvx_cache* cache, void* out,
-                         float* lse) {
+                         float* lse, void* split_ws) {
     const int hd = H_kv * d_h;
     AttnArgs at{};
+    at.n_split = 1;
     at.qkv = qkv; at.ld = (H_q + 2 * H_kv) * d_h;
     at.H_q = H_q; at.H_kv = H_kv; at.d_h = d_h;
     at.rope = rope;
@@ -577,6 +601,16 @@ hipError_t run_attention(hipStream_t s, int32_t dtype, int32_t layer, const void
             at.blk_cu[b + 1] = at.blk_cu[b] + (k + at.bq - 1) / at.bq;
         }
         at.n_blocks = at.blk_cu[bi.n_req];
+        if (split_ws) {
+            at.n_split = attn_bf16_split(at.n_blocks, H_kv, bi.max_T);
+            if (at.n_split > 1) {
+                const int max_tiles = (bi.max_T + ATTN_KEY_TILE - 1) / ATTN_KEY_TILE;
+                at.split_len = (max_tiles + at.n_split - 1) / at.n_split;
+                at.part = (float*)split_ws;
+                at.part_ml = at.part + round256((size_t)bi.n_sel * H_q * at.n_split * d_h * 4) / 4;
+                at.n_rows_total = bi.n_sel;
+            }
+        }
         return launch_attn_bf16(at, s);
     }
     at.bq = 1;
@@ -619,7 +653,7 @@ struct LayerWs {
     size_t xn, qkv, attn, mlp, split, total;
 };
 
-LayerWs layer_ws(int64_t k, int D, int F, int H_q, int H_kv, int d_h) {
+LayerWs layer_ws(int64_t k, int D, int F, int H_q, int H_kv, int d_h, size_t attn_split) {
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     LayerWs w{};
     w.xn = round256((size_t)k * D * 2);
@@ -628,6 +662,7 @@ LayerWs layer_ws(int64_t k, int D, int F, int H_q, int H_kv, int d_h) {
     w.mlp = round256((size_t)k * F * 2);
     w.split = std::max(std::max(gemm_split_ws(k, n_qkv, D, EPI_QKV), gemm_split_ws(k, D, H_q * d_h, EPI_RESID)),
                        std::max(gemm_split_ws(k, 2 * F, D, EPI_SWIGLU), gemm_split_ws(k, D, F, EPI_RESID)));
+    w.split = std::max(w.split, attn_split);
     w.total = w.xn + w.qkv + w.attn + w.mlp + w.split;
     return w;
 }
@@ -715,7 +750,7 @@ kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t layer, cons
 kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
                                 int32_t H_kv, int32_t d_h, const float* rope, int32_t max_pos,
                                 const kvx_batch* batch, const int32_t* sel, const kvx_cache* cache, void* out,
-                                float* lse) {
+                                float* lse, void* ws, size_t ws_bytes) {
     if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
     BatchInfo bi;
     if (kvx_status st = check_batch(batch, &bi)) return st;
@@ -727,8 +762,16 @@ kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, cons
     KVX_REQUIRE_PTR(qkv, "qkv");
     KVX_REQUIRE_PTR(out, "out");
     if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+    // no workspace: no key-range split; otherwise the full size is required
+    const size_t need = attn_split_bytes(dtype, batch, bi, H_q, H_kv, d_h);
+    const bool split = need && (ws || ws_bytes);
+    if (split) {
+        if (!ws || ws_bytes < need)
+            return fail(KVX_ERR_WORKSPACE, "sparse_attention needs %zu workspace bytes (got %zu)", need, ws_bytes);
+        KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    }
     return hip_status(run_attention((hipStream_t)stream, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel,
-                                    cache, out, lse), "sparse_attention");
+                                    cache, out, lse, split ? ws : nullptr), "sparse_attention");
 }
 
 kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const void* x_l, const void* w_qkv,
@@ -759,10 +802,11 @@ kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const 
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     const size_t qkv_bytes = round256((size_t)bi.n_sel * n_qkv * elem_size(dtype));
     void* split_ws = qkv_split_bytes(dtype, bi.n_sel, D, n_qkv) ? (char*)ws + qkv_bytes : nullptr;
+    void* attn_ws = attn_split_bytes(dtype, batch, bi, H_q, H_kv, d_h) ? (char*)ws + qkv_bytes : nullptr;
     KVX_TRY_HIP(run_qkv_rope_scatter(s, dtype, layer, x_l, w_qkv, D, H_q, H_kv, d_h, rope, batch, bi, sel, cache,
                                      ws, split_ws), "recompute qkv/rope/scatter");
-    return hip_status(run_attention(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse),
-                      "attention");
+    return hip_status(run_attention(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse,
+                                    attn_ws), "attention");
 }
 
 kvx_status kvx_gather_rows(void* stream, int32_t dtype, const void* src, int32_t D, const kvx_batch* batch,
@@ -854,7 +898,7 @@ kvx_status kvx_target_layer_workspace(int32_t dtype, const kvx_batch* batch, int
     KVX_REQUIRE(bytes, "bytes must not be null");
     KVX_REQUIRE(D > 0 && F > 0 && H_q > 0 && H_kv > 0 && d_h > 0 && F <= INT32_MAX / 2,
                 "D, F, H_q, H_kv and d_h must be positive");
-    *bytes = layer_ws(bi.n_sel, D, F, H_q, H_kv, d_h).total;
+    *bytes = layer_ws(bi.n_sel, D, F, H_q, H_kv, d_h, attn_split_bytes(dtype, batch, bi, H_q, H_kv, d_h)).total;
     return ok();
 }
 
@@ -888,7 +932,8 @@ kvx_status kvx_target_layer(void* stream, int32_t dtype, int32_t layer, void* x,
     if (attn_out) KVX_REQUIRE(aligned16(attn_out), "attn_out must be 16-byte aligned");
     if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
     const int64_t k = bi.n_sel;
-    const LayerWs L = layer_ws(k, D, F, H_q, H_kv, d_h);
+    const size_t attn_split = attn_split_bytes(dtype, batch, bi, H_q, H_kv, d_h);
+    const LayerWs L = layer_ws(k, D, F, H_q, H_kv, d_h, attn_split);
     if (!ws || ws_bytes < L.total)
         return fail(KVX_ERR_WORKSPACE, "target_layer needs %zu workspace bytes (got %zu)", L.total, ws_bytes);
     KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
@@ -903,8 +948,8 @@ kvx_status kvx_target_layer(void* stream, int32_t dtype, int32_t layer, void* x,
     KVX_TRY_HIP(launch_rmsnorm_bf16(xr, (const bf16*)w->gamma_in, eps, k, D, xn, s), "input norm");
     KVX_TRY_HIP(run_qkv_rope_scatter(s, dtype, layer, xn, w->w_qkv, D, H_q, H_kv, d_h, rope, batch, bi, sel, cache,
                                      qkv, split, true), "qkv/rope/scatter");
-    KVX_TRY_HIP(run_attention(s, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel, cache, attn, lse),
-                "attention");
+    KVX_TRY_HIP(run_attention(s, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel, cache, attn, lse,
+                              attn_split ? split : nullptr), "attention");
     KVX_TRY_HIP(run_linear_residual(s, attn, w->w_o, xr, xr, k, D, H_q * d_h, split), "output projection");
     KVX_TRY_HIP(launch_rmsnorm_bf16(xr, (const bf16*)w->gamma_post, eps, k, D, xn, s), "post-attention norm");
     KVX_TRY_HIP(run_swiglu(s, xn, w->w_gate, w->w_up, mlp, k, D, F, split), "gate/up");

@@ -39,6 +39,7 @@ hipError_t launch_rope_scatter(const ScatterArgs& a, int dtype, hipStream_t s);
 
 // Requests per recompute_attn call: the query-block plan travels in the kernel arguments.
 constexpr int MAX_ATTN_REQ = 256;
+constexpr int ATTN_KEY_TILE = 64;     // keys per tile of the bf16 attention
 
 struct AttnArgs {
     const void* qkv; int64_t ld;      // Q heads are the first H_q*d_h columns
@@ -50,8 +51,20 @@ struct AttnArgs {
     SlotMap slots;
     const void* kc; const void* vc;   // layer base pointers
     void* out; float* lse;
+    // key-range split (bf16 path): chunk c of a query block is the c-th run of split_len key
+    // tiles counted back from the block's last tile (n_split chunks, one workgroup each; short
+    // blocks leave the later chunks empty).  A chunk leaves its unnormalised output rows (fp32)
+    // in part[(row * n_split + c) * d_h] and (m, l) in part_ml[(row * n_split + c) * 2], row =
+    // i * H_q + h, l = 0 for rows without keys in it; a combine kernel merges them.
+    // n_split = 1: no split, no partials.
+    int n_split; int split_len; float* part; float* part_ml; int64_t n_rows_total;
     int32_t blk_cu[MAX_ATTN_REQ + 1];  // blk_cu[b] = sum_{b' < b} ceil(k_b' / bq)
 };
+// chunks per query block for the key-range split: enough workgroups to fill the GPU twice
+// over, chunks of at least 4 key tiles
+int attn_bf16_split(int n_blocks, int H_kv, int max_T);
+// fp32 partial workspace of a split attention over n_sel selected rows
+size_t attn_bf16_split_bytes(int64_t n_sel, int H_q, int d_h, int n_split);
 // bf16 matrix-core path (d_h 64 or 128); returns the number of queries per block it uses
 int attn_bf16_block_queries(int g);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);

@@ -78,8 +78,9 @@ _SIGS = {
                           ctypes.POINTER(_Cache)], _I32),
     "kvx_qkv_rope_scatter": ([_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch),
                               _P, ctypes.POINTER(_Cache), _P, _P, _SZ], _I32),
+    "kvx_sparse_attention_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_sparse_attention": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
-                              ctypes.POINTER(_Cache), _P, _P], _I32),
+                              ctypes.POINTER(_Cache), _P, _P, _P, _SZ], _I32),
     "kvx_gather_rows": ([_P, _I32, _P, _I32, ctypes.POINTER(_Batch), _P, _P], _I32),
     "kvx_rmsnorm": ([_P, _I32, _P, _P, ctypes.c_float, _I64, _I32, _P], _I32),
     "kvx_linear_residual_workspace": ([_I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
@@ -390,12 +391,26 @@ def qkv_rope_scatter(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: in
     return qkv
 
 
+def sparse_attention_workspace(dtype: int, batch: Batch, H_q: int, H_kv: int, d_h: int) -> int:
+    b = _SZ()
+    _check("kvx_sparse_attention_workspace",
+           lib().kvx_sparse_attention_workspace(dtype, ctypes.byref(batch.c), H_q, H_kv, d_h, ctypes.byref(b)))
+    return b.value
+
+
 def sparse_attention(layer: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, rope: torch.Tensor,
                      batch: Batch, sel: torch.Tensor, cache: Cache, out: torch.Tensor,
-                     lse: Optional[torch.Tensor] = None):
+                     lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, split: bool = True):
+    """Causal attention of the selected queries; with split=False no workspace is passed and
+    the keys of a query block are never cut into chunks."""
+    dt = _dtype(qkv)
+    need = sparse_attention_workspace(dt, batch, H_q, H_kv, d_h) if split else 0
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=qkv.device)
     _check("kvx_sparse_attention", lib().kvx_sparse_attention(
-        _stream(qkv.device), _dtype(qkv), layer, _ptr(qkv), H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
-        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(out), _ptr(lse)))
+        _stream(qkv.device), dt, layer, _ptr(qkv), H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
+        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(out), _ptr(lse),
+        _ptr(ws) if need else None, ws.numel() if need else 0))
     return out
 
 

@@ -190,8 +190,8 @@ KVX_API kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_
  *   with max_pos > every T_b; sel (device) [cu_sel[n_req]]; out (device, out)
  *   [cu_sel[n_req]][H_q][d_h]; lse (device, out, nullable) [cu_sel[n_req]][H_q] fp32.
  *   d_h must be 64 or 128, H_q % H_kv == 0, H_q / H_kv <= 16; bf16 needs D % 64 == 0.
- *   ws (device) of kvx_recompute_attn_workspace() bytes (the qkv rows, then the
- *   workspace of kvx_qkv_project). */
+ *   ws (device) of kvx_recompute_attn_workspace() bytes (the qkv rows, then one region
+ *   that serves the projection's split tail and then the attention's key-range split). */
 KVX_API kvx_status kvx_recompute_attn_workspace(int32_t dtype, const kvx_batch* batch, int32_t D,
                                         int32_t H_q, int32_t H_kv, int32_t d_h, size_t* bytes);
 KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const void* x_l,
@@ -242,12 +242,21 @@ KVX_API kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t lay
 
 /* kvx_sparse_attention: step 4, causal attention of the selected queries (the q part of
  * the qkv rows, rotated at their true positions inside the kernel) over layer `layer` of
- * the cache; out and lse as in kvx_recompute_attn.  d_h must be 64 or 128. */
+ * the cache; out and lse as in kvx_recompute_attn.  d_h must be 64 or 128.
+ * ws (device): kvx_sparse_attention_workspace() bytes.  When the query blocks are too few
+ * to fill the GPU (bf16), each block's keys are cut into equal chunks that run as separate
+ * workgroups; every chunk leaves fp32 partial rows (unnormalised output, maximum and sum) in
+ * ws, and a second kernel merges them in chunk order (results do not depend on timing).
+ * ws = NULL with ws_bytes = 0 runs without the split (slower on small batches; the result
+ * differs from the split one only by rounding); a non-NULL ws must hold the full size. */
+KVX_API kvx_status kvx_sparse_attention_workspace(int32_t dtype, const kvx_batch* batch,
+                                                  int32_t H_q, int32_t H_kv, int32_t d_h,
+                                                  size_t* bytes);
 KVX_API kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, const void* qkv,
                                         int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
                                         int32_t max_pos, const kvx_batch* batch,
                                         const int32_t* sel, const kvx_cache* cache, void* out,
-                                        float* lse);
+                                        float* lse, void* ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------------------
  * Target layer chaining (bf16 only; KVX_ERR_UNSUPPORTED for KVX_F32).  PANORAMA abstract:

@@ -351,6 +351,9 @@ RECOMPUTE_CASES = {
     # D = 2048: the projection's tiles fill under half a round, so they are split along D
     "bf16-g4-wide-D": small("rc-bf16-wide-D", H_q=8, H_kv=2, d_h=64, D=2048, T=600, pct=40),
     "bf16-g8-wide-D": small("rc-bf16-g8-wide-D", H_q=16, H_kv=2, D=2048, T=600, pct=40),
+    # longer paged requests: few query blocks, each cut into key chunks
+    "bf16-g8-batched-paged-long": small("rc-bf16-batched-long", H_q=16, H_kv=2, n_req=3, t_min=700, t_max=1500,
+                                        pct_choices=(20, 30, 40), paged=True),
 }
 
 
@@ -448,3 +451,52 @@ def test_map_split_all_tiles():
     torch.cuda.synchronize()
     assert torch.equal(z1, z2)
     assert_close(f64(z1), O.map_latent(f64(x), f64(w)), 2e-2, "split map")
+
+
+@pytest.mark.parametrize("name", ["bf16-g8", "bf16-g5", "bf16-g7-d64", "bf16-g8-batched-paged-long"])
+def test_attention_key_split(name):
+    """Few query blocks: the keys of every block are cut into chunks run as separate
+    workgroups and merged by a second kernel.  Both that path and the unsplit one match the
+    oracle, and they agree with each other to rounding."""
+    wl = RECOMPUTE_CASES[name]
+    say(f"[key split] {name}")
+    inp = synth.generate(wl, 91, DEV)
+    batch = kvx.Batch.for_budgets(inp.lengths, inp.pcts, DEV)
+    assert kvx.sparse_attention_workspace(kvx.BF16, batch, wl.H_q, wl.H_kv, wl.d_h) > 0, "expected a split"
+    S_list = [synth.random_subset(t, k, 91 + b) for b, (t, k) in enumerate(zip(inp.lengths, batch.n_sel))]
+    sel = torch.from_numpy(np.concatenate(S_list).astype(np.int32)).to(DEV)
+    n_slots = inp.n_pages * wl.page_size if wl.paged else batch.n_tokens
+    pt = inp.page_table if wl.paged else None
+    shape = (wl.L_t, n_slots, wl.H_kv, wl.d_h)
+    cache = kvx.Cache(synth.cache_fill(shape, 92, device=DEV), synth.cache_fill(shape, 93, device=DEV), wl.L_t,
+                      n_slots, pt, wl.page_size)
+    rope = kvx.rope_table(wl.rope_base, wl.d_h, max(inp.lengths), DEV)
+    qkv = synth.latent(batch.total_sel, wl.n_qkv, 94, device=DEV)
+    k = batch.total_sel
+    o1 = torch.empty((k, wl.H_q, wl.d_h), dtype=torch.bfloat16, device=DEV)
+    o2 = torch.empty_like(o1)
+    o3 = torch.empty_like(o1)
+    l1 = torch.empty((k, wl.H_q), dtype=torch.float32, device=DEV)
+    l2 = torch.empty_like(l1)
+    kvx.sparse_attention(0, qkv, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, cache, o1, l1)
+    kvx.sparse_attention(0, qkv, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, cache, o2, l2, split=False)
+    kvx.sparse_attention(0, qkv, wl.H_q, wl.H_kv, wl.d_h, rope, batch, sel, cache, o3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3), "split attention is not deterministic"
+    q_all = f64(qkv[:, :wl.H_q * wl.d_h]).reshape(k, wl.H_q, wl.d_h)
+    cu, cs = batch.cu_tokens, batch.cu_sel
+    ptn = inp.page_table.cpu().numpy() if wl.paged else None
+    for b, T in enumerate(inp.lengths):
+        S = S_list[b]
+        if len(S) == 0:
+            continue
+        K0 = logical(cache.k, 0, b, T, cu, ptn, wl.page_size)
+        V0 = logical(cache.v, 0, b, T, cu, ptn, wl.page_size)
+        q = O.rope(q_all[cs[b]:cs[b + 1]], S[:, None], wl.rope_base)
+        o_ref, lse_ref = O.sparse_causal_attention(q, K0, V0, S)
+        for o, l, what in ((o1, l1, "split"), (o2, l2, "unsplit")):
+            ob = f64(o[cs[b]:cs[b + 1]])
+            assert min_row_cosine(ob, o_ref) >= 0.999, what
+            assert_close(ob, o_ref, 2e-2, f"attention ({what})")
+            assert np.abs(f64(l[cs[b]:cs[b + 1]]) - lse_ref).max() <= 2e-2, what
+    assert rel_norm(f64(o1), f64(o2)) < 1e-2
