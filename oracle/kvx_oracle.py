@@ -301,6 +301,42 @@ def chained_layers(x0_rows: np.ndarray, S: np.ndarray, K_tr: np.ndarray, V_tr: n
     return dict(X=X, K=K, V=V, O=O, LSE=LSE)
 
 
+# ------------------------------------------------------------------------------------
+# first token after the handoff
+# ------------------------------------------------------------------------------------
+
+def lm_head(x: np.ndarray, gamma: np.ndarray, w_lm: np.ndarray, eps: float) -> np.ndarray:
+    """Logits of rows x: the final RMS normalisation, then the vocabulary projection
+    w_lm [V, D] (output-major)."""
+    return rmsnorm(x, gamma, eps) @ w_lm.T
+
+
+def argmax_lowest(logits: np.ndarray) -> np.ndarray:
+    """Index of the largest logit of every row; ties go to the lowest index."""
+    return np.argmax(logits, axis=-1)
+
+
+def first_token(x0_last: np.ndarray, p_last: int, K: np.ndarray, V: np.ndarray,
+                layers: Sequence[Dict[str, np.ndarray]], gamma_final: np.ndarray, w_lm: np.ndarray,
+                H_q: int, H_kv: int, d_h: int, base: float = 10000.0, eps: float = 1e-6):
+    """The first target token after a handoff (the time-to-first-token step).
+
+    The last prompt position p_last runs through every target layer as a single recomputed
+    row over the layer's mixed cache K[l], V[l] [T, H_kv, d_h] (its own k, v recomputed and
+    written there), starting from the target's input row x0_last [D]; its final row is
+    normalised and projected onto the vocabulary.  Returns the logits [V], the token (the
+    argmax, ties to the lowest index) and the updated cache.
+    """
+    S = np.array([p_last])
+    x = x0_last[None, :]
+    K = K.copy()
+    V = V.copy()
+    for l, w in enumerate(layers):
+        x, K[l], V[l], _, _ = target_layer(x, S, K[l], V[l], w, H_q, H_kv, d_h, base, eps)
+    logits = lm_head(x, gamma_final, w_lm, eps)[0]
+    return logits, int(argmax_lowest(logits)), K, V
+
+
 def score_gap(s: np.ndarray, k: int) -> float:
     """Relative gap between the k-th and (k+1)-th largest scores (inf when k is 0 or T)."""
     T = s.shape[0]

@@ -574,6 +574,39 @@ def pin_chained_full_budget_is_dense_forward():
         assert np.abs(out["X"][l + 1] - x).max() < 1e-10, l
 
 
+def pin_argmax_ties_lowest():
+    assert O.argmax_lowest(np.array([1.0, 3.0, 3.0, 2.0])) == 1
+    assert list(O.argmax_lowest(np.array([[0.0, 0.0], [-1.0, -2.0]]))) == [0, 0]
+
+
+def pin_lm_head_hand():
+    """rmsnorm([3, 4], gain 1) = [3, 4] / sqrt(12.5); against w rows e1, e2, e1 + e2."""
+    x = np.array([[3.0, 4.0]])
+    w = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    r = math.sqrt(12.5)
+    assert np.abs(O.lm_head(x, np.ones(2), w, 0.0) - np.array([[3 / r, 4 / r, 7 / r]])).max() < 1e-15
+
+
+def pin_first_token_full_budget_is_last_dense_row():
+    """After a 100% budget the cache is the target's own, and the first-token step for the
+    last position reproduces the dense forward's last row: its logits are the LM head of
+    that row, and its rewritten cache rows are unchanged."""
+    rng = _rng(49)
+    T, D, F, H_q, H_kv, d_h, L, Vv = 6, 8, 10, 4, 2, 4, 2, 11
+    layers = _tiny_layers(50, L, D, F, H_q, H_kv, d_h)
+    x0 = rng.standard_normal((T, D))
+    full = O.chained_layers(x0, np.arange(T), rng.standard_normal((L, T, H_kv, d_h)),
+                            rng.standard_normal((L, T, H_kv, d_h)), layers, H_q, H_kv, d_h)
+    g = rng.uniform(0.5, 1.5, D)
+    w_lm = rng.standard_normal((Vv, D))
+    logits, tok, K, V = O.first_token(x0[T - 1], T - 1, full["K"], full["V"], layers, g, w_lm, H_q, H_kv, d_h)
+    last = full["X"][-1][T - 1]
+    want = (last / np.sqrt(np.mean(last ** 2) + 1e-6) * g) @ w_lm.T
+    assert np.abs(logits - want).max() < 1e-10
+    assert tok == int(np.argmax(want))
+    assert np.abs(K - full["K"]).max() < 1e-12 and np.abs(V - full["V"]).max() < 1e-12
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 
@@ -681,6 +714,15 @@ def _mut_layer_no_residual(x_rows, S, K, V, w, H_q, H_kv, d_h, base, eps):
 O_SILU = O.silu
 TARGET_LAYER = O.target_layer
 
+
+def _mut_lm_head_no_norm(x, gamma, w_lm, eps):
+    return (x * gamma) @ w_lm.T
+
+
+def _mut_argmax_highest(logits):
+    a = np.asarray(logits)
+    return a.shape[-1] - 1 - np.argmax(a[..., ::-1], axis=-1)
+
 MUTANTS = {
     "rope_sign": ("rope", _mut_rope_sign),
     "rope_interleaved": ("rope", _mut_rope_interleaved),
@@ -698,6 +740,8 @@ MUTANTS = {
     "silu_is_sigmoid": ("silu", _mut_silu_sigmoid),
     "mlp_gate_up_swapped": ("swiglu_mlp", _mut_mlp_gate_up_swapped),
     "layer_no_residual": ("target_layer", _mut_layer_no_residual),
+    "lm_head_no_norm": ("lm_head", _mut_lm_head_no_norm),
+    "argmax_ties_highest": ("argmax_lowest", _mut_argmax_highest),
 }
 
 
