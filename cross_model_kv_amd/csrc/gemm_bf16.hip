@@ -206,13 +206,14 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     // ---- epilogue: lane owns rows wm*WTM + i*16 + 4*lq + v and columns nl0 .. nl0+FN-1
     const int nl0 = wn * WTN + lr * FN;
     const int ng = n0 + nl0;
-    if (tail) {                               // fp32 partial tile [BM][BN] of this K slice
+    if (tail) {                               // fp32 partial tile [BM][BN] of this K slice (valid rows)
         float* pt = a.split_ws + (int64_t)unit * BM * BN;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int ml = wm * WTM + i * 16 + 4 * lq + v;
+                if (s_src[ml] < 0) continue;
 #pragma unroll
                 for (int j = 0; j < FN; j += 4)
                     *(f32x4*)(pt + ml * BN + nl0 + j) =
@@ -465,7 +466,8 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
 //   split tail (split s):   floor(tiles / CUs) + ceil(rem * s / CUs) / s, rem = tiles % CUs
 //   every tile split (s):   ceil(tiles * s / CUs) / s
 // plus, for split plans, the HBM time of writing and re-reading the fp32 partial tiles
-// (512 KB per partial at ~5 TB/s) in units of one tile's compute (2*256*256*K flops at
+// (only the valid rows are written: min(M, 256) * 256 * 4 bytes each way per partial, at
+// ~5 TB/s) in units of one tile's compute (2*256*256*K flops at
 // ~4.7 TFLOP/s per CU, the rate these tiles reach).  The cheapest wins (ties keep fewer
 // partials); every K slice spans at least 4 k-tiles.
 SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
@@ -480,7 +482,7 @@ SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
     int64_t best_parts = 0;
     auto consider = [&](int full, int rem, int split) {
         const int64_t parts = (int64_t)rem * split;
-        const double partial_s = parts * 524288.0 / 5e12;
+        const double partial_s = parts * (std::min(M, 256) * 256.0 * 4.0 * 2.0) / 5e12;
         const double tile_s = 2.0 * 65536.0 * K / 4.7e12;
         const double t = (double)(full / cu) + (double)((rem * (int64_t)split + cu - 1) / cu) / split +
                          partial_s / tile_s;

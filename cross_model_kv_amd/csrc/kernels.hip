@@ -1,6 +1,7 @@
 // Non-matrix-core kernels of the handoff: the fp64 score-operator preparation, the radix
 // top-k selection, the rotary table, rotate-and-scatter of recomputed K/V, and the fp32
 // storage path (GEMM, row dot, attention).
+#include <climits>
 #include <math.h>
 
 #include "kvx_internal.h"
@@ -498,6 +499,33 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_bf16_kernel(const bf16* 
     }
 }
 
+// out[i] = the index of the largest logits[i][j]; ties go to the lowest index (one row per
+// block: per-thread strided scan, then a wave and a block reduction on (value, index))
+__global__ __launch_bounds__(256) void argmax_bf16_kernel(const bf16* logits, int V, int32_t* out) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const bf16* row = logits + (int64_t)blockIdx.x * V;
+    float best = -INFINITY;
+    int bi = INT_MAX;
+    for (int j = threadIdx.x; j < V; j += 256) {
+        const float x = (float)row[j];
+        if (x > best) { best = x; bi = j; }          // ascending j: the first maximum stays
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+    }
+    if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (sv[w] > best || (sv[w] == best && si[w] < bi)) { best = sv[w]; bi = si[w]; }
+        out[blockIdx.x] = bi == INT_MAX ? 0 : bi;
+    }
+}
+
 // dst[i] = src[cu_tok[b] + sel[i]] (the selected rows of a batch, compact)
 __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(const bf16* src, int D, const int32_t* sel,
                                                                 const int32_t* cu_tok, const int32_t* cu_sel,
@@ -519,6 +547,13 @@ hipError_t launch_rmsnorm_bf16(const bf16* x, const bf16* gamma, float eps, int6
     if (n == 0) return hipSuccess;
     if (D % 8 || D > rmsnorm_max_dim() || n > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3((unsigned)n), dim3(NORM_THREADS), 0, s, x, gamma, eps, D, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_argmax_bf16(const bf16* logits, int64_t n, int V, int32_t* out, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    if (n > INT32_MAX || V <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(argmax_bf16_kernel, dim3((unsigned)n), dim3(256), 0, s, logits, V, out);
     return hipGetLastError();
 }
 

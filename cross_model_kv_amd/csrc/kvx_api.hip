@@ -637,6 +637,17 @@ hipError_t run_linear_residual(hipStream_t s, const void* a, const void* w, cons
     return launch_gemm_bf16(g, s);
 }
 
+// out = a w^T (compact rows)
+hipError_t run_linear(hipStream_t s, const void* a, const void* w, void* out, int64_t M, int N, int K, void* split_ws) {
+    GemmArgs g{};
+    g.A = (const bf16*)a; g.lda = K; g.K_a = K;
+    g.B = (const bf16*)w; g.ldb = K;
+    g.M = (int)M; g.N = N; g.K = K; g.groups = 1;
+    g.epi = EPI_STORE; g.C = (bf16*)out; g.ldc = N;
+    g.split_ws = (float*)split_ws;
+    return launch_gemm_bf16(g, s);
+}
+
 // h = silu(x w_gate^T) * (x w_up^T)
 hipError_t run_swiglu(hipStream_t s, const void* x, const void* w_gate, const void* w_up, void* h, int64_t M, int D,
                       int F, void* split_ws) {
@@ -954,6 +965,39 @@ kvx_status kvx_target_layer(void* stream, int32_t dtype, int32_t layer, void* x,
     KVX_TRY_HIP(launch_rmsnorm_bf16(xr, (const bf16*)w->gamma_post, eps, k, D, xn, s), "post-attention norm");
     KVX_TRY_HIP(run_swiglu(s, xn, w->w_gate, w->w_up, mlp, k, D, F, split), "gate/up");
     return hip_status(run_linear_residual(s, mlp, w->w_down, xr, xr, k, D, F, split), "down projection");
+}
+
+kvx_status kvx_linear_workspace(int32_t dtype, int64_t M, int32_t N, int32_t K, size_t* bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "linear")) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(M >= 0 && M <= INT32_MAX && N > 0 && K > 0, "M must be in [0, 2^31), N and K positive");
+    *bytes = gemm_split_ws(M, N, K, EPI_STORE);
+    return ok();
+}
+
+kvx_status kvx_linear(void* stream, int32_t dtype, const void* a, const void* w, void* out, int64_t M, int32_t N,
+                      int32_t K, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_bf16_only(dtype, "linear")) return st;
+    KVX_REQUIRE(M >= 0 && M <= INT32_MAX, "M must be in [0, 2^31)");
+    KVX_REQUIRE(N > 0 && N % 8 == 0, "N must be a positive multiple of 8 (got %d)", N);
+    KVX_REQUIRE(K > 0 && K % 64 == 0, "K must be a positive multiple of 64 (got %d)", K);
+    if (M == 0) return ok();
+    KVX_REQUIRE_PTR(a, "a");
+    KVX_REQUIRE_PTR(w, "w");
+    KVX_REQUIRE_PTR(out, "out");
+    const size_t need = gemm_split_ws(M, N, K, EPI_STORE);
+    if (kvx_status st = check_ws(need, ws, ws_bytes, "linear")) return st;
+    return hip_status(run_linear((hipStream_t)stream, a, w, out, M, N, K, need ? ws : nullptr), "linear");
+}
+
+kvx_status kvx_argmax(void* stream, int32_t dtype, const void* logits, int64_t n, int32_t V, int32_t* out) {
+    if (kvx_status st = check_bf16_only(dtype, "argmax")) return st;
+    KVX_REQUIRE(n >= 0 && n <= INT32_MAX, "n must be in [0, 2^31)");
+    KVX_REQUIRE(V > 0, "V must be positive (got %d)", V);
+    if (n == 0) return ok();
+    KVX_REQUIRE_PTR(logits, "logits");
+    KVX_REQUIRE(out && aligned16(out), "out must be a 16-byte aligned pointer");
+    return hip_status(launch_argmax_bf16((const bf16*)logits, n, V, out, (hipStream_t)stream), "argmax");
 }
 
 }  // extern "C"

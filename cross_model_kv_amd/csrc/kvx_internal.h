@@ -90,6 +90,8 @@ hipError_t launch_rowdot_f32(const float* P, const float* Z, int64_t n, int r, f
 int rmsnorm_max_dim();
 hipError_t launch_rmsnorm_bf16(const bf16* x, const bf16* gamma, float eps, int64_t n, int D, bf16* y,
                                hipStream_t s);
+// index of each row's largest logit, ties to the lowest index
+hipError_t launch_argmax_bf16(const bf16* logits, int64_t n, int V, int32_t* out, hipStream_t s);
 hipError_t launch_gather_rows_bf16(const bf16* src, int D, const int32_t* sel, const int32_t* cu_tok,
                                    const int32_t* cu_sel, int n_req, int64_t n_sel, bf16* dst, hipStream_t s);
 

@@ -121,3 +121,35 @@ class ChainedHandoff(Handoff):
         self.start_rows()
         for l in range(self.wl.L_t):
             self.chain_layer(l)
+
+    # first token --------------------------------------------------------------------
+    def prepare_first_token(self):
+        """Buffers of the first-token step: a one-row-per-request batch at the last prompt
+        positions, the row buffer, logits and tokens."""
+        wl, dev = self.wl, self.device
+        if self.cw.w_lm is None:
+            raise ValueError("workload has no vocabulary")
+        lengths = self.batch.lengths
+        self.last_batch = kvx.Batch(lengths, [1] * len(lengths), dev)
+        self.last_sel = torch.tensor([t - 1 for t in lengths], dtype=torch.int32, device=dev)
+        n = len(lengths)
+        self.x_last = torch.empty((n, wl.D), dtype=self.x.dtype, device=dev)
+        self.xn_last = torch.empty_like(self.x_last)
+        self.logits = torch.empty((n, wl.vocab), dtype=self.x.dtype, device=dev)
+        self.token = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+        dt = kvx._dtype(self.x)
+        need = max(kvx.target_layer_workspace(dt, self.last_batch, wl.D, wl.F, wl.H_q, wl.H_kv, wl.d_h),
+                   kvx.linear_workspace(dt, n, wl.vocab, wl.D))
+        self.ws_last = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+    def first_token(self):
+        """The last prompt position through every layer over the mixed cache, then the
+        final norm, the vocabulary projection and the argmax."""
+        wl = self.wl
+        kvx.gather_rows(self.inp.x_l[0], self.last_batch, self.last_sel, self.x_last)
+        for l in range(wl.L_t):
+            kvx.target_layer(l, self.x_last, self.layers[l], wl.F, wl.H_q, wl.H_kv, wl.d_h, wl.norm_eps, self.rope,
+                             self.last_batch, self.last_sel, self.cache, ws=self.ws_last)
+        kvx.rmsnorm(self.x_last, self.cw.gamma_final, wl.norm_eps, y=self.xn_last)
+        kvx.linear(self.xn_last, self.cw.w_lm, self.logits, self.ws_last)
+        kvx.argmax(self.logits, self.token)

@@ -87,6 +87,9 @@ _SIGS = {
     "kvx_linear_residual": ([_P, _I32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _SZ], _I32),
     "kvx_swiglu_workspace": ([_I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_swiglu": ([_P, _I32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _SZ], _I32),
+    "kvx_linear_workspace": ([_I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "kvx_linear": ([_P, _I32, _P, _P, _P, _I64, _I32, _I32, _P, _SZ], _I32),
+    "kvx_argmax": ([_P, _I32, _P, _I64, _I32, _P], _I32),
     "kvx_target_layer_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
                                    _I32),
     "kvx_target_layer": ([_P, _I32, _I32, _P, ctypes.POINTER(_LayerWeights), _I32, _I32, _I32, _I32, _I32,
@@ -501,3 +504,32 @@ def target_layer(layer: int, x: torch.Tensor, w: LayerWeights, F: int, H_q: int,
         rope.shape[0], ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c),
         _ptr(attn_out), _ptr(lse), _ptr(ws), ws.numel()))
     return x
+
+
+def linear_workspace(dtype: int, M: int, N: int, K: int) -> int:
+    b = _SZ()
+    _check("kvx_linear_workspace", lib().kvx_linear_workspace(dtype, M, N, K, ctypes.byref(b)))
+    return b.value
+
+
+def linear(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+           ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = a w^T."""
+    M, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    b = _SZ()
+    _check("kvx_linear_workspace", lib().kvx_linear_workspace(_dtype(a), M, N, K, ctypes.byref(b)))
+    wp, wn = _ws(b.value, ws, a.device)
+    _check("kvx_linear", lib().kvx_linear(_stream(a.device), _dtype(a), _ptr(a), _ptr(w), _ptr(out), M, N, K, wp, wn))
+    return out
+
+
+def argmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index of each row's largest logit (ties to the lowest index), int32."""
+    n, V = logits.shape
+    if out is None:
+        out = torch.empty(max(n, 1), dtype=torch.int32, device=logits.device)
+    _check("kvx_argmax", lib().kvx_argmax(_stream(logits.device), _dtype(logits), _ptr(logits), n, V, _ptr(out)))
+    return out[:n]

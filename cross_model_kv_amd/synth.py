@@ -186,14 +186,17 @@ class ChainWeights:
     w_gate: torch.Tensor        # [L_t, F, D]    ~ N(0, 1/D)
     w_up: torch.Tensor          # [L_t, F, D]    ~ N(0, 1/D)
     w_down: torch.Tensor        # [L_t, D, F]    ~ N(0, 1/F)
+    gamma_final: Optional[torch.Tensor] = None   # [D]      U(0.5, 1.5)   (vocab > 0)
+    w_lm: Optional[torch.Tensor] = None          # [V, D]   ~ N(0, 1/D)
 
 
-_CHAIN_SUBSEEDS = ("gamma_in", "w_o", "gamma_post", "w_gate", "w_up", "w_down")
+_CHAIN_SUBSEEDS = ("gamma_in", "w_o", "gamma_post", "w_gate", "w_up", "w_down", "gamma_final", "w_lm")
 
 
 def chain_weights(wl: Workload, seed: int, device="cpu", where: str = "auto") -> ChainWeights:
-    """Weights of the chained layers of workload ``wl`` (bf16).  Sub-seeds come from
-    ``SeedSequence([seed, 404]).spawn(6)`` so the handoff's own inputs are unchanged."""
+    """Weights of the chained layers of workload ``wl`` (bf16), and the final norm and
+    vocabulary projection when the workload has a vocabulary.  Sub-seeds come from
+    ``SeedSequence([seed, 404]).spawn(8)`` so the handoff's own inputs are unchanged."""
     if wl.F <= 0:
         raise ValueError(f"workload {wl.name} has no MLP width")
     ss = dict(zip(_CHAIN_SUBSEEDS, np.random.SeedSequence([seed, 404]).spawn(len(_CHAIN_SUBSEEDS))))
@@ -220,9 +223,14 @@ def chain_weights(wl: Workload, seed: int, device="cpu", where: str = "auto") ->
             rows[i:i + blk.shape[0]].copy_(blk.mul_(std))
         return out
 
-    return ChainWeights(gains("gamma_in"), normal("w_o", (L, D, HD), 1.0 / math.sqrt(HD)), gains("gamma_post"),
-                        normal("w_gate", (L, F, D), 1.0 / math.sqrt(D)), normal("w_up", (L, F, D), 1.0 / math.sqrt(D)),
-                        normal("w_down", (L, D, F), 1.0 / math.sqrt(F)))
+    cw = ChainWeights(gains("gamma_in"), normal("w_o", (L, D, HD), 1.0 / math.sqrt(HD)), gains("gamma_post"),
+                      normal("w_gate", (L, F, D), 1.0 / math.sqrt(D)), normal("w_up", (L, F, D), 1.0 / math.sqrt(D)),
+                      normal("w_down", (L, D, F), 1.0 / math.sqrt(F)))
+    if wl.vocab > 0:
+        rng = np.random.Generator(np.random.PCG64(ss["gamma_final"]))
+        cw.gamma_final = torch.from_numpy(rng.uniform(0.5, 1.5, size=D).astype(np.float32)).to(torch.bfloat16).to(dev)
+        cw.w_lm = normal("w_lm", (wl.vocab, D), 1.0 / math.sqrt(D))
+    return cw
 
 
 # ---------------------------------------------------------------------------------

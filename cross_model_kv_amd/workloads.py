@@ -5,8 +5,9 @@ the target attention shape, the calibration rank and the recompute budget.  The
 shapes follow the model pairs that the PANORAMA abstract (Qwen3 8B to 32B at 16K
 tokens) and the RaReCache abstract (Qwen3-0.6B to 14B at a 30% budget, Llama3-8B
 to 70B at 40%) report on; the tiny one is a small fp32 case for exact checks.  The MLP
-widths F of the chained variant are those of the named target models' public configurations
-(Qwen3-14B 17408, Qwen3-32B 25600, Llama-3-70B 28672); the pages do not print them.
+widths F and vocabulary sizes of the chained variant are those of the named target models'
+public configurations (Qwen3-14B F 17408, Qwen3-32B F 25600, both 151936 tokens; Llama-3-70B F 28672,
+128256 tokens); the pages do not print them.
 
 This module only holds sizes.  It does no arithmetic of the method.
 """
@@ -44,6 +45,8 @@ class Workload:
     # and the RMS-norm epsilon; F = 0 means the workload has no chained variant
     F: int = 0
     norm_eps: float = 1e-6
+    # first-token step: vocabulary size of the target (0: no first-token variant)
+    vocab: int = 0
 
     @property
     def d_src(self) -> int:
@@ -75,19 +78,19 @@ TINY_F32 = Workload(
 
 QWEN_0P6B_14B = Workload(
     name="0.6B-to-14B-shape-T4096", dtype="bf16", T=4096, L_s=28, H_s=8, d_hs=128,
-    r=1024, L_t=40, H_q=40, H_kv=8, d_h=128, D=5120, c=512, pct=30, F=17408)
+    r=1024, L_t=40, H_q=40, H_kv=8, d_h=128, D=5120, c=512, pct=30, F=17408, vocab=151936)
 
 QWEN_8B_32B_16K = Workload(
     name="8B-to-32B-shape-T16384", dtype="bf16", T=16384, L_s=36, H_s=8, d_hs=128,
-    r=1024, L_t=64, H_q=64, H_kv=8, d_h=128, D=5120, c=512, pct=30, F=25600)
+    r=1024, L_t=64, H_q=64, H_kv=8, d_h=128, D=5120, c=512, pct=30, F=25600, vocab=151936)
 
 LLAMA_8B_70B = Workload(
     name="8B-to-70B-shape-T8192", dtype="bf16", T=8192, L_s=32, H_s=8, d_hs=128,
-    r=1536, L_t=80, H_q=64, H_kv=8, d_h=128, D=8192, c=768, pct=40, F=28672)
+    r=1536, L_t=80, H_q=64, H_kv=8, d_h=128, D=8192, c=768, pct=40, F=28672, vocab=128256)
 
 BATCHED_16 = Workload(
     name="batched-16req-paged16", dtype="bf16", T=0, L_s=36, H_s=8, d_hs=128,
     r=1024, L_t=64, H_q=64, H_kv=8, d_h=128, D=5120, c=512, pct=30,
-    n_req=16, t_min=1024, t_max=16384, pct_choices=(20, 30, 40), paged=True, page_size=16, F=25600)
+    n_req=16, t_min=1024, t_max=16384, pct_choices=(20, 30, 40), paged=True, page_size=16, F=25600, vocab=151936)
 
 ALL = {w.name: w for w in (TINY_F32, QWEN_0P6B_14B, QWEN_8B_32B_16K, LLAMA_8B_70B, BATCHED_16)}

@@ -330,6 +330,27 @@ KVX_API kvx_status kvx_target_layer(void* stream, int32_t dtype, int32_t layer, 
                                     const int32_t* sel, const kvx_cache* cache, void* attn_out,
                                     float* lse, void* ws, size_t ws_bytes);
 
+/* ---------------------------------------------------------------------------------------
+ * First token after the handoff (bf16 only).  The time to first token is the handoff plus
+ * one step for the last prompt position: that row runs through every target layer as a
+ * one-row kvx_target_layer call (its k and v recomputed over the mixed cache), then the
+ * final RMS norm (kvx_rmsnorm), the vocabulary projection (kvx_linear) and kvx_argmax.
+ * (RaReCache abstract: time to first token at the target's saturation load; PANORAMA
+ * abstract: handoff latency against a full re-prefill.) */
+
+/* out = a W^T: a (device) [M][K], w (device) [N][K], out (device, out) [M][N]; fp32
+ * accumulation, one bf16 rounding.  K % 64 == 0, N % 8 == 0.  ws as in kvx_qkv_project
+ * (split K-slice partials; for a few rows every output tile is split so that all CUs stream
+ * the weight, and only the valid rows of a partial are written). */
+KVX_API kvx_status kvx_linear_workspace(int32_t dtype, int64_t M, int32_t N, int32_t K, size_t* bytes);
+KVX_API kvx_status kvx_linear(void* stream, int32_t dtype, const void* a, const void* w, void* out,
+                              int64_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes);
+
+/* out[i] = index of the largest of logits[i][0..V), ties to the lowest index.
+ * logits (device) [n][V]; out (device, out) [n] int32. */
+KVX_API kvx_status kvx_argmax(void* stream, int32_t dtype, const void* logits, int64_t n, int32_t V,
+                              int32_t* out);
+
 #ifdef __cplusplus
 }
 #endif

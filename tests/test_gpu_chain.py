@@ -177,3 +177,85 @@ def test_layer_pass_through_bitexact():
     assert torch.equal(x_in, inp.x_l[0][sel.long()]), "gathered rows differ"  # one request: rows = positions
     assert torch.equal(c1.k, c2.k) and torch.equal(c1.v, c2.v), "caches differ"
     assert torch.equal(o1, o2), "attention rows differ"
+
+
+# ------------------------------------------------------------------------------ first token
+
+@pytest.mark.parametrize("M,N,K", [(1, 5000, 1024), (3, 2048, 4096), (300, 520, 512)])
+def test_linear(M, N, K):
+    """Plain projection, including the few-row shapes of the first-token step (every tile
+    split along K, only the valid rows of a partial written)."""
+    say(f"[first token] linear M={M} N={N} K={K}")
+    a, w = normal((M, K), 101), normal((N, K), 102, 1 / math.sqrt(K))
+    out = kvx.linear(a, w)
+    out2 = kvx.linear(a, w)
+    torch.cuda.synchronize()
+    assert_close(f64(out), f64(a) @ f64(w).T, 2e-2, "linear")
+    assert torch.equal(out, out2)
+
+
+def test_argmax_ties_lowest():
+    """Exact decisions on the stored values: ties (including many equal maxima) go to the
+    lowest index; compared with the brute-force argmax of the same bf16 values."""
+    say("[first token] argmax")
+    rng = np.random.default_rng(103)
+    rows = [rng.standard_normal(5000), np.zeros(777), np.full(300, -3.0), rng.integers(-3, 4, 4096).astype(float)]
+    for r in rows:
+        x = torch.tensor(r, dtype=torch.float32).to(torch.bfloat16).to(DEV)[None, :]
+        got = int(kvx.argmax(x).cpu()[0])
+        vals = x.float().cpu().numpy()[0]
+        assert got == int(np.argmax(vals)), (got, int(np.argmax(vals)))
+
+
+FT_CASES = {
+    "ft-g4-d128": small("ft-g4-d128", vocab=1000),
+    "ft-g8-batched-paged": small("ft-g8-batched-paged", H_q=16, H_kv=2, n_req=3, t_min=60, t_max=500,
+                                 pct_choices=(20, 30, 40), paged=True, F=640, L_t=2, vocab=2048),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FT_CASES))
+def test_first_token(name):
+    """Chained handoff, then the first-token step: logits and the last position's cache rows
+    match the oracle; the token is the argmax of the GPU's own logits (an exact decision)
+    and its oracle logit lies within the bf16 tolerance of the oracle's maximum."""
+    wl = FT_CASES[name]
+    seed = 41
+    say(f"[first token] {name}")
+    inp = synth.generate(wl, seed, DEV)
+    cw = synth.chain_weights(wl, seed, DEV)
+    h = ChainedHandoff(inp, cw, DEV)
+    h.run()
+    h.prepare_first_token()
+    h.first_token()
+    torch.cuda.synchronize()
+    layers = _layer_dicts(inp, cw, wl)
+    cu, cs = h.batch.cu_tokens, h.batch.cu_sel
+    pt = inp.page_table.cpu().numpy() if wl.paged else None
+    S_all = h.S.cpu().numpy()
+    logits = f64(h.logits)
+    tokens = h.token.cpu().numpy()
+    for b, T in enumerate(inp.lengths):
+        S = S_all[cs[b]:cs[b + 1]]
+        z = O.map_latent(f64(inp.x_src[cu[b]:cu[b + 1]]), f64(inp.w_s))
+        K_tr, V_tr, _ = O.reconstruct(z, f64(inp.w_l), wl.H_kv, wl.d_h)
+        if len(S):
+            ch = O.chained_layers(f64(inp.x_l[0, cu[b]:cu[b + 1]])[S], S, K_tr, V_tr, layers, wl.H_q, wl.H_kv,
+                                  wl.d_h, wl.rope_base, wl.norm_eps)
+            K_m, V_m = ch["K"], ch["V"]
+        else:
+            K_m, V_m = K_tr, V_tr
+        ref_logits, ref_tok, K_f, V_f = O.first_token(f64(inp.x_l[0, cu[b] + T - 1]), T - 1, K_m, V_m, layers,
+                                                      f64(cw.gamma_final), f64(cw.w_lm), wl.H_q, wl.H_kv, wl.d_h,
+                                                      wl.rope_base, wl.norm_eps)
+        say(f"  request {b} (T={T}): logits normwise {rel_norm(logits[b], ref_logits):.2e}, token {tokens[b]} "
+            f"(oracle {ref_tok})")
+        assert_close(logits[b], ref_logits, 2e-2, "first-token logits")
+        assert tokens[b] == int(np.argmax(logits[b])), "token is not the argmax of the stored logits"
+        span = ref_logits.max() - ref_logits.min()
+        assert ref_logits.max() - ref_logits[tokens[b]] <= 2e-2 * span
+        for l in range(wl.L_t):
+            Kg = logical(h.cache.k, l, b, T, cu, pt, wl.page_size)
+            Vg = logical(h.cache.v, l, b, T, cu, pt, wl.page_size)
+            assert_close(Kg[T - 1], K_f[l][T - 1], 2e-2, f"last position K, layer {l}")
+            assert_close(Vg[T - 1], V_f[l][T - 1], 2e-2, f"last position V, layer {l}")
