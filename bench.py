@@ -273,10 +273,68 @@ def main_chain(args, wl):
                      "traffic": None, "algorithmic_flops_per_launch": sw_flops, "avg_launch_ms": round(swiglu_ms, 5)},
         "stages": stages,
     }
+    if wl.vocab > 0:
+        line["ttft"] = time_to_first_token(args, wl, inp, cw, h, elapsed * 1e3 / args.steps)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         line["cpu_baseline"] = chain_cpu_baseline(inp, cw, wl, S, T, k, pos_sum)
     print(json.dumps(line), flush=True)
+
+
+def time_to_first_token(args, wl, inp, cw, h, handoff_ms):
+    """Time to first token: the chained handoff plus the first-token step (the last prompt
+    position through every layer over the mixed cache, final norm, vocabulary projection,
+    argmax), against a full re-prefill with the same kernels (every position recomputed,
+    then the LM head of the last row)."""
+    import dataclasses
+    from cross_model_kv_amd import kvx
+    from cross_model_kv_amd.handoff import ChainedHandoff
+
+    stream = torch.cuda.current_stream(h.device)
+    h.prepare_first_token()
+    for _ in range(2):
+        h.first_token()
+    n_rep = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_rep):
+        h.first_token()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ft_ms = e0.elapsed_time(e1) / n_rep
+    # full re-prefill: the same inputs with a 100% budget (mapper stages run with nothing to do)
+    log("[bench] full re-prefill for the TTFT comparison")
+    full = ChainedHandoff(dataclasses.replace(inp, pcts=[100] * len(inp.lengths)), cw, h.device,
+                          keep_all_outputs=False)
+    last_rows = torch.tensor([c - 1 for c in full.batch.cu_tokens[1:]], dtype=torch.long, device=h.device)
+    xn = torch.empty((len(inp.lengths), wl.D), dtype=torch.bfloat16, device=h.device)
+    logits = torch.empty((len(inp.lengths), wl.vocab), dtype=torch.bfloat16, device=h.device)
+    ws = torch.empty(max(kvx.linear_workspace(kvx.BF16, len(inp.lengths), wl.vocab, wl.D), 16), dtype=torch.uint8,
+                     device=h.device)
+
+    def prefill():
+        full.run()
+        kvx.rmsnorm(full.x[last_rows], cw.gamma_final, wl.norm_eps, y=xn)
+        kvx.linear(xn, cw.w_lm, logits, ws)
+        kvx.argmax(logits)
+
+    prefill()
+    torch.cuda.synchronize()
+    n_full = 2
+    e0.record(stream)
+    for _ in range(n_full):
+        prefill()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    full_ms = e0.elapsed_time(e1) / n_full
+    ttft = handoff_ms + ft_ms
+    del full
+    torch.cuda.empty_cache()
+    return {"handoff_ms": round(handoff_ms, 3), "first_token_ms": round(ft_ms, 3), "ttft_ms": round(ttft, 3),
+            "full_prefill_ttft_ms": round(full_ms, 3), "speedup_vs_full_prefill": round(full_ms / ttft, 3),
+            "ttft_saved": round(1.0 - ttft / full_ms, 4),
+            "note": "full prefill = every position through every chained layer with the same kernels, then the "
+                    "LM head of the last row; both on this GPU, inputs resident"}
 
 
 def main():
