@@ -405,40 +405,40 @@ void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Merge of a split attention: out = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over the
-// chunks with l_c > 0 (m their largest m_c), in chunk order; one thread per 8 output columns.
+// chunks with l_c > 0 (m their largest m_c), in chunk order.  One wave per (row, head): lane
+// c < n_split holds chunk c's weight, every lane then sums D_H / 64 output columns over the
+// chunks (the weights broadcast from their lanes).
 template <int D_H>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, const float* ml, int n_split,
                                                             int64_t rows, bf16* out, float* lse) {
-    constexpr int G = D_H / 8;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= rows * G) return;
-    const int64_t row = idx / G;
-    const int d0 = (int)(idx % G) * 8;
+    constexpr int CPL = D_H / 64;                 // output columns per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
     const float* mlr = ml + row * n_split * 2;
-    float m = -INFINITY;
-    for (int c = 0; c < n_split; ++c)
-        if (mlr[2 * c + 1] > 0.f) m = fmaxf(m, mlr[2 * c]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    for (int c = 0; c < n_split; ++c) {
-        const float lc = mlr[2 * c + 1];
-        if (!(lc > 0.f)) continue;
-        const float wgt = __builtin_amdgcn_exp2f(mlr[2 * c] - m);
-        L += wgt * lc;
-        const f32x4* pc = (const f32x4*)(part + (row * n_split + c) * D_H + d0);
-        const f32x4 x0 = pc[0], x1 = pc[1];
+    const float mc = lane < n_split ? mlr[2 * lane] : 0.f;
+    const float lc = lane < n_split ? mlr[2 * lane + 1] : 0.f;
+    float m = lc > 0.f ? mc : -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            acc[v] += wgt * x0[v];
-            acc[4 + v] += wgt * x1[v];
-        }
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float wgt = lc > 0.f ? __builtin_amdgcn_exp2f(mc - m) : 0.f;
+    // chunk-ordered sum of the weighted row sums (lane 0 adds them one by one)
+    float L = 0.f;
+    for (int c = 0; c < n_split; ++c) L += __shfl(wgt, c) * __shfl(lc, c);
+    float acc[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
+    for (int c = 0; c < n_split; ++c) {
+        const float wc = __shfl(wgt, c);
+        if (wc == 0.f) continue;                  // uniform over the wave
+        const float* pc = part + (row * n_split + c) * D_H + lane * CPL;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) acc[j] += wc * pc[j];
     }
     const float inv = 1.f / L;
-    bf16x8 o;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) o[v] = (bf16)(acc[v] * inv);
-    *(bf16x8*)(out + row * D_H + d0) = o;
-    if (lse && d0 == 0) lse[row] = (m + __log2f(L)) * 0.6931471805599453f;
+    for (int j = 0; j < CPL; ++j) out[row * D_H + lane * CPL + j] = (bf16)(acc[j] * inv);
+    if (lse && lane == 0) lse[row] = (m + __log2f(L)) * 0.6931471805599453f;
 }
 
 template <int D_H>
@@ -450,8 +450,8 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
     if (a.n_split == 1) return hipGetLastError();
     if (hipError_t e = hipGetLastError()) return e;
     const int64_t rows = a.n_rows_total * a.H_q;   // (selected row, query head) rows
-    const int64_t threads = rows * (D_H / 8);
-    hipLaunchKernelGGL((attn_combine_kernel<D_H>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+    if (a.n_split > 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_combine_kernel<D_H>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
                        (const float*)a.part, (const float*)a.part_ml, a.n_split, rows, (bf16*)a.out, a.lse);
     return hipGetLastError();
 }

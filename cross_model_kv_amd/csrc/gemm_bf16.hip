@@ -371,6 +371,84 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     }
 }
 
+// Few rows (M <= GEMV_MAX_M): the product is bound by streaming the weight, and 256-row
+// matrix-core tiles would spend almost all their work on padding.  Every output tile becomes a
+// split unit (full = 0, rem = tiles): workgroup (unit, 32-column group, K slice) computes the
+// fp32 dot products of its 32 columns with the M rows over its K slice and writes them to the
+// unit's partial tile (only the M valid rows), so gemm_split_reduce_kernel applies the usual
+// epilogue.  A wave takes 8 columns at a time: lane l reads 16 bytes of column l/8 at k offset
+// 8*(l%8) of each 64-wide k step (each column's 128-byte k chunk in one request), and the
+// eight k lanes of a column are summed in a fixed order at the end.
+constexpr int GEMV_MAX_M = 16;
+
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int item = blockIdx.x;
+    const int sl = item % sp.split;                        // K slice
+    const int cg = (item / sp.split) % 8;                  // 32-column group of the tile
+    const int unit = item / (sp.split * 8);
+    const Tile t = tile_at(unit, mt, nt, a.groups, gm);
+    const int M = a.M;                                     // <= GEMV_MAX_M
+    const int ks = a.K / sp.split, k_begin = sl * ks;
+    const int c_in = lane >> 3, kl = lane & 7;
+    const int nl = cg * 32 + wave * 8 + c_in;              // column within the tile
+    const int n = t.tn * 256 + nl;
+    const bool col_ok = n < a.N;
+    const bf16* brow;
+    if (a.epi == EPI_SWIGLU)
+        brow = ((n >> 3) & 1 ? a.B2 : a.B) + (int64_t)((n >> 4) * 8 + (n & 7)) * a.ldb;
+    else
+        brow = a.B + (int64_t)n * a.ldb;
+    if (!col_ok) brow = a.B;                               // never read past the weight
+    const bf16* arow[GEMV_MAX_M];
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_M; ++m) arow[m] = a.A + (int64_t)(m < M ? row_info(a.rows, m).src : 0) * a.lda;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float acc[GEMV_MAX_M];
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_M; ++m) acc[m] = 0.f;
+    if (col_ok) {
+        for (int k = k_begin + kl * 8; k < k_begin + ks; k += 64) {
+            const bf16x8 w = *(const bf16x8*)(brow + k);
+#pragma unroll
+            for (int m = 0; m < GEMV_MAX_M; ++m) {
+                if (m >= M) break;
+                const bf16x8 x = *(const bf16x8*)(arow[m] + k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x2 wv = {w[2 * j], w[2 * j + 1]}, xv = {x[2 * j], x[2 * j + 1]};
+                    acc[m] = __builtin_amdgcn_fdot2_f32_bf16(wv, xv, acc[m], false);
+                }
+            }
+        }
+    }
+    float* pt = a.split_ws + ((int64_t)unit * sp.split + sl) * 65536;
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_M; ++m) {
+        if (m >= M) break;
+        float v = acc[m];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        if (kl == 0 && col_ok) pt[m * 256 + nl] = v;
+    }
+}
+
+// GEMV plan: all tiles are split units; K slices so that about 1024 workgroups stream the
+// weight (each slice a whole number of 64-wide k steps, at least 4 of them)
+static SplitPlan plan_gemv(int N, int K) {
+    const int tiles = cdiv(N, 256);
+    const int nk = K / BK;
+    int split = 1;
+    while (split < 16 && (int64_t)tiles * 8 * split < 1024 && nk % (split * 2) == 0 && nk / (split * 2) >= 4) split *= 2;
+    return SplitPlan{0, tiles, split};
+}
+
+static bool gemv_eligible(const GemmArgs& a) {
+    return a.M >= 1 && a.M <= GEMV_MAX_M && a.groups == 1 && a.K_a == a.K &&
+           (a.epi == EPI_STORE || a.epi == EPI_QKV || a.epi == EPI_RESID || a.epi == EPI_SWIGLU);
+}
+
 // C rows of the tail tiles: out = sum over the K slices, in slice order.  One thread per 8
 // consecutive columns of one tile row.
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
@@ -505,7 +583,9 @@ SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
 int gemm_bf16_block_n() { return 256; }
 
 size_t gemm_bf16_split_bytes(int M, int N, int K, int groups, int epi) {
-    const SplitPlan sp = plan_split(M, N, K, groups, epi);
+    GemmArgs probe{};
+    probe.M = M; probe.N = N; probe.K = K; probe.K_a = K; probe.groups = groups; probe.epi = epi;
+    const SplitPlan sp = gemv_eligible(probe) ? plan_gemv(N, K) : plan_split(M, N, K, groups, epi);
     return sp.rem ? (size_t)sp.rem * sp.split * 65536 * sizeof(float) : 0;
 }
 
@@ -532,6 +612,13 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     // groups' weights: walking all row panels first streams each weight panel through an XCD
     // once while the row operand stays resident in the last-level cache (measured fastest).
     const int gm = a.groups > 1 ? mt : pick_group_rows(mt, nt * a.groups, 256.0 * a.K_a, 256.0 * a.K);
+    if (a.split_ws && gemv_eligible(a)) {           // few rows: stream the weight, reduce with the epilogue
+        const SplitPlan sp = plan_gemv(a.N, a.K);
+        hipLaunchKernelGGL(gemv_bf16_kernel, dim3((unsigned)(sp.rem * 8 * sp.split)), dim3(256), 0, s, a, mt, nt, gm, sp);
+        if (hipError_t e = hipGetLastError()) return e;
+        hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3(65536 / (256 * 8), sp.rem), dim3(256), 0, s, a, mt, nt, gm, sp);
+        return hipGetLastError();
+    }
     SplitPlan sp = plan_split(a.M, a.N, a.K, a.groups, a.epi);
     if (sp.rem && !a.split_ws) sp = SplitPlan{sp.full + sp.rem, 0, 1};   // no workspace: whole tiles
     const int64_t grid = (int64_t)sp.full + (int64_t)sp.rem * sp.split;

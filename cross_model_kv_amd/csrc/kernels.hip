@@ -499,17 +499,29 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_bf16_kernel(const bf16* 
     }
 }
 
-// out[i] = the index of the largest logits[i][j]; ties go to the lowest index (one row per
-// block: per-thread strided scan, then a wave and a block reduction on (value, index))
-__global__ __launch_bounds__(256) void argmax_bf16_kernel(const bf16* logits, int V, int32_t* out) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
+// out[i] = the index of the largest logits[i][j]; ties go to the lowest index (one 1024-thread
+// block per row: per-thread scan of 8-element chunks in ascending order, then a wave and a
+// block reduction on (value, index))
+constexpr int ARGMAX_THREADS = 1024;
+__global__ __launch_bounds__(ARGMAX_THREADS) void argmax_bf16_kernel(const bf16* logits, int V, int32_t* out) {
+    __shared__ float sv[ARGMAX_THREADS / 64];
+    __shared__ int si[ARGMAX_THREADS / 64];
     const bf16* row = logits + (int64_t)blockIdx.x * V;
     float best = -INFINITY;
     int bi = INT_MAX;
-    for (int j = threadIdx.x; j < V; j += 256) {
-        const float x = (float)row[j];
-        if (x > best) { best = x; bi = j; }          // ascending j: the first maximum stays
+    const bool vec = (V % 8) == 0;
+    if (vec) {
+        for (int c = threadIdx.x; c < V / 8; c += ARGMAX_THREADS) {
+            const bf16x8 x = *(const bf16x8*)(row + (int64_t)c * 8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if ((float)x[j] > best) { best = (float)x[j]; bi = c * 8 + j; }   // first maximum stays
+        }
+    } else {
+        for (int j = threadIdx.x; j < V; j += ARGMAX_THREADS) {
+            const float x = (float)row[j];
+            if (x > best) { best = x; bi = j; }
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -520,7 +532,7 @@ __global__ __launch_bounds__(256) void argmax_bf16_kernel(const bf16* logits, in
     if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < 4; ++w)
+        for (int w = 1; w < ARGMAX_THREADS / 64; ++w)
             if (sv[w] > best || (sv[w] == best && si[w] < bi)) { best = sv[w]; bi = si[w]; }
         out[blockIdx.x] = bi == INT_MAX ? 0 : bi;
     }
@@ -553,7 +565,7 @@ hipError_t launch_rmsnorm_bf16(const bf16* x, const bf16* gamma, float eps, int6
 hipError_t launch_argmax_bf16(const bf16* logits, int64_t n, int V, int32_t* out, hipStream_t s) {
     if (n == 0) return hipSuccess;
     if (n > INT32_MAX || V <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(argmax_bf16_kernel, dim3((unsigned)n), dim3(256), 0, s, logits, V, out);
+    hipLaunchKernelGGL(argmax_bf16_kernel, dim3((unsigned)n), dim3(ARGMAX_THREADS), 0, s, logits, V, out);
     return hipGetLastError();
 }
 

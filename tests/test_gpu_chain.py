@@ -48,7 +48,7 @@ def test_rmsnorm(n, D):
     assert torch.equal(y, x2)
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (64, 4096, 4096)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (64, 4096, 4096), (1, 520, 1024), (5, 4096, 4096)])
 def test_linear_residual(M, N, K):
     say(f"[chain] linear+residual M={M} N={N} K={K}")
     a, w, r = normal((M, K), 93), normal((N, K), 94, 1 / math.sqrt(K)), normal((M, N), 95)
@@ -60,7 +60,7 @@ def test_linear_residual(M, N, K):
     assert torch.equal(out, r2)
 
 
-@pytest.mark.parametrize("M,D,F", [(300, 512, 776), (64, 4096, 512)])
+@pytest.mark.parametrize("M,D,F", [(300, 512, 776), (64, 4096, 512), (2, 512, 776), (16, 1024, 2048)])
 def test_swiglu(M, D, F):
     say(f"[chain] swiglu M={M} D={D} F={F}")
     x, wg, wu = normal((M, D), 96), normal((F, D), 97, 1 / math.sqrt(D)), normal((F, D), 98, 1 / math.sqrt(D))
@@ -181,10 +181,11 @@ def test_layer_pass_through_bitexact():
 
 # ------------------------------------------------------------------------------ first token
 
-@pytest.mark.parametrize("M,N,K", [(1, 5000, 1024), (3, 2048, 4096), (300, 520, 512)])
+@pytest.mark.parametrize("M,N,K", [(1, 5000, 1024), (3, 2048, 4096), (16, 1000, 25600), (17, 520, 512),
+                                   (300, 520, 512)])
 def test_linear(M, N, K):
-    """Plain projection, including the few-row shapes of the first-token step (every tile
-    split along K, only the valid rows of a partial written)."""
+    """Plain projection, including the few-row shapes of the first-token step (up to 16 rows:
+    the weight-streaming kernel, every output tile reduced with the usual epilogue)."""
     say(f"[first token] linear M={M} N={N} K={K}")
     a, w = normal((M, K), 101), normal((N, K), 102, 1 / math.sqrt(K))
     out = kvx.linear(a, w)
