@@ -428,12 +428,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, co
     float acc[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
-    for (int c = 0; c < n_split; ++c) {
-        const float wc = __shfl(wgt, c);
-        if (wc == 0.f) continue;                  // uniform over the wave
-        const float* pc = part + (row * n_split + c) * D_H + lane * CPL;
+    // eight chunks per pass: their loads are issued together, the sums stay in chunk order
+    for (int c0 = 0; c0 < n_split; c0 += 8) {
+        float v[8][CPL];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) acc[j] += wc * pc[j];
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + u;
+            const bool use = c < n_split && __shfl(wgt, c < n_split ? c : 0) != 0.f;
+            const float* pc = part + (row * n_split + (use ? c : 0)) * D_H + lane * CPL;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) v[u][j] = use ? pc[j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + u;
+            const float wc = c < n_split ? __shfl(wgt, c) : 0.f;
+            if (wc == 0.f) continue;              // uniform over the wave
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) acc[j] += wc * v[u][j];
+        }
     }
     const float inv = 1.f / L;
 #pragma unroll

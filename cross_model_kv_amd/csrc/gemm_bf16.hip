@@ -381,6 +381,7 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
 // eight k lanes of a column are summed in a fixed order at the end.
 constexpr int GEMV_MAX_M = 16;
 
+template <int MR>   // rows handled (M <= MR; rows past M read row 0 and are not written)
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int item = blockIdx.x;
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs a, int mt, int 
     const int cg = (item / sp.split) % 8;                  // 32-column group of the tile
     const int unit = item / (sp.split * 8);
     const Tile t = tile_at(unit, mt, nt, a.groups, gm);
-    const int M = a.M;                                     // <= GEMV_MAX_M
+    const int M = a.M;
     const int ks = a.K / sp.split, k_begin = sl * ks;
     const int c_in = lane >> 3, kl = lane & 7;
     const int nl = cg * 32 + wave * 8 + c_in;              // column within the tile
@@ -399,38 +400,52 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs a, int mt, int 
         brow = ((n >> 3) & 1 ? a.B2 : a.B) + (int64_t)((n >> 4) * 8 + (n & 7)) * a.ldb;
     else
         brow = a.B + (int64_t)n * a.ldb;
-    if (!col_ok) brow = a.B;                               // never read past the weight
-    const bf16* arow[GEMV_MAX_M];
+    if (!col_ok) brow = a.B;                               // in bounds; the result is not written
+    brow += k_begin + kl * 8;
+    const bf16* arow[MR];
 #pragma unroll
-    for (int m = 0; m < GEMV_MAX_M; ++m) arow[m] = a.A + (int64_t)(m < M ? row_info(a.rows, m).src : 0) * a.lda;
+    for (int m = 0; m < MR; ++m)
+        arow[m] = a.A + (int64_t)(m < M ? row_info(a.rows, m).src : 0) * a.lda + k_begin + kl * 8;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    float acc[GEMV_MAX_M];
+    float acc[MR];
 #pragma unroll
-    for (int m = 0; m < GEMV_MAX_M; ++m) acc[m] = 0.f;
-    if (col_ok) {
-        for (int k = k_begin + kl * 8; k < k_begin + ks; k += 64) {
-            const bf16x8 w = *(const bf16x8*)(brow + k);
+    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+    auto dot8 = [&](const bf16x8& w, const bf16x8& x, float c) __attribute__((always_inline)) {
 #pragma unroll
-            for (int m = 0; m < GEMV_MAX_M; ++m) {
-                if (m >= M) break;
-                const bf16x8 x = *(const bf16x8*)(arow[m] + k);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bf16x2 wv = {w[2 * j], w[2 * j + 1]}, xv = {x[2 * j], x[2 * j + 1]};
-                    acc[m] = __builtin_amdgcn_fdot2_f32_bf16(wv, xv, acc[m], false);
-                }
-            }
+        for (int j = 0; j < 4; ++j) {
+            const bf16x2 wv = {w[2 * j], w[2 * j + 1]}, xv = {x[2 * j], x[2 * j + 1]};
+            c = __builtin_amdgcn_fdot2_f32_bf16(wv, xv, c, false);
         }
+        return c;
+    };
+    const int steps = ks / 64;
+    int st = 0;
+    for (; st + 4 <= steps; st += 4) {                     // four 64-wide k steps per pass
+        bf16x8 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = *(const bf16x8*)(brow + (st + u) * 64);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            bf16x8 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = *(const bf16x8*)(arow[m] + (st + u) * 64);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[m] = dot8(w[u], x[u], acc[m]);
+        }
+    }
+    for (; st < steps; ++st) {
+        const bf16x8 w = *(const bf16x8*)(brow + st * 64);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m] = dot8(w, *(const bf16x8*)(arow[m] + st * 64), acc[m]);
     }
     float* pt = a.split_ws + ((int64_t)unit * sp.split + sl) * 65536;
 #pragma unroll
-    for (int m = 0; m < GEMV_MAX_M; ++m) {
-        if (m >= M) break;
+    for (int m = 0; m < MR; ++m) {
         float v = acc[m];
         v += __shfl_xor(v, 1);
         v += __shfl_xor(v, 2);
         v += __shfl_xor(v, 4);
-        if (kl == 0 && col_ok) pt[m * 256 + nl] = v;
+        if (kl == 0 && col_ok && m < M) pt[m * 256 + nl] = v;
     }
 }
 
@@ -614,7 +629,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     const int gm = a.groups > 1 ? mt : pick_group_rows(mt, nt * a.groups, 256.0 * a.K_a, 256.0 * a.K);
     if (a.split_ws && gemv_eligible(a)) {           // few rows: stream the weight, reduce with the epilogue
         const SplitPlan sp = plan_gemv(a.N, a.K);
-        hipLaunchKernelGGL(gemv_bf16_kernel, dim3((unsigned)(sp.rem * 8 * sp.split)), dim3(256), 0, s, a, mt, nt, gm, sp);
+        const dim3 grid((unsigned)(sp.rem * 8 * sp.split));
+        if (a.M <= 1) hipLaunchKernelGGL(gemv_bf16_kernel<1>, grid, dim3(256), 0, s, a, mt, nt, gm, sp);
+        else if (a.M <= 2) hipLaunchKernelGGL(gemv_bf16_kernel<2>, grid, dim3(256), 0, s, a, mt, nt, gm, sp);
+        else if (a.M <= 4) hipLaunchKernelGGL(gemv_bf16_kernel<4>, grid, dim3(256), 0, s, a, mt, nt, gm, sp);
+        else if (a.M <= 8) hipLaunchKernelGGL(gemv_bf16_kernel<8>, grid, dim3(256), 0, s, a, mt, nt, gm, sp);
+        else hipLaunchKernelGGL(gemv_bf16_kernel<16>, grid, dim3(256), 0, s, a, mt, nt, gm, sp);
         if (hipError_t e = hipGetLastError()) return e;
         hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3(65536 / (256 * 8), sp.rem), dim3(256), 0, s, a, mt, nt, gm, sp);
         return hipGetLastError();
