@@ -177,6 +177,25 @@ void attn_bf16_kernel(AttnArgs a) {
             }
             return;
         }
+        if (UNIFORM && paged && psh >= 0 && psz >= KPB && (kt + 1) * KT <= T_b) {
+            // each 1 KB block holds KPB consecutive keys of one page: one wave-uniform
+            // page-table read per block (a scalar load), the lane's key and chunk added on top
+#pragma unroll
+            for (int c = 0; c < NBW; ++c) {
+                const int q = w + c * W;
+                const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                const int j0 = kt * KT + ql * KPB;
+                const int page = ptab[__builtin_amdgcn_readfirstlane(j0 >> psh)];
+                const int64_t slot0 = (int64_t)page * psz + (j0 & (psz - 1));
+                const int lk = lane / NCH;
+                const int ch = (lane % NCH) ^ kv_swz<D_H>(ql * KPB + lk);
+                const int64_t o = ((slot0 + lk) * H_kv + hk) * D_H + ch * 8 + (kv ? vdelta : 0);
+                __builtin_amdgcn_global_load_lds((const void*)(kbase + o),
+                                                 (__attribute__((address_space(3))) void*)(st + kv * TILE + ql * 512),
+                                                 16, 0, 0);
+            }
+            return;
+        }
         int64_t off[NBW];
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
