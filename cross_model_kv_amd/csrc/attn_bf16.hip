@@ -66,7 +66,8 @@ void attn_bf16_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) bf16 lds1[2 * TILE];
     __shared__ int32_t s_pt[PT_MAX];           // the request's page table (paged caches)
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int hf = lane >> 5, lr = lane & 31;
     const int H_kv = a.H_kv, g = a.H_q / H_kv;
     const int hk = blockIdx.x % H_kv;
@@ -160,12 +161,14 @@ void attn_bf16_kernel(AttnArgs a) {
     // when W divides 16 every block of the wave sits a lane-independent distance from the
     // wave's first block (same swizzle, keys a multiple of 16 apart): one lane address serves all
     constexpr bool UNIFORM = 16 % W == 0;
+    // lane part of every load address: the lane's key within its block, its head and its
+    // (swizzled) chunk; blocks add a wave-uniform key offset
     const int key0 = (w % (NBLK / 2)) * KPB + lane / NCH;
-    const bf16* src0 = kbase + ((int64_t)(tok0 + key0) * H_kv + hk) * D_H + (((lane % NCH) ^ kv_swz<D_H>(key0)) << 3);
+    const bf16* lane0 = kbase + ((int64_t)(lane / NCH) * H_kv + hk) * D_H + (((lane % NCH) ^ kv_swz<D_H>(key0)) << 3);
     const int64_t tile_stride = (int64_t)KT * H_kv * D_H;
     auto issue = [&](bf16* st, int kt) {
         if (UNIFORM && !paged && (kt + 1) * KT <= T_b) {
-            const bf16* base = src0 + kt * tile_stride;
+            const bf16* base = lane0 + (int64_t)(tok0 + (w % (NBLK / 2)) * KPB) * H_kv * D_H + kt * tile_stride;
 #pragma unroll
             for (int c = 0; c < NBW; ++c) {
                 const int q = w + c * W;
@@ -187,10 +190,9 @@ void attn_bf16_kernel(AttnArgs a) {
                 const int j0 = kt * KT + ql * KPB;
                 const int page = ptab[__builtin_amdgcn_readfirstlane(j0 >> psh)];
                 const int64_t slot0 = (int64_t)page * psz + (j0 & (psz - 1));
-                const int lk = lane / NCH;
-                const int ch = (lane % NCH) ^ kv_swz<D_H>(ql * KPB + lk);
-                const int64_t o = ((slot0 + lk) * H_kv + hk) * D_H + ch * 8 + (kv ? vdelta : 0);
-                __builtin_amdgcn_global_load_lds((const void*)(kbase + o),
+                // same swizzle as the wave's first block: the blocks' keys differ by multiples of 16
+                const int64_t o = slot0 * H_kv * D_H + (kv ? vdelta : 0);
+                __builtin_amdgcn_global_load_lds((const void*)(lane0 + o),
                                                  (__attribute__((address_space(3))) void*)(st + kv * TILE + ql * 512),
                                                  16, 0, 0);
             }
@@ -386,11 +388,18 @@ void attn_bf16_kernel(AttnArgs a) {
     }
 
     const float l_run = l_lane + other_half(l_lane);
-    if (!valid) return;
+    // this lane's output row, formed again from the lane id (behind an opaque copy, so that
+    // none of the prologue's row values has to stay live across the key loop)
+    int lane_e = __lane_id();
+    asm volatile("" : "+v"(lane_e));
+    const int row_e = w * 32 + (lane_e & 31);
+    const int qi_e = row_e / g;
+    if (qi_e >= nq) return;
+    const int64_t out_row = (int64_t)(i0 + qi_e) * a.H_q + hk * g + (row_e - qi_e * g);
     if (a.n_split > 1) {           // partial rows of this chunk: unnormalised O, m (log2), l
         // rows without keys in the chunk leave only l = 0 (the merge skips their output)
         const bool has = active && t_lo < t_hi;
-        const int64_t prow = ((int64_t)(i0 + qi) * a.H_q + h) * a.n_split + chunk;
+        const int64_t prow = out_row * a.n_split + chunk;
         float* po = a.part + prow * D_H;
         if (has)
 #pragma unroll
@@ -409,7 +418,7 @@ void attn_bf16_kernel(AttnArgs a) {
         return;
     }
     const float inv = 1.f / l_run;
-    bf16* orow = (bf16*)a.out + ((int64_t)(i0 + qi) * a.H_q + h) * D_H;
+    bf16* orow = (bf16*)a.out + out_row * D_H;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -420,7 +429,7 @@ void attn_bf16_kernel(AttnArgs a) {
             *(bf16x4*)(orow + d * 32 + 8 * q4 + 4 * hf) = o;
         }
     if (a.lse && hf == 0)
-        a.lse[(int64_t)(i0 + qi) * a.H_q + h] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
+        a.lse[out_row] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
 }
 
 // Merge of a split attention: out = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over the
