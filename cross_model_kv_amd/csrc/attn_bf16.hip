@@ -16,7 +16,9 @@
 //    arrive by direct global -> LDS loads (global_load_lds_dwordx4): each wave fills whole
 //    1 KB blocks, every lane fetching the chunk that belongs at its slot; the next tile's
 //    loads are in flight while the current tile is consumed.  Keys past the request's end
-//    load key 0 instead (finite data; such keys are always masked).
+//    load key 0 instead (finite data; such keys are always masked).  The direct loads are
+//    issued from asm and waited for before each barrier, so the fragment reads stay alone on
+//    the LDS counter and the look-ahead reads are waited for one at a time.
 //  * q is rotated (rotate-half, table angles at the query's true position) and scaled by
 //    log2(e)/sqrt(d_h) while it is loaded; k was rotated when it was scattered into the cache.
 //  * VALU work per tile is kept small, because on gfx950 a wave's VALU instructions do not
@@ -38,6 +40,15 @@ namespace kvx {
 namespace {
 
 constexpr int KT = ATTN_KEY_TILE;
+
+// 16-byte direct global -> LDS load of one wave (lane i fills bytes 16i..16i+15 of the 1 KB
+// block at dst).  Written as asm so that the compiler does not count it among the LDS events
+// (it would then treat the LDS counter as out of order and drain every fragment read with
+// lgkmcnt(0)); the key loop waits for these loads itself before each barrier.
+__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+}
 // LDS fragment reads kept in flight ahead of the MFMAs that consume them (measured best)
 constexpr int PF_K = 4;   // K fragments (one per MFMA)
 constexpr int PF_V = 8;   // transposed V reads (two per MFMA)
@@ -174,9 +185,7 @@ void attn_bf16_kernel(AttnArgs a) {
                 const int q = w + c * W;
                 const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
                 const int64_t d = (int64_t)(ql - w % (NBLK / 2)) * KPB * H_kv * D_H + (kv ? vdelta : 0);
-                __builtin_amdgcn_global_load_lds((const void*)(base + d),
-                                                 (__attribute__((address_space(3))) void*)(st + kv * TILE + ql * 512),
-                                                 16, 0, 0);
+                lds_dma16(base + d, st + kv * TILE + ql * 512);
             }
             return;
         }
@@ -192,9 +201,7 @@ void attn_bf16_kernel(AttnArgs a) {
                 const int64_t slot0 = (int64_t)page * psz + (j0 & (psz - 1));
                 // same swizzle as the wave's first block: the blocks' keys differ by multiples of 16
                 const int64_t o = slot0 * H_kv * D_H + (kv ? vdelta : 0);
-                __builtin_amdgcn_global_load_lds((const void*)(lane0 + o),
-                                                 (__attribute__((address_space(3))) void*)(st + kv * TILE + ql * 512),
-                                                 16, 0, 0);
+                lds_dma16(lane0 + o, st + kv * TILE + ql * 512);
             }
             return;
         }
@@ -222,9 +229,7 @@ void attn_bf16_kernel(AttnArgs a) {
             const int q = w + c * W;
             if (NBLK % W == 0 || q < NBLK) {
                 const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
-                __builtin_amdgcn_global_load_lds((const void*)(kbase + off[c]),
-                                                 (__attribute__((address_space(3))) void*)(st + kv * TILE + ql * 512),
-                                                 16, 0, 0);
+                lds_dma16(kbase + off[c], st + kv * TILE + ql * 512);
             }
         }
     };

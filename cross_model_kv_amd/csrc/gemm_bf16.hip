@@ -9,6 +9,9 @@
 //    fills whole 1 KB blocks of the stage, each lane fetching the chunk that belongs at its
 //    slot of the XOR-swizzled layout.  No VGPRs hold the next tile; the two LDS stages are
 //    separate objects so the next tile's loads stay in flight while the current one is read.
+//    The direct loads are issued from asm and waited for explicitly before each barrier, so
+//    the compiler sees only fragment reads on the LDS counter and waits for them one group at
+//    a time; every fragment is read one group of MFMAs ahead of its use.
 //  * Row pointers of the gathered A rows and of the B rows are computed once per block;
 //    rows past M or N are clamped to row 0 (their outputs are never stored), so the K loop
 //    has no branches.
@@ -66,6 +69,28 @@ constexpr int CU_COUNT = 256;             // MI355X compute units
 struct SplitPlan { int full, rem, split; };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16-byte direct global -> LDS load of one wave (lane i fills bytes 16i..16i+15 of the 1 KB
+// block at dst).  Written as asm so that the compiler does not count it among the LDS events:
+// the K loop waits for these loads explicitly (s_waitcnt before each barrier), and the
+// compiler can then wait for the fragment reads with partial lgkmcnt values.
+__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_ptr_t)dst;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+}
+
+// Issue order of one stage of the GEMM's K loop (see compute): before group g its look-ahead
+// reads (the next A fragment; during the first substep also FN / FM second-substep B
+// fragments), then its FN MFMAs.
+template <int G, int FM, int FN>
+__device__ __forceinline__ void group_order() {
+    if constexpr (G < 2 * FM) {
+        constexpr int nr = (G + 1 < 2 * FM ? 1 : 0) + (G < FM ? FN / FM : 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+        group_order<G + 1, FM, FN>();
+    }
+}
 
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
@@ -142,12 +167,10 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
         const int ka = (kt * BK) % a.K_a;
 #pragma unroll
         for (int c = 0; c < A_I; ++c)
-            __builtin_amdgcn_global_load_lds((const void*)(asrc[c] + ka),
-                                             (lds_ptr_t)(st + (c * NW + wave) * 512), 16, 0, 0);
+            lds_dma16(asrc[c] + ka, st + (c * NW + wave) * 512);
 #pragma unroll
         for (int c = 0; c < B_I; ++c)
-            __builtin_amdgcn_global_load_lds((const void*)(bsrc[c] + kt * BK),
-                                             (lds_ptr_t)(st + BM * BK + (c * NW + wave) * 512), 16, 0, 0);
+            lds_dma16(bsrc[c] + kt * BK, st + BM * BK + (c * NW + wave) * 512);
     };
 
     f32x4 acc[FM][FN];
@@ -157,34 +180,42 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int lr = lane & 15, lq = lane >> 4;
+    // One stage = two 32-deep substeps = 2*FM groups of FN MFMAs (group g: A fragment g % FM of
+    // substep g / FM against the substep's FN B fragments).  Reads run one group ahead: before
+    // group g the A fragment of group g+1 is read, and during the first substep's groups the
+    // second substep's B fragments (FN / FM per group), so only the stage's first reads wait.
+    static_assert(BK == 64 && FN % FM == 0, "two substeps per stage, B reads spread over FM groups");
     auto compute = [&](const bf16* st) {
         const bf16* la = st;
         const bf16* lb = st + BM * BK;
+        auto rd_b = [&](int ks, int j) {
+            const int R = wn * WTN + j * 16 + lr;
+            return *(const bf16x8*)(lb + R * BK + (((ks * 4 + lq) ^ swz(R)) << 3));
+        };
+        auto rd_a = [&](int ks, int i) {
+            const int ml = wm * WTM + i * 16 + lr;
+            return *(const bf16x8*)(la + ml * BK + (((ks * 4 + lq) ^ swz(ml)) << 3));
+        };
+        bf16x8 b0[FN], b1[FN], af[2];
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            const int ch = ks * 4 + lq;
-            bf16x8 bfr[FN];
+        for (int j = 0; j < FN; ++j) b0[j] = rd_b(0, j);
+        af[0] = rd_a(0, 0);
+        constexpr int BPG = FN / FM;        // second-substep B reads per first-substep group
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int R = wn * WTN + j * 16 + lr;
-                bfr[j] = *(const bf16x8*)(lb + R * BK + ((ch ^ swz(R)) << 3));
+        for (int g = 0; g < 2 * FM; ++g) {
+            const int ks = g / FM, i = g % FM;
+            if (g + 1 < 2 * FM) af[(g + 1) & 1] = rd_a((g + 1) / FM, (g + 1) % FM);
+            if (g < FM) {
+#pragma unroll
+                for (int u = 0; u < BPG; ++u) b1[g * BPG + u] = rd_b(1, g * BPG + u);
             }
-            bf16x8 afr[2];
-            {
-                const int ml = wm * WTM + lr;
-                afr[0] = *(const bf16x8*)(la + ml * BK + ((ch ^ swz(ml)) << 3));
-            }
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                if (i + 1 < FM) {
-                    const int ml = wm * WTM + (i + 1) * 16 + lr;
-                    afr[(i + 1) & 1] = *(const bf16x8*)(la + ml * BK + ((ch ^ swz(ml)) << 3));
-                }
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i & 1], bfr[j], acc[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[g & 1], ks ? b1[j] : b0[j], acc[i][j], 0, 0, 0);
         }
+        // issue order: the first reads, then per group its look-ahead reads and its MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);
+        group_order<0, FM, FN>();
     };
 
     issue(lds0, k_first);
