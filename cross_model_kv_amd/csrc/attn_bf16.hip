@@ -192,6 +192,8 @@ void attn_bf16_kernel(AttnArgs a) {
         if (UNIFORM && paged && psh >= 0 && psz >= KPB && (kt + 1) * KT <= T_b) {
             // each 1 KB block holds KPB consecutive keys of one page: one wave-uniform
             // page-table read per block (a scalar load), the lane's key and chunk added on top
+            // (all page-table reads before the first load: the loads' asm orders memory accesses)
+            int64_t o[NBW];
 #pragma unroll
             for (int c = 0; c < NBW; ++c) {
                 const int q = w + c * W;
@@ -200,8 +202,13 @@ void attn_bf16_kernel(AttnArgs a) {
                 const int page = ptab[__builtin_amdgcn_readfirstlane(j0 >> psh)];
                 const int64_t slot0 = (int64_t)page * psz + (j0 & (psz - 1));
                 // same swizzle as the wave's first block: the blocks' keys differ by multiples of 16
-                const int64_t o = slot0 * H_kv * D_H + (kv ? vdelta : 0);
-                lds_dma16(lane0 + o, st + kv * TILE + ql * 512);
+                o[c] = slot0 * H_kv * D_H + (kv ? vdelta : 0);
+            }
+#pragma unroll
+            for (int c = 0; c < NBW; ++c) {
+                const int q = w + c * W;
+                const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                lds_dma16(lane0 + o[c], st + kv * TILE + ql * 512);
             }
             return;
         }
