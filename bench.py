@@ -10,8 +10,9 @@ All inputs are synthetic (seeded) and resident in HBM before timing.
 
 Prints one JSON line: handoff tokens/s (positions handed off per second), the roofline of
 the dominant kernel (the sparse attention, timed with HIP events on its launch stream
-over the timed steps), per-stage times, and the fp64 CPU oracle timed on a bounded sample
-of the same workload.
+over the timed steps), per-stage times, the HBM rate of the standalone RoPE + scatter entry
+point on the same rows (outside the timed steps), and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -432,6 +433,29 @@ def main():
     S = h.S.cpu().numpy()
     pos_sum = float(np.sum(S.astype(np.float64) + 1.0))
     work = stage_work(wl, T, k, pos_sum)
+
+    # The step fuses RoPE + scatter into the projection's epilogue.  The standalone entry point
+    # (kvx_rope_scatter, HBM-bound) is timed here on the same selected rows, after the timed
+    # steps and outside them, for its bandwidth: 2 * k * H_kv * d_h bf16 values read and written.
+    for l in range(2):
+        kvx.rope_scatter(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache)
+    reps = 4
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        for l in range(wl.L_t):
+            kvx.rope_scatter(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sc_ms = e0.elapsed_time(e1) / (reps * wl.L_t)
+    sc_bytes = 8.0 * k * wl.H_kv * wl.d_h
+    sc_gbs = sc_bytes / (sc_ms * 1e-3) / 1e9
+    scatter = {"kernel": "rope_scatter (kvx_rope_scatter on the step's selected rows; outside the timed step, "
+                         "which fuses RoPE + scatter into the projection)",
+               "bound": "hbm", "achieved": round(sc_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+               "frac": round(sc_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": sc_bytes,
+               "avg_launch_ms": round(sc_ms, 5)}
     stages = {}
     for n in names:
         t = avg_launch_ms[n] * 1e-3
@@ -473,6 +497,7 @@ def main():
                      "traffic": traffic, "algorithmic_flops_per_launch": work["sparse_attention"]["flops"],
                      "avg_launch_ms": round(avg_launch_ms["sparse_attention"], 5)},
         "stages": stages,
+        "scatter_standalone": scatter,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

@@ -304,6 +304,47 @@ __global__ void rope_scatter_kernel(ScatterArgs a) {
     vd[j + half] = vr[j + half];
 }
 
+// bf16 with 16-byte rows: one thread per (selected row, KV head, run of 8 rotation pairs).  It
+// reads 16 bytes of k at j0 and at j0 + d_h/2, the same of v, and the 8 (cos, sin) pairs, and
+// writes four 16-byte chunks; the rotation is the same rope_lo / rope_hi as the scalar kernel.
+__global__ __launch_bounds__(256) void rope_scatter_vec_kernel(ScatterArgs a) {
+    const int half = a.d_h / 2, runs = half / 8;
+    const int64_t per_row = (int64_t)a.H_kv * runs;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= a.n_sel * per_row) return;
+    const int i = (int)(idx / per_row);
+    const int rem = (int)(idx % per_row);
+    const int h = rem / runs, j0 = (rem % runs) * 8;
+    const int b = find_request(a.cu_sel, a.n_req, i);
+    const int p = a.sel[i];
+    const int64_t slot = a.slots.slot(b, p);
+    const bf16* row = (const bf16*)a.qkv + (int64_t)i * a.ld;
+    const bf16* kr = row + (int64_t)(a.H_q + h) * a.d_h + j0;
+    const bf16* vr = row + (int64_t)(a.H_q + a.H_kv + h) * a.d_h + j0;
+    const bf16x8 k1 = *(const bf16x8*)kr, k2 = *(const bf16x8*)(kr + half);
+    const bf16x8 v1 = *(const bf16x8*)vr, v2 = *(const bf16x8*)(vr + half);
+    const float4* cs = (const float4*)(a.rope + ((int64_t)p * half + j0) * 2);
+    bf16x8 o1, o2;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        const float4 t = cs[e2];       // (cos, sin) of pairs j0 + 2 e2 and j0 + 2 e2 + 1
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = 2 * e2 + u;
+            const float c = u ? t.z : t.x, sn = u ? t.w : t.y;
+            const float x1 = (float)k1[e], x2 = (float)k2[e];
+            o1[e] = (bf16)rope_lo(x1, x2, c, sn);
+            o2[e] = (bf16)rope_hi(x1, x2, c, sn);
+        }
+    }
+    bf16* kd = (bf16*)a.kc + (slot * a.H_kv + h) * a.d_h + j0;
+    bf16* vd = (bf16*)a.vc + (slot * a.H_kv + h) * a.d_h + j0;
+    *(bf16x8*)kd = o1;
+    *(bf16x8*)(kd + half) = o2;
+    *(bf16x8*)vd = v1;
+    *(bf16x8*)(vd + half) = v2;
+}
+
 // =========================================================================== fp32 path
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args a) {
     __shared__ float As[16][65];
@@ -637,7 +678,13 @@ hipError_t launch_rope_scatter(const ScatterArgs& a, int dtype, hipStream_t s) {
     const int64_t n = a.n_sel * a.H_kv * (a.d_h / 2);
     if (n == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((n + 255) / 256);
-    if (dtype == KVX_BF16) hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+    // 16-byte path: d_h / 2 a multiple of 8 and every row start (and the rotary table) 16-byte aligned
+    const bool vec = dtype == KVX_BF16 && a.d_h % 16 == 0 && a.ld % 8 == 0 &&
+                     ((uintptr_t)a.qkv | (uintptr_t)a.kc | (uintptr_t)a.vc | (uintptr_t)a.rope) % 16 == 0;
+    if (vec) {
+        const int64_t nv = n / 8;
+        hipLaunchKernelGGL(rope_scatter_vec_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s, a);
+    } else if (dtype == KVX_BF16) hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
