@@ -97,8 +97,12 @@ __global__ void pack_operator_kernel(const double* A, int r, int dtype, void* op
 // min and max keys; the histogram's top-down cumulative count picks each digit.  Keys equal
 // to the k-th are taken lowest position first, then positions are written in ascending
 // order with two block-wide prefix sums.  Integer-only after the scores: deterministic.
+// The keys are formed once (summing the score GEMM's per-column-block partials) and kept in
+// LDS for every later pass when the request has at most SEL_CAP positions (else re-read from
+// the scores written by the first pass).
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_CAP = 32768;
 
 __device__ __forceinline__ uint32_t order_key(float s) {
     uint32_t u = __float_as_uint(s);
@@ -138,6 +142,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
                                                             const int32_t* cu_sel, int32_t* sel,
                                                             int32_t* rest) {
     __shared__ int hist[SEL_WAVES][256];
+    __shared__ uint32_t s_key[SEL_CAP];
     __shared__ int s_wave[SEL_WAVES];
     __shared__ uint32_t s_mm[2][SEL_WAVES];
     __shared__ int s_bc[2];
@@ -154,8 +159,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
         for (int p = 0; p < n_part; ++p) s += partial[(int64_t)p * n_rows + base + t];
         return s;
     };
-    if (n_part > 0)
-        for (int t = tid; t < T; t += SEL_THREADS) scores[base + t] = score_at(t);
+    const bool in_lds = T <= SEL_CAP;
+    for (int t = tid; t < T; t += SEL_THREADS) {
+        const float sc = score_at(t);
+        if (n_part > 0) scores[base + t] = sc;
+        if (in_lds) s_key[t] = order_key(sc);
+    }
+    __syncthreads();
+    auto key_at = [&](int t) -> uint32_t { return in_lds ? s_key[t] : order_key(scores[base + t]); };
     if (k == 0) {
         for (int t = tid; t < T; t += SEL_THREADS) ro[t] = t;
         return;
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
     // common prefix of all keys of this request
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     for (int t = tid; t < T; t += SEL_THREADS) {
-        const uint32_t key = order_key(score_at(t));
+        const uint32_t key = key_at(t);
         kmin = min(kmin, key);
         kmax = max(kmax, key);
     }
@@ -195,7 +206,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
         for (int i = tid; i < SEL_WAVES * 256; i += SEL_THREADS) (&hist[0][0])[i] = 0;
         __syncthreads();
         for (int t = tid; t < T; t += SEL_THREADS) {
-            const uint32_t key = order_key(score_at(t));
+            const uint32_t key = key_at(t);
             if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & (nbins - 1)], 1);
         }
         __syncthreads();
@@ -245,20 +256,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
     const int chunk = (T + SEL_THREADS - 1) / SEL_THREADS;
     const int t0 = min(T, tid * chunk), t1 = min(T, t0 + chunk);
     int n_eq = 0;
-    for (int t = t0; t < t1; ++t) n_eq += order_key(score_at(t)) == tau;
+    for (int t = t0; t < t1; ++t) n_eq += key_at(t) == tau;
     const int eq_before = block_excl_scan(n_eq, s_wave, nullptr);
     int n_take = 0;
     {
         int e = eq_before;
         for (int t = t0; t < t1; ++t) {
-            const uint32_t key = order_key(score_at(t));
+            const uint32_t key = key_at(t);
             n_take += key > tau || (key == tau && e++ < take_eq);
         }
     }
     int j = block_excl_scan(n_take, s_wave, nullptr);
     int e = eq_before;
     for (int t = t0; t < t1; ++t) {
-        const uint32_t key = order_key(score_at(t));
+        const uint32_t key = key_at(t);
         const bool take = key > tau || (key == tau && e++ < take_eq);
         if (take) so[j++] = t;
         else ro[t - j] = t;
