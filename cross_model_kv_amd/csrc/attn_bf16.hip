@@ -516,9 +516,9 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
 int attn_bf16_split(int n_blocks, int H_kv, int max_T) {
     constexpr int CUS = 256;
     const int64_t items = (int64_t)n_blocks * H_kv;
-    if (items <= 0 || items >= 2 * CUS) return 1;
+    if (items <= 0 || items >= CUS) return 1;
     const int max_tiles = (max_T + KT - 1) / KT;
-    int c = (int)((2 * CUS + items - 1) / items);
+    int c = (int)(CUS / items);         // at most one round of workgroups
     c = std::min(c, std::min(max_tiles / 4, 64));
     return std::max(c, 1);
 }

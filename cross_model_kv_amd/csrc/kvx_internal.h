@@ -60,8 +60,8 @@ struct AttnArgs {
     int n_split; int split_len; float* part; float* part_ml; int64_t n_rows_total;
     int32_t blk_cu[MAX_ATTN_REQ + 1];  // blk_cu[b] = sum_{b' < b} ceil(k_b' / bq)
 };
-// chunks per query block for the key-range split: enough workgroups to fill the GPU twice
-// over, chunks of at least 4 key tiles
+// chunks per query block for the key-range split: as many as fit the workgroups in one round
+// over the CUs (none when the blocks alone fill a round), chunks of at least 4 key tiles
 int attn_bf16_split(int n_blocks, int H_kv, int max_T);
 // fp32 partial workspace of a split attention over n_sel selected rows
 size_t attn_bf16_split_bytes(int64_t n_sel, int H_q, int d_h, int n_split);
