@@ -99,9 +99,6 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
-    constexpr int A_I = BM / 8 / NW;     // 1 KB direct loads per wave per A tile
-    constexpr int B_I = BN / 8 / NW;
-    static_assert(A_I * NW * 8 == BM && B_I * NW * 8 == BN, "tiles split into whole 1 KB blocks per wave");
     static_assert(FN == 4 || FN == 8, "lanes own 4 or 8 consecutive output columns");
     constexpr int STAGE = (BM + BN) * BK;
     __shared__ __attribute__((aligned(1024))) bf16 lds0[STAGE];
@@ -145,7 +142,8 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     const bf16* Bg = a.B + (int64_t)t.group * a.b_group_stride;
     // loader waves: only the first NL waves (one per SIMD) issue the direct loads
     constexpr int NL = NW / 2;
-    constexpr int A_L = BM / 8 / NL, B_L = BN / 8 / NL;
+    constexpr int A_L = BM / 8 / NL, B_L = BN / 8 / NL;   // 1 KB direct loads per loader wave
+    static_assert(A_L * NL * 8 == BM && B_L * NL * 8 == BN, "tiles split into whole 1 KB blocks per loader wave");
     const int lw = wave % NL;
     const bf16* asrc[A_L];
     const bf16* bsrc[B_L];
