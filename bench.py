@@ -10,9 +10,10 @@ All inputs are synthetic (seeded) and resident in HBM before timing.
 
 Prints one JSON line: handoff tokens/s (positions handed off per second), the roofline of
 the dominant kernel (the sparse attention, timed with HIP events on its launch stream
-over the timed steps), per-stage times, the HBM rate of the standalone RoPE + scatter entry
-point on the same rows (outside the timed steps), and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+over the timed steps), per-stage times, the same step captured in a HIP graph and replayed
+(time per step and a bit-for-bit check against the eager outputs), the HBM rate of the standalone
+RoPE + scatter entry point on the same rows (outside the timed steps), and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -434,6 +435,39 @@ def main():
     pos_sum = float(np.sum(S.astype(np.float64) + 1.0))
     work = stage_work(wl, T, k, pos_sum)
 
+    # The same step captured once in a HIP graph (no entry point allocates, copies or synchronises)
+    # and replayed: its time per step, and whether every replay reproduces the eager outputs bit
+    # for bit.  Reported beside the eager line; the step above is the measured one.
+    graph = None
+    try:
+        ref_out, ref_sel = h.out.clone(), h.S.clone()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        same = True
+        g.replay()
+        torch.cuda.synchronize()
+        same = same and torch.equal(h.out, ref_out) and torch.equal(h.S, ref_sel)
+        ge0 = torch.cuda.Event(enable_timing=True)
+        ge1 = torch.cuda.Event(enable_timing=True)
+        ge0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        ge1.record(stream)
+        torch.cuda.synchronize()
+        same = same and torch.equal(h.out, ref_out) and torch.equal(h.S, ref_sel)
+        graph = {"ms_per_step": round(ge0.elapsed_time(ge1) / args.steps, 3), "replays_equal_eager": bool(same)}
+        del g
+    except RuntimeError as e:          # reported, not fatal: the eager line is the measurement
+        graph = {"error": str(e)[:200]}
+
     # The step fuses RoPE + scatter into the projection's epilogue.  The standalone entry point
     # (kvx_rope_scatter, HBM-bound) is timed here on the same selected rows, after the timed
     # steps and outside them, for its bandwidth: 2 * k * H_kv * d_h bf16 values read and written.
@@ -498,6 +532,7 @@ def main():
                      "avg_launch_ms": round(avg_launch_ms["sparse_attention"], 5)},
         "stages": stages,
         "scatter_standalone": scatter,
+        "graph": graph,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
