@@ -12,8 +12,9 @@ Prints one JSON line: handoff tokens/s (positions handed off per second), the ro
 the dominant kernel (the sparse attention, timed with HIP events on its launch stream
 over the timed steps), per-stage times, the same step captured in a HIP graph and replayed
 (time per step and a bit-for-bit check against the eager outputs), the HBM rate of the standalone
-RoPE + scatter entry point on the same rows (outside the timed steps), and the fp64 CPU oracle
-timed on a bounded sample of the same workload.
+RoPE + scatter entry point on the same rows (outside the timed steps), the rates this GPU reaches
+on a large library GEMM and a device copy, and the fp64 CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -132,6 +133,38 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each_way": 2 * n, "launches": 5}))
+
+
+def measured_peaks(stream):
+    """What this GPU reaches on a large square bf16 product through the vendor library
+    (torch.matmul, 8192^3) and on a 1 GiB device copy: context for the datasheet fractions."""
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        c = a @ b
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+    del a, b, c
+    m = 1 << 29
+    x = torch.ones(m, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    e0.record(stream)
+    for _ in range(10):
+        y.copy_(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * 2 * m / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    return {"bf16_gemm_tflops": round(gemm_tflops, 1), "gemm": "torch.matmul 8192x8192x8192 bf16",
+            "copy_gbs": round(copy_gbs, 1), "copy": "1 GiB device copy (read + write)"}
 
 
 def chain_layer_work(wl, k, pos_sum):
@@ -508,6 +541,9 @@ def main():
         with open(ATTN_SOURCE, "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() == rec.get("kernel_source_sha256"):
                 traffic = rec.get("hbm_bytes_per_launch")
+    peaks = measured_peaks(stream)
+    peaks["attention_frac_of_gemm"] = round(achieved / peaks["bf16_gemm_tflops"], 4)
+    peaks["scatter_frac_of_copy"] = round(sc_gbs / peaks["copy_gbs"], 4)
     line = {
         "metric": METRIC,
         "value": T * args.steps / elapsed,
@@ -533,6 +569,7 @@ def main():
         "stages": stages,
         "scatter_standalone": scatter,
         "graph": graph,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
