@@ -117,7 +117,16 @@ def cpu_baseline(inp, wl, S, T, k, pos_sum):
     dt = time.perf_counter() - t0
     parts["sparse_attention"] = dt * pos_sum / float(np.sum(sel_rows[qi] + 1)) * wl.L_t
     total = sum(parts.values())
-    return {"value": T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    host = {"cpu_model": cpu_model, "nproc": os.cpu_count(),
+            "blas_threads_env": {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")
+                                 if os.environ.get(v) is not None}}
+    return {"value": T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "host": host,
             "sample": (f"fp64 numpy oracle on the {wl.name} workload: map 512 rows, reconstruct+score 256 rows "
                        f"x {wl.L_t} layers, full select, 1 layer of qkv (512 rows), scatter, attention (24 queries); "
                        "each part scaled to one handoff (rows, layers, sum of causal lengths)"),
