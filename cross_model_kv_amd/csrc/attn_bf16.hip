@@ -83,8 +83,9 @@ void attn_bf16_kernel(AttnArgs a) {
     const int H_kv = a.H_kv, g = a.H_q / H_kv;
     const int hk = blockIdx.x % H_kv;
     const int item = (int)(blockIdx.x / H_kv);
-    const int qb = a.n_blocks - 1 - item / a.n_split;   // longest first
-    const int chunk = item % a.n_split;
+    // chunk-major order: every block's chunk 0 (longest blocks first), then the chunk 1s, ...
+    const int qb = a.n_blocks - 1 - item % a.n_blocks;
+    const int chunk = item / a.n_blocks;
 
     // request of this query block
     int b = 0;
@@ -115,7 +116,10 @@ void attn_bf16_kernel(AttnArgs a) {
     if (a.n_split > 1) {           // chunk c: the c-th run of split_len tiles from the block's end
         t_hi = max(n_tiles_all - chunk * a.split_len, 0);
         t_lo = max(t_hi - a.split_len, 0);
+        if (t_lo >= t_hi) return;  // the block is shorter: nothing to do, nothing written
     }
+    // a block of at most split_len tiles is whole in its chunk 0, which writes the final rows
+    const bool whole = a.n_split == 1 || n_tiles_all <= a.split_len;
     // a row whose position lies before the chunk has no key in it: its work is discarded
     const bool active = p_row >= t_lo * KT;
 
@@ -408,9 +412,9 @@ void attn_bf16_kernel(AttnArgs a) {
     const int qi_e = row_e / g;
     if (qi_e >= nq) return;
     const int64_t out_row = (int64_t)(i0 + qi_e) * a.H_q + hk * g + (row_e - qi_e * g);
-    if (a.n_split > 1) {           // partial rows of this chunk: unnormalised O, m (log2), l
+    if (!whole) {                  // partial rows of this chunk: unnormalised O, m (log2), l
         // rows without keys in the chunk leave only l = 0 (the merge skips their output)
-        const bool has = active && t_lo < t_hi;
+        const bool has = active;
         const int64_t prow = out_row * a.n_split + chunk;
         float* po = a.part + prow * D_H;
         if (has)
@@ -450,31 +454,50 @@ void attn_bf16_kernel(AttnArgs a) {
 // chunks (the weights broadcast from their lanes).
 template <int D_H>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, const float* ml, int n_split,
-                                                            int64_t rows, bf16* out, float* lse) {
+                                                            int split_len, int64_t rows, int H_q,
+                                                            const int32_t* sel, const int32_t* cu_sel, int n_req,
+                                                            int bq, bf16* out, float* lse) {
     constexpr int CPL = D_H / 64;                 // output columns per lane
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
+    // the row's query block: its last query's position gives the block's key tiles, and so the
+    // chunks that hold partials (none when the block was whole in its chunk 0)
+    const int i = (int)(row / H_q);
+    int b = 0;
+    {
+        int lo = 0, hi = n_req - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu_sel[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+    }
+    const int qi = i - cu_sel[b];
+    const int last = min(cu_sel[b] + (qi / bq + 1) * bq, cu_sel[b + 1]) - 1;
+    const int n_tiles = sel[last] / KT + 1;
+    if (n_tiles <= split_len) return;
+    const int nch = min((n_tiles + split_len - 1) / split_len, n_split);
     const float* mlr = ml + row * n_split * 2;
-    const float mc = lane < n_split ? mlr[2 * lane] : 0.f;
-    const float lc = lane < n_split ? mlr[2 * lane + 1] : 0.f;
+    const float mc = lane < nch ? mlr[2 * lane] : 0.f;
+    const float lc = lane < nch ? mlr[2 * lane + 1] : 0.f;
     float m = lc > 0.f ? mc : -INFINITY;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     const float wgt = lc > 0.f ? __builtin_amdgcn_exp2f(mc - m) : 0.f;
     // chunk-ordered sum of the weighted row sums (lane 0 adds them one by one)
     float L = 0.f;
-    for (int c = 0; c < n_split; ++c) L += __shfl(wgt, c) * __shfl(lc, c);
+    for (int c = 0; c < nch; ++c) L += __shfl(wgt, c) * __shfl(lc, c);
     float acc[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
     // eight chunks per pass: their loads are issued together, the sums stay in chunk order
-    for (int c0 = 0; c0 < n_split; c0 += 8) {
+    for (int c0 = 0; c0 < nch; c0 += 8) {
         float v[8][CPL];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int c = c0 + u;
-            const bool use = c < n_split && __shfl(wgt, c < n_split ? c : 0) != 0.f;
+            const bool use = c < nch && __shfl(wgt, c < nch ? c : 0) != 0.f;
             const float* pc = part + (row * n_split + (use ? c : 0)) * D_H + lane * CPL;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) v[u][j] = use ? pc[j] : 0.f;
@@ -482,7 +505,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, co
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int c = c0 + u;
-            const float wc = c < n_split ? __shfl(wgt, c) : 0.f;
+            const float wc = c < nch ? __shfl(wgt, c) : 0.f;
             if (wc == 0.f) continue;              // uniform over the wave
 #pragma unroll
             for (int j = 0; j < CPL; ++j) acc[j] += wc * v[u][j];
@@ -505,7 +528,8 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
     const int64_t rows = a.n_rows_total * a.H_q;   // (selected row, query head) rows
     if (a.n_split > 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_combine_kernel<D_H>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
-                       (const float*)a.part, (const float*)a.part_ml, a.n_split, rows, (bf16*)a.out, a.lse);
+                       (const float*)a.part, (const float*)a.part_ml, a.n_split, a.split_len, rows, a.H_q, a.sel,
+                       a.cu_sel, a.n_req, a.bq, (bf16*)a.out, a.lse);
     return hipGetLastError();
 }
 
@@ -518,7 +542,8 @@ int attn_bf16_split(int n_blocks, int H_kv, int max_T) {
     const int64_t items = (int64_t)n_blocks * H_kv;
     if (items <= 0 || items >= CUS) return 1;
     const int max_tiles = (max_T + KT - 1) / KT;
-    int c = (int)(CUS / items);         // at most one round of workgroups
+    // c = round(1.25 * CUS / items), fitted by measurement (200 workgroups: 2 chunks, 104: 3, 50: 6)
+    int c = (int)((5 * CUS + 2 * items) / (4 * items));
     c = std::min(c, std::min(max_tiles / 4, 64));
     return std::max(c, 1);
 }

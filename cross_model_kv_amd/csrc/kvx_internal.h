@@ -52,16 +52,18 @@ struct AttnArgs {
     const void* kc; const void* vc;   // layer base pointers
     void* out; float* lse;
     // key-range split (bf16 path): chunk c of a query block is the c-th run of split_len key
-    // tiles counted back from the block's last tile (n_split chunks, one workgroup each; short
-    // blocks leave the later chunks empty).  A chunk leaves its unnormalised output rows (fp32)
-    // in part[(row * n_split + c) * d_h] and (m, l) in part_ml[(row * n_split + c) * 2], row =
-    // i * H_q + h, l = 0 for rows without keys in it; a combine kernel merges them.
-    // n_split = 1: no split, no partials.
+    // tiles counted back from the block's last tile (n_split chunks, one workgroup each,
+    // chunk-major: every block's chunk 0 first).  A block of at most split_len tiles is whole in
+    // its chunk 0, which writes the final rows; its other chunks are empty and write nothing.
+    // Each chunk of a longer block leaves its unnormalised output rows (fp32) in
+    // part[(row * n_split + c) * d_h] and (m, l) in part_ml[(row * n_split + c) * 2], row =
+    // i * H_q + h, l = 0 for rows without keys in it; a combine kernel merges the chunks of those
+    // rows only.  n_split = 1: no split, no partials.
     int n_split; int split_len; float* part; float* part_ml; int64_t n_rows_total;
     int32_t blk_cu[MAX_ATTN_REQ + 1];  // blk_cu[b] = sum_{b' < b} ceil(k_b' / bq)
 };
-// chunks per query block for the key-range split: as many as fit the workgroups in one round
-// over the CUs (none when the blocks alone fill a round), chunks of at least 4 key tiles
+// chunks per query block for the key-range split: round(1.25 * 256 / workgroups) (none when the
+// blocks alone fill the CUs), chunks of at least 4 key tiles
 int attn_bf16_split(int n_blocks, int H_kv, int max_T);
 // fp32 partial workspace of a split attention over n_sel selected rows
 size_t attn_bf16_split_bytes(int64_t n_sel, int H_q, int d_h, int n_split);
