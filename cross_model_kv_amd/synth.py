@@ -117,10 +117,15 @@ def _host_normal(ss, shape, std=1.0):
     return rng.standard_normal(size=shape) * std
 
 
-def generate(wl: Workload, seed: int, device="cpu", where: str = "auto") -> Inputs:
-    """Draw every input of the handoff for workload ``wl``; tensors land on ``device``."""
+def generate(wl: Workload, seed: int, device="cpu", where: str = "auto",
+             lengths: Optional[List[int]] = None, pcts: Optional[List[int]] = None) -> Inputs:
+    """Draw every input of the handoff for workload ``wl``; tensors land on ``device``.
+    ``lengths`` / ``pcts`` replace the drawn request lengths and budgets (ragged edge cases)."""
     ss = _subseeds(seed)
-    lengths, pcts = draw_lengths_budgets(wl, seed)
+    if lengths is None:
+        lengths, pcts = draw_lengths_budgets(wl, seed)
+    else:
+        lengths, pcts = [int(t) for t in lengths], [int(p) for p in pcts]
     N = int(sum(lengths))
     dt = storage_dtype(wl)
     dev = torch.device(device)

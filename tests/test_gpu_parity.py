@@ -126,6 +126,50 @@ def test_end_to_end_small(name):
             assert_close(o, ref["O"], tol, "attention output")
 
 
+EDGE_LENGTHS = [1, 2, 63, 64, 65, 300, 129]
+EDGE_PCTS = [100, 50, 30, 0, 40, 20, 100]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_end_to_end_ragged_edges(paged):
+    """Requests of 1, 2, 63, 64, 65, 300 and 129 positions with budgets of 100, 50, 30, 0, 40, 20
+    and 100%: one-position requests, empty and full selections, tile-edge lengths and ragged
+    tails in one batch, contiguous and paged (16-token pages), against the oracle per request."""
+    wl = small("edges-" + ("paged" if paged else "contiguous"), H_q=16, H_kv=2, n_req=len(EDGE_LENGTHS),
+               t_min=1, t_max=300, pct_choices=(30,), paged=paged, page_size=16)
+    say(f"[e2e] {wl.name}")
+    inp = synth.generate(wl, 13, DEV, lengths=EDGE_LENGTHS, pcts=EDGE_PCTS)
+    h = Handoff(inp, DEV)
+    h.cache.k.zero_()
+    h.cache.v.zero_()
+    h.run()
+    torch.cuda.synchronize()
+    z = f64(h.z)
+    scores = f64(h.scores)
+    S_all = h.S.cpu().numpy()
+    cu, cs = inp.cu_tokens, h.batch.cu_sel
+    compared = 0
+    for b, T in enumerate(inp.lengths):
+        ref = oracle_request(inp, b)
+        assert_close(z[cu[b]:cu[b + 1]], ref["z"], 2e-2, f"Z[{b}]")
+        assert rel_max(scores[cu[b]:cu[b + 1]], ref["s"]) <= 1e-2, b
+        S = S_all[cs[b]:cs[b + 1]]
+        assert len(S) == O.budget(T, inp.pcts[b]) and np.all(np.diff(S) > 0), b
+        band_check(S, ref["s"], len(S), 2e-3)
+        K, V = cache_views(h, b, T)
+        if set(S.tolist()) != set(ref["S"].tolist()):
+            continue                         # ties inside the band: the cache halves differ by design
+        assert_close(K, ref["K"], 2e-2, f"K[{b}]")
+        assert_close(V, ref["V"], 2e-2, f"V[{b}]")
+        if len(S):
+            o = f64(h.out[:, cs[b]:cs[b + 1]])
+            assert min_row_cosine(o, ref["O"]) >= 0.999, b
+            assert_close(o, ref["O"], 2e-2, f"attention output[{b}]")
+        compared += 1
+    say(f"  {compared} of {len(EDGE_LENGTHS)} requests compared in full")
+    assert compared >= len(EDGE_LENGTHS) - 1
+
+
 def test_full_budget_equals_causal_prefill():
     """A 100% budget recomputes every position: the outputs are plain causal attention of
     the target's own Q/K/V, whatever the translated cache held."""
