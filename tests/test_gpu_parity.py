@@ -274,11 +274,13 @@ def test_identity_mapper_bitexact(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_score_select_stagewise(dtype):
+@pytest.mark.parametrize("T", [700, 40000])
+def test_score_select_stagewise(dtype, T):
     """Scores from a given latent: per-position relative error against the oracle's
     explicit residual energy, the selected set exactly the top-k of the returned scores,
-    and equal to the oracle's set outside a 1e-5 band."""
-    wl = small(f"score-{dtype}", dtype=dtype, T=700, L_t=3, r=128, c=64)
+    and equal to the oracle's set outside a 1e-5 band.  T = 40000 is longer than the select
+    kernel keeps in LDS (its later passes re-read the scores the first pass wrote)."""
+    wl = small(f"score-{dtype}", dtype=dtype, T=T, L_t=3, r=128, c=64)
     say(f"[score] {wl.name}")
     dt = torch.float32 if dtype == "f32" else torch.bfloat16
     inp = synth.generate(wl, 31, DEV)
@@ -320,7 +322,7 @@ def test_in_span_scores_zero():
 
 @pytest.mark.parametrize("kind", ["equal", "few_values", "signed_zeros", "ulp", "normal", "positive"])
 def test_select_topk_adversarial(kind):
-    lengths = [1, 2, 63, 1000, 4097]
+    lengths = [1, 2, 63, 1000, 4097, 40000]   # the last one is longer than the LDS key copy
     rng = np.random.default_rng(41)
     ks = [int(rng.integers(0, t + 1)) for t in lengths]
     ks[3], ks[4] = 0, 4097            # empty and full selections
