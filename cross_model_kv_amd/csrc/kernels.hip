@@ -288,10 +288,10 @@ __global__ void rope_table_kernel(double base, int d_h, int max_pos, float* tabl
     table[2 * idx + 1] = (float)sin(ang);
 }
 
-// one thread per (selected row, KV head, rotation pair j): rotates k's pair and copies v's
+// fp32: one thread per (selected row, KV head, rotation pair j): rotates k's pair and copies v's
 // two elements at j and j + d_h/2
-template <typename TE>
 __global__ void rope_scatter_kernel(ScatterArgs a) {
+    typedef float TE;
     const int half = a.d_h / 2;
     const int64_t per_row = (int64_t)a.H_kv * half;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -688,15 +688,17 @@ hipError_t launch_rope_table(double base, int d_h, int max_pos, float* table, hi
 hipError_t launch_rope_scatter(const ScatterArgs& a, int dtype, hipStream_t s) {
     const int64_t n = a.n_sel * a.H_kv * (a.d_h / 2);
     if (n == 0) return hipSuccess;
-    const unsigned blocks = (unsigned)((n + 255) / 256);
-    // 16-byte path: d_h / 2 a multiple of 8 and every row start (and the rotary table) 16-byte aligned
-    const bool vec = dtype == KVX_BF16 && a.d_h % 16 == 0 && a.ld % 8 == 0 &&
-                     ((uintptr_t)a.qkv | (uintptr_t)a.kc | (uintptr_t)a.vc | (uintptr_t)a.rope) % 16 == 0;
-    if (vec) {
+    if (dtype == KVX_BF16) {
+        // 16-byte rows: d_h / 2 a multiple of 8 (d_h is 64 or 128) and 16-byte aligned rows and table
+        // (the C ABI checks the alignment of every pointer)
+        if (a.d_h % 16 != 0 || a.ld % 8 != 0 ||
+            ((uintptr_t)a.qkv | (uintptr_t)a.kc | (uintptr_t)a.vc | (uintptr_t)a.rope) % 16 != 0)
+            return hipErrorInvalidValue;
         const int64_t nv = n / 8;
         hipLaunchKernelGGL(rope_scatter_vec_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s, a);
-    } else if (dtype == KVX_BF16) hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(rope_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
