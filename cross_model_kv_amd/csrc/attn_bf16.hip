@@ -31,6 +31,10 @@
 //    and rescale O and l (the ratio O / l does not depend on the reference used).
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
 //    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
+//  * With fewer blocks than CUs the keys of the long blocks are cut into runs counted back
+//    from the block's last tile: a block short enough for one run is done by its chunk 0,
+//    which writes the final rows; each run of a longer block writes fp32 partial rows that
+//    attn_combine_kernel merges.  Workgroups go chunk-major (every block's chunk 0 first).
 #include <algorithm>
 #include <climits>
 
