@@ -45,14 +45,6 @@ namespace {
 
 constexpr int KT = ATTN_KEY_TILE;
 
-// 16-byte direct global -> LDS load of one wave (lane i fills bytes 16i..16i+15 of the 1 KB
-// block at dst).  Written as asm so that the compiler does not count it among the LDS events
-// (it would then treat the LDS counter as out of order and drain every fragment read with
-// lgkmcnt(0)); the key loop waits for these loads itself before each barrier.
-__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst;
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
-}
 // LDS fragment reads kept in flight ahead of the MFMAs that consume them (measured best)
 constexpr int PF_K = 4;   // K fragments (one per MFMA)
 constexpr int PF_V = 8;   // transposed V reads (two per MFMA)

@@ -71,14 +71,6 @@ struct SplitPlan { int full, rem, split; };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// 16-byte direct global -> LDS load of one wave (lane i fills bytes 16i..16i+15 of the 1 KB
-// block at dst).  Written as asm so that the compiler does not count it among the LDS events:
-// the K loop waits for these loads explicitly (s_waitcnt before each barrier), and the
-// compiler can then wait for the fragment reads with partial lgkmcnt values.
-__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_ptr_t)dst;
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
-}
 
 // Issue order of one stage of the GEMM's K loop (see compute): before group g its look-ahead
 // reads (the next A fragment; during the first substep also FN / FM second-substep B

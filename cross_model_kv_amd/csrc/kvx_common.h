@@ -70,6 +70,17 @@ __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 // ds_read_b128 throughput on gfx950 for this access pattern (Gray code of the row).
 __device__ __forceinline__ int swz(int key) { return (key ^ (key >> 1)) & 7; }
 
+// 16-byte direct global -> LDS load of one wave: lane i fills bytes 16i..16i+15 of the 1 KB
+// block at dst (M0 holds the block's LDS address).  Written as asm so that the compiler does
+// not count it among the LDS events: with such a load in flight it would take the LDS counter
+// as out of order and drain every fragment read with lgkmcnt(0).  Callers wait for these loads
+// themselves (s_waitcnt) before the barrier that publishes the block.  No register outputs, so
+// nothing the compiler allocates can be overwritten while a load is in flight.
+__device__ __forceinline__ void lds_dma16(const bf16* src, bf16* dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+}
+
 }  // namespace kvx
 
 // ----------------------------------------------------------------------------- launchers
