@@ -723,6 +723,45 @@ def _mut_argmax_highest(logits):
     a = np.asarray(logits)
     return a.shape[-1] - 1 - np.argmax(a[..., ::-1], axis=-1)
 
+def _mut_scatter_kv_swapped(K, V, S, k_new, v_new):
+    return SCATTER(K, V, S, v_new, k_new)
+
+
+def _mut_scatter_shifted(K, V, S, k_new, v_new):
+    return SCATTER(K, V, np.minimum(np.asarray(S) + 1, K.shape[0] - 1), k_new, v_new)
+
+
+def _mut_recompute_v_rotated(x_rows, w_qkv, pos, H_q, H_kv, d_h, base):
+    q, k, v = RECOMPUTE(x_rows, w_qkv, pos, H_q, H_kv, d_h, base)
+    return q, k, O.rope(v, np.asarray(pos)[:, None], base)
+
+
+def _mut_recompute_rank_positions(x_rows, w_qkv, pos, H_q, H_kv, d_h, base):
+    return RECOMPUTE(x_rows, w_qkv, np.arange(len(pos)), H_q, H_kv, d_h, base)
+
+
+def _mut_chained_from_input(x0_rows, S, K_tr, V_tr, layers, H_q, H_kv, d_h, base=10000.0, eps=1e-6):
+    out = CHAINED(x0_rows, S, K_tr, V_tr, layers[:1], H_q, H_kv, d_h, base, eps)
+    for l in range(1, len(layers)):
+        o = CHAINED(x0_rows, S, K_tr[l:l + 1], V_tr[l:l + 1], layers[l:l + 1], H_q, H_kv, d_h, base, eps)
+        for key in ("K", "V", "O", "LSE"):
+            out[key] = np.concatenate([out[key], o[key]])
+        out["X"] = np.concatenate([out["X"], o["X"][1:]])
+    return out
+
+
+def _mut_first_token_one_layer(x0_last, p_last, K, V, layers, gamma_final, w_lm, H_q, H_kv, d_h,
+                               base=10000.0, eps=1e-6):
+    logits, tok, K1, V1 = FIRST_TOKEN(x0_last, p_last, K[:1], V[:1], layers[:1], gamma_final, w_lm,
+                                      H_q, H_kv, d_h, base, eps)
+    return logits, tok, np.concatenate([K1, K[1:]]), np.concatenate([V1, V[1:]])
+
+
+SCATTER = O.scatter
+RECOMPUTE = O.recompute_qkv
+CHAINED = O.chained_layers
+FIRST_TOKEN = O.first_token
+
 MUTANTS = {
     "rope_sign": ("rope", _mut_rope_sign),
     "rope_interleaved": ("rope", _mut_rope_interleaved),
@@ -742,6 +781,12 @@ MUTANTS = {
     "layer_no_residual": ("target_layer", _mut_layer_no_residual),
     "lm_head_no_norm": ("lm_head", _mut_lm_head_no_norm),
     "argmax_ties_highest": ("argmax_lowest", _mut_argmax_highest),
+    "scatter_kv_swapped": ("scatter", _mut_scatter_kv_swapped),
+    "scatter_shifted": ("scatter", _mut_scatter_shifted),
+    "recompute_v_rotated": ("recompute_qkv", _mut_recompute_v_rotated),
+    "recompute_rank_positions": ("recompute_qkv", _mut_recompute_rank_positions),
+    "chained_from_input": ("chained_layers", _mut_chained_from_input),
+    "first_token_one_layer": ("first_token", _mut_first_token_one_layer),
 }
 
 
@@ -755,6 +800,6 @@ def test_planted_mistakes(mutant, monkeypatch):
             continue
         try:
             pin()
-        except Exception:
+        except AssertionError:          # a crash is not a catch: the pin must see a wrong value
             caught.append(name)
     assert caught, f"no pin caught the planted mistake {mutant}"
