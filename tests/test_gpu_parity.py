@@ -546,3 +546,39 @@ def test_attention_key_split(name):
             assert_close(ob, o_ref, 2e-2, f"attention ({what})")
             assert np.abs(f64(l[cs[b]:cs[b + 1]]) - lse_ref).max() <= 2e-2, what
     assert rel_norm(f64(o1), f64(o2)) < 1e-2
+
+
+@pytest.mark.parametrize("k", [100, 1311])
+def test_attention_long_request(k):
+    """One 131,072-position request (2048 key tiles for its last query block) with 100 or
+    1311 selected queries: 4 or 41 query blocks, so the keys are cut into the most chunks the
+    split allows (64) or into 8; the merge then walks its chunks in several passes.  Sampled
+    rows (the first, the last and evenly spaced ones) against the oracle; split and unsplit
+    agree to rounding."""
+    T, H_q, H_kv, d_h = 131072, 8, 1, 128
+    say(f"[long request] T={T} k={k}")
+    batch = kvx.Batch([T], [k], DEV)
+    S = synth.random_subset(T - 1, k - 1, 95 + k)
+    S = np.append(S, T - 1).astype(np.int32)        # the last position: the longest walk
+    sel = torch.from_numpy(S).to(DEV)
+    shape = (1, T, H_kv, d_h)
+    cache = kvx.Cache(synth.cache_fill(shape, 96, device=DEV), synth.cache_fill(shape, 97, device=DEV), 1, T)
+    rope = kvx.rope_table(1e6, d_h, T, DEV)
+    qkv = synth.latent(k, (H_q + 2 * H_kv) * d_h, 98, device=DEV)
+    assert kvx.sparse_attention_workspace(kvx.BF16, batch, H_q, H_kv, d_h) > 0, "expected a split"
+    o1 = torch.empty((k, H_q, d_h), dtype=torch.bfloat16, device=DEV)
+    o2 = torch.empty_like(o1)
+    l1 = torch.empty((k, H_q), dtype=torch.float32, device=DEV)
+    l2 = torch.empty_like(l1)
+    kvx.sparse_attention(0, qkv, H_q, H_kv, d_h, rope, batch, sel, cache, o1, l1)
+    kvx.sparse_attention(0, qkv, H_q, H_kv, d_h, rope, batch, sel, cache, o2, l2, split=False)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, k - 1, np.linspace(0, k - 1, 22).astype(int)])
+    q = O.rope(f64(qkv[:, :H_q * d_h]).reshape(k, H_q, d_h)[rows], S[rows][:, None], 1e6)
+    o_ref, lse_ref = O.sparse_causal_attention(q, f64(cache.k[0]), f64(cache.v[0]), S[rows])
+    for o, l, what in ((o1, l1, "split"), (o2, l2, "unsplit")):
+        ob = f64(o)[rows]
+        assert min_row_cosine(ob, o_ref) >= 0.999, what
+        assert_close(ob, o_ref, 2e-2, f"long-request attention ({what})")
+        assert np.abs(f64(l)[rows] - lse_ref).max() <= 2e-2, what
+    assert rel_norm(f64(o1), f64(o2)) < 1e-2
