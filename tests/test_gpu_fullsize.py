@@ -1,6 +1,7 @@
 """Parity at the full workload sizes, in the call sequence bench.py times, on sampled outputs.
 
-For every large workload (0.6B->14B-, 8B->32B-, 8B->70B-shaped and the 16-request paged batch)
+For every large workload (0.6B->14B-, 8B->32B-, 8B->70B-shaped, the 16-request paged batch and a
+131,072-position context with the 8B->32B shapes)
 one whole handoff runs on the GPU, then the fp64 oracle recomputes sampled outputs one by one
 from the generated inputs:
 
@@ -24,9 +25,16 @@ from oracle import kvx_oracle as O
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 DEV = "cuda:0"
-LARGE = ["0.6B-to-14B-shape-T4096", "8B-to-32B-shape-T16384", "8B-to-70B-shape-T8192", "batched-16req-paged16"]
+# a long context: the 8B->32B head shapes, latent and hidden sizes at 131,072 positions, with two
+# source and two target layers so the inputs stay a few GB (select runs past its LDS key copy,
+# the last query blocks walk 2048 key tiles)
+LONG = workloads.ALL["8B-to-32B-shape-T16384"].shrink(name="8B-to-32B-heads-T131072-2-layers", T=131072,
+                                                      L_s=2, L_t=2, pct=2)
+WORKLOADS = dict(workloads.ALL, **{LONG.name: LONG})
+LARGE = ["0.6B-to-14B-shape-T4096", "8B-to-32B-shape-T16384", "8B-to-70B-shape-T8192", "batched-16req-paged16",
+         LONG.name]
 SEEDS = {"0.6B-to-14B-shape-T4096": 2, "8B-to-32B-shape-T16384": 3, "8B-to-70B-shape-T8192": 4,
-         "batched-16req-paged16": 5}
+         "batched-16req-paged16": 5, LONG.name: 6}
 
 
 def say(msg):
@@ -40,7 +48,7 @@ def _rows(t, idx):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", LARGE)
 def test_fullsize_sampled(name):
-    wl = workloads.ALL[name]
+    wl = WORKLOADS[name]
     seed = SEEDS[name]
     say(f"[fullsize] {name} seed {seed}: generating inputs")
     inp = synth.generate(wl, seed, DEV)
