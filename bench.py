@@ -6,15 +6,19 @@ to the latent, score and select the top-30% positions, reconstruct the translate
 the complement, then for each of the 64 target layers project Q/K/V of the selected
 positions, rotate and scatter K/V into the mixed cache (one kernel) and run the sparse causal
 attention.
-All inputs are synthetic (seeded) and resident in HBM before timing.
+All inputs are synthetic (seeded) and resident in HBM before timing.  Each timed step is
+bracketed by HIP events on its launch stream, with a 512 MiB device write before it (outside
+its events) so that it starts with cold caches; the value is T / the median step time.
 
 Prints one JSON line: handoff tokens/s (positions handed off per second), the roofline of
 the dominant kernel (the sparse attention, timed with HIP events on its launch stream
-over the timed steps), per-stage times, the same step captured in a HIP graph and replayed
-(time per step and a bit-for-bit check against the eager outputs), the HBM rate of the standalone
-RoPE + scatter entry point on the same rows (outside the timed steps), the rates this GPU reaches
-on a large library GEMM and a device copy, and the fp64 CPU oracle timed on a bounded sample of
-the same workload.
+over the timed steps), per-stage times, the score GEMM and the top-k apart, the same step
+captured in a HIP graph and replayed (time per step and a bit-for-bit check against the eager
+outputs), the HBM rate of the standalone RoPE + scatter entry point on the same rows (outside
+the timed steps), the rates this GPU reaches on a large library GEMM and a device copy, the
+fp64 CPU oracle timed on a bounded sample of the same workload (extrapolated to one handoff),
+and the same measurement, with fewer steps, of the 0.6B-to-14B-shaped 4K, the 8B-to-70B-shaped
+8K and the batched paged workloads (other_workloads).
 """
 from __future__ import annotations
 
@@ -127,9 +131,11 @@ def cpu_baseline(inp, wl, S, T, k, pos_sum):
             "blas_threads_env": {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")
                                  if os.environ.get(v) is not None}}
     return {"value": T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "host": host,
-            "sample": (f"fp64 numpy oracle on the {wl.name} workload: map 512 rows, reconstruct+score 256 rows "
-                       f"x {wl.L_t} layers, full select, 1 layer of qkv (512 rows), scatter, attention (24 queries); "
-                       "each part scaled to one handoff (rows, layers, sum of causal lengths)"),
+            "extrapolated": True,
+            "sample": (f"extrapolated: fp64 numpy oracle on a sample of the {wl.name} workload (map 512 rows, "
+                       f"reconstruct+score 256 rows x {wl.L_t} layers, full select, 1 layer of qkv (512 rows), "
+                       "scatter, attention of 24 queries of 1 layer), each part scaled linearly to one handoff "
+                       "(rows, layers, sum of causal lengths); the attention part dominates the total"),
             "seconds_per_handoff": total, "parts_s": {k2: round(v2, 4) for k2, v2 in parts.items()}}
 
 
@@ -215,7 +221,7 @@ def chain_cpu_baseline(inp, cw, wl, S, T, k, pos_sum):
     return base
 
 
-def main_chain(args, wl):
+def main_chain(args, wl, flush):
     """The handoff with the selected rows chained through every target layer."""
     from cross_model_kv_amd import kvx, synth
     from cross_model_kv_amd.handoff import ChainedHandoff
@@ -250,27 +256,10 @@ def main_chain(args, wl):
             h.chain_layer(l)
             mark("target_layer")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = {}
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(events)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    times, marks, wall = timed_steps(step, stream, args.steps, args.warmup, flush)
     order = ["map_latent", "score_select", "reconstruct", "gather_rows"] + ["target_layer"] * wl.L_t
-    stage_ms = {n: 0.0 for n in names}
-    launches = {n: 0 for n in names}
-    idx = {n: 0 for n in names}
-    for st in range(args.steps):
-        prev = events["t0"][st]
-        for n in order:
-            e = events[n][idx[n]]
-            idx[n] += 1
-            stage_ms[n] += prev.elapsed_time(e)
-            launches[n] += 1
-            prev = e
+    step_stage_ms, avg_launch_ms = stage_times(marks, order, names, args.steps)
+    med = float(np.median(times))
 
     # the dominant kernel of a chained layer, the gated MLP's gate/up GEMM, timed live on its
     # launch stream with the layer-0 weights and the chain's own rows
@@ -294,10 +283,10 @@ def main_chain(args, wl):
     pos_sum = float(np.sum(S.astype(np.float64) + 1.0))
     parts = chain_layer_work(wl, k, pos_sum)
     layer_flops = sum(f for f, _ in parts.values())
-    layer_ms = stage_ms["target_layer"] / launches["target_layer"]
+    layer_ms = avg_launch_ms["target_layer"]
     hand = stage_work(wl, T, k, pos_sum)
-    stages = {n: {"ms_per_step": round(stage_ms[n] / args.steps, 4),
-                  "ms_per_launch": round(stage_ms[n] / launches[n], 5)} for n in names}
+    stages = {n: {"ms_per_step": round(step_stage_ms[n], 4),
+                  "ms_per_launch": round(avg_launch_ms[n], 5)} for n in names}
     for n in ("map_latent", "score_select", "reconstruct"):
         stages[n]["tflops"] = round(hand[n]["flops"] / (stages[n]["ms_per_launch"] * 1e-3) / 1e12, 2)
     stages["target_layer"]["tflops"] = round(layer_flops / (layer_ms * 1e-3) / 1e12, 2)
@@ -306,8 +295,8 @@ def main_chain(args, wl):
     achieved = sw_flops / (swiglu_ms * 1e-3) / 1e12
     line = {
         "metric": "chained handoff tokens/s (map+select+recompute through every target layer) at 16K",
-        "value": T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True,
+        "value": T / (med * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": med, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name + "-chained", "T": T, "requests": h.batch.n_req, "target_layers": wl.L_t,
                    "H_q": wl.H_q, "H_kv": wl.H_kv, "d_h": wl.d_h, "D": wl.D, "F": wl.F, "selected": k,
@@ -318,7 +307,7 @@ def main_chain(args, wl):
         "stages": stages,
     }
     if wl.vocab > 0:
-        line["ttft"] = time_to_first_token(args, wl, inp, cw, h, elapsed * 1e3 / args.steps)
+        line["ttft"] = time_to_first_token(args, wl, inp, cw, h, med)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         line["cpu_baseline"] = chain_cpu_baseline(inp, cw, wl, S, T, k, pos_sum)
@@ -381,35 +370,54 @@ def time_to_first_token(args, wl, inp, cw, h, handoff_ms):
                     "LM head of the last row; both on this GPU, inputs resident"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8B-to-32B-shape-T16384")
-    ap.add_argument("--seed", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--chain", action="store_true",
-                    help="chain the selected rows through every target layer (norms, output projection, MLP)")
-    args = ap.parse_args()
+FLUSH_BYTES = 512 << 20        # written between timed steps: more than the 256 MB last-level cache
 
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the handoff path here is single-GPU.",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
 
-    from cross_model_kv_amd import kvx, synth, workloads
+def timed_steps(step, stream, steps, warmup, flush):
+    """W untimed warmups, then K steps each bracketed by its own HIP events on the launch stream,
+    with a 512 MiB device write before every timed step (outside its events) so that no step
+    starts with the previous step's operands in the last-level cache or the L2s.  Returns the
+    per-step times (ms), the per-stage event marks and the wall time of the timed loop (s)."""
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    marks = {}
+    ends = []
+    t0 = time.perf_counter()
+    for s in range(steps):
+        flush.fill_(s & 0x7F)
+        step(marks)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ends.append(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = [marks["t0"][s].elapsed_time(ends[s]) for s in range(steps)]
+    return times, marks, wall
+
+
+def stage_times(marks, order, names, steps):
+    """Per-stage ms per step and per launch from the marks (each stage ends where the next begins)."""
+    idx = {n: 0 for n in names}
+    stage_ms = {n: 0.0 for n in names}
+    launches = {n: 0 for n in names}
+    for s in range(steps):
+        prev = marks["t0"][s]
+        for n in order:
+            e = marks[n][idx[n]]
+            idx[n] += 1
+            stage_ms[n] += prev.elapsed_time(e)
+            launches[n] += 1
+            prev = e
+    return ({n: stage_ms[n] / steps for n in names}, {n: stage_ms[n] / launches[n] for n in names})
+
+
+def measure_handoff(wl, args, steps, warmup, flush, dev):
+    """Inputs of workload wl generated and resident, then K timed handoffs.  Returns the Handoff,
+    its inputs and the measurements (median step time, per-stage times and rates)."""
+    from cross_model_kv_amd import kvx, synth
     from cross_model_kv_amd.handoff import Handoff
 
-    wl = workloads.ALL[args.workload]
-    if args.chain:
-        main_chain(args, wl)
-        return
-    dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     inp = synth.generate(wl, args.seed, dev)
     h = Handoff(inp, dev)
@@ -418,9 +426,8 @@ def main():
     T = h.batch.n_tokens           # all positions of the batch (one request: T)
     k = h.batch.total_sel
     qkv = h.ws_attn[: k * wl.n_qkv * 2].view(torch.bfloat16).view(k, wl.n_qkv)
-    ws_qkv = h.ws_attn[(k * wl.n_qkv * 2 + 255) // 256 * 256:]     # the projection's split-tail workspace
+    ws_qkv = h.ws_attn[(k * wl.n_qkv * 2 + 255) // 256 * 256:]     # split-tail / key-split workspace
     stream = torch.cuda.current_stream(dev)
-
     names = ["map_latent", "score_select", "reconstruct", "qkv_rope_scatter", "sparse_attention"]
 
     def step(ev=None):
@@ -444,38 +451,100 @@ def main():
                                  ws_qkv)
             mark("sparse_attention")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = {}
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(events)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-
-    # per-stage GPU times from the events (each stage ends where the next begins)
-    seq = []
+    times, marks, wall = timed_steps(step, stream, steps, warmup, flush)
     order = ["map_latent", "score_select", "reconstruct"] + ["qkv_rope_scatter", "sparse_attention"] * wl.L_t
-    idx = {n: 0 for n in names}
-    starts = events["t0"]
-    stage_ms = {n: 0.0 for n in names}
-    launches = {n: 0 for n in names}
-    for s in range(args.steps):
-        prev = starts[s]
-        for n in order:
-            e = events[n][idx[n]]
-            idx[n] += 1
-            stage_ms[n] += prev.elapsed_time(e)
-            launches[n] += 1
-            prev = e
-    avg_launch_ms = {n: stage_ms[n] / launches[n] for n in names}
-    step_stage_ms = {n: stage_ms[n] / args.steps for n in names}
-
+    step_stage_ms, avg_launch_ms = stage_times(marks, order, names, steps)
+    med = float(np.median(times))
     S = h.S.cpu().numpy()
     pos_sum = float(np.sum(S.astype(np.float64) + 1.0))
     work = stage_work(wl, T, k, pos_sum)
+    stages = {}
+    for n in names:
+        t = avg_launch_ms[n] * 1e-3
+        w = work[n]
+        stages[n] = {"ms_per_step": round(step_stage_ms[n], 4), "ms_per_launch": round(avg_launch_ms[n], 5),
+                     "tflops": round(w["flops"] / t / 1e12, 2) if w["flops"] else None,
+                     "gbs": round(w["bytes"] / t / 1e9, 1)}
+    att_ms = avg_launch_ms["sparse_attention"]
+    achieved = work["sparse_attention"]["flops"] / (att_ms * 1e-3) / 1e12
+    # the handoff at 100% of every stage's roofline (bf16 peak for the matrix-core stages)
+    roof_ms = sum(w["flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3 * (wl.L_t if n in ("qkv_rope_scatter",
+                                                                                 "sparse_attention") else 1)
+                  for n, w in work.items())
+    res = {
+        "value": T / (med * 1e-3), "ms_per_step": med, "T": T, "k": k,
+        "step_ms": {"median": round(med, 4), "mean": round(float(np.mean(times)), 4),
+                    "min": round(float(np.min(times)), 4), "max": round(float(np.max(times)), 4)},
+        "wall_ms_per_step_with_flush": round(wall * 1e3 / steps, 4),
+        "stages": stages,
+        "roofline": {"kernel": "sparse_attention", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "algorithmic_flops_per_launch": work["sparse_attention"]["flops"],
+                     "avg_launch_ms": round(att_ms, 5)},
+        "handoff_at_roofline_ms": round(roof_ms, 3),
+        "frac_of_roofline_time": round(roof_ms / med, 4),
+    }
+    ctx = dict(h=h, inp=inp, step=step, qkv=qkv, ws_qkv=ws_qkv, S=S, pos_sum=pos_sum, work=work, stream=stream)
+    return res, ctx
+
+
+def score_select_split(h, stream, reps=20):
+    """The score GEMM and the top-k kernel apart (outside the timed steps): kvx_select_topk alone
+    on the step's own scores, timed with HIP events; the score GEMM is the rest of kvx_score_select."""
+    from cross_model_kv_amd import kvx
+    sc = h.scores.clone()
+    out = (torch.empty_like(h.sel), torch.empty_like(h.rest))
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(2):
+        h.select()
+        kvx.select_topk(sc, h.batch, out)
+    e0.record(stream)
+    for _ in range(reps):
+        h.select()
+    e1.record(stream)
+    for _ in range(reps):
+        kvx.select_topk(sc, h.batch, out)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    both = e0.elapsed_time(e1) / reps
+    sel = e1.elapsed_time(e2) / reps
+    return both, sel
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="8B-to-32B-shape-T16384")
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the headline workload (no 4K, 70B-shaped and batched lines)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--chain", action="store_true",
+                    help="chain the selected rows through every target layer (norms, output projection, MLP)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the handoff path here is single-GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from cross_model_kv_amd import kvx, workloads
+
+    wl = workloads.ALL[args.workload]
+    dev = torch.device("cuda:0")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    if args.chain:
+        main_chain(args, wl, flush)
+        return
+    res, ctx = measure_handoff(wl, args, args.steps, args.warmup, flush, dev)
+    h, inp, step, qkv, stream = ctx["h"], ctx["inp"], ctx["step"], ctx["qkv"], ctx["stream"]
+    T, k, S, pos_sum, work = res["T"], res["k"], ctx["S"], ctx["pos_sum"], ctx["work"]
 
     # The same step captured once in a HIP graph (no entry point allocates, copies or synchronises)
     # and replayed: its time per step, and whether every replay reproduces the eager outputs bit
@@ -497,15 +566,18 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         same = same and torch.equal(h.out, ref_out) and torch.equal(h.S, ref_sel)
-        ge0 = torch.cuda.Event(enable_timing=True)
-        ge1 = torch.cuda.Event(enable_timing=True)
-        ge0.record(stream)
-        for _ in range(args.steps):
+        gt = []
+        for i in range(args.steps):
+            flush.fill_(i & 0x7F)
+            ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ge0.record(stream)
             g.replay()
-        ge1.record(stream)
+            ge1.record(stream)
+            gt.append((ge0, ge1))
         torch.cuda.synchronize()
         same = same and torch.equal(h.out, ref_out) and torch.equal(h.S, ref_sel)
-        graph = {"ms_per_step": round(ge0.elapsed_time(ge1) / args.steps, 3), "replays_equal_eager": bool(same)}
+        graph = {"ms_per_step": round(float(np.median([a.elapsed_time(b) for a, b in gt])), 3),
+                 "replays_equal_eager": bool(same)}
         del g
     except RuntimeError as e:          # reported, not fatal: the eager line is the measurement
         graph = {"error": str(e)[:200]}
@@ -532,15 +604,21 @@ def main():
                "bound": "hbm", "achieved": round(sc_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                "frac": round(sc_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": sc_bytes,
                "avg_launch_ms": round(sc_ms, 5)}
-    stages = {}
-    for n in names:
-        t = avg_launch_ms[n] * 1e-3
-        w = work[n]
-        stages[n] = {"ms_per_step": round(step_stage_ms[n], 4), "ms_per_launch": round(avg_launch_ms[n], 5),
-                     "tflops": round(w["flops"] / t / 1e12, 2) if w["flops"] else None,
-                     "gbs": round(w["bytes"] / t / 1e9, 1)}
-    att_t = avg_launch_ms["sparse_attention"] * 1e-3
-    achieved = work["sparse_attention"]["flops"] / att_t / 1e12
+
+    # score GEMM and top-k apart: the score is a dense contraction (matrix cores, executed as
+    # 2 T r 2r flops with the hi/lo operator), the top-k a latency-bound pass over T scores
+    both_ms, sel_ms = score_select_split(h, stream)
+    gemm_ms = max(both_ms - sel_ms, 1e-6)
+    r = wl.r
+    score_split = {
+        "score_gemm": {"ms": round(gemm_ms, 5), "bound": "mfma",
+                       "tflops_executed": round(2.0 * T * r * 2 * r / (gemm_ms * 1e-3) / 1e12, 2),
+                       "frac_of_bf16_peak": round(2.0 * T * r * 2 * r / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "gbs": round((2.0 * T * r + 2.0 * r * 2 * r + 4.0 * T * (r // 256)) / (gemm_ms * 1e-3) / 1e9, 1)},
+        "select": {"ms": round(sel_ms, 5), "bound": "latency",
+                   "note": "one workgroup per request; radix passes over the request's keys in LDS"},
+    }
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE) and wl.name == "8B-to-32B-shape-T16384":
         # HBM bytes counted by rocprofv3 (FETCH_SIZE, WRITE_SIZE scaled by a 1 GiB copy); valid only for
@@ -550,17 +628,19 @@ def main():
         with open(ATTN_SOURCE, "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() == rec.get("kernel_source_sha256"):
                 traffic = rec.get("hbm_bytes_per_launch")
+    roofline = dict(res["roofline"])
+    roofline["traffic"] = traffic
     peaks = measured_peaks(stream)
-    peaks["attention_frac_of_gemm"] = round(achieved / peaks["bf16_gemm_tflops"], 4)
+    peaks["attention_frac_of_gemm"] = round(roofline["achieved"] / peaks["bf16_gemm_tflops"], 4)
     peaks["scatter_frac_of_copy"] = round(sc_gbs / peaks["copy_gbs"], 4)
     line = {
         "metric": METRIC,
-        "value": T * args.steps / elapsed,
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -571,11 +651,14 @@ def main():
                    "target_layers": wl.L_t, "H_q": wl.H_q, "H_kv": wl.H_kv, "d_h": wl.d_h, "D": wl.D,
                    "calibration_rank": wl.c, "budget_pct": list(h.inp.pcts) if wl.batched else wl.pct,
                    "selected": k, "cache": "paged" if wl.paged else "contiguous", "parallelism": "none"},
-        "roofline": {"kernel": "sparse_attention", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "algorithmic_flops_per_launch": work["sparse_attention"]["flops"],
-                     "avg_launch_ms": round(avg_launch_ms["sparse_attention"], 5)},
-        "stages": stages,
+        "timing": {"per_step": "HIP events on the launch stream around each step; value = T / median step",
+                   "flush_between_steps_bytes": FLUSH_BYTES, **res["step_ms"],
+                   "wall_ms_per_step_with_flush": res["wall_ms_per_step_with_flush"]},
+        "roofline": roofline,
+        "handoff_at_roofline_ms": res["handoff_at_roofline_ms"],
+        "frac_of_roofline_time": res["frac_of_roofline_time"],
+        "stages": res["stages"],
+        "score_select_split": score_split,
         "scatter_standalone": scatter,
         "graph": graph,
         "measured_peaks": peaks,
@@ -583,6 +666,26 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         line["cpu_baseline"] = cpu_baseline(inp, wl, S, T, k, pos_sum)
+    del h, inp, ctx, qkv, step
+    torch.cuda.empty_cache()
+
+    # the other workloads of the pages' model pairs, each timed the same way (fewer steps)
+    if not args.no_other_workloads:
+        others = {}
+        for name in ("0.6B-to-14B-shape-T4096", "8B-to-70B-shape-T8192", "batched-16req-paged16"):
+            if name == wl.name:
+                continue
+            o_res, o_ctx = measure_handoff(workloads.ALL[name], args, max(3, min(args.steps, 5)),
+                                           max(1, min(args.warmup, 2)), flush, dev)
+            others[name] = {"tokens_per_s": round(o_res["value"], 1), "ms_per_step": round(o_res["ms_per_step"], 4),
+                            "T": o_res["T"], "selected": o_res["k"], "step_ms": o_res["step_ms"],
+                            "roofline": o_res["roofline"], "handoff_at_roofline_ms": o_res["handoff_at_roofline_ms"],
+                            "frac_of_roofline_time": o_res["frac_of_roofline_time"],
+                            "stages": {n: {kk: v for kk, v in st.items() if kk in ("ms_per_step", "tflops")}
+                                       for n, st in o_res["stages"].items()}}
+            del o_ctx
+            torch.cuda.empty_cache()
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
 

@@ -534,7 +534,7 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
 // Blocks of 8 waves (256 rows): floor(256 / g) queries, so a g that does not divide 256 leaves
 // fewer than g rows of the last wave idle (measured faster than g-wave blocks of 32 queries).
 int attn_bf16_split(int n_blocks, int H_kv, int max_T) {
-    constexpr int CUS = 256;
+    const int64_t CUS = device_shape().cus;
     const int64_t items = (int64_t)n_blocks * H_kv;
     if (items <= 0 || items >= CUS) return 1;
     const int max_tiles = (max_T + KT - 1) / KT;

@@ -26,6 +26,7 @@
 //  * Tiles are numbered so that every XCD owns one contiguous range of tiles, walked in
 //    groups of row panels sized so the tiles in flight on an XCD share operand panels in L2.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 
 #include "kvx_common.h"
@@ -57,16 +58,15 @@ __device__ __forceinline__ Tile tile_at(int lin, int mt, int nt, int groups, int
 }
 
 // linear tile index of workgroup bid among `total` tiles: XCD x owns one contiguous range
-__device__ __forceinline__ int xcd_linear(int bid, int total) {
-    const int xcd = bid & 7, j = bid >> 3;
-    const int per = total >> 3, rem = total & 7;
+__device__ __forceinline__ int xcd_linear(int bid, int total, int nx) {
+    const int xcd = bid % nx, j = bid / nx;
+    const int per = total / nx, rem = total % nx;
     return xcd * per + min(xcd, rem) + j;
 }
 
 // Split tail.  When the last round of tiles would leave most CUs idle, the workgroups past
 // the whole rounds each take one K slice of a tail tile and write its fp32 partial tile; a
 // second kernel adds the slices in order and stores the result (deterministic).
-constexpr int CU_COUNT = 256;             // MI355X compute units
 struct SplitPlan { int full, rem, split; };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -87,7 +87,7 @@ __device__ __forceinline__ void group_order() {
 
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
-void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
+void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xcd) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -108,7 +108,7 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp) {
     const bool tail = bid >= sp.full;                 // a K slice of a tail tile
     const int unit = bid - sp.full;
     const Tile t = tail ? tile_at(sp.full + unit / sp.split, mt, nt, a.groups, gm)
-                        : tile_at(xcd_linear(bid, sp.full), mt, nt, a.groups, gm);
+                        : tile_at(xcd_linear(bid, sp.full, n_xcd), mt, nt, a.groups, gm);
     const int k_first = tail ? (unit % sp.split) * (nk_all / sp.split) : 0;
     const int nk = tail ? nk_all / sp.split : nk_all;
     const int m0 = t.tm * BM, n0 = t.tn * BN;
@@ -476,13 +476,14 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemmArgs a, int mt, int 
     }
 }
 
-// GEMV plan: all tiles are split units; K slices so that about 1024 workgroups stream the
-// weight (each slice a whole number of 64-wide k steps, at least 4 of them)
+// GEMV plan: all tiles are split units; K slices so that about four workgroups per CU stream
+// the weight (each slice a whole number of 64-wide k steps, at least 4 of them)
 static SplitPlan plan_gemv(int N, int K) {
     const int tiles = cdiv(N, 256);
     const int nk = K / BK;
+    const int64_t target = 4 * (int64_t)device_shape().cus;
     int split = 1;
-    while (split < 16 && (int64_t)tiles * 8 * split < 1024 && nk % (split * 2) == 0 && nk / (split * 2) >= 4) split *= 2;
+    while (split < 16 && (int64_t)tiles * 8 * split < target && nk % (split * 2) == 0 && nk / (split * 2) >= 4) split *= 2;
     return SplitPlan{0, tiles, split};
 }
 
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
     }
 }
 
-// K splits of a plain store (one group).  Time is counted in tile-times on CU_COUNT CUs:
+// K splits of a plain store (one group).  Time is counted in tile-times on the device's CUs:
 //   whole tiles:            ceil(tiles / CUs)
 //   split tail (split s):   floor(tiles / CUs) + ceil(rem * s / CUs) / s, rem = tiles % CUs
 //   every tile split (s):   ceil(tiles * s / CUs) / s
@@ -597,7 +598,7 @@ SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
         tiles > INT32_MAX / 8)
         return best;
     const int nk = K / BK;
-    const int64_t cu = CU_COUNT;
+    const int64_t cu = device_shape().cus;
     double best_t = (double)((tiles + cu - 1) / cu);
     int64_t best_parts = 0;
     auto consider = [&](int full, int rem, int split) {
@@ -621,6 +622,35 @@ SplitPlan plan_split(int M, int N, int K, int groups, int epi) {
 
 }  // namespace
 
+// Compute units and XCDs of the current device, queried once per device.  Without a usable
+// device (workspace sizing on a host that has none) the planners assume a whole MI355X: 256
+// CUs in 8 XCDs.  A failed query's error is cleared so that it does not surface at the next
+// launch check.
+DeviceShape device_shape() {
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV];     // (cus << 8) | xcds, 0 = not queried yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) {
+        (void)hipGetLastError();
+        return DeviceShape{256, 8};
+    }
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, xcds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds <= 0) {
+            (void)hipGetLastError();
+            xcds = 1;
+        }
+        v = (cus << 8) | std::min(xcds, 255);
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return DeviceShape{v >> 8, v & 255};
+}
+
 // Score partial sums are written per 256-column block of the output.
 int gemm_bf16_block_n() { return 256; }
 
@@ -632,14 +662,14 @@ size_t gemm_bf16_split_bytes(int M, int N, int K, int groups, int epi) {
 }
 
 // Row-panel group size of the tile order: the one that fetches the fewest operand panel bytes
-// per window of 32 concurrent tiles (an XCD's share of one round).
-static int pick_group_rows(int mt, int cols, double a_panel, double b_panel) {
+// per window of w concurrent tiles (an XCD's share of one round: its CUs).
+static int pick_group_rows(int mt, int cols, double a_panel, double b_panel, int w) {
     int best = 1;
     double best_bytes = 0.0;
-    for (int gm = 1; gm <= 32; gm *= 2) {
+    for (int gm = 1; gm <= w; gm *= 2) {
         const int rows_w = std::min(gm, mt);
-        const int cols_w = std::min(cols, std::max(1, 32 / rows_w));
-        const int rows_eff = std::min(mt, std::max(rows_w, 32 / cols_w));
+        const int cols_w = std::min(cols, std::max(1, w / rows_w));
+        const int rows_eff = std::min(mt, std::max(rows_w, w / cols_w));
         const double bytes = rows_eff * a_panel + cols_w * b_panel;
         if (gm == 1 || bytes < best_bytes) { best = gm; best_bytes = bytes; }
     }
@@ -653,7 +683,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     // A row operand shared by several groups (the per-layer reconstruction) is small next to the
     // groups' weights: walking all row panels first streams each weight panel through an XCD
     // once while the row operand stays resident in the last-level cache (measured fastest).
-    const int gm = a.groups > 1 ? mt : pick_group_rows(mt, nt * a.groups, 256.0 * a.K_a, 256.0 * a.K);
+    const DeviceShape dv = device_shape();
+    const int gm = a.groups > 1 ? mt
+                                : pick_group_rows(mt, nt * a.groups, 256.0 * a.K_a, 256.0 * a.K,
+                                                  std::max(1, dv.cus / dv.xcds));
     if (a.split_ws && gemv_eligible(a)) {           // few rows: stream the weight, reduce with the epilogue
         const SplitPlan sp = plan_gemv(a.N, a.K);
         const dim3 grid((unsigned)(sp.rem * 8 * sp.split));
@@ -669,7 +702,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     SplitPlan sp = plan_split(a.M, a.N, a.K, a.groups, a.epi);
     if (sp.rem && !a.split_ws) sp = SplitPlan{sp.full + sp.rem, 0, 1};   // no workspace: whole tiles
     const int64_t grid = (int64_t)sp.full + (int64_t)sp.rem * sp.split;
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)grid), dim3(512), 0, s, a, mt, nt, gm, sp);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)grid), dim3(512), 0, s, a, mt, nt, gm, sp,
+                       dv.xcds);
     if (sp.rem) {
         if (hipError_t e = hipGetLastError()) return e;
         hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3(65536 / (256 * 8), sp.rem), dim3(256), 0, s, a, mt, nt, gm, sp);

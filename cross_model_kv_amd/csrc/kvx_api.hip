@@ -54,12 +54,12 @@ size_t qkv_split_bytes(int32_t dtype, int64_t n_sel, int32_t D, int n_qkv) {
 }
 
 
+// KVX_DEBUG set to anything but "" or "0": every call first copies the device-side index data
+// it is about to trust (batch prefix arrays, position lists, page tables) to the host and checks
+// it.  Read on every call, so a process can switch it on and off.
 bool debug_checks() {
-    static const int on = [] {
-        const char* v = getenv("KVX_DEBUG");
-        return (v && v[0] && v[0] != '0') ? 1 : 0;
-    }();
-    return on != 0;
+    const char* v = getenv("KVX_DEBUG");
+    return v && v[0] && v[0] != '0';
 }
 
 #define KVX_REQUIRE(cond, ...)                                         \
@@ -102,6 +102,7 @@ kvx_status check_batch(const kvx_batch* bt, BatchInfo* out) {
         if (T > max_T) max_T = T;
     }
     if (debug_checks()) {
+        KVX_TRY_HIP(hipDeviceSynchronize(), "debug synchronisation");
         std::vector<int32_t> t(bt->n_req + 1), s(bt->n_req + 1);
         KVX_TRY_HIP(hipMemcpy(t.data(), bt->cu_tokens_d, t.size() * 4, hipMemcpyDeviceToHost), "debug copy");
         KVX_TRY_HIP(hipMemcpy(s.data(), bt->cu_sel_d, s.size() * 4, hipMemcpyDeviceToHost), "debug copy");
@@ -141,6 +142,7 @@ kvx_status check_cache(const kvx_cache* c, const BatchInfo& bi, int32_t dtype, i
 
 kvx_status check_page_table_debug(const kvx_cache* c, const kvx_batch* bt) {
     if (!debug_checks() || c->layout != KVX_PAGED) return KVX_OK;
+    KVX_TRY_HIP(hipDeviceSynchronize(), "debug synchronisation");
     std::vector<int32_t> pt((size_t)bt->n_req * c->max_pages);
     KVX_TRY_HIP(hipMemcpy(pt.data(), c->page_table, pt.size() * 4, hipMemcpyDeviceToHost), "debug copy");
     const int64_t n_pages = c->n_slots / c->page_size;
@@ -154,6 +156,35 @@ kvx_status check_page_table_debug(const kvx_cache* c, const kvx_batch* bt) {
                         (long long)n_pages);
             KVX_REQUIRE(!used[p], "page %d is mapped twice", p);
             used[p] = 1;
+        }
+    }
+    return KVX_OK;
+}
+
+// KVX_DEBUG: a per-request position list (selected positions, or with `rest` the complement
+// lists, which start at cu_tokens[b] - cu_sel[b]) must be strictly ascending within each request
+// and inside [0, T_b): the kernels index the rotary table, the cache slots and the query blocks'
+// key ranges with these values without checking them.
+kvx_status check_positions_debug(const int32_t* list, const kvx_batch* bt, bool rest, const char* name) {
+    if (!debug_checks() || !list) return KVX_OK;
+    const int n_req = bt->n_req;
+    const int64_t count = rest ? (int64_t)bt->cu_tokens_h[n_req] - bt->cu_sel_h[n_req] : bt->cu_sel_h[n_req];
+    if (count <= 0) return KVX_OK;
+    KVX_TRY_HIP(hipDeviceSynchronize(), "debug synchronisation");
+    std::vector<int32_t> h((size_t)count);
+    KVX_TRY_HIP(hipMemcpy(h.data(), list, h.size() * 4, hipMemcpyDeviceToHost), "debug copy");
+    for (int b = 0; b < n_req; ++b) {
+        const int T = bt->cu_tokens_h[b + 1] - bt->cu_tokens_h[b];
+        const int k = bt->cu_sel_h[b + 1] - bt->cu_sel_h[b];
+        const int64_t start = rest ? (int64_t)bt->cu_tokens_h[b] - bt->cu_sel_h[b] : bt->cu_sel_h[b];
+        const int n = rest ? T - k : k;
+        for (int i = 0; i < n; ++i) {
+            const int32_t v = h[(size_t)(start + i)];
+            KVX_REQUIRE(v >= 0 && v < T, "%s[%lld] = %d (request %d) is outside [0, %d)", name,
+                        (long long)(start + i), v, b, T);
+            KVX_REQUIRE(i == 0 || v > h[(size_t)(start + i - 1)],
+                        "%s of request %d is not strictly ascending at entry %lld (%d after %d)", name, b,
+                        (long long)(start + i), v, h[(size_t)(start + i - 1)]);
         }
     }
     return KVX_OK;
@@ -392,6 +423,7 @@ kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const voi
     if (kvx_status st = check_cache(cache, bi, dtype, H_kv, d_h, L_t)) return st;
     if (kvx_status st = check_page_table_debug(cache, batch)) return st;
     if (rows) KVX_REQUIRE(aligned16(rows), "rows must be 16-byte aligned");
+    if (kvx_status st = check_positions_debug(rows, batch, true, "rows")) return st;
     const int64_t M = rows ? bi.n_rest : bi.n_tokens;
     if (M == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -708,6 +740,7 @@ kvx_status kvx_qkv_project(void* stream, int32_t dtype, const void* x_l, const v
     if (bi.n_sel == 0) return ok();
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
     KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
     KVX_REQUIRE_PTR(qkv, "qkv");
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     const size_t need = qkv_split_bytes(dtype, bi.n_sel, D, n_qkv);
@@ -727,6 +760,7 @@ kvx_status kvx_rope_scatter(void* stream, int32_t dtype, int32_t layer, const vo
     if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
     if (bi.n_sel == 0) return ok();
     KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
     KVX_REQUIRE_PTR(qkv, "qkv");
     return hip_status(run_scatter((hipStream_t)stream, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel,
                                   cache), "rope_scatter");
@@ -747,6 +781,7 @@ kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t layer, cons
     if (bi.n_sel == 0) return ok();
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
     KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
     KVX_REQUIRE_PTR(qkv, "qkv");
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     const size_t need = qkv_split_bytes(dtype, bi.n_sel, D, n_qkv);
@@ -770,6 +805,7 @@ kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, cons
     if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
     if (bi.n_sel == 0) return ok();
     KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
     KVX_REQUIRE_PTR(qkv, "qkv");
     KVX_REQUIRE_PTR(out, "out");
     if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
@@ -804,6 +840,7 @@ kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const 
     if (bi.n_sel == 0) return ok();
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
     KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
     KVX_REQUIRE_PTR(out, "out");
     if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
     if (!ws || ws_bytes < need)
@@ -830,6 +867,7 @@ kvx_status kvx_gather_rows(void* stream, int32_t dtype, const void* src, int32_t
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
     KVX_REQUIRE_PTR(src, "src");
     KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
     KVX_REQUIRE_PTR(dst, "dst");
     return hip_status(launch_gather_rows_bf16((const bf16*)src, D, sel, batch->cu_tokens_d, batch->cu_sel_d, bi.n_req,
                                               bi.n_sel, (bf16*)dst, (hipStream_t)stream),
@@ -940,6 +978,7 @@ kvx_status kvx_target_layer(void* stream, int32_t dtype, int32_t layer, void* x,
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
     KVX_REQUIRE_PTR(x, "x");
     KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
     if (attn_out) KVX_REQUIRE(aligned16(attn_out), "attn_out must be 16-byte aligned");
     if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
     const int64_t k = bi.n_sel;

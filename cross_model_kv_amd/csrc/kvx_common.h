@@ -152,6 +152,10 @@ struct GemmArgs {
 __device__ __forceinline__ float rope_lo(float x1, float x2, float c, float s) { return __builtin_fmaf(x1, c, -(x2 * s)); }
 __device__ __forceinline__ float rope_hi(float x1, float x2, float c, float s) { return __builtin_fmaf(x2, c, x1 * s); }
 
+// Compute units and XCDs of the current device (host side; planners size their work to them)
+struct DeviceShape { int cus, xcds; };
+DeviceShape device_shape();
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 int gemm_bf16_block_n();
 // Workspace bytes the bf16 GEMM needs to split its last, partly filled round of tiles along K

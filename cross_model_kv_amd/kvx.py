@@ -248,10 +248,13 @@ def score_prepare(w_l: torch.Tensor, u: torch.Tensor) -> torch.Tensor:
     return op
 
 
-def select_topk(scores: torch.Tensor, batch: Batch):
+def select_topk(scores: torch.Tensor, batch: Batch, out=None):
     dev = scores.device
-    sel = torch.empty(max(batch.total_sel, 1), dtype=torch.int32, device=dev)
-    rest = torch.empty(max(batch.total_rest, 1), dtype=torch.int32, device=dev)
+    if out is None:
+        sel = torch.empty(max(batch.total_sel, 1), dtype=torch.int32, device=dev)
+        rest = torch.empty(max(batch.total_rest, 1), dtype=torch.int32, device=dev)
+    else:
+        sel, rest = out
     _check("kvx_select_topk", lib().kvx_select_topk(_stream(dev), _ptr(scores), ctypes.byref(batch.c),
                                                     _ptr(sel), _ptr(rest)))
     return sel[:batch.total_sel], rest[:batch.total_rest]

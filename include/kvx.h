@@ -31,6 +31,14 @@
  *    index fastest.
  *  - Weights are stored output-major: row j holds the weights that produce output j
  *    (y = W x is computed as y_j = sum_c W[j][c] x[c]).
+ *  - Device index data is trusted by the kernels, not checked: a position list (`sel`, or
+ *    the complement list `rows`) must be strictly ascending within each request with every
+ *    entry in [0, T_b); a paged cache's table must map the pages a request uses to distinct
+ *    pages inside the pool; the device prefix arrays must equal the host ones.  Violations
+ *    give wrong results or out-of-bounds accesses.  With the environment variable KVX_DEBUG
+ *    set (to anything but "" or "0"; read on every call), each call first synchronises the
+ *    device, copies these arrays to the host and checks them; a violation returns
+ *    KVX_ERR_INVALID with nothing enqueued.
  *
  * Shapes (one request of T positions, or a ragged batch of n_req requests flattened
  * into N = sum T_b rows; positions restart at 0 in every request)
@@ -165,7 +173,9 @@ KVX_API kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, 
  *                                 V_l[slot(b,p)] = y[H_kv d_h : 2 H_kv d_h].
  *   rows (device) NULL = every position; else the complement list from
  *   kvx_score_select (positions about to be recomputed are skipped: kvx_recompute_attn
- *   overwrites them).  w_l (device) [L_t][d_t][r].  bf16 needs r % 64 == 0.
+ *   overwrites them): [N - cu_sel[n_req]], request b's T_b - k_b entries starting at
+ *   cu_tokens[b] - cu_sel[b], strictly ascending, each in [0, T_b).
+ *   w_l (device) [L_t][d_t][r].  bf16 needs r % 64 == 0.
  *   cache->n_layers must be >= L_t.  No workspace. */
 KVX_API kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const void* w_l,
                            int32_t L_t, int32_t r, int32_t H_kv, int32_t d_h,
@@ -187,7 +197,9 @@ KVX_API kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_
  *      h / (H_q / H_kv) of request b's cache;  lse[i][h] = natural log-sum-exp of the
  *      scaled logits.
  *   x_l (device) [N][D]; w_qkv (device) [n_qkv][D]; rope (device) from kvx_rope_table
- *   with max_pos > every T_b; sel (device) [cu_sel[n_req]]; out (device, out)
+ *   with max_pos >= every T_b; sel (device) [cu_sel[n_req]]: request b's k_b positions
+ *   start at cu_sel[b], strictly ascending, each in [0, T_b) (the attention takes a query
+ *   block's key range from its last entry); out (device, out)
  *   [cu_sel[n_req]][H_q][d_h]; lse (device, out, nullable) [cu_sel[n_req]][H_q] fp32.
  *   d_h must be 64 or 128, H_q % H_kv == 0, H_q / H_kv <= 16; bf16 needs D % 64 == 0.
  *   ws (device) of kvx_recompute_attn_workspace() bytes (the qkv rows, then one region
@@ -205,6 +217,9 @@ KVX_API kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer
  * individually.  kvx_recompute_attn is kvx_qkv_rope_scatter followed by kvx_sparse_attention;
  * kvx_qkv_project followed by kvx_rope_scatter gives the same cache and q rows (and also the
  * unrotated k and v columns of qkv).
+ *
+ * Every step takes `sel` as kvx_recompute_attn does (strictly ascending per request, entries
+ * in [0, T_b)).
  *
  * kvx_qkv_project: step 1, qkv (device, out) [cu_sel[n_req]][n_qkv] in the storage dtype,
  *   row i = W_qkv x_l[cu_tokens[b] + sel[i]] (not rotated).  bf16 needs D % 64 == 0.
@@ -286,7 +301,7 @@ typedef struct kvx_layer_weights {
 
 /* dst[i] = src[cu_tokens[b] + sel[i]] for every selected row i (request b owning row i):
  * the compact input rows of the chain.  src (device) [N][D], dst (device, out)
- * [cu_sel[n_req]][D]; D % 8 == 0. */
+ * [cu_sel[n_req]][D]; D % 8 == 0; sel as in kvx_recompute_attn. */
 KVX_API kvx_status kvx_gather_rows(void* stream, int32_t dtype, const void* src, int32_t D,
                                    const kvx_batch* batch, const int32_t* sel, void* dst);
 

@@ -63,3 +63,23 @@ def band_check(S_gpu, s_ora: np.ndarray, k: int, eps: float):
     a, b = set(int(x) for x in S_gpu), set(S_ora.tolist())
     assert a - band == b - band, f"selection differs outside the band: {sorted((a ^ b) - band)[:10]}"
     return len(band), len(a ^ b), O.score_gap(s_ora, k)
+
+
+def oracle_downstream(K_tr: np.ndarray, V_tr: np.ndarray, x_l: np.ndarray, w_qkv: np.ndarray, S: np.ndarray,
+                      H_q: int, H_kv: int, d_h: int, base: float):
+    """The oracle's recompute, scatter and attention steps on a given selected set S (the GPU's
+    own set, so that both sides attend with the same queries).  K_tr, V_tr [L_t, T, H_kv, d_h]
+    is the oracle's translated cache, x_l [L_t, T, D].  Returns the mixed cache K, V and the
+    outputs O [L_t, k, H_q, d_h], LSE [L_t, k, H_q]."""
+    from oracle import kvx_oracle as O
+    S = np.asarray(S, dtype=np.int64)
+    L = K_tr.shape[0]
+    K, V = K_tr.copy(), V_tr.copy()
+    out = np.zeros((L, len(S), H_q, d_h))
+    lse = np.zeros((L, len(S), H_q))
+    for l in range(L):
+        q, kk, vv = O.recompute_qkv(x_l[l][S], w_qkv[l], S, H_q, H_kv, d_h, base)
+        K[l], V[l] = O.scatter(K[l], V[l], S, kk, vv)
+        if len(S):
+            out[l], lse[l] = O.sparse_causal_attention(q, K[l], V[l], S)
+    return K, V, out, lse

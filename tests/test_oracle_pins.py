@@ -607,6 +607,22 @@ def pin_first_token_full_budget_is_last_dense_row():
     assert np.abs(K - full["K"]).max() < 1e-12 and np.abs(V - full["V"]).max() < 1e-12
 
 
+def pin_score_gap_hand():
+    # scores 5, 3, 3, 1 (shuffled): the gap after the k-th largest, relative to it, worked by hand
+    s = np.array([3.0, 1.0, 5.0, 3.0])
+    assert O.score_gap(s, 1) == pytest.approx(2.0 / 5.0, abs=1e-15)   # 5 vs 3
+    assert O.score_gap(s, 2) == 0.0                                   # 3 vs 3: a tie at the boundary
+    assert O.score_gap(s, 3) == pytest.approx(2.0 / 3.0, abs=1e-15)   # 3 vs 1
+    assert O.score_gap(s, 0) == math.inf and O.score_gap(s, 4) == math.inf
+    # a negative k-th score divides by its magnitude; a zero one leaves the plain difference
+    assert O.score_gap(np.array([-4.0, -3.0]), 1) == pytest.approx(1.0 / 3.0, abs=1e-15)   # -3 vs -4
+    assert O.score_gap(np.array([0.0, -0.25]), 1) == 0.25
+    # the gap does not depend on the order of the positions
+    rng = _rng(77)
+    t = rng.standard_normal(50)
+    assert O.score_gap(t, 17) == O.score_gap(t[rng.permutation(50)], 17)
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 
@@ -757,6 +773,14 @@ def _mut_first_token_one_layer(x0_last, p_last, K, V, layers, gamma_final, w_lm,
     return logits, tok, np.concatenate([K1, K[1:]]), np.concatenate([V1, V[1:]])
 
 
+def _mut_score_gap_wrong_neighbour(s, k):
+    T = s.shape[0]
+    if k == 0 or k == T:
+        return math.inf
+    srt = np.sort(s)[::-1]
+    return float((srt[k - 2] - srt[k - 1]) / abs(srt[k - 1])) if k >= 2 else float(srt[0] - srt[1]) / abs(srt[0])
+
+
 SCATTER = O.scatter
 RECOMPUTE = O.recompute_qkv
 CHAINED = O.chained_layers
@@ -787,6 +811,7 @@ MUTANTS = {
     "recompute_rank_positions": ("recompute_qkv", _mut_recompute_rank_positions),
     "chained_from_input": ("chained_layers", _mut_chained_from_input),
     "first_token_one_layer": ("first_token", _mut_first_token_one_layer),
+    "score_gap_wrong_neighbour": ("score_gap", _mut_score_gap_wrong_neighbour),
 }
 
 
