@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -351,11 +352,16 @@ kvx_status kvx_score_select_workspace(int32_t dtype, int32_t r, int64_t n, size_
     return ok();
 }
 
-kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, const void* op, int32_t r,
-                            const kvx_batch* batch, const int32_t* budget_pct, float* scores,
-                            int32_t* sel, int32_t* rest, void* ws, size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of kvx_score_select other than its workspace.
+kvx_status check_score_select(int32_t dtype, const void* z, const void* op, int32_t r, const kvx_batch* batch,
+                              const int32_t* budget_pct, const float* scores, const int32_t* sel,
+                              const int32_t* rest, BatchInfo* bi_out) {
     if (kvx_status st = check_dtype(dtype)) return st;
-    BatchInfo bi;
+    BatchInfo& bi = *bi_out;
     if (kvx_status st = check_batch(batch, &bi)) return st;
     KVX_REQUIRE_PTR(z, "z");
     KVX_REQUIRE_PTR(op, "op");
@@ -373,14 +379,16 @@ kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, const vo
         KVX_REQUIRE(k == budget_of(T, budget_pct[b]), "request %d: cu_sel gives %d positions but the "
                     "budget of %d%% of %d is %d", b, k, budget_pct[b], T, budget_of(T, budget_pct[b]));
     }
-    size_t need = 0;
-    kvx_score_select_workspace(dtype, r, bi.n_tokens, &need);
-    if (!ws || ws_bytes < need)
-        return fail(KVX_ERR_WORKSPACE, "score_select needs %zu workspace bytes (got %zu)", need, ws_bytes);
-    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
     KVX_REQUIRE(bi.n_tokens <= INT32_MAX, "too many rows");
+    return KVX_OK;
+}
+
+// Score GEMM (bf16: per-256-column-block partial sums of z^T A z in ws; fp32: P = z A and the
+// row dots in ws) and the top-k.  Every byte of ws that is read was written by this call.
+kvx_status run_score_select(hipStream_t s, int32_t dtype, const void* z, const void* op, int32_t r,
+                            const kvx_batch* batch, const BatchInfo& bi, float* scores, int32_t* sel, int32_t* rest,
+                            void* ws) {
     if (bi.n_tokens == 0) return ok();
-    hipStream_t s = (hipStream_t)stream;
     if (dtype == KVX_BF16) {
         GemmArgs a{};
         a.A = (const bf16*)z; a.lda = r; a.K_a = r;
@@ -407,6 +415,66 @@ kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, const vo
     return hip_status(launch_select(partial, 1, bi.n_tokens, scores, batch->cu_tokens_d, batch->cu_sel_d,
                                     bi.n_req, sel, rest, s),
                       "select");
+}
+
+// Scratch of kvx_score_select_noalloc: one array per device, in the code object (so it exists
+// from the library's load on that device until the process ends).  Host code never uses the
+// array's name as an address: its device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)KVX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+kvx_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    KVX_TRY_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return fail(KVX_ERR_UNSUPPORTED, "device %d: the no-allocation scratch covers devices 0..%d", dev,
+                    NOALLOC_MAX_DEVICES - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        KVX_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(KVX_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, const void* op, int32_t r,
+                            const kvx_batch* batch, const int32_t* budget_pct, float* scores,
+                            int32_t* sel, int32_t* rest, void* ws, size_t ws_bytes) {
+    BatchInfo bi;
+    if (kvx_status st = check_score_select(dtype, z, op, r, batch, budget_pct, scores, sel, rest, &bi)) return st;
+    size_t need = 0;
+    kvx_score_select_workspace(dtype, r, bi.n_tokens, &need);
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "score_select needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    return run_score_select((hipStream_t)stream, dtype, z, op, r, batch, bi, scores, sel, rest, ws);
+}
+
+kvx_status kvx_score_select_noalloc(void* stream, int32_t dtype, const void* z, const void* op, int32_t r,
+                                    const kvx_batch* batch, const int32_t* budget_pct, float* scores,
+                                    int32_t* sel, int32_t* rest) {
+    BatchInfo bi;
+    if (kvx_status st = check_score_select(dtype, z, op, r, batch, budget_pct, scores, sel, rest, &bi)) return st;
+    size_t need = 0;
+    kvx_score_select_workspace(dtype, r, bi.n_tokens, &need);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(KVX_ERR_WORKSPACE, "score_select_noalloc: this batch needs %zu scratch bytes, more than the "
+                    "%zu the library holds (use kvx_score_select with a workspace)", need, NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (kvx_status st = scratch_of_current_device(&ws)) return st;
+    return run_score_select((hipStream_t)stream, dtype, z, op, r, batch, bi, scores, sel, rest, ws);
 }
 
 kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t L_t,

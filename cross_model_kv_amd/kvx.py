@@ -63,6 +63,8 @@ _SIGS = {
     "kvx_score_select_workspace": ([_I32, _I32, _I64, ctypes.POINTER(_SZ)], _I32),
     "kvx_score_select": ([_P, _I32, _P, _P, _I32, ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P, _P,
                           _P, _P, _SZ], _I32),
+    "kvx_score_select_noalloc": ([_P, _I32, _P, _P, _I32, ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P, _P,
+                                  _P], _I32),
     "kvx_reconstruct": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P,
                          ctypes.POINTER(_Cache)], _I32),
     "kvx_rope_table": ([_P, ctypes.c_double, _I32, _I32, _P], _I32),
@@ -284,6 +286,24 @@ def score_select(z: torch.Tensor, op: torch.Tensor, batch: Batch, pcts: Sequence
     _check("kvx_score_select", lib().kvx_score_select(_stream(dev), dt, _ptr(z), _ptr(op), r,
                                                       ctypes.byref(batch.c), pct, _ptr(scores), _ptr(sel),
                                                       _ptr(rest), _ptr(ws), need))
+    return scores, sel[:batch.total_sel], rest[:batch.total_rest]
+
+
+def score_select_noalloc(z: torch.Tensor, op: torch.Tensor, batch: Batch, pcts: Sequence[int], out=None):
+    """kvx_score_select with the library's fixed scratch instead of a workspace (no allocation
+    in the library; out = (scores, sel, rest) avoids the allocations here as well)."""
+    dev = z.device
+    r = z.shape[1]
+    if out is None:
+        scores = torch.empty(batch.n_tokens, dtype=torch.float32, device=dev)
+        sel = torch.empty(max(batch.total_sel, 1), dtype=torch.int32, device=dev)
+        rest = torch.empty(max(batch.total_rest, 1), dtype=torch.int32, device=dev)
+    else:
+        scores, sel, rest = out
+    pct = (ctypes.c_int32 * batch.n_req)(*[int(p) for p in pcts])
+    _check("kvx_score_select_noalloc", lib().kvx_score_select_noalloc(_stream(dev), _dtype(z), _ptr(z), _ptr(op), r,
+                                                                      ctypes.byref(batch.c), pct, _ptr(scores),
+                                                                      _ptr(sel), _ptr(rest)))
     return scores, sel[:batch.total_sel], rest[:batch.total_rest]
 
 

@@ -167,6 +167,22 @@ KVX_API kvx_status kvx_score_select(void* stream, int32_t dtype, const void* z, 
                             float* scores, int32_t* sel, int32_t* rest, void* ws,
                             size_t ws_bytes);
 
+/* kvx_score_select without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as kvx_score_select; its scratch (what
+ * kvx_score_select_workspace would return for this call) comes from a fixed array of
+ * KVX_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on until the
+ * process ends.  A call needing more returns KVX_ERR_WORKSPACE with nothing enqueued (bf16:
+ * 4 * N * ceil(r / 256) bytes, e.g. N up to 1M positions at r = 1024; fp32: about 4 * N * (r + 1)).
+ * The first call on a device looks up that device's array (with the device current), and it
+ * allocates nothing.  All calls on one device share its array, and the scratch of a call is
+ * fully written before it is read, so nothing carries over between calls, but calls that
+ * overlap in time on one device (concurrent streams, or threads) race on it: serialise them. */
+#define KVX_NOALLOC_SCRATCH_BYTES (16u << 20)
+KVX_API kvx_status kvx_score_select_noalloc(void* stream, int32_t dtype, const void* z, const void* op,
+                                            int32_t r, const kvx_batch* batch, const int32_t* budget_pct,
+                                            float* scores, int32_t* sel, int32_t* rest);
+
 /* Layer-specific target reconstruction (PANORAMA abstract) into the translated cache:
  * for every layer l and listed position p of request b,
  *   y = W_l z[cu_tokens[b] + p];  K_l[slot(b,p)] = y[0 : H_kv d_h],

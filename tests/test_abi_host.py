@@ -123,6 +123,22 @@ def test_score_select_validation():
     status(L.kvx_score_select(*args(pct, wsb=need.value - 1)), WORKSPACE)
 
 
+def test_score_select_noalloc_validation():
+    """The no-allocation variant validates like kvx_score_select and refuses, before touching
+    the device, a batch whose scratch exceeds the fixed array it uses."""
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    pct = (ctypes.c_int32 * 2)(30, 30)
+    args = lambda p, r=128, b=bt: (None, 1, A16, A16, r, ctypes.byref(b.c), p, A16, A16, A16)
+    status(L.kvx_score_select_noalloc(*args(pct, r=96)), INVALID, "r % 64")
+    status(L.kvx_score_select_noalloc(*args(None)), INVALID, "budget_pct")
+    status(L.kvx_score_select_noalloc(*args((ctypes.c_int32 * 2)(30, 40))), INVALID, "budget")
+    # bf16 scratch is 4 * N * ceil(r / 256) bytes: r = 1024 and N = 2^20 + 64 is over 16 MiB
+    big_T = (1 << 20) + 64
+    big = FakeBatch([big_T], [kvx.budget(big_T, 30)])
+    status(L.kvx_score_select_noalloc(*args((ctypes.c_int32 * 1)(30), r=1024, b=big)), WORKSPACE, "scratch")
+
+
 def test_reconstruct_validation():
     L = kvx.lib()
     bt = FakeBatch([100, 50], [30, 15])
