@@ -25,8 +25,9 @@
 //    overlap its own MFMAs: the causal mask runs only on tiles that reach past the smallest
 //    query position of the wave; the scores leave the MFMAs already shifted by a reference
 //    maximum (the accumulators start at -m_ref); the row sum is a packed bf16 dot product of
-//    the rounded P that the MFMA consumes (so O and l use the same weights), kept per lane
-//    until the end.  The common tile is exp2, bf16 packing and 16 dot products; only when a
+//    the rounded P that the MFMA consumes (so O and l use the same weights; four independent
+//    partial sums, since one serial chain of 16 dependent dot products measured 2.5% slower),
+//    kept per lane until the end.  The common tile is exp2, bf16 packing and 16 dot products; only when a
 //    lane sum exceeds 2^16 (a score far above m_ref) does a slow path take the true maximum
 //    and rescale O and l (the ratio O / l does not depend on the reference used).
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
@@ -303,9 +304,10 @@ void attn_bf16_kernel(AttnArgs a) {
                 }
         }
         bf16x8 pf[2][2];
-        // P = bf16(exp2(sacc + shift)) (no shift on the common path); returns the lane sum
+        // P = bf16(exp2(sacc + shift)) (no shift on the common path); returns the lane sum, kept
+        // in four partial sums so that the packed dot products do not form one serial chain
         auto exp_pack = [&](bool shifted, float shift) -> float {
-            float rs = 0.f;
+            float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -315,9 +317,9 @@ void attn_bf16_kernel(AttnArgs a) {
                     pp[1] = (bf16)__builtin_amdgcn_exp2f(shifted ? sacc[kb][i + 1] + shift : sacc[kb][i + 1]);
                     pf[kb][i >> 3][i & 7] = pp[0];
                     pf[kb][i >> 3][(i & 7) + 1] = pp[1];
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs, false);
+                    rs[2 * kb + ((i >> 1) & 1)] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs[2 * kb + ((i >> 1) & 1)], false);
                 }
-            return rs;
+            return (rs[0] + rs[1]) + (rs[2] + rs[3]);
         };
         float rs = exp_pack(false, 0.f);
         if (__any(!have_ref || !(rs <= 65536.f))) {   // no reference yet, or a score far above it (rare)
