@@ -32,6 +32,12 @@ plain pre-norm decoder layer those families share - RMS normalisation with a per
 gain, the recomputed attention, an output projection and a residual add, a second RMS
 normalisation, a SiLU-gated MLP and a second residual add - with no norm on q or k.
 
+Fitting (before the path): the mapper is fitted in closed form to paired calibration KV of the
+two models - reduced-rank ridge regression, the rank-r least-squares map from source KV to the
+target KV of all layers, factored into the shared projection and the per-layer reconstructions -
+and each layer's calibration subspace is the span of the top left singular vectors of the mapped
+calibration KV.
+
 Every function takes float64 numpy arrays (exact upcasts of the stored values) and
 computes its result by its plain definition.
 """
@@ -335,6 +341,51 @@ def first_token(x0_last: np.ndarray, p_last: int, K: np.ndarray, V: np.ndarray,
         x, K[l], V[l], _, _ = target_layer(x, S, K[l], V[l], w, H_q, H_kv, d_h, base, eps)
     logits = lm_head(x, gamma_final, w_lm, eps)[0]
     return logits, int(argmax_lowest(logits)), K, V
+
+
+# ------------------------------------------------------------------------------------
+# fitting the mapper and the calibration subspaces from paired calibration data
+# ------------------------------------------------------------------------------------
+
+def fit_mapper(x: np.ndarray, y: np.ndarray, r: int, lam: float, L: int):
+    """Closed-form least-squares fit of the factorized mapper (PANORAMA abstract: the mapper
+    is factorized into one shared source projection and a layer-specific reconstruction, and is
+    first fitted for translation alone; RaReCache abstract: closed-form linear maps translate
+    KV between models).
+
+    Read here as reduced-rank ridge regression: the rank-r linear map B_r from source KV to the
+    target KV of all layers that minimises ||x B_r - y||^2 among maps in the row space of the
+    ridge solution.  x [n, d_src] source KV of n calibration positions; y [n, L * d_t] the
+    target K|V of the same positions, layer-major (layer l is columns l*d_t .. (l+1)*d_t).
+    Steps: the ridge least-squares map B = argmin ||x B - y||^2 + lam ||B||^2 (solved as an
+    ordinary least-squares problem on x stacked over sqrt(lam) I); the fitted values x B; their
+    top-r right singular vectors V [L * d_t, r]; then B_r = B V V^T, factored as the shared
+    projection w_s = (B V)^T [r, d_src] and the per-layer reconstructions w_l = V's rows of
+    layer l [L, d_t, r].  The factorization is unique up to a rotation of the latent.
+    """
+    n, d = x.shape
+    m = y.shape[1]
+    xa = np.vstack([x, math.sqrt(lam) * np.eye(d)])
+    ya = np.vstack([y, np.zeros((d, m))])
+    B = np.linalg.lstsq(xa, ya, rcond=None)[0]
+    _, _, vt = np.linalg.svd(x @ B, full_matrices=False)
+    V = vt[:r].T
+    w_s = (B @ V).T
+    w_l = V.reshape(L, m // L, r)
+    return w_s, w_l
+
+
+def calibration_basis(z: np.ndarray, w_l: np.ndarray, c: int) -> np.ndarray:
+    """Calibration subspace of every target layer (RaReCache abstract: output directions the
+    calibration data supports): U_l = the top-c left singular vectors of the mapped calibration
+    KV, the d_t x n matrix whose column t is w_l z_t.  z [n, r] latents of the calibration
+    positions, w_l [L, d_t, r].  Returns u [L, d_t, c] (orthonormal columns)."""
+    L, d_t, _ = w_l.shape
+    u = np.zeros((L, d_t, c))
+    for l in range(L):
+        left, _, _ = np.linalg.svd(w_l[l] @ z.T, full_matrices=False)
+        u[l] = left[:, :c]
+    return u
 
 
 def score_gap(s: np.ndarray, k: int) -> float:

@@ -623,6 +623,113 @@ def pin_score_gap_hand():
     assert O.score_gap(t, 17) == O.score_gap(t[rng.permutation(50)], 17)
 
 
+# ------------------------------------------------------------------------- fitting
+
+def _planted_pair(seed, n, d, L, d_t, r, noise=0.0):
+    """Source KV x [n, d] with per-channel scales, a planted rank-r map W [L d_t, d] and the
+    target KV y = x W^T (+ noise) of all L layers, layer-major."""
+    rng = _rng(seed)
+    x = rng.standard_normal((n, d)) * rng.uniform(0.5, 2.0, d)
+    W = rng.standard_normal((L * d_t, r)) @ (rng.standard_normal((r, d)) / math.sqrt(d))
+    y = x @ W.T + noise * rng.standard_normal((n, L * d_t))
+    return x, y, W
+
+
+def _principal_sines(a, b):
+    """Sines of the principal angles between the column spans of a and b (equal dimensions):
+    the singular values of the part of b's orthonormal basis outside a's span (accurate for
+    small angles, unlike 1 - cos^2)."""
+    qa, _ = np.linalg.qr(a)
+    qb, _ = np.linalg.qr(b)
+    return np.linalg.svd(qb - qa @ (qa.T @ qb), compute_uv=False)
+
+
+def pin_fit_recovers_planted_map():
+    # a noise-free rank-5 map, more calibration positions than source channels, no ridge term:
+    # the fitted composite map (reconstruction times projection) is the planted map
+    x, y, W = _planted_pair(60, n=120, d=24, L=3, d_t=10, r=5)
+    w_s, w_l = O.fit_mapper(x, y, 5, 0.0, 3)
+    assert w_s.shape == (5, 24) and w_l.shape == (3, 10, 5)
+    comp = w_l.reshape(30, 5) @ w_s
+    assert np.abs(comp - W).max() <= 1e-10 * np.abs(W).max()
+
+
+def pin_fit_reduced_rank_residual():
+    # no ridge term: the rank-r fit's residual is the least-squares residual plus the energy of
+    # the fitted values' discarded singular directions (Pythagoras + Eckart-Young); the fitted
+    # values are formed here from an orthonormal basis of x's columns (QR), their singular
+    # values from the eigenvalues of their Gram matrix
+    x, y, _ = _planted_pair(61, n=80, d=20, L=2, d_t=12, r=6, noise=0.3)
+    r = 6
+    w_s, w_l = O.fit_mapper(x, y, r, 0.0, 2)
+    comp = w_l.reshape(24, r) @ w_s
+    q, _ = np.linalg.qr(x)
+    yhat = q @ (q.T @ y)
+    sig2 = np.sort(np.linalg.eigvalsh(yhat.T @ yhat))[::-1]
+    want = np.sum((y - yhat) ** 2) + np.sum(sig2[r:])
+    got = np.sum((x @ comp.T - y) ** 2)
+    assert abs(got - want) <= 1e-9 * want
+
+
+def pin_fit_ridge_normal_equations():
+    # full rank (r = all outputs): the composite is the ridge solution itself, which satisfies
+    # the normal equations (x^T x + lam I) B = x^T y
+    x, y, _ = _planted_pair(62, n=30, d=40, L=2, d_t=6, r=3, noise=0.5)
+    lam = 2.5
+    w_s, w_l = O.fit_mapper(x, y, 12, lam, 2)
+    comp = w_l.reshape(12, 12) @ w_s                     # [L d_t, d] = B^T
+    lhs = (x.T @ x + lam * np.eye(40)) @ comp.T
+    assert np.abs(lhs - x.T @ y).max() <= 1e-9 * np.abs(x.T @ y).max()
+
+
+def pin_fit_invariances():
+    # orthonormal reconstruction columns; the composite scales with y and ignores the order of
+    # the calibration positions
+    x, y, _ = _planted_pair(63, n=50, d=16, L=3, d_t=8, r=4, noise=0.2)
+    w_s, w_l = O.fit_mapper(x, y, 4, 0.7, 3)
+    V = w_l.reshape(24, 4)
+    assert np.abs(V.T @ V - np.eye(4)).max() <= 1e-12
+    comp = V @ w_s
+    w_s2, w_l2 = O.fit_mapper(x, 3.0 * y, 4, 0.7, 3)
+    assert np.abs(w_l2.reshape(24, 4) @ w_s2 - 3.0 * comp).max() <= 1e-10 * np.abs(comp).max()
+    perm = _rng(64).permutation(50)
+    w_s3, w_l3 = O.fit_mapper(x[perm], y[perm], 4, 0.7, 3)
+    assert np.abs(w_l3.reshape(24, 4) @ w_s3 - comp).max() <= 1e-10 * np.abs(comp).max()
+
+
+def pin_calibration_planted_span():
+    # every mapped calibration vector lies in a planted 3-dim subspace P of each layer: the
+    # basis spans exactly P (principal angles 0)
+    rng = _rng(65)
+    L, d_t, r, n, c = 2, 12, 6, 40, 3
+    z = rng.standard_normal((n, r)) * np.array([3.0, 2.0, 1.5, 1.0, 0.7, 0.4])
+    P = [np.linalg.qr(rng.standard_normal((d_t, c)))[0] for _ in range(L)]
+    w_l = np.stack([P[l] @ rng.standard_normal((c, r)) for l in range(L)])
+    u = O.calibration_basis(z, w_l, c)
+    for l in range(L):
+        assert np.abs(u[l].T @ u[l] - np.eye(c)).max() <= 1e-12
+        assert _principal_sines(u[l], P[l]).max() <= 1e-10
+
+
+def pin_calibration_energy_is_discarded_spectrum():
+    # summed over the calibration positions, the rank-disagreement score of the mapped KV
+    # equals the energy of each layer's discarded singular directions (Eckart-Young); the
+    # singular values come from the eigenvalues of the d_t x d_t Gram matrix
+    rng = _rng(66)
+    L, d_t, r, n, c = 3, 10, 7, 30, 4
+    z = rng.standard_normal((n, r)) * rng.uniform(0.3, 3.0, r)
+    w_l = rng.standard_normal((L, d_t, r))
+    u = O.calibration_basis(z, w_l, c)
+    _, _, Y = O.reconstruct(z, w_l, 1, d_t // 2)
+    total = np.sum(O.rank_disagreement(Y, u))
+    want = 0.0
+    for l in range(L):
+        m = w_l[l] @ z.T
+        ev = np.sort(np.linalg.eigvalsh(m @ m.T))[::-1]
+        want += np.sum(ev[c:])
+    assert abs(total - want) <= 1e-9 * want
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 
@@ -781,6 +888,39 @@ def _mut_score_gap_wrong_neighbour(s, k):
     return float((srt[k - 2] - srt[k - 1]) / abs(srt[k - 1])) if k >= 2 else float(srt[0] - srt[1]) / abs(srt[0])
 
 
+FIT = O.fit_mapper
+def _mut_fit_on_targets(x, y, r, lam, L):
+    # singular vectors of the targets instead of the fitted values
+    n, d = x.shape
+    m = y.shape[1]
+    B = np.linalg.lstsq(np.vstack([x, math.sqrt(lam) * np.eye(d)]), np.vstack([y, np.zeros((d, m))]), rcond=None)[0]
+    V = np.linalg.svd(y, full_matrices=False)[2][:r].T
+    return (B @ V).T, V.reshape(L, m // L, r)
+
+
+def _mut_fit_no_ridge(x, y, r, lam, L):
+    return FIT(x, y, r, 0.0, L)
+
+
+def _mut_fit_trailing(x, y, r, lam, L):
+    n, d = x.shape
+    m = y.shape[1]
+    B = np.linalg.lstsq(np.vstack([x, math.sqrt(lam) * np.eye(d)]), np.vstack([y, np.zeros((d, m))]), rcond=None)[0]
+    vt = np.linalg.svd(x @ B, full_matrices=False)[2]
+    V = vt[-r:].T
+    return (B @ V).T, V.reshape(L, m // L, r)
+
+
+def _mut_calibration_trailing(z, w_l, c):
+    L, d_t, _ = w_l.shape
+    return np.stack([np.linalg.svd(w_l[l] @ z.T, full_matrices=False)[0][:, -c:] for l in range(L)])
+
+
+def _mut_calibration_no_latent(z, w_l, c):
+    L, d_t, _ = w_l.shape
+    return np.stack([np.linalg.svd(w_l[l], full_matrices=False)[0][:, :c] for l in range(L)])
+
+
 SCATTER = O.scatter
 RECOMPUTE = O.recompute_qkv
 CHAINED = O.chained_layers
@@ -812,6 +952,11 @@ MUTANTS = {
     "chained_from_input": ("chained_layers", _mut_chained_from_input),
     "first_token_one_layer": ("first_token", _mut_first_token_one_layer),
     "score_gap_wrong_neighbour": ("score_gap", _mut_score_gap_wrong_neighbour),
+    "fit_svd_of_targets": ("fit_mapper", _mut_fit_on_targets),
+    "fit_no_ridge": ("fit_mapper", _mut_fit_no_ridge),
+    "fit_trailing_directions": ("fit_mapper", _mut_fit_trailing),
+    "calibration_trailing_directions": ("calibration_basis", _mut_calibration_trailing),
+    "calibration_without_latents": ("calibration_basis", _mut_calibration_no_latent),
 }
 
 
