@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvx.so")
-SOURCES = ["kvx_api.hip", "gemm_bf16.hip", "attn_bf16.hip", "kernels.hip"]
+SOURCES = ["kvx_api.hip", "gemm_bf16.hip", "attn_bf16.hip", "kernels.hip", "fit.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -359,6 +359,20 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
         return;
     }
     if (ng >= a.N) return;
+    if (a.epi == EPI_F32) {                  // fp32 store (Gram matrices of the mapper fit)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ml = wm * WTM + i * 16 + 4 * lq + v;
+                if (s_src[ml] < 0) continue;
+                float* dst = a.C32 + (int64_t)(m0 + ml) * a.ldc + ng;
+#pragma unroll
+                for (int j = 0; j < FN; j += 4)
+                    *(f32x4*)(dst + j) = f32x4{acc[i][j][v], acc[i][j + 1][v], acc[i][j + 2][v], acc[i][j + 3][v]};
+            }
+        return;
+    }
     if (a.epi == EPI_RESID) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {

@@ -643,6 +643,9 @@ hipError_t launch_gemm_f64(int M, int N, int K, double alpha, const void* A, int
     else if (ta == ET_F32 && tb == ET_F32) KVX_F64_CASE(float, float);
     else if (ta == ET_F32 && tb == ET_F64) KVX_F64_CASE(float, double);
     else if (ta == ET_F64 && tb == ET_F64) KVX_F64_CASE(double, double);
+    else if (ta == ET_BF16 && tb == ET_F64) KVX_F64_CASE(bf16, double);
+    else if (ta == ET_F64 && tb == ET_BF16) KVX_F64_CASE(double, bf16);
+    else if (ta == ET_F64 && tb == ET_F32) KVX_F64_CASE(double, float);
     else return hipErrorInvalidValue;
 #undef KVX_F64_CASE
     return hipGetLastError();

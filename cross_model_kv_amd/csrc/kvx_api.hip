@@ -327,6 +327,85 @@ kvx_status kvx_score_prepare(void* stream, int32_t dtype, const void* w_l, const
     return hip_status(launch_pack_operator(A, r, dtype, op, s), "score_prepare");
 }
 
+}  // extern "C"
+
+namespace {
+
+kvx_status check_fit_mapper(int32_t dtype, int32_t n, int32_t d_src, int32_t L_t, int32_t d_t, int32_t r) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    KVX_REQUIRE(n > 0 && d_src > 0 && L_t > 0 && d_t > 0 && r > 0, "n, d_src, L_t, d_t and r must be positive");
+    KVX_REQUIRE((int64_t)L_t * d_t <= INT32_MAX, "L_t * d_t too large");
+    const int m = L_t * d_t;
+    KVX_REQUIRE(r <= n && r <= d_src && r <= m, "r (%d) must not exceed n (%d), d_src (%d) or L_t * d_t (%d): the "
+                "fitted values have at most that rank", r, n, d_src, m);
+    if (dtype == KVX_BF16) {
+        KVX_REQUIRE(d_src % 64 == 0 && m % 64 == 0, "bf16 needs d_src %% 64 == 0 and L_t * d_t %% 64 == 0");
+        KVX_REQUIRE(n % 8 == 0, "bf16 needs n %% 8 == 0 (got %d)", n);
+    }
+    return KVX_OK;
+}
+
+kvx_status check_fit_calibration(int32_t n, int32_t L_t, int32_t d_t, int32_t r, int32_t c) {
+    KVX_REQUIRE(n > 0 && L_t > 0 && d_t > 0 && r > 0 && c > 0, "n, L_t, d_t, r and c must be positive");
+    KVX_REQUIRE(c <= d_t && c <= r && c <= n, "c (%d) must not exceed d_t (%d), r (%d) or n (%d): the mapped "
+                "calibration KV has at most that rank", c, d_t, r, n);
+    return KVX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvx_status kvx_fit_mapper_workspace(int32_t dtype, int32_t n, int32_t d_src, int32_t L_t, int32_t d_t, int32_t r,
+                                    size_t* bytes) {
+    if (kvx_status st = check_fit_mapper(dtype, n, d_src, L_t, d_t, r)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    *bytes = fit_mapper_bytes(n, d_src, L_t * d_t, r);
+    return ok();
+}
+
+kvx_status kvx_fit_mapper(void* stream, int32_t dtype, const void* x, const void* y, int32_t n, int32_t d_src,
+                          int32_t L_t, int32_t d_t, int32_t r, double lambda, int32_t iters, void* w_s, void* w_l,
+                          void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_fit_mapper(dtype, n, d_src, L_t, d_t, r)) return st;
+    KVX_REQUIRE_PTR(x, "x");
+    KVX_REQUIRE_PTR(y, "y");
+    KVX_REQUIRE_PTR(w_s, "w_s");
+    KVX_REQUIRE_PTR(w_l, "w_l");
+    KVX_REQUIRE(lambda > 0.0 && lambda < INFINITY, "lambda must be positive and finite");
+    KVX_REQUIRE(iters >= 1 && iters <= 10000, "iters must be in [1, 10000] (got %d)", iters);
+    const size_t need = fit_mapper_bytes(n, d_src, L_t * d_t, r);
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "fit_mapper needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    return hip_status(launch_fit_mapper((hipStream_t)stream, dtype, x, y, n, d_src, L_t * d_t, r, lambda, iters, w_s,
+                                        w_l, ws),
+                      "fit_mapper");
+}
+
+kvx_status kvx_fit_calibration_workspace(int32_t n, int32_t L_t, int32_t d_t, int32_t r, int32_t c, size_t* bytes) {
+    if (kvx_status st = check_fit_calibration(n, L_t, d_t, r, c)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    *bytes = fit_calibration_bytes(n, d_t, r, c);
+    return ok();
+}
+
+kvx_status kvx_fit_calibration(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t n, int32_t L_t,
+                               int32_t d_t, int32_t r, int32_t c, int32_t iters, float* u, void* ws, size_t ws_bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    if (kvx_status st = check_fit_calibration(n, L_t, d_t, r, c)) return st;
+    KVX_REQUIRE_PTR(z, "z");
+    KVX_REQUIRE_PTR(w_l, "w_l");
+    KVX_REQUIRE_PTR(u, "u");
+    KVX_REQUIRE(iters >= 1 && iters <= 10000, "iters must be in [1, 10000] (got %d)", iters);
+    const size_t need = fit_calibration_bytes(n, d_t, r, c);
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "fit_calibration needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    return hip_status(launch_fit_calibration((hipStream_t)stream, dtype, z, w_l, n, L_t, d_t, r, c, iters, u, ws),
+                      "fit_calibration");
+}
+
 kvx_status kvx_select_topk(void* stream, const float* scores, const kvx_batch* batch, int32_t* sel,
                            int32_t* rest) {
     BatchInfo bi;

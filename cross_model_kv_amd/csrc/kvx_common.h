@@ -118,7 +118,7 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& rm, int m) {
     return r;
 }
 
-enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2, EPI_QKV = 3, EPI_RESID = 4, EPI_SWIGLU = 5 };
+enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2, EPI_QKV = 3, EPI_RESID = 4, EPI_SWIGLU = 5, EPI_F32 = 6 };
 
 struct GemmArgs {
     // C[m][n] = sum_k A[src(m)][k mod K_a] * B[n][k]
@@ -127,8 +127,8 @@ struct GemmArgs {
     int32_t M, N, K, groups;
     RowMap rows;
     int32_t epi;
-    // EPI_STORE
-    bf16* C; int64_t ldc;
+    // EPI_STORE (and EPI_F32: C32[m][n] = acc in fp32, leading dimension ldc)
+    bf16* C; int64_t ldc; float* C32;
     // EPI_CACHE (group = layer)
     bf16* kc; bf16* vc; int64_t layer_elems; int32_t hd; SlotMap slots;
     // EPI_SCORE: partial[n_block][m] = sum_{n in block} C[m][n] * Z[m][n]

@@ -17,6 +17,15 @@ hipError_t launch_zero_f64(double* dst, int64_t n, hipStream_t s);
 // op = hi/lo bf16 [r][2r] or fp32 [r][r] from the fp64 operator
 hipError_t launch_pack_operator(const double* A, int r, int dtype, void* op, hipStream_t s);
 
+// ---- closed-form fit of the mapper (reduced-rank ridge regression in the n x n Gram space of
+//      the calibration positions) and of the calibration subspaces; workspace sizes in bytes
+size_t fit_mapper_bytes(int n, int d_src, int m, int r);
+size_t fit_calibration_bytes(int n, int d_t, int r, int c);
+hipError_t launch_fit_mapper(hipStream_t s, int dtype, const void* x, const void* y, int n, int d_src, int m, int r,
+                             double lambda, int iters, void* w_s, void* w_l, void* ws);
+hipError_t launch_fit_calibration(hipStream_t s, int dtype, const void* z, const void* w_l, int n, int L, int d_t,
+                                  int r, int c, int iters, float* u, void* ws);
+
 // ---- selection: scores[t] = sum_p partial[p][t] (when n_part > 0), then the k_b largest per
 //      request (ties to the lower position) written ascending to sel, the rest to rest.
 hipError_t launch_select(const float* partial, int n_part, int64_t n_rows, float* scores,

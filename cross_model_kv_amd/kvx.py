@@ -65,6 +65,11 @@ _SIGS = {
                           _P, _P, _SZ], _I32),
     "kvx_score_select_noalloc": ([_P, _I32, _P, _P, _I32, ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P, _P,
                                   _P], _I32),
+    "kvx_fit_mapper_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "kvx_fit_mapper": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _I32, _P, _P, _P, _SZ],
+                       _I32),
+    "kvx_fit_calibration_workspace": ([_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "kvx_fit_calibration": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ], _I32),
     "kvx_reconstruct": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P,
                          ctypes.POINTER(_Cache)], _I32),
     "kvx_rope_table": ([_P, ctypes.c_double, _I32, _I32, _P], _I32),
@@ -305,6 +310,35 @@ def score_select_noalloc(z: torch.Tensor, op: torch.Tensor, batch: Batch, pcts: 
                                                                       ctypes.byref(batch.c), pct, _ptr(scores),
                                                                       _ptr(sel), _ptr(rest)))
     return scores, sel[:batch.total_sel], rest[:batch.total_rest]
+
+
+def fit_mapper(x: torch.Tensor, y: torch.Tensor, L_t: int, r: int, lam: float, iters: int = 30):
+    """Closed-form fit of the factorized mapper to paired calibration KV: x [n, d_src], y [n, L_t * d_t]
+    (layer-major).  Returns w_s [r, d_src] and w_l [L_t, d_t, r] in x's dtype."""
+    n, d_src = x.shape
+    d_t = y.shape[1] // L_t
+    dt = _dtype(x)
+    b = _SZ()
+    _check("kvx_fit_mapper_workspace", lib().kvx_fit_mapper_workspace(dt, n, d_src, L_t, d_t, r, ctypes.byref(b)))
+    ws = torch.empty(b.value, dtype=torch.uint8, device=x.device)
+    w_s = torch.empty((r, d_src), dtype=x.dtype, device=x.device)
+    w_l = torch.empty((L_t, d_t, r), dtype=x.dtype, device=x.device)
+    _check("kvx_fit_mapper", lib().kvx_fit_mapper(_stream(x.device), dt, _ptr(x), _ptr(y), n, d_src, L_t, d_t, r,
+                                                  float(lam), iters, _ptr(w_s), _ptr(w_l), _ptr(ws), b.value))
+    return w_s, w_l
+
+
+def fit_calibration(z: torch.Tensor, w_l: torch.Tensor, c: int, iters: int = 30) -> torch.Tensor:
+    """Calibration subspaces: u [L_t, d_t, c] fp32 from the calibration latents z [n, r] and w_l [L_t, d_t, r]."""
+    n, r = z.shape
+    L_t, d_t, _ = w_l.shape
+    b = _SZ()
+    _check("kvx_fit_calibration_workspace", lib().kvx_fit_calibration_workspace(n, L_t, d_t, r, c, ctypes.byref(b)))
+    ws = torch.empty(b.value, dtype=torch.uint8, device=z.device)
+    u = torch.empty((L_t, d_t, c), dtype=torch.float32, device=z.device)
+    _check("kvx_fit_calibration", lib().kvx_fit_calibration(_stream(z.device), _dtype(z), _ptr(z), _ptr(w_l), n, L_t,
+                                                            d_t, r, c, iters, _ptr(u), _ptr(ws), b.value))
+    return u
 
 
 def reconstruct(z: torch.Tensor, w_l: torch.Tensor, H_kv: int, d_h: int, batch: Batch, cache: Cache,

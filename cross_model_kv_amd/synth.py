@@ -295,3 +295,23 @@ def adversarial_scores(kind: str, T: int, seed: int) -> np.ndarray:
     if kind == "positive":
         return np.abs(rng.standard_normal(T)).astype(np.float32) * 100
     raise ValueError(kind)
+
+
+def calibration_pair(n: int, d_src: int, L_t: int, d_t: int, r: int, seed: int, strong: int, noise: float = 0.05,
+                     dtype=torch.float32, device="cpu"):
+    """Paired calibration KV with a planted linear relation, for fitting the mapper.
+
+    x [n, d_src]: N(0,1) times one U(0.5, 2) factor per channel (as ``x_src``);
+    y [n, L_t d_t] = x Q diag(s) P^T + N(0, noise^2), with Q [d_src, r] orthonormal columns,
+    P the stack of L_t independent [d_t, r] orthonormal blocks (one per layer, so every layer
+    sees all r directions) and s_j = 1 for the first ``strong`` directions and 0.3 for the rest
+    (a spectral step that separates the top ``strong`` directions of each layer).
+    Drawn in float64 on the host, returned in ``dtype`` (y computed before rounding)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 505])))
+    x = rng.standard_normal((n, d_src)) * rng.uniform(0.5, 2.0, d_src)[None, :]
+    q = orthonormal_basis(rng, d_src, r)
+    p = np.vstack([orthonormal_basis(rng, d_t, r) for _ in range(L_t)])
+    s = np.where(np.arange(r) < strong, 1.0, 0.3)
+    y = (x @ q) * s[None, :] @ p.T + noise * rng.standard_normal((n, L_t * d_t))
+    cast = lambda a: torch.from_numpy(a.astype(np.float32)).to(dtype).to(device)
+    return cast(x), cast(y)

@@ -149,6 +149,47 @@ KVX_API kvx_status kvx_score_prepare(void* stream, int32_t dtype, const void* w_
                              int32_t L_t, int32_t r, int32_t d_t, int32_t c, void* op,
                              void* ws, size_t ws_bytes);
 
+/* ---------------------------------------------------------------------------------------
+ * Fitting the mapper and the calibration subspaces (one-time, per model pair, before any
+ * handoff).
+ *
+ * kvx_fit_mapper: closed-form fit of the factorized mapper to paired calibration KV of the two
+ * models (PANORAMA abstract: the mapper, a shared source projection and layer-specific
+ * reconstructions, is fitted for translation; RaReCache abstract: closed-form linear maps
+ * translate KV between models).  Reduced-rank ridge regression: with B the ridge least-squares
+ * map from x to y (argmin |x B - y|^2 + lambda |B|^2) and V [L_t d_t][r] an orthonormal basis
+ * of the top-r right singular space of the fitted values x B, the fitted mapper is the rank-r
+ * map B V V^T, factored as w_s = (B V)^T and w_l = the rows of V of layer l.  The latent is
+ * defined up to a rotation: every quantity the handoff uses (mapped KV, composite map, scores)
+ * does not depend on it.
+ *   x (device) [n][d_src] source KV of n calibration positions (channel order as x_src);
+ *   y (device) [n][L_t * d_t] the target's K|V of the same positions, layer-major (layer l is
+ *   columns l*d_t .. (l+1)*d_t, [K heads | V heads] as a reconstructed layer);
+ *   w_s (device, out) [r][d_src], w_l (device, out) [L_t][d_t][r], storage dtype.
+ *   lambda > 0; iters in [1, 10000] block power steps for the singular space (the subspace
+ *   error shrinks by the ratio of the (r+1)-th to the r-th squared singular value of x B per
+ *   step, so a gap there is needed).  r <= min(n, d_src, L_t d_t).  bf16 needs d_src and
+ *   L_t d_t multiples of 64 and n a multiple of 8.  Work and memory are those of n x n
+ *   matrices (fp64): ws (device) of kvx_fit_mapper_workspace() bytes. */
+KVX_API kvx_status kvx_fit_mapper_workspace(int32_t dtype, int32_t n, int32_t d_src, int32_t L_t, int32_t d_t,
+                                            int32_t r, size_t* bytes);
+KVX_API kvx_status kvx_fit_mapper(void* stream, int32_t dtype, const void* x, const void* y, int32_t n,
+                                  int32_t d_src, int32_t L_t, int32_t d_t, int32_t r, double lambda, int32_t iters,
+                                  void* w_s, void* w_l, void* ws, size_t ws_bytes);
+
+/* kvx_fit_calibration: the calibration subspace of every target layer (RaReCache abstract:
+ * output directions the calibration data supports): u[l] = an orthonormal basis of the top-c
+ * left singular space of the layer's mapped calibration KV (the d_t x n matrix whose column t is
+ * w_l z_t), found by iters block power steps on w_l (z^T z) w_l^T in fp64.
+ *   z (device) [n][r] latents of the calibration positions (kvx_map_latent of their source KV);
+ *   w_l (device) [L_t][d_t][r]; u (device, out) [L_t][d_t][c] fp32, ready for kvx_score_prepare.
+ *   c <= min(d_t, r, n); iters in [1, 10000].  ws (device) of kvx_fit_calibration_workspace(). */
+KVX_API kvx_status kvx_fit_calibration_workspace(int32_t n, int32_t L_t, int32_t d_t, int32_t r, int32_t c,
+                                                 size_t* bytes);
+KVX_API kvx_status kvx_fit_calibration(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t n,
+                                       int32_t L_t, int32_t d_t, int32_t r, int32_t c, int32_t iters, float* u,
+                                       void* ws, size_t ws_bytes);
+
 /* Top-k of given scores per request: the k_b largest scores of request b, ties to the
  * lower position, -0.0 equal to +0.0.  scores (device) [N] fp32, finite.
  * sel (device, out) [cu_sel[n_req]] request-local positions, ascending per request;

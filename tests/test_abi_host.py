@@ -93,6 +93,43 @@ def test_score_prepare_validation():
     status(L.kvx_score_prepare(None, 1, A16, A16, 2, 8, 16, 20, A16, A16, 1 << 20), INVALID, "calibration")
 
 
+def test_fit_validation():
+    """The mapper and calibration fits check ranks, alignment, lambda, iteration count and
+    workspace before any device work."""
+    L = kvx.lib()
+    b = ctypes.c_size_t()
+    # (dtype, n, d_src, L_t, d_t, r)
+    status(L.kvx_fit_mapper_workspace(1, 64, 128, 2, 64, 65, ctypes.byref(b)), INVALID, "must not exceed n")
+    status(L.kvx_fit_mapper_workspace(1, 256, 32, 2, 64, 40, ctypes.byref(b)), INVALID, "d_src")
+    status(L.kvx_fit_mapper_workspace(1, 60, 128, 2, 64, 16, ctypes.byref(b)), INVALID, "n % 8")
+    status(L.kvx_fit_mapper_workspace(1, 64, 100, 2, 64, 16, ctypes.byref(b)), INVALID, "d_src % 64")
+    status(L.kvx_fit_mapper_workspace(7, 64, 128, 2, 64, 16, ctypes.byref(b)), UNSUPPORTED, "dtype")
+    status(L.kvx_fit_mapper_workspace(1, 64, 128, 0, 64, 16, ctypes.byref(b)), INVALID, "positive")
+    assert L.kvx_fit_mapper_workspace(0, 60, 100, 3, 10, 16, ctypes.byref(b)) == 0 and b.value > 60 * 60 * 8
+    need = ctypes.c_size_t()
+    assert L.kvx_fit_mapper_workspace(1, 64, 128, 2, 64, 16, ctypes.byref(need)) == 0
+    fit = lambda x=A16, lam=1.0, iters=10, ws=A16, wsb=need.value: L.kvx_fit_mapper(
+        None, 1, x, A16, 64, 128, 2, 64, 16, ctypes.c_double(lam), iters, A16, A16B, ws, wsb)
+    status(fit(x=None), INVALID, "x")
+    status(fit(x=MIS), INVALID, "aligned")
+    status(fit(lam=0.0), INVALID, "lambda")
+    status(fit(lam=float("inf")), INVALID, "lambda")
+    status(fit(lam=float("nan")), INVALID, "lambda")
+    status(fit(iters=0), INVALID, "iters")
+    status(fit(ws=None), WORKSPACE)
+    status(fit(wsb=need.value - 1), WORKSPACE)
+    # (n, L_t, d_t, r, c)
+    status(L.kvx_fit_calibration_workspace(64, 2, 32, 16, 17, ctypes.byref(b)), INVALID, "must not exceed")
+    status(L.kvx_fit_calibration_workspace(8, 2, 32, 16, 9, ctypes.byref(b)), INVALID, "must not exceed")
+    assert L.kvx_fit_calibration_workspace(64, 2, 32, 16, 8, ctypes.byref(need)) == 0 and need.value > 0
+    cal = lambda z=A16, u=A16B, iters=10, ws=A16, wsb=need.value: L.kvx_fit_calibration(
+        None, 1, z, A16, 64, 2, 32, 16, 8, iters, u, ws, wsb)
+    status(cal(z=None), INVALID, "z")
+    status(cal(u=MIS), INVALID, "aligned")
+    status(cal(iters=20000), INVALID, "iters")
+    status(cal(wsb=need.value - 1), WORKSPACE)
+
+
 def test_batch_validation():
     L = kvx.lib()
     bad = FakeBatch([10, 5], [3, 6])                      # k > T
