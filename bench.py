@@ -51,10 +51,11 @@ def f64(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def stage_work(wl, T, k, pos_sum):
-    """Algorithmic flops / bytes of every stage of one handoff (per launch for per-layer stages)."""
+def stage_work(wl, T, k, pos_sum, layers_per_launch=1.0):
+    """Algorithmic flops / bytes of every stage of one handoff (per launch for the per-layer
+    stages, which process layers_per_launch layers per launch)."""
     d_t, n_qkv = wl.d_t, wl.n_qkv
-    return {
+    w = {
         "map_latent": dict(flops=2.0 * T * wl.d_src * wl.r, bytes=2.0 * (T * wl.d_src + wl.d_src * wl.r + T * wl.r)),
         "score_select": dict(flops=2.0 * T * wl.r * wl.r, bytes=2.0 * T * wl.r + 4.0 * wl.r * wl.r + 4.0 * T),
         "reconstruct": dict(flops=2.0 * (T - k) * wl.r * d_t * wl.L_t,
@@ -65,6 +66,9 @@ def stage_work(wl, T, k, pos_sum):
         "sparse_attention": dict(flops=4.0 * wl.H_q * wl.d_h * pos_sum,
                                  bytes=2.0 * (T * d_t + 2.0 * k * wl.H_q * wl.d_h)),
     }
+    for n in ("qkv_rope_scatter", "sparse_attention"):
+        w[n] = {key: v * layers_per_launch for key, v in w[n].items()}
+    return w
 
 
 def cpu_baseline(inp, wl, S, T, k, pos_sum):
@@ -425,8 +429,13 @@ def measure_handoff(wl, args, steps, warmup, flush, dev):
     log(f"[bench] {wl.name}: inputs and one-time preparation {time.perf_counter() - t_gen:.1f}s")
     T = h.batch.n_tokens           # all positions of the batch (one request: T)
     k = h.batch.total_sel
-    qkv = h.ws_attn[: k * wl.n_qkv * 2].view(torch.bfloat16).view(k, wl.n_qkv)
-    ws_qkv = h.ws_attn[(k * wl.n_qkv * 2 + 255) // 256 * 256:]     # split-tail / key-split workspace
+    # the target layers run in chunks (Handoff.chunks): one projection launch and one attention
+    # launch per chunk, every layer of a chunk at once
+    chunks = h.chunks
+    lc = max(n for _, n in chunks)
+    qkv_l = torch.empty((lc, max(k, 1), wl.n_qkv), dtype=torch.bfloat16, device=dev)
+    qkv = qkv_l[0]
+    ws_qkv = h.ws_attn
     stream = torch.cuda.current_stream(dev)
     names = ["map_latent", "score_select", "reconstruct", "qkv_rope_scatter", "sparse_attention"]
 
@@ -443,21 +452,30 @@ def measure_handoff(wl, args, steps, warmup, flush, dev):
         mark("score_select")
         h.reconstruct()
         mark("reconstruct")
-        for l in range(wl.L_t):
-            kvx.qkv_rope_scatter(l, inp.x_l[l], inp.w_qkv[l], wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S,
-                                 h.cache, qkv, ws_qkv)
+        for l0, n in chunks:
+            if n == 1:                 # a layer alone: the single-layer calls with their workspaces
+                kvx.qkv_rope_scatter(l0, inp.x_l[l0], inp.w_qkv[l0], wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch,
+                                     h.S, h.cache, qkv, ws_qkv)
+                mark("qkv_rope_scatter")
+                kvx.sparse_attention(l0, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache, h.out[l0],
+                                     h.lse[l0], ws_qkv)
+                mark("sparse_attention")
+                continue
+            kvx.qkv_rope_scatter_layers(l0, inp.x_l[l0:l0 + n], inp.w_qkv[l0:l0 + n], wl.H_q, wl.H_kv, wl.d_h,
+                                        h.rope, h.batch, h.S, h.cache, qkv_l[:n])
             mark("qkv_rope_scatter")
-            kvx.sparse_attention(l, qkv, wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache, h.out[l], h.lse[l],
-                                 ws_qkv)
+            kvx.sparse_attention_layers(l0, qkv_l[:n], wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch, h.S, h.cache,
+                                        h.out[l0:l0 + n], h.lse[l0:l0 + n])
             mark("sparse_attention")
 
     times, marks, wall = timed_steps(step, stream, steps, warmup, flush)
-    order = ["map_latent", "score_select", "reconstruct"] + ["qkv_rope_scatter", "sparse_attention"] * wl.L_t
+    order = ["map_latent", "score_select", "reconstruct"] + ["qkv_rope_scatter", "sparse_attention"] * len(chunks)
     step_stage_ms, avg_launch_ms = stage_times(marks, order, names, steps)
     med = float(np.median(times))
     S = h.S.cpu().numpy()
     pos_sum = float(np.sum(S.astype(np.float64) + 1.0))
-    work = stage_work(wl, T, k, pos_sum)
+    # per launch: the per-layer stages cover L_t / len(chunks) layers on average
+    work = stage_work(wl, T, k, pos_sum, wl.L_t / len(chunks))
     stages = {}
     for n in names:
         t = avg_launch_ms[n] * 1e-3
@@ -468,8 +486,8 @@ def measure_handoff(wl, args, steps, warmup, flush, dev):
     att_ms = avg_launch_ms["sparse_attention"]
     achieved = work["sparse_attention"]["flops"] / (att_ms * 1e-3) / 1e12
     # the handoff at 100% of every stage's roofline (bf16 peak for the matrix-core stages)
-    roof_ms = sum(w["flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3 * (wl.L_t if n in ("qkv_rope_scatter",
-                                                                                 "sparse_attention") else 1)
+    roof_ms = sum(w["flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3 * (len(chunks) if n in ("qkv_rope_scatter",
+                                                                                      "sparse_attention") else 1)
                   for n, w in work.items())
     res = {
         "value": T / (med * 1e-3), "ms_per_step": med, "T": T, "k": k,
@@ -483,6 +501,7 @@ def measure_handoff(wl, args, steps, warmup, flush, dev):
                      "avg_launch_ms": round(att_ms, 5)},
         "handoff_at_roofline_ms": round(roof_ms, 3),
         "frac_of_roofline_time": round(roof_ms / med, 4),
+        "layers_per_launch": [n for _, n in chunks],
     }
     ctx = dict(h=h, inp=inp, step=step, qkv=qkv, ws_qkv=ws_qkv, S=S, pos_sum=pos_sum, work=work, stream=stream)
     return res, ctx
@@ -657,6 +676,7 @@ def main():
         "roofline": roofline,
         "handoff_at_roofline_ms": res["handoff_at_roofline_ms"],
         "frac_of_roofline_time": res["frac_of_roofline_time"],
+        "layers_per_launch": res["layers_per_launch"],
         "stages": res["stages"],
         "score_select_split": score_split,
         "scatter_standalone": scatter,
@@ -681,6 +701,7 @@ def main():
                             "T": o_res["T"], "selected": o_res["k"], "step_ms": o_res["step_ms"],
                             "roofline": o_res["roofline"], "handoff_at_roofline_ms": o_res["handoff_at_roofline_ms"],
                             "frac_of_roofline_time": o_res["frac_of_roofline_time"],
+                            "layers_per_launch": o_res["layers_per_launch"],
                             "stages": {n: {kk: v for kk, v in st.items() if kk in ("ms_per_step", "tflops")}
                                        for n, st in o_res["stages"].items()}}
             del o_ctx

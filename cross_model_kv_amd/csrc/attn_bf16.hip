@@ -78,8 +78,12 @@ void attn_bf16_kernel(AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int hf = lane >> 5, lr = lane & 31;
     const int H_kv = a.H_kv, g = a.H_q / H_kv;
-    const int hk = blockIdx.x % H_kv;
-    const int item = (int)(blockIdx.x / H_kv);
+    // layer of this workgroup (the slowest index), then the KV head, then the block item
+    const int per_layer = a.n_blocks * a.n_split * H_kv;
+    const int layer = (int)(blockIdx.x / per_layer);
+    const int wg = (int)(blockIdx.x - layer * per_layer);
+    const int hk = wg % H_kv;
+    const int item = wg / H_kv;
     // chunk-major order: every block's chunk 0 (longest blocks first), then the chunk 1s, ...
     const int qb = a.n_blocks - 1 - item % a.n_blocks;
     const int chunk = item / a.n_blocks;
@@ -124,7 +128,8 @@ void attn_bf16_kernel(AttnArgs a) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)D_H);
     bf16x8 qf[QC];
     {
-        const bf16* qrow = (const bf16*)a.qkv + (int64_t)(i0 + (valid ? qi : 0)) * a.ld + (int64_t)h * D_H;
+        const bf16* qrow = (const bf16*)a.qkv + layer * a.q_layer_stride + (int64_t)(i0 + (valid ? qi : 0)) * a.ld +
+                           (int64_t)h * D_H;
 #pragma unroll
         for (int c = 0; c < QC; ++c) {
             if (valid) qf[c] = *(const bf16x8*)(qrow + 16 * c + 8 * hf);
@@ -154,8 +159,8 @@ void attn_bf16_kernel(AttnArgs a) {
     }
 
     // ---- K/V tile staging: block q of a tile holds KPB consecutive keys of K (q < NBLK/2) or V
-    const bf16* kbase = (const bf16*)a.kc;
-    const int64_t vdelta = (const bf16*)a.vc - kbase;   // V addressed relative to K
+    const bf16* kbase = (const bf16*)a.kc + layer * a.kv_layer_elems;
+    const int64_t vdelta = (const bf16*)a.vc - (const bf16*)a.kc;   // V addressed relative to K
     // slots of the keys first (page-table loads complete before any of the tile's direct
     // loads is issued), then the direct loads themselves
     constexpr int NBW = (NBLK + W - 1) / W;   // blocks per wave
@@ -432,7 +437,7 @@ void attn_bf16_kernel(AttnArgs a) {
         return;
     }
     const float inv = 1.f / l_run;
-    bf16* orow = (bf16*)a.out + out_row * D_H;
+    bf16* orow = (bf16*)a.out + layer * a.out_layer_stride + out_row * D_H;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -443,7 +448,7 @@ void attn_bf16_kernel(AttnArgs a) {
             *(bf16x4*)(orow + d * 32 + 8 * q4 + 4 * hf) = o;
         }
     if (a.lse && hf == 0)
-        a.lse[out_row] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
+        a.lse[layer * a.lse_layer_stride + out_row] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
 }
 
 // Merge of a split attention: out = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over the
@@ -519,7 +524,10 @@ template <int D_H>
 hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
     if (W != 8) return hipErrorInvalidValue;
     if (a.n_split < 1 || (a.n_split > 1 && (!a.part || !a.part_ml))) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((int64_t)a.n_blocks * a.n_split * a.H_kv));
+    if (a.n_layers < 1 || (a.n_layers > 1 && a.n_split != 1)) return hipErrorInvalidValue;
+    const int64_t wgs = (int64_t)a.n_blocks * a.n_split * a.H_kv * a.n_layers;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
     hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8>), grid, dim3(8 * 64), 0, s, a);
     if (a.n_split == 1) return hipGetLastError();
     if (hipError_t e = hipGetLastError()) return e;

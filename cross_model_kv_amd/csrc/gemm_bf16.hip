@@ -107,8 +107,19 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
     const int bid = blockIdx.x;
     const bool tail = bid >= sp.full;                 // a K slice of a tail tile
     const int unit = bid - sp.full;
-    const Tile t = tail ? tile_at(sp.full + unit / sp.split, mt, nt, a.groups, gm)
-                        : tile_at(xcd_linear(bid, sp.full, n_xcd), mt, nt, a.groups, gm);
+    Tile t;
+    if (a.a_group_stride != 0) {
+        // independent groups, one after another in dispatch order, each spread over every XCD
+        // like a single-group launch: the CUs work on one group's operands at a time, which
+        // keep fitting in the last-level cache
+        const int per = mt * nt;
+        const int grp = bid / per;
+        t = tile_at(xcd_linear(bid - grp * per, per, n_xcd), mt, nt, 1, gm);
+        t.group = grp;
+    } else {
+        t = tail ? tile_at(sp.full + unit / sp.split, mt, nt, a.groups, gm)
+                 : tile_at(xcd_linear(bid, sp.full, n_xcd), mt, nt, a.groups, gm);
+    }
     const int k_first = tail ? (unit % sp.split) * (nk_all / sp.split) : 0;
     const int nk = tail ? nk_all / sp.split : nk_all;
     const int m0 = t.tm * BM, n0 = t.tn * BN;
@@ -144,7 +155,7 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
         const int P = (c * NL + lw) * 64 + lane;
         const int row = P >> 3, ch = (P & 7) ^ swz(row);
         const int src = max(s_src[row], 0);
-        asrc[c] = a.A + (int64_t)src * a.lda + ch * 8;
+        asrc[c] = a.A + (int64_t)t.group * a.a_group_stride + (int64_t)src * a.lda + ch * 8;
     }
 #pragma unroll
     for (int c = 0; c < B_L; ++c) {
@@ -326,8 +337,9 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
 #pragma unroll
                     for (int j = 0; j < 8; ++j) o[j] = (bf16)x[j];
                 }
-                bf16* dst = ng < a.q_cols ? a.C + (int64_t)(m0 + ml) * a.ldc + ng
-                                          : (is_k ? a.kc : a.vc) + s_slot[ml] * a.hd + (is_k ? cc : cc - a.hd);
+                bf16* dst = ng < a.q_cols ? a.C + (int64_t)t.group * a.c_group_stride + (int64_t)(m0 + ml) * a.ldc + ng
+                                          : (is_k ? a.kc : a.vc) + (int64_t)t.group * a.layer_elems +
+                                                s_slot[ml] * a.hd + (is_k ? cc : cc - a.hd);
                 *(bf16x8*)dst = o;
             }
         }
@@ -698,9 +710,11 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     // groups' weights: walking all row panels first streams each weight panel through an XCD
     // once while the row operand stays resident in the last-level cache (measured fastest).
     const DeviceShape dv = device_shape();
-    const int gm = a.groups > 1 ? mt
-                                : pick_group_rows(mt, nt * a.groups, 256.0 * a.K_a, 256.0 * a.K,
-                                                  std::max(1, dv.cus / dv.xcds));
+    const bool indep = a.a_group_stride != 0;
+    if (indep && (a.epi != EPI_QKV || a.split_ws)) return hipErrorInvalidValue;
+    const int gm = a.groups > 1 && !indep ? mt
+                                          : pick_group_rows(mt, nt * (indep ? 1 : a.groups), 256.0 * a.K_a,
+                                                            256.0 * a.K, std::max(1, dv.cus / dv.xcds));
     if (a.split_ws && gemv_eligible(a)) {           // few rows: stream the weight, reduce with the epilogue
         const SplitPlan sp = plan_gemv(a.N, a.K);
         const dim3 grid((unsigned)(sp.rem * 8 * sp.split));

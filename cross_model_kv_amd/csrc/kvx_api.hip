@@ -757,13 +757,50 @@ hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, con
     return launch_gemm_bf16(a, s);
 }
 
+// Layers [layer, layer + n) of one launch (bf16 only when n > 1): q columns, outputs and
+// log-sum-exps of layer layer + j at qkv, out, lse + j * the strides (elements).
+struct LayerSpan {
+    int n;
+    int64_t q_stride, out_stride, lse_stride;
+};
+
+// Steps 1-3 of layers [l0, l0 + n) in one grouped GEMM (bf16): group j reads x + j * N * D and
+// w_qkv + j * n_qkv * D, keeps its q columns in qkv + j * q_stride and writes its rotated k
+// and v into cache layer l0 + j.  The same epilogue arithmetic as run_qkv_rope_scatter, without a
+// K split: a whole tile of a group accumulates in the order a single-layer call without a
+// workspace uses, so the two agree bit for bit.
+hipError_t run_qkv_rope_scatter_layers(hipStream_t s, int32_t l0, int32_t n, const void* x, const void* w_qkv,
+                                       int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
+                                       const kvx_batch* batch, const BatchInfo& bi, const int32_t* sel,
+                                       const kvx_cache* cache, void* qkv, int64_t q_stride) {
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    const int hd = H_kv * d_h;
+    GemmArgs a{};
+    a.A = (const bf16*)x; a.lda = D; a.K_a = D; a.a_group_stride = bi.n_tokens * D;
+    a.B = (const bf16*)w_qkv; a.ldb = D; a.b_group_stride = (int64_t)n_qkv * D;
+    a.M = (int)bi.n_sel; a.N = n_qkv; a.K = D; a.groups = n;
+    a.rows = sel_rows(batch, sel, bi.n_req);
+    a.epi = EPI_QKV; a.C = (bf16*)qkv; a.ldc = n_qkv; a.c_group_stride = q_stride;
+    a.kc = (bf16*)layer_base(cache->k, cache, l0, hd, KVX_BF16);
+    a.vc = (bf16*)layer_base(cache->v, cache, l0, hd, KVX_BF16);
+    a.layer_elems = cache->n_slots * hd; a.hd = hd; a.slots = slot_map(cache, batch);
+    a.rope = rope; a.q_cols = H_q * d_h; a.d_h = d_h;
+    return launch_gemm_bf16(a, s);
+}
+
 hipError_t run_attention(hipStream_t s, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,
                          int32_t H_kv, int32_t d_h, const float* rope, const kvx_batch* batch,
                          const BatchInfo& bi, const int32_t* sel, const kvx_cache* cache, void* out,
-                         float* lse, void* split_ws) {
+                         float* lse, void* split_ws, const LayerSpan& span = LayerSpan{1, 0, 0, 0}) {
     const int hd = H_kv * d_h;
     AttnArgs at{};
     at.n_split = 1;
+    at.n_layers = span.n;
+    at.q_layer_stride = span.q_stride;
+    at.kv_layer_elems = cache->n_slots * hd;
+    at.out_layer_stride = span.out_stride;
+    at.lse_layer_stride = span.lse_stride;
+    if (span.n > 1 && dtype != KVX_BF16) return hipErrorInvalidValue;
     at.qkv = qkv; at.ld = (H_q + 2 * H_kv) * d_h;
     at.H_q = H_q; at.H_kv = H_kv; at.d_h = d_h;
     at.rope = rope;
@@ -780,7 +817,7 @@ hipError_t run_attention(hipStream_t s, int32_t dtype, int32_t layer, const void
             at.blk_cu[b + 1] = at.blk_cu[b] + (k + at.bq - 1) / at.bq;
         }
         at.n_blocks = at.blk_cu[bi.n_req];
-        if (split_ws) {
+        if (split_ws && span.n == 1) {
             at.n_split = attn_bf16_split(at.n_blocks, H_kv, bi.max_T);
             if (at.n_split > 1) {
                 const int max_tiles = (bi.max_T + ATTN_KEY_TILE - 1) / ATTN_KEY_TILE;
@@ -1002,6 +1039,151 @@ kvx_status kvx_recompute_attn(void* stream, int32_t dtype, int32_t layer, const 
                                      ws, split_ws), "recompute qkv/rope/scatter");
     return hip_status(run_attention(s, dtype, layer, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse,
                                     attn_ws), "attention");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the several-layer entry points.
+kvx_status check_layers(const kvx_cache* cache, const kvx_batch* batch, const BatchInfo& bi, int32_t dtype,
+                        int32_t H_kv, int32_t d_h, int32_t l0, int32_t n_layers, const float* rope,
+                        int32_t max_pos) {
+    KVX_REQUIRE(n_layers >= 1, "n_layers must be >= 1 (got %d)", n_layers);
+    if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, l0, rope, max_pos)) return st;
+    KVX_REQUIRE((int64_t)l0 + n_layers <= cache->n_layers, "layers [%d, %d) outside the cache's %d layers", l0,
+                l0 + n_layers, cache->n_layers);
+    return KVX_OK;
+}
+
+size_t layers_qkv_bytes(int32_t dtype, int64_t n_sel, int n_qkv) {
+    return round256((size_t)n_sel * n_qkv * elem_size(dtype));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvx_status kvx_qkv_rope_scatter_layers(void* stream, int32_t dtype, int32_t l0, int32_t n_layers, const void* x,
+                                       const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h,
+                                       const float* rope, int32_t max_pos, const kvx_batch* batch,
+                                       const int32_t* sel, const kvx_cache* cache, void* qkv) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(x, "x");
+    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
+    KVX_REQUIRE(D > 0, "D must be positive");
+    if (dtype == KVX_BF16) KVX_REQUIRE(D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    if (kvx_status st = check_layers(cache, batch, bi, dtype, H_kv, d_h, l0, n_layers, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
+    KVX_REQUIRE_PTR(qkv, "qkv");
+    hipStream_t s = (hipStream_t)stream;
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    if (dtype == KVX_BF16)
+        return hip_status(run_qkv_rope_scatter_layers(s, l0, n_layers, x, w_qkv, D, H_q, H_kv, d_h, rope, batch, bi,
+                                                      sel, cache, qkv, bi.n_sel * n_qkv), "qkv_rope_scatter_layers");
+    for (int j = 0; j < n_layers; ++j)       // fp32: the single-layer kernels, layer by layer
+        KVX_TRY_HIP(run_qkv_rope_scatter(s, dtype, l0 + j, (const float*)x + (int64_t)j * bi.n_tokens * D,
+                                         (const float*)w_qkv + (int64_t)j * n_qkv * D, D, H_q, H_kv, d_h, rope,
+                                         batch, bi, sel, cache, (float*)qkv + (int64_t)j * bi.n_sel * n_qkv,
+                                         nullptr), "qkv_rope_scatter_layers");
+    return ok();
+}
+
+kvx_status kvx_sparse_attention_layers(void* stream, int32_t dtype, int32_t l0, int32_t n_layers, const void* qkv,
+                                       int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope, int32_t max_pos,
+                                       const kvx_batch* batch, const int32_t* sel, const kvx_cache* cache,
+                                       void* out, float* lse) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    if (bi.n_req > MAX_ATTN_REQ)
+        return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
+    if (kvx_status st = check_layers(cache, batch, bi, dtype, H_kv, d_h, l0, n_layers, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
+    KVX_REQUIRE_PTR(qkv, "qkv");
+    KVX_REQUIRE_PTR(out, "out");
+    if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    const int64_t q_stride = bi.n_sel * n_qkv, o_stride = bi.n_sel * H_q * d_h, l_stride = bi.n_sel * H_q;
+    if (dtype == KVX_BF16)
+        return hip_status(run_attention(s, dtype, l0, qkv, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse,
+                                        nullptr, LayerSpan{n_layers, q_stride, o_stride, l_stride}),
+                          "sparse_attention_layers");
+    for (int j = 0; j < n_layers; ++j)
+        KVX_TRY_HIP(run_attention(s, dtype, l0 + j, (const float*)qkv + j * q_stride, H_q, H_kv, d_h, rope, batch,
+                                  bi, sel, cache, (float*)out + j * o_stride, lse ? lse + j * l_stride : nullptr,
+                                  nullptr), "sparse_attention_layers");
+    return ok();
+}
+
+kvx_status kvx_recompute_attn_layers_workspace(int32_t dtype, const kvx_batch* batch, int32_t D, int32_t H_q,
+                                               int32_t H_kv, int32_t d_h, int32_t n_layers, size_t* bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(H_q > 0 && H_kv > 0 && d_h > 0 && D > 0, "D, H_q, H_kv and d_h must be positive");
+    KVX_REQUIRE(n_layers >= 1, "n_layers must be >= 1 (got %d)", n_layers);
+    *bytes = (size_t)n_layers * layers_qkv_bytes(dtype, bi.n_sel, (H_q + 2 * H_kv) * d_h);
+    return ok();
+}
+
+kvx_status kvx_recompute_attn_layers(void* stream, int32_t dtype, int32_t l0, int32_t n_layers, const void* x,
+                                     const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h,
+                                     const float* rope, int32_t max_pos, const kvx_batch* batch,
+                                     const int32_t* sel, const kvx_cache* cache, void* out, float* lse, void* ws,
+                                     size_t ws_bytes) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(x, "x");
+    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
+    KVX_REQUIRE(D > 0, "D must be positive");
+    if (dtype == KVX_BF16) KVX_REQUIRE(D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    if (bi.n_req > MAX_ATTN_REQ)
+        return fail(KVX_ERR_UNSUPPORTED, "at most %d requests per call (got %d)", MAX_ATTN_REQ, bi.n_req);
+    if (kvx_status st = check_layers(cache, batch, bi, dtype, H_kv, d_h, l0, n_layers, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
+    KVX_REQUIRE_PTR(out, "out");
+    if (lse) KVX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+    const size_t per = layers_qkv_bytes(dtype, bi.n_sel, (H_q + 2 * H_kv) * d_h);
+    const size_t need = (size_t)n_layers * per;
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "recompute_attn_layers needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int n_qkv = (H_q + 2 * H_kv) * d_h;
+    const int64_t q_stride = (int64_t)(per / elem_size(dtype)), o_stride = bi.n_sel * H_q * d_h,
+                  l_stride = bi.n_sel * H_q;
+    if (dtype == KVX_BF16) {
+        // the q rows of layer j sit at ws + j * per; the grouped GEMM writes them there
+        KVX_TRY_HIP(run_qkv_rope_scatter_layers(s, l0, n_layers, x, w_qkv, D, H_q, H_kv, d_h, rope, batch, bi, sel,
+                                                cache, ws, q_stride), "recompute_attn_layers qkv/rope/scatter");
+        return hip_status(run_attention(s, dtype, l0, ws, H_q, H_kv, d_h, rope, batch, bi, sel, cache, out, lse,
+                                        nullptr, LayerSpan{n_layers, q_stride, o_stride, l_stride}),
+                          "recompute_attn_layers attention");
+    }
+    for (int j = 0; j < n_layers; ++j) {
+        void* q = (char*)ws + j * per;
+        KVX_TRY_HIP(run_qkv_rope_scatter(s, dtype, l0 + j, (const float*)x + (int64_t)j * bi.n_tokens * D,
+                                         (const float*)w_qkv + (int64_t)j * n_qkv * D, D, H_q, H_kv, d_h, rope,
+                                         batch, bi, sel, cache, q, nullptr), "recompute_attn_layers qkv");
+        KVX_TRY_HIP(run_attention(s, dtype, l0 + j, q, H_q, H_kv, d_h, rope, batch, bi, sel, cache,
+                                  (float*)out + j * o_stride, lse ? lse + j * l_stride : nullptr, nullptr),
+                    "recompute_attn_layers attention");
+    }
+    return ok();
 }
 
 kvx_status kvx_gather_rows(void* stream, int32_t dtype, const void* src, int32_t D, const kvx_batch* batch,

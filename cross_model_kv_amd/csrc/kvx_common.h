@@ -125,6 +125,10 @@ struct GemmArgs {
     const bf16* A; int64_t lda; int32_t K_a;
     const bf16* B; int64_t ldb; int64_t b_group_stride;
     int32_t M, N, K, groups;
+    // independent groups (a_group_stride != 0, EPI_QKV): group g reads its own A rows at
+    // A + g * a_group_stride and writes its q columns at C + g * c_group_stride and its K/V into
+    // cache layer g (kc, vc + g * layer_elems); the tiles run group by group
+    int64_t a_group_stride; int64_t c_group_stride;
     RowMap rows;
     int32_t epi;
     // EPI_STORE (and EPI_F32: C32[m][n] = acc in fp32, leading dimension ldc)

@@ -69,6 +69,10 @@ struct AttnArgs {
     // i * H_q + h, l = 0 for rows without keys in it; a combine kernel merges the chunks of those
     // rows only.  n_split = 1: no split, no partials.
     int n_split; int split_len; float* part; float* part_ml; int64_t n_rows_total;
+    // several layers in one launch (bf16, n_split = 1): workgroups run layer by layer; layer j
+    // reads its q columns at qkv + j * q_layer_stride and the cache at kc, vc + j * kv_layer_elems,
+    // and writes out + j * out_layer_stride, lse + j * lse_layer_stride (elements)
+    int n_layers; int64_t q_layer_stride, kv_layer_elems, out_layer_stride, lse_layer_stride;
     int32_t blk_cu[MAX_ATTN_REQ + 1];  // blk_cu[b] = sum_{b' < b} ceil(k_b' / bq)
 };
 // chunks per query block for the key-range split: round(1.25 * 256 / workgroups) (none when the

@@ -1,10 +1,13 @@
 """One cross-model KV handoff on the GPU: buffers and the call order of the C ABI.
 
-map_latent -> score_select -> reconstruct(complement rows) -> per target layer
-recompute_attn.  Selection runs before reconstruction because the score needs only the
-latent; the selected rows are then left for recompute_attn to write, so reconstruction
+map_latent -> score_select -> reconstruct(complement rows) -> recompute_attn_layers over
+chunks of target layers.  Selection runs before reconstruction because the score needs only
+the latent; the selected rows are then left for the recomputation to write, so reconstruction
 computes the complement only (the translated values it would write there are overwritten
-before anything reads them).  No arithmetic happens here.
+before anything reads them).  Every layer recomputes from its own given input rows, so the
+layers are independent and a chunk of them runs as one projection launch and one attention
+launch (chunks sized so that their q rows stay within LAYER_WS_BYTES).  No arithmetic
+happens here.
 """
 from __future__ import annotations
 
@@ -14,6 +17,18 @@ import torch
 
 from . import kvx
 from .synth import ChainWeights, Inputs
+
+
+LAYER_WS_BYTES = 1 << 30      # q rows of one chunk of layers
+
+
+def layer_chunks(L: int, per_layer_bytes: int):
+    """Chunks [(l0, n)] covering L layers: as few as keep n * per_layer_bytes <= LAYER_WS_BYTES,
+    with sizes as equal as possible."""
+    lc = max(1, min(L, LAYER_WS_BYTES // max(per_layer_bytes, 1)))
+    n_chunks = -(-L // lc)
+    sizes = [L // n_chunks + (1 if i < L % n_chunks else 0) for i in range(n_chunks)]
+    return [(sum(sizes[:i]), n) for i, n in enumerate(sizes)]
 
 
 class Handoff:
@@ -46,7 +61,14 @@ class Handoff:
                                          page_table=inp.page_table, page_size=wl.page_size)
         else:
             self.cache = kvx.Cache.empty(wl.L_t, N, wl.H_kv, wl.d_h, dt, self.device)
-        n_out = wl.L_t if keep_all_outputs else 1
+        dti = kvx._dtype(self.z)
+        per_layer = kvx.recompute_attn_layers_workspace(dti, self.batch, wl.D, wl.H_q, wl.H_kv, wl.d_h, 1)
+        self.chunks = layer_chunks(wl.L_t, per_layer)
+        lc = max(n for _, n in self.chunks)
+        self.ws_layers_bytes = max(per_layer * lc, 16)
+        self.ws_layers = None          # allocated on first use
+        self.keep_all = keep_all_outputs
+        n_out = wl.L_t if keep_all_outputs else lc
         k = max(self.batch.total_sel, 1)
         self.out = torch.empty((n_out, k, wl.H_q, wl.d_h), dtype=dt, device=self.device)
         self.lse = torch.empty((n_out, k, wl.H_q), dtype=torch.float32, device=self.device)
@@ -64,18 +86,37 @@ class Handoff:
         kvx.reconstruct(self.z, self.inp.w_l, self.wl.H_kv, self.wl.d_h, self.batch, self.cache, rows=rows)
 
     def recompute(self, layer: int):
+        """One layer through the single-layer entry point (output slot 0 unless all are kept)."""
         wl = self.wl
-        slot = layer if self.out.shape[0] > 1 else 0
+        slot = layer if self.keep_all else 0
         kvx.recompute_attn(layer, self.inp.x_l[layer], self.inp.w_qkv[layer], wl.H_q, wl.H_kv, wl.d_h,
                            self.rope, self.batch, self.sel[:self.batch.total_sel], self.cache,
                            out=self.out[slot], lse=self.lse[slot], ws=self.ws_attn)
+
+    def recompute_layers(self, l0: int, n: int):
+        """Layers l0 .. l0 + n - 1 in one call (outputs at their layers, or slots 0 .. n - 1).  A
+        chunk of one layer takes the single-layer entry point, whose workspace lets it split
+        the last round of projection tiles and the keys of too few query blocks."""
+        wl = self.wl
+        if n == 1:
+            slot = l0 if self.keep_all else 0
+            kvx.recompute_attn(l0, self.inp.x_l[l0], self.inp.w_qkv[l0], wl.H_q, wl.H_kv, wl.d_h, self.rope,
+                               self.batch, self.sel[:self.batch.total_sel], self.cache, out=self.out[slot],
+                               lse=self.lse[slot], ws=self.ws_attn)
+            return
+        s0 = l0 if self.keep_all else 0
+        if self.ws_layers is None:
+            self.ws_layers = torch.empty(self.ws_layers_bytes, dtype=torch.uint8, device=self.device)
+        kvx.recompute_attn_layers(l0, self.inp.x_l[l0:l0 + n], self.inp.w_qkv[l0:l0 + n], wl.H_q, wl.H_kv, wl.d_h,
+                                  self.rope, self.batch, self.sel[:self.batch.total_sel], self.cache,
+                                  out=self.out[s0:s0 + n], lse=self.lse[s0:s0 + n], ws=self.ws_layers)
 
     def run(self, all_rows: bool = False):
         self.map()
         self.select()
         self.reconstruct(all_rows)
-        for l in range(self.wl.L_t):
-            self.recompute(l)
+        for l0, n in self.chunks:
+            self.recompute_layers(l0, n)
 
     # views --------------------------------------------------------------------------
     @property
@@ -109,7 +150,7 @@ class ChainedHandoff(Handoff):
 
     def chain_layer(self, layer: int):
         wl = self.wl
-        slot = layer if self.out.shape[0] > 1 else 0
+        slot = layer if self.keep_all else 0
         kvx.target_layer(layer, self.x, self.layers[layer], wl.F, wl.H_q, wl.H_kv, wl.d_h, wl.norm_eps, self.rope,
                          self.batch, self.S, self.cache, attn_out=self.out[slot], lse=self.lse[slot],
                          ws=self.ws_layer)

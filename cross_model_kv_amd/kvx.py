@@ -81,6 +81,14 @@ _SIGS = {
                             ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P, _P, _P, _SZ], _I32),
     "kvx_qkv_project": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P, _P, _P, _SZ],
                         _I32),
+    "kvx_recompute_attn_layers_workspace": ([_I32, ctypes.POINTER(_Batch), _I32, _I32, _I32, _I32, _I32,
+                                             ctypes.POINTER(_SZ)], _I32),
+    "kvx_recompute_attn_layers": ([_P, _I32, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
+                                   ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P, _P, _P, _SZ], _I32),
+    "kvx_qkv_rope_scatter_layers": ([_P, _I32, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
+                                     ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P], _I32),
+    "kvx_sparse_attention_layers": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch),
+                                     _P, ctypes.POINTER(_Cache), _P, _P], _I32),
     "kvx_rope_scatter": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
                           ctypes.POINTER(_Cache)], _I32),
     "kvx_qkv_rope_scatter": ([_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch),
@@ -471,6 +479,63 @@ def sparse_attention(layer: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: in
         _stream(qkv.device), dt, layer, _ptr(qkv), H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
         ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(out), _ptr(lse),
         _ptr(ws) if need else None, ws.numel() if need else 0))
+    return out
+
+
+def recompute_attn_layers_workspace(dtype: int, batch: Batch, D: int, H_q: int, H_kv: int, d_h: int,
+                                    n_layers: int) -> int:
+    b = _SZ()
+    _check("kvx_recompute_attn_layers_workspace",
+           lib().kvx_recompute_attn_layers_workspace(dtype, ctypes.byref(batch.c), D, H_q, H_kv, d_h, n_layers,
+                                                     ctypes.byref(b)))
+    return b.value
+
+
+def recompute_attn_layers(l0: int, x: torch.Tensor, w_qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int,
+                          rope: torch.Tensor, batch: Batch, sel: torch.Tensor, cache: Cache,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvx_recompute_attn of layers l0 .. l0 + n - 1 in one call: x [n, N, D], w_qkv [n, n_qkv, D];
+    returns out [n, total_sel, H_q, d_h]."""
+    dev = x.device
+    dt = _dtype(x)
+    n, _, D = x.shape
+    need = recompute_attn_layers_workspace(dt, batch, D, H_q, H_kv, d_h, n)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((n, max(batch.total_sel, 1), H_q, d_h), dtype=x.dtype, device=dev)
+    _check("kvx_recompute_attn_layers", lib().kvx_recompute_attn_layers(
+        _stream(dev), dt, l0, n, _ptr(x), _ptr(w_qkv), D, H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
+        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(out), _ptr(lse),
+        _ptr(ws), ws.numel()))
+    return out
+
+
+def qkv_rope_scatter_layers(l0: int, x: torch.Tensor, w_qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int,
+                            rope: torch.Tensor, batch: Batch, sel: torch.Tensor, cache: Cache,
+                            qkv: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Steps 1-3 of layers l0 .. l0 + n - 1 in one launch; returns qkv [n, total_sel, n_qkv] (q columns)."""
+    dev = x.device
+    n, _, D = x.shape
+    n_qkv = (H_q + 2 * H_kv) * d_h
+    if qkv is None:
+        qkv = torch.empty((n, max(batch.total_sel, 1), n_qkv), dtype=x.dtype, device=dev)
+    _check("kvx_qkv_rope_scatter_layers", lib().kvx_qkv_rope_scatter_layers(
+        _stream(dev), _dtype(x), l0, n, _ptr(x), _ptr(w_qkv), D, H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
+        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(qkv)))
+    return qkv
+
+
+def sparse_attention_layers(l0: int, qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int, rope: torch.Tensor,
+                            batch: Batch, sel: torch.Tensor, cache: Cache, out: torch.Tensor,
+                            lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal attention of layers l0 .. l0 + n - 1 in one launch: qkv [n, total_sel, n_qkv],
+    out [n, total_sel, H_q, d_h], lse [n, total_sel, H_q] or None."""
+    n = qkv.shape[0]
+    _check("kvx_sparse_attention_layers", lib().kvx_sparse_attention_layers(
+        _stream(qkv.device), _dtype(qkv), l0, n, _ptr(qkv), H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
+        ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(out), _ptr(lse)))
     return out
 
 

@@ -330,6 +330,42 @@ KVX_API kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t lay
                                         const int32_t* sel, const kvx_cache* cache, void* out,
                                         float* lse, void* ws, size_t ws_bytes);
 
+/* Several target layers in one call: kvx_recompute_attn of layers l0 .. l0 + n_layers - 1
+ * (PANORAMA abstract, as above), for the path where every layer recomputes from its own given
+ * input rows (x of each layer known up front).  Each layer's attention still reads its cache
+ * layer only after all of that layer's k and v are written; layers are independent, so the
+ * projections of all n_layers run as one grouped launch and the attentions as another, which
+ * fills the GPU when one layer's work would not (few selected positions).
+ *   x (device) [n_layers][N][D] (layer j's input at x + j N D); w_qkv (device)
+ *   [n_layers][n_qkv][D]; out (device, out) [n_layers][cu_sel[n_req]][H_q][d_h]; lse (device,
+ *   out, nullable) [n_layers][cu_sel[n_req]][H_q]; l0 + n_layers <= cache->n_layers; the
+ *   other arguments as in kvx_recompute_attn.
+ *   No K split in the projections and no key-range split in the attention (bf16): each layer's
+ *   results equal, bit for bit, kvx_qkv_rope_scatter and kvx_sparse_attention of that layer
+ *   called without workspaces.  fp32: the single-layer kernels, layer by layer.
+ *   ws (device) of kvx_recompute_attn_layers_workspace() bytes: the qkv rows of every layer.
+ * kvx_qkv_rope_scatter_layers / kvx_sparse_attention_layers: the two launches apart (no
+ *   workspace); qkv (device) [n_layers][cu_sel[n_req]][n_qkv], only the q columns written. */
+KVX_API kvx_status kvx_recompute_attn_layers_workspace(int32_t dtype, const kvx_batch* batch, int32_t D,
+                                                       int32_t H_q, int32_t H_kv, int32_t d_h,
+                                                       int32_t n_layers, size_t* bytes);
+KVX_API kvx_status kvx_recompute_attn_layers(void* stream, int32_t dtype, int32_t l0, int32_t n_layers,
+                                             const void* x, const void* w_qkv, int32_t D, int32_t H_q,
+                                             int32_t H_kv, int32_t d_h, const float* rope,
+                                             int32_t max_pos, const kvx_batch* batch,
+                                             const int32_t* sel, const kvx_cache* cache, void* out,
+                                             float* lse, void* ws, size_t ws_bytes);
+KVX_API kvx_status kvx_qkv_rope_scatter_layers(void* stream, int32_t dtype, int32_t l0, int32_t n_layers,
+                                               const void* x, const void* w_qkv, int32_t D, int32_t H_q,
+                                               int32_t H_kv, int32_t d_h, const float* rope,
+                                               int32_t max_pos, const kvx_batch* batch,
+                                               const int32_t* sel, const kvx_cache* cache, void* qkv);
+KVX_API kvx_status kvx_sparse_attention_layers(void* stream, int32_t dtype, int32_t l0, int32_t n_layers,
+                                               const void* qkv, int32_t H_q, int32_t H_kv, int32_t d_h,
+                                               const float* rope, int32_t max_pos,
+                                               const kvx_batch* batch, const int32_t* sel,
+                                               const kvx_cache* cache, void* out, float* lse);
+
 /* ---------------------------------------------------------------------------------------
  * Target layer chaining (bf16 only; KVX_ERR_UNSUPPORTED for KVX_F32).  PANORAMA abstract:
  * the recomputed positions let the target model's own computation use the translated
