@@ -1,6 +1,8 @@
 // Sparse-query causal GQA flash attention for gfx950 (bf16 storage, fp32 softmax/accumulate).
 //
-// A workgroup serves one KV head of one block of consecutive selected queries of a request:
+// A workgroup serves one KV head of one block of consecutive selected queries of a request (a
+// request's first block holds the remainder of its queries over the block size, so the partly
+// filled block is the one with the fewest key tiles):
 // rows = (query, head) pairs for the g = H_q / H_kv query heads that share the KV head, 32
 // rows per wave.  The block walks the request's mixed cache in 64-key tiles up to the
 // position of its last query; each row masks keys beyond its own position (inclusive).
@@ -99,8 +101,12 @@ void attn_bf16_kernel(AttnArgs a) {
         b = lo;
     }
     const int ks0 = a.cu_sel[b], k_b = a.cu_sel[b + 1] - ks0;
-    const int qi0 = (qb - a.blk_cu[b]) * a.bq;
-    const int nq = min(a.bq, k_b - qi0);
+    // request b's first block takes the remainder k_b - (blocks - 1) * bq, the others bq each: the
+    // partly filled block is the one with the fewest key tiles
+    const int jb = qb - a.blk_cu[b];
+    const int first = k_b - (a.blk_cu[b + 1] - a.blk_cu[b] - 1) * a.bq;
+    const int qi0 = jb == 0 ? 0 : first + (jb - 1) * a.bq;
+    const int nq = jb == 0 ? first : a.bq;
     const int i0 = ks0 + qi0;
     const int T_b = a.slots.cu_tok[b + 1] - a.slots.cu_tok[b];
     const int p_max = a.sel[i0 + nq - 1];
@@ -477,7 +483,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, co
         b = lo;
     }
     const int qi = i - cu_sel[b];
-    const int last = min(cu_sel[b] + (qi / bq + 1) * bq, cu_sel[b + 1]) - 1;
+    // the row's block (the request's first block holds the remainder of k_b over bq): its last query
+    const int k_b = cu_sel[b + 1] - cu_sel[b];
+    const int first = k_b - ((k_b + bq - 1) / bq - 1) * bq;
+    const int last = cu_sel[b] + (qi < first ? first : first + ((qi - first) / bq + 1) * bq) - 1;
     const int n_tiles = sel[last] / KT + 1;
     if (n_tiles <= split_len) return;
     const int nch = min((n_tiles + split_len - 1) / split_len, n_split);
