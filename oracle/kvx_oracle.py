@@ -92,6 +92,16 @@ def reconstruct(z: np.ndarray, w_l: np.ndarray, H_kv: int, d_h: int):
     return K, V, Y
 
 
+def reconstruct_rotated(z: np.ndarray, w_l: np.ndarray, H_kv: int, d_h: int, pos: np.ndarray,
+                        base: float):
+    """The reconstruction for a mapper whose keys carry no rotary phase (the other reading of
+    whether translated K is cache-ready; the pages do not say): every translated key head is
+    rotated at its own position, as recomputed keys are, and V is left as it is.
+    pos [N] is each row's position in its request.  Returns K, V [L_t, N, H_kv, d_h], Y."""
+    K, V, Y = reconstruct(z, w_l, H_kv, d_h)
+    return rope(K, np.asarray(pos)[None, :, None], base), V, Y
+
+
 # ------------------------------------------------------------------------------------
 # rank-disagreement score and top-budget selection
 # ------------------------------------------------------------------------------------

@@ -281,6 +281,31 @@ def pin_rope_norm_and_relative():
         assert abs(rq @ rk - rel @ k) < 1e-10
 
 
+def pin_reconstruct_rotated_matrix_form():
+    """Rotated translated keys: every key head of every layer times the block-diagonal plane
+    rotation of its row's position (pair (j, j + d_h/2) by the angle p * base^(-2j/d_h)), built
+    here as explicit 2x2 matrices; V and the mapped vectors as the plain reconstruction."""
+    rng = _rng(70)
+    H_kv, d_h, L, r, N = 2, 6, 3, 5, 7
+    z = rng.standard_normal((N, r))
+    w_l = rng.standard_normal((L, 2 * H_kv * d_h, r))
+    pos = np.array([0, 3, 1, 40, 7, 1000, 2])
+    K, V, Y = O.reconstruct_rotated(z, w_l, H_kv, d_h, pos, 100.0)
+    Y_plain = np.stack([z @ w_l[l].T for l in range(L)])
+    assert np.abs(Y - Y_plain).max() < 1e-12
+    assert np.abs(V - Y_plain[:, :, H_kv * d_h:].reshape(L, N, H_kv, d_h)).max() < 1e-12
+    K_plain = Y_plain[:, :, :H_kv * d_h].reshape(L, N, H_kv, d_h)
+    half = d_h // 2
+    for t in range(N):
+        R = np.zeros((d_h, d_h))
+        for j in range(half):
+            a = pos[t] * 100.0 ** (-2.0 * j / d_h)
+            R[j, j], R[j, j + half] = math.cos(a), -math.sin(a)
+            R[j + half, j], R[j + half, j + half] = math.sin(a), math.cos(a)
+        want = K_plain[:, t] @ R.T
+        assert np.abs(K[:, t] - want).max() < 1e-10
+
+
 def pin_recompute_identity_weights():
     """w_qkv made of identity blocks returns the hidden rows themselves (q, k rotated)."""
     rng = _rng(15)
@@ -926,6 +951,16 @@ RECOMPUTE = O.recompute_qkv
 CHAINED = O.chained_layers
 FIRST_TOKEN = O.first_token
 
+def _mut_reconstruct_rotated_v(z, w_l, H_kv, d_h, pos, base):
+    K, V, Y = O.reconstruct(z, w_l, H_kv, d_h)
+    return K, O.rope(V, np.asarray(pos)[None, :, None], base), Y
+
+
+def _mut_reconstruct_rotated_row_index(z, w_l, H_kv, d_h, pos, base):
+    K, V, Y = O.reconstruct(z, w_l, H_kv, d_h)
+    return O.rope(K, np.arange(len(pos))[None, :, None], base), V, Y
+
+
 MUTANTS = {
     "rope_sign": ("rope", _mut_rope_sign),
     "rope_interleaved": ("rope", _mut_rope_interleaved),
@@ -937,6 +972,8 @@ MUTANTS = {
     "score_one_layer": ("rank_disagreement", _mut_score_one_layer),
     "map_untransposed": ("map_latent", _mut_map_no_transpose),
     "reconstruct_kv_swapped": ("reconstruct", _mut_reconstruct_kv_swapped),
+    "reconstruct_rotated_v": ("reconstruct_rotated", _mut_reconstruct_rotated_v),
+    "reconstruct_rotated_row_index": ("reconstruct_rotated", _mut_reconstruct_rotated_row_index),
     "budget_floor": ("budget", _mut_budget_floor),
     "rmsnorm_no_root": ("rmsnorm", _mut_rmsnorm_no_root),
     "rmsnorm_sum_not_mean": ("rmsnorm", _mut_rmsnorm_sum),
