@@ -624,6 +624,25 @@ def main():
                "frac": round(sc_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": sc_bytes,
                "avg_launch_ms": round(sc_ms, 5)}
 
+    # The reconstruction for a mapper whose keys carry no rotary phase (kvx_reconstruct_rope:
+    # translated keys rotated at their positions in the same GEMM's epilogue), timed on the
+    # step's complement rows beside the plain reconstruction, outside the timed steps.
+    def time_rec(rope_t, reps=5):
+        for _ in range(2):
+            kvx.reconstruct(h.z, inp.w_l, wl.H_kv, wl.d_h, h.batch, h.cache, rows=h.C, rope=rope_t)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(reps):
+            kvx.reconstruct(h.z, inp.w_l, wl.H_kv, wl.d_h, h.batch, h.cache, rows=h.C, rope=rope_t)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        return r0.elapsed_time(r1) / reps
+    rec_plain_ms, rec_rope_ms = time_rec(None), time_rec(h.rope)
+    rec_flops = work["reconstruct"]["flops"]
+    rotated_keys = {"kernel": "reconstruct with rotated translated keys (kvx_reconstruct_rope), outside the timed step",
+                    "ms": round(rec_rope_ms, 5), "tflops": round(rec_flops / (rec_rope_ms * 1e-3) / 1e12, 2),
+                    "plain_ms": round(rec_plain_ms, 5)}
+
     # score GEMM and top-k apart: the score is a dense contraction (matrix cores, executed as
     # 2 T r 2r flops with the hi/lo operator), the top-k a latency-bound pass over T scores
     both_ms, sel_ms = score_select_split(h, stream)
@@ -680,6 +699,7 @@ def main():
         "stages": res["stages"],
         "score_select_split": score_split,
         "scatter_standalone": scatter,
+        "reconstruct_rotated_keys": rotated_keys,
         "graph": graph,
         "measured_peaks": peaks,
     }

@@ -401,6 +401,60 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
         }
         return;
     }
+    if (a.epi == EPI_CACHE && a.rope) {
+        // translated keys rotated at their rows' positions (the key columns [0, hd) of each
+        // layer), with the rounding and rotation order of the fused QKV epilogue: the value is
+        // rounded to bf16, rotated in fp32 with its partner column j +- d_h/2 (held by
+        // lane ^ (d_h/16)), and rounded again; V columns are stored as they are
+        static_assert(FN == 8, "the rotating cache epilogue expects 8 columns per lane");
+        const int half = a.d_h / 2;
+        const int slab0 = n0 + wn * WTN;
+        const bool k_slab = slab0 < a.hd;
+        const bool is_k = ng < a.hd;
+        const int j0 = (ng % a.d_h) % half;
+        const bool lo = (ng % a.d_h) < half;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ml = wm * WTM + i * 16 + 4 * lq + v;
+                float x[8], y[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = (float)(bf16)acc[i][j][v];
+                if (k_slab) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int xi = __float_as_int(x[j]);
+                        const int pi = a.d_h == 128 ? __builtin_amdgcn_update_dpp(0, xi, 0x128, 0xF, 0xF, false)
+                                                    : __shfl_xor(xi, 4);
+                        y[j] = __int_as_float(pi);
+                    }
+                }
+                if (s_src[ml] < 0) continue;
+                bf16x8 o;
+                if (is_k) {
+                    const float4* cs = (const float4*)(a.rope + ((int64_t)s_pos[ml] * half + j0) * 2);
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) {
+                        const float4 t2 = cs[j2];
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int j = 2 * j2 + u;
+                            const float c = u ? t2.z : t2.x, sn = u ? t2.w : t2.y;
+                            o[j] = (bf16)(lo ? rope_lo(x[j], y[j], c, sn) : rope_hi(y[j], x[j], c, sn));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) o[j] = (bf16)x[j];
+                }
+                bf16* dst = (is_k ? a.kc : a.vc) + (int64_t)t.group * a.layer_elems + s_slot[ml] * a.hd +
+                            (is_k ? ng : ng - a.hd);
+                *(bf16x8*)dst = o;
+            }
+        }
+        return;
+    }
     typedef __bf16 vecN __attribute__((ext_vector_type(FN)));
 #pragma unroll
     for (int i = 0; i < FM; ++i) {

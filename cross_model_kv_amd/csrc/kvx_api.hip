@@ -556,10 +556,15 @@ kvx_status kvx_score_select_noalloc(void* stream, int32_t dtype, const void* z, 
     return run_score_select((hipStream_t)stream, dtype, z, op, r, batch, bi, scores, sel, rest, ws);
 }
 
-kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t L_t,
-                           int32_t r, int32_t H_kv, int32_t d_h, const kvx_batch* batch,
+}  // extern "C"
+
+namespace {
+
+// Reconstruction of the listed rows (all rows when rows is null) into every layer's cache; with
+// rope set (bf16 only) the key columns are rotated at their rows' positions on the way.
+kvx_status run_reconstruct(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t L_t, int32_t r,
+                           int32_t H_kv, int32_t d_h, const float* rope, const kvx_batch* batch,
                            const int32_t* rows, const kvx_cache* cache) {
-    if (kvx_status st = check_dtype(dtype)) return st;
     BatchInfo bi;
     if (kvx_status st = check_batch(batch, &bi)) return st;
     KVX_REQUIRE_PTR(z, "z");
@@ -591,6 +596,7 @@ kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const voi
         a.epi = EPI_CACHE;
         a.kc = (bf16*)cache->k; a.vc = (bf16*)cache->v;
         a.layer_elems = cache->n_slots * hd; a.hd = hd; a.slots = slot_map(cache, batch);
+        a.rope = rope; a.d_h = d_h;
         return hip_status(launch_gemm_bf16(a, s), "reconstruct");
     }
     GemmF32Args a{};
@@ -602,6 +608,30 @@ kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const voi
     a.kc = (float*)cache->k; a.vc = (float*)cache->v;
     a.layer_elems = cache->n_slots * hd; a.hd = hd; a.slots = slot_map(cache, batch);
     return hip_status(launch_gemm_f32(a, s), "reconstruct");
+}
+
+}  // namespace
+
+extern "C" {
+
+kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t L_t,
+                           int32_t r, int32_t H_kv, int32_t d_h, const kvx_batch* batch,
+                           const int32_t* rows, const kvx_cache* cache) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    return run_reconstruct(stream, dtype, z, w_l, L_t, r, H_kv, d_h, nullptr, batch, rows, cache);
+}
+
+kvx_status kvx_reconstruct_rope(void* stream, int32_t dtype, const void* z, const void* w_l, int32_t L_t,
+                                int32_t r, int32_t H_kv, int32_t d_h, const float* rope, int32_t max_pos,
+                                const kvx_batch* batch, const int32_t* rows, const kvx_cache* cache) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    if (dtype != KVX_BF16) return fail(KVX_ERR_UNSUPPORTED, "reconstruct_rope supports KVX_BF16 only");
+    if (d_h != 64 && d_h != 128) return fail(KVX_ERR_UNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+    KVX_REQUIRE_PTR(rope, "rope");
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(max_pos >= bi.max_T, "rope table has %d positions, the longest request %d", max_pos, bi.max_T);
+    return run_reconstruct(stream, dtype, z, w_l, L_t, r, H_kv, d_h, rope, batch, rows, cache);
 }
 
 kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_t max_pos, float* table) {

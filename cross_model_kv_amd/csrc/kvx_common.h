@@ -141,7 +141,8 @@ struct GemmArgs {
     float* split_ws;
     // EPI_QKV (the gathered QKV projection of one layer): columns [0, q_cols) go to C like a
     // store; the K columns are rounded to bf16, rotated (rotate-half, table rope at the row's
-    // position) and written with the V columns to the layer's cache slots (kc, vc, hd, slots)
+    // position) and written with the V columns to the layer's cache slots (kc, vc, hd, slots).
+    // EPI_CACHE with rope set: the K columns [0, hd) rotated the same way before they are stored
     const float* rope; int32_t q_cols; int32_t d_h;
     // EPI_RESID: C[m][n] = R[m][n] + acc (C may be R: every element is read, then written, by
     // one thread)

@@ -70,6 +70,8 @@ _SIGS = {
                        _I32),
     "kvx_fit_calibration_workspace": ([_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_fit_calibration": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ], _I32),
+    "kvx_reconstruct_rope": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
+                              ctypes.POINTER(_Cache)], _I32),
     "kvx_reconstruct": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P,
                          ctypes.POINTER(_Cache)], _I32),
     "kvx_rope_table": ([_P, ctypes.c_double, _I32, _I32, _P], _I32),
@@ -350,7 +352,9 @@ def fit_calibration(z: torch.Tensor, w_l: torch.Tensor, c: int, iters: int = 30)
 
 
 def reconstruct(z: torch.Tensor, w_l: torch.Tensor, H_kv: int, d_h: int, batch: Batch, cache: Cache,
-                rows: Optional[torch.Tensor] = None):
+                rows: Optional[torch.Tensor] = None, rope: Optional[torch.Tensor] = None):
+    """Translated K/V of the listed rows (all rows when rows is None) into every layer's cache;
+    with a rotary table the keys are rotated at their positions (kvx_reconstruct_rope)."""
     L_t, _, r = w_l.shape
     if rows is None:
         rp = None                                   # every position
@@ -358,6 +362,11 @@ def reconstruct(z: torch.Tensor, w_l: torch.Tensor, H_kv: int, d_h: int, batch: 
         rp = _ptr(_placeholder(z.device))           # an empty list: nothing to reconstruct
     else:
         rp = _ptr(rows)
+    if rope is not None:
+        _check("kvx_reconstruct_rope", lib().kvx_reconstruct_rope(
+            _stream(z.device), _dtype(z), _ptr(z), _ptr(w_l), L_t, r, H_kv, d_h, _ptr(rope), rope.shape[0],
+            ctypes.byref(batch.c), rp, ctypes.byref(cache.c)))
+        return
     _check("kvx_reconstruct", lib().kvx_reconstruct(_stream(z.device), _dtype(z), _ptr(z), _ptr(w_l), L_t, r,
                                                     H_kv, d_h, ctypes.byref(batch.c), rp,
                                                     ctypes.byref(cache.c)))

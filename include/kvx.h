@@ -239,6 +239,19 @@ KVX_API kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, c
                            const kvx_batch* batch, const int32_t* rows,
                            const kvx_cache* cache);
 
+/* kvx_reconstruct for a mapper whose keys carry no rotary phase (the pages do not say whether
+ * translated keys are cache-ready; kvx_reconstruct takes them as they are): every key head of
+ * every layer is rotated at its row's position as recomputed keys are (rotate-half, pair
+ * (j, j + d_h/2) by angle p * base^(-2j/d_h), the table of kvx_rope_table), V unchanged:
+ *   K_l[slot(b,p)] = rope(y[0 : H_kv d_h], p) head by head,  V_l[slot(b,p)] = y[H_kv d_h : ].
+ * Each key value is rounded to bf16, rotated in fp32 with its partner and rounded again (the
+ * order of the fused QKV projection).  bf16 only (KVX_ERR_UNSUPPORTED for KVX_F32); d_h 64 or
+ * 128; rope (device) with max_pos >= every T_b; other arguments as in kvx_reconstruct. */
+KVX_API kvx_status kvx_reconstruct_rope(void* stream, int32_t dtype, const void* z, const void* w_l,
+                                        int32_t L_t, int32_t r, int32_t H_kv, int32_t d_h,
+                                        const float* rope, int32_t max_pos, const kvx_batch* batch,
+                                        const int32_t* rows, const kvx_cache* cache);
+
 /* Rotary table for positions [0, max_pos): table[p][j] = (cos, sin)(p * base^(-2j/d_h)),
  * j < d_h/2, angles formed in fp64, stored fp32.  table (device, out) [max_pos][d_h/2][2]. */
 KVX_API kvx_status kvx_rope_table(void* stream, double base, int32_t d_h, int32_t max_pos,

@@ -201,6 +201,18 @@ def test_reconstruct_validation():
            INVALID, "rows")
 
 
+def test_reconstruct_rope_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    c = cache()
+    args = lambda dt=1, d_h=64, rope=A16B, max_pos=100: (None, dt, A16, A16, 2, 128, 2, d_h, rope, max_pos,
+                                                          ctypes.byref(bt.c), None, ctypes.byref(c))
+    status(L.kvx_reconstruct_rope(*args(dt=0)), UNSUPPORTED, "BF16")
+    status(L.kvx_reconstruct_rope(*args(d_h=96)), UNSUPPORTED, "d_h")
+    status(L.kvx_reconstruct_rope(*args(rope=None)), INVALID, "rope")
+    status(L.kvx_reconstruct_rope(*args(max_pos=99)), INVALID, "positions")
+
+
 def test_rope_table_validation():
     L = kvx.lib()
     status(L.kvx_rope_table(None, 10000.0, 7, 10, A16), INVALID, "even")
