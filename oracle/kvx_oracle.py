@@ -123,6 +123,20 @@ def rank_disagreement(Y: np.ndarray, u: np.ndarray) -> np.ndarray:
     return s
 
 
+def rank_disagreement_normalized(Y: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """The score as a share instead of an energy (an unranked variant of the RaReCache abstract's
+    score; the pages do not say which): the energy of a token's mapped KV outside the calibration
+    subspaces divided by the energy of all of its mapped KV, both summed over the target layers,
+    so the score lies in [0, 1] and does not grow with the size of the vectors.  A token whose
+    mapped KV is zero in every layer scores 0.  Y [L_t, N, d_t], u [L_t, d_t, c]."""
+    outside = rank_disagreement(Y, u)
+    total = np.sum(Y * Y, axis=(0, 2))
+    out = np.zeros_like(outside)
+    nz = total > 0
+    out[nz] = outside[nz] / total[nz]
+    return out
+
+
 def select(s: np.ndarray, k: int):
     """The k positions with the largest score; ties go to the lower position.
 

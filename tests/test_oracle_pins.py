@@ -632,6 +632,37 @@ def pin_first_token_full_budget_is_last_dense_row():
     assert np.abs(K - full["K"]).max() < 1e-12 and np.abs(V - full["V"]).max() < 1e-12
 
 
+def pin_score_normalized_angle():
+    """One layer, d_t = 2, span(U) the first axis: a vector at angle a to that axis scores sin^2(a)
+    whatever its length; a second layer adds its energies to both sums."""
+    u = np.array([[[1.0], [0.0]]])
+    for a, rad in ((0.0, 2.0), (0.3, 1.0), (math.pi / 4, 5.0), (1.2, 0.01), (math.pi / 2, 3.0)):
+        Y = np.array([[[rad * math.cos(a), rad * math.sin(a)]]])
+        assert abs(O.rank_disagreement_normalized(Y, u)[0] - math.sin(a) ** 2) < 1e-12
+    u2 = np.stack([u[0], u[0]])
+    Y2 = np.array([[[3.0, 4.0]], [[0.0, 0.0]]])          # second layer empty: same as one layer
+    assert abs(O.rank_disagreement_normalized(Y2, u2)[0] - 16.0 / 25.0) < 1e-12
+    Y3 = np.array([[[3.0, 4.0]], [[1.0, 0.0]]])          # (16) / (25 + 1)
+    assert abs(O.rank_disagreement_normalized(Y3, u2)[0] - 16.0 / 26.0) < 1e-12
+    assert O.rank_disagreement_normalized(np.zeros((2, 1, 2)), u2)[0] == 0.0
+
+
+def pin_score_normalized_bounds_and_scale():
+    rng = _rng(71)
+    L, N, d_t, c = 3, 40, 8, 3
+    Y = rng.standard_normal((L, N, d_t))
+    u = np.stack([np.linalg.qr(rng.standard_normal((d_t, c)))[0] for _ in range(L)])
+    s = O.rank_disagreement_normalized(Y, u)
+    assert np.all(s >= 0) and np.all(s <= 1)
+    scale = rng.uniform(0.1, 10.0, N)                    # per-token scaling leaves the share alone
+    assert np.abs(O.rank_disagreement_normalized(Y * scale[None, :, None], u) - s).max() < 1e-12
+    # in-span tokens score 0, tokens orthogonal to every span score 1
+    Yin = np.stack([rng.standard_normal((N, c)) @ u[l].T for l in range(L)])
+    assert np.abs(O.rank_disagreement_normalized(Yin, u)).max() < 1e-12
+    Yout = np.stack([Y[l] - (Y[l] @ u[l]) @ u[l].T for l in range(L)])
+    assert np.abs(O.rank_disagreement_normalized(Yout, u) - 1.0).max() < 1e-12
+
+
 def pin_score_gap_hand():
     # scores 5, 3, 3, 1 (shuffled): the gap after the k-th largest, relative to it, worked by hand
     s = np.array([3.0, 1.0, 5.0, 3.0])
@@ -961,6 +992,22 @@ def _mut_reconstruct_rotated_row_index(z, w_l, H_kv, d_h, pos, base):
     return O.rope(K, np.arange(len(pos))[None, :, None], base), V, Y
 
 
+def _mut_normalized_by_span(Y, u):
+    outside = O.rank_disagreement(Y, u)
+    inside = np.sum(Y * Y, axis=(0, 2)) - outside
+    return np.where(inside > 0, outside / np.where(inside > 0, inside, 1.0), 0.0)
+
+
+def _mut_normalized_mean_of_layers(Y, u):
+    L = Y.shape[0]
+    acc = np.zeros(Y.shape[1])
+    for l in range(L):
+        tot = np.sum(Y[l] * Y[l], axis=1)
+        res = O.rank_disagreement(Y[l:l + 1], u[l:l + 1])
+        acc += np.where(tot > 0, res / np.where(tot > 0, tot, 1.0), 0.0)
+    return acc / L
+
+
 MUTANTS = {
     "rope_sign": ("rope", _mut_rope_sign),
     "rope_interleaved": ("rope", _mut_rope_interleaved),
@@ -970,6 +1017,8 @@ MUTANTS = {
     "select_ties_high_index": ("select", _mut_select_high_index),
     "score_projection_energy": ("rank_disagreement", _mut_score_projection),
     "score_one_layer": ("rank_disagreement", _mut_score_one_layer),
+    "normalized_by_span_energy": ("rank_disagreement_normalized", _mut_normalized_by_span),
+    "normalized_mean_of_layer_shares": ("rank_disagreement_normalized", _mut_normalized_mean_of_layers),
     "map_untransposed": ("map_latent", _mut_map_no_transpose),
     "reconstruct_kv_swapped": ("reconstruct", _mut_reconstruct_kv_swapped),
     "reconstruct_rotated_v": ("reconstruct_rotated", _mut_reconstruct_rotated_v),
