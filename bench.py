@@ -638,6 +638,20 @@ def main():
         torch.cuda.synchronize()
         return r0.elapsed_time(r1) / reps
     rec_plain_ms, rec_rope_ms = time_rec(None), time_rec(h.rope)
+    # the normalized score (outside energy over total energy: two score GEMMs, one select) on
+    # the step's latent, outside the timed steps
+    op_tot = kvx.score_prepare(inp.w_l, inp.u[:, :, :0])
+    nbuf = (torch.empty_like(h.scores), torch.empty_like(h.sel), torch.empty_like(h.rest))
+    for _ in range(2):
+        kvx.score_select_normalized(h.z, h.op, op_tot, h.batch, inp.pcts, out=nbuf)
+    n0, n1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n0.record(stream)
+    for _ in range(10):
+        kvx.score_select_normalized(h.z, h.op, op_tot, h.batch, inp.pcts, out=nbuf)
+    n1.record(stream)
+    torch.cuda.synchronize()
+    normalized = {"kernel": "score_select_normalized (two score GEMMs and one select), outside the timed step",
+                  "ms": round(n0.elapsed_time(n1) / 10, 5)}
     rec_flops = work["reconstruct"]["flops"]
     rotated_keys = {"kernel": "reconstruct with rotated translated keys (kvx_reconstruct_rope), outside the timed step",
                     "ms": round(rec_rope_ms, 5), "tflops": round(rec_flops / (rec_rope_ms * 1e-3) / 1e12, 2),
@@ -700,6 +714,7 @@ def main():
         "score_select_split": score_split,
         "scatter_standalone": scatter,
         "reconstruct_rotated_keys": rotated_keys,
+        "score_select_normalized": normalized,
         "graph": graph,
         "measured_peaks": peaks,
     }

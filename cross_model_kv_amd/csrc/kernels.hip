@@ -137,6 +137,7 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partial, int n_part,
+                                                            const float* partial2, int n_part2,
                                                             int64_t n_rows, float* scores,
                                                             const int32_t* cu_tok,
                                                             const int32_t* cu_sel, int32_t* sel,
@@ -153,10 +154,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
     int32_t* so = sel + cu_sel[b];
     int32_t* ro = rest + (base - cu_sel[b]);
 
+    // the score: the sum of the partials, or (n_part2 > 0) that sum over the sum of partial2's
+    // partials (0 where the denominator is 0), each sum in partial order
     auto score_at = [&](int t) -> float {
         if (n_part == 0) return scores[base + t];
         float s = 0.f;
         for (int p = 0; p < n_part; ++p) s += partial[(int64_t)p * n_rows + base + t];
+        if (n_part2 > 0) {
+            float d = 0.f;
+            for (int p = 0; p < n_part2; ++p) d += partial2[(int64_t)p * n_rows + base + t];
+            s = d > 0.f ? s / d : 0.f;
+        }
         return s;
     };
     const bool in_lds = T <= SEL_CAP;
@@ -674,10 +682,10 @@ hipError_t launch_pack_operator(const double* A, int r, int dtype, void* op, hip
 
 hipError_t launch_select(const float* partial, int n_part, int64_t n_rows, float* scores,
                          const int32_t* cu_tok, const int32_t* cu_sel, int n_req, int32_t* sel,
-                         int32_t* rest, hipStream_t s) {
+                         int32_t* rest, hipStream_t s, const float* partial2, int n_part2) {
     if (n_req == 0) return hipSuccess;
-    hipLaunchKernelGGL(select_kernel, dim3(n_req), dim3(SEL_THREADS), 0, s, partial, n_part, n_rows,
-                       scores, cu_tok, cu_sel, sel, rest);
+    hipLaunchKernelGGL(select_kernel, dim3(n_req), dim3(SEL_THREADS), 0, s, partial, n_part, partial2, n_part2,
+                       n_rows, scores, cu_tok, cu_sel, sel, rest);
     return hipGetLastError();
 }
 

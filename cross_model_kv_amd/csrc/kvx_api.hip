@@ -462,12 +462,11 @@ kvx_status check_score_select(int32_t dtype, const void* z, const void* op, int3
     return KVX_OK;
 }
 
-// Score GEMM (bf16: per-256-column-block partial sums of z^T A z in ws; fp32: P = z A and the
-// row dots in ws) and the top-k.  Every byte of ws that is read was written by this call.
-kvx_status run_score_select(hipStream_t s, int32_t dtype, const void* z, const void* op, int32_t r,
-                            const kvx_batch* batch, const BatchInfo& bi, float* scores, int32_t* sel, int32_t* rest,
-                            void* ws) {
-    if (bi.n_tokens == 0) return ok();
+// Partial sums of z^T A z per row into ws (bf16: one per 256-column block of the operator, from the
+// score GEMM's epilogue; fp32: P = z A, then one row dot per row).  Returns the number of partials
+// per row and where they start.
+hipError_t score_partials(hipStream_t s, int32_t dtype, const void* z, const void* op, int32_t r,
+                          const BatchInfo& bi, void* ws, const float** partial, int* n_part) {
     if (dtype == KVX_BF16) {
         GemmArgs a{};
         a.A = (const bf16*)z; a.lda = r; a.K_a = r;
@@ -475,24 +474,46 @@ kvx_status run_score_select(hipStream_t s, int32_t dtype, const void* z, const v
         a.M = (int)bi.n_tokens; a.N = r; a.K = 2 * r; a.groups = 1;
         a.rows.mode = 0;
         a.epi = EPI_SCORE; a.partial = (float*)ws; a.Z = (const bf16*)z; a.ldz = r;
-        KVX_TRY_HIP(launch_gemm_bf16(a, s), "score");
-        const int nt = cdiv(r, gemm_bf16_block_n());
-        return hip_status(launch_select((const float*)ws, nt, bi.n_tokens, scores, batch->cu_tokens_d,
-                                        batch->cu_sel_d, bi.n_req, sel, rest, s),
-                          "select");
+        *partial = (const float*)ws;
+        *n_part = cdiv(r, gemm_bf16_block_n());
+        return launch_gemm_bf16(a, s);
     }
     float* P = (float*)ws;
-    float* partial = (float*)((char*)ws + round256((size_t)bi.n_tokens * r * 4));
+    float* rows = (float*)((char*)ws + round256((size_t)bi.n_tokens * r * 4));
     GemmF32Args a{};
     a.A = (const float*)z; a.lda = r; a.K_a = r;
     a.B = (const float*)op; a.ldb = r;
     a.M = (int)bi.n_tokens; a.N = r; a.K = r; a.groups = 1;
     a.rows.mode = 0;
     a.epi = EPI_STORE; a.C = P; a.ldc = r;
-    KVX_TRY_HIP(launch_gemm_f32(a, s), "score");
-    KVX_TRY_HIP(launch_rowdot_f32(P, (const float*)z, bi.n_tokens, r, partial, s), "score");
-    return hip_status(launch_select(partial, 1, bi.n_tokens, scores, batch->cu_tokens_d, batch->cu_sel_d,
-                                    bi.n_req, sel, rest, s),
+    if (hipError_t e = launch_gemm_f32(a, s)) return e;
+    *partial = rows;
+    *n_part = 1;
+    return launch_rowdot_f32(P, (const float*)z, bi.n_tokens, r, rows, s);
+}
+
+size_t score_ws_bytes(int32_t dtype, int32_t r, int64_t n) {
+    size_t b = 0;
+    kvx_score_select_workspace(dtype, r, n, &b);
+    return b;
+}
+
+// Score GEMM and the top-k.  Every byte of ws that is read was written by this call.  With op2
+// (the total-energy operator) the score is the ratio of the two quadratic forms; its partials go
+// to the second half of ws.
+kvx_status run_score_select(hipStream_t s, int32_t dtype, const void* z, const void* op, int32_t r,
+                            const kvx_batch* batch, const BatchInfo& bi, float* scores, int32_t* sel, int32_t* rest,
+                            void* ws, const void* op2 = nullptr) {
+    if (bi.n_tokens == 0) return ok();
+    const float* part = nullptr;
+    const float* part2 = nullptr;
+    int np = 0, np2 = 0;
+    KVX_TRY_HIP(score_partials(s, dtype, z, op, r, bi, ws, &part, &np), "score");
+    if (op2)
+        KVX_TRY_HIP(score_partials(s, dtype, z, op2, r, bi, (char*)ws + score_ws_bytes(dtype, r, bi.n_tokens), &part2,
+                                   &np2), "score (total energy)");
+    return hip_status(launch_select(part, np, bi.n_tokens, scores, batch->cu_tokens_d, batch->cu_sel_d, bi.n_req,
+                                    sel, rest, s, part2, np2),
                       "select");
 }
 
@@ -554,6 +575,27 @@ kvx_status kvx_score_select_noalloc(void* stream, int32_t dtype, const void* z, 
     void* ws = nullptr;
     if (kvx_status st = scratch_of_current_device(&ws)) return st;
     return run_score_select((hipStream_t)stream, dtype, z, op, r, batch, bi, scores, sel, rest, ws);
+}
+
+kvx_status kvx_score_select_normalized_workspace(int32_t dtype, int32_t r, int64_t n, size_t* bytes) {
+    if (kvx_status st = kvx_score_select_workspace(dtype, r, n, bytes)) return st;
+    *bytes *= 2;
+    return ok();
+}
+
+kvx_status kvx_score_select_normalized(void* stream, int32_t dtype, const void* z, const void* op,
+                                       const void* op_total, int32_t r, const kvx_batch* batch,
+                                       const int32_t* budget_pct, float* scores, int32_t* sel, int32_t* rest,
+                                       void* ws, size_t ws_bytes) {
+    BatchInfo bi;
+    if (kvx_status st = check_score_select(dtype, z, op, r, batch, budget_pct, scores, sel, rest, &bi)) return st;
+    KVX_REQUIRE_PTR(op_total, "op_total");
+    size_t need = 0;
+    kvx_score_select_normalized_workspace(dtype, r, bi.n_tokens, &need);
+    if (!ws || ws_bytes < need)
+        return fail(KVX_ERR_WORKSPACE, "score_select_normalized needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    KVX_REQUIRE(aligned16(ws), "ws must be 16-byte aligned");
+    return run_score_select((hipStream_t)stream, dtype, z, op, r, batch, bi, scores, sel, rest, ws, op_total);
 }
 
 }  // extern "C"

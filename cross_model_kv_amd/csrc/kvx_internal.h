@@ -26,11 +26,12 @@ hipError_t launch_fit_mapper(hipStream_t s, int dtype, const void* x, const void
 hipError_t launch_fit_calibration(hipStream_t s, int dtype, const void* z, const void* w_l, int n, int L, int d_t,
                                   int r, int c, int iters, float* u, void* ws);
 
-// ---- selection: scores[t] = sum_p partial[p][t] (when n_part > 0), then the k_b largest per
+// ---- selection: scores[t] = sum_p partial[p][t] (when n_part > 0; divided by
+//      sum_p partial2[p][t] when n_part2 > 0, 0 where that is 0), then the k_b largest per
 //      request (ties to the lower position) written ascending to sel, the rest to rest.
 hipError_t launch_select(const float* partial, int n_part, int64_t n_rows, float* scores,
                          const int32_t* cu_tok, const int32_t* cu_sel, int n_req, int32_t* sel,
-                         int32_t* rest, hipStream_t s);
+                         int32_t* rest, hipStream_t s, const float* partial2 = nullptr, int n_part2 = 0);
 
 // ---- rotary table [max_pos][d_h/2][2] (cos, sin), angles in fp64
 hipError_t launch_rope_table(double base, int d_h, int max_pos, float* table, hipStream_t s);

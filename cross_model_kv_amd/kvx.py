@@ -65,6 +65,9 @@ _SIGS = {
                           _P, _P, _SZ], _I32),
     "kvx_score_select_noalloc": ([_P, _I32, _P, _P, _I32, ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P, _P,
                                   _P], _I32),
+    "kvx_score_select_normalized_workspace": ([_I32, _I32, ctypes.c_int64, ctypes.POINTER(_SZ)], _I32),
+    "kvx_score_select_normalized": ([_P, _I32, _P, _P, _P, _I32, ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P,
+                                     _P, _P, _P, _SZ], _I32),
     "kvx_fit_mapper_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_fit_mapper": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _I32, _P, _P, _P, _SZ],
                        _I32),
@@ -301,6 +304,31 @@ def score_select(z: torch.Tensor, op: torch.Tensor, batch: Batch, pcts: Sequence
     _check("kvx_score_select", lib().kvx_score_select(_stream(dev), dt, _ptr(z), _ptr(op), r,
                                                       ctypes.byref(batch.c), pct, _ptr(scores), _ptr(sel),
                                                       _ptr(rest), _ptr(ws), need))
+    return scores, sel[:batch.total_sel], rest[:batch.total_rest]
+
+
+def score_select_normalized(z: torch.Tensor, op: torch.Tensor, op_total: torch.Tensor, batch: Batch,
+                            pcts: Sequence[int], ws: Optional[torch.Tensor] = None, out=None):
+    """Scores as shares (outside energy over total energy) and their top-budget selection."""
+    dev = z.device
+    r = z.shape[1]
+    dt = _dtype(z)
+    b = _SZ()
+    _check("kvx_score_select_normalized_workspace",
+           lib().kvx_score_select_normalized_workspace(dt, r, batch.n_tokens, ctypes.byref(b)))
+    need = b.value
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        scores = torch.empty(batch.n_tokens, dtype=torch.float32, device=dev)
+        sel = torch.empty(max(batch.total_sel, 1), dtype=torch.int32, device=dev)
+        rest = torch.empty(max(batch.total_rest, 1), dtype=torch.int32, device=dev)
+    else:
+        scores, sel, rest = out
+    pct = (ctypes.c_int32 * batch.n_req)(*[int(p) for p in pcts])
+    _check("kvx_score_select_normalized", lib().kvx_score_select_normalized(
+        _stream(dev), dt, _ptr(z), _ptr(op), _ptr(op_total), r, ctypes.byref(batch.c), pct, _ptr(scores), _ptr(sel),
+        _ptr(rest), _ptr(ws), ws.numel()))
     return scores, sel[:batch.total_sel], rest[:batch.total_rest]
 
 

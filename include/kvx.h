@@ -190,6 +190,19 @@ KVX_API kvx_status kvx_fit_calibration(void* stream, int32_t dtype, const void* 
                                        int32_t L_t, int32_t d_t, int32_t r, int32_t c, int32_t iters, float* u,
                                        void* ws, size_t ws_bytes);
 
+/* The score as a share (an unranked variant of the RaReCache abstract's score; the pages do not
+ * say which): s_t = z_t^T A z_t / z_t^T A_tot z_t, the energy of the token's mapped KV outside the
+ * calibration subspaces over the energy of all of it (0 where that is 0), then the selection of
+ * kvx_score_select.  op: kvx_score_prepare(w_l, u); op_total: kvx_score_prepare(w_l, none), c = 0
+ * (A_tot = sum_l W_l^T W_l), same storage.  Both quadratic forms run on the score GEMM; the ratio
+ * and the selection in one pass.  ws (device) of kvx_score_select_normalized_workspace() bytes
+ * (twice kvx_score_select's); other arguments as in kvx_score_select. */
+KVX_API kvx_status kvx_score_select_normalized_workspace(int32_t dtype, int32_t r, int64_t n, size_t* bytes);
+KVX_API kvx_status kvx_score_select_normalized(void* stream, int32_t dtype, const void* z, const void* op,
+                                               const void* op_total, int32_t r, const kvx_batch* batch,
+                                               const int32_t* budget_pct, float* scores, int32_t* sel,
+                                               int32_t* rest, void* ws, size_t ws_bytes);
+
 /* Top-k of given scores per request: the k_b largest scores of request b, ties to the
  * lower position, -0.0 equal to +0.0.  scores (device) [N] fp32, finite.
  * sel (device, out) [cu_sel[n_req]] request-local positions, ascending per request;

@@ -176,6 +176,21 @@ def test_score_select_noalloc_validation():
     status(L.kvx_score_select_noalloc(*args((ctypes.c_int32 * 1)(30), r=1024, b=big)), WORKSPACE, "scratch")
 
 
+def test_score_select_normalized_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    pct = (ctypes.c_int32 * 2)(30, 30)
+    need = ctypes.c_size_t()
+    one = ctypes.c_size_t()
+    assert L.kvx_score_select_normalized_workspace(1, 128, 150, ctypes.byref(need)) == 0
+    assert L.kvx_score_select_workspace(1, 128, 150, ctypes.byref(one)) == 0 and need.value == 2 * one.value
+    args = lambda opt=A16B, ws=A16, wsb=need.value: (None, 1, A16, A16, opt, 128, ctypes.byref(bt.c), pct, A16,
+                                                      A16, A16, ws, wsb)
+    status(L.kvx_score_select_normalized(*args(opt=None)), INVALID, "op_total")
+    status(L.kvx_score_select_normalized(*args(ws=None)), WORKSPACE)
+    status(L.kvx_score_select_normalized(*args(wsb=need.value - 1)), WORKSPACE)
+
+
 def test_reconstruct_validation():
     L = kvx.lib()
     bt = FakeBatch([100, 50], [30, 15])
