@@ -196,6 +196,24 @@ def recompute_qkv(x_rows: np.ndarray, w_qkv: np.ndarray, pos: np.ndarray,
     return q, k, v
 
 
+def recompute_qkv_qknorm(x_rows: np.ndarray, w_qkv: np.ndarray, pos: np.ndarray, H_q: int, H_kv: int,
+                         d_h: int, base: float, q_gain: np.ndarray, k_gain: np.ndarray, eps: float):
+    """recompute_qkv for a target whose layers normalise q and k per head before the rotation
+    (QK-norm, an unranked variant: one of the target families the pages name uses it, the pages
+    do not describe the block): every q head and every k head is RMS-normalised over its d_h
+    channels with its own per-channel gain (q_gain, k_gain [d_h], shared by the heads of the
+    layer), then rotated at its true position; v is left as it is."""
+    qkv = x_rows @ w_qkv.T
+    n = x_rows.shape[0]
+    q = qkv[:, :H_q * d_h].reshape(n, H_q, d_h)
+    k = qkv[:, H_q * d_h:(H_q + H_kv) * d_h].reshape(n, H_kv, d_h)
+    v = qkv[:, (H_q + H_kv) * d_h:].reshape(n, H_kv, d_h)
+    pos = np.asarray(pos)
+    q = rope(rmsnorm(q, q_gain, eps), pos[:, None], base)
+    k = rope(rmsnorm(k, k_gain, eps), pos[:, None], base)
+    return q, k, v
+
+
 def scatter(K: np.ndarray, V: np.ndarray, S: np.ndarray, k_new: np.ndarray, v_new: np.ndarray):
     """Mixed cache: recomputed K/V replace the translated ones at the selected positions."""
     K = K.copy()

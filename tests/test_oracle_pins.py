@@ -306,6 +306,48 @@ def pin_reconstruct_rotated_matrix_form():
         assert np.abs(K[:, t] - want).max() < 1e-10
 
 
+def pin_qknorm_head_norms():
+    """Each normalised head has squared norm d_h * ms / (ms + eps) with unit gains (ms its mean
+    square before normalising), at every position (the rotation keeps norms); with eps = 0 the
+    heads do not change when the hidden rows are scaled; v is the plain projection."""
+    rng = _rng(72)
+    H_q, H_kv, d_h, D, n = 2, 1, 6, 10, 5
+    x = rng.standard_normal((n, D))
+    w = rng.standard_normal(((H_q + 2 * H_kv) * d_h, D))
+    pos = np.array([0, 5, 17, 300, 2])
+    ones = np.ones(d_h)
+    eps = 0.25
+    q, k, v = O.recompute_qkv_qknorm(x, w, pos, H_q, H_kv, d_h, 10000.0, ones, ones, eps)
+    raw = x @ w.T
+    rq = raw[:, :H_q * d_h].reshape(n, H_q, d_h)
+    rk = raw[:, H_q * d_h:(H_q + H_kv) * d_h].reshape(n, H_kv, d_h)
+    for got, r in ((q, rq), (k, rk)):
+        ms = np.mean(r * r, axis=-1)
+        assert np.abs(np.sum(got * got, axis=-1) - d_h * ms / (ms + eps)).max() < 1e-10
+    assert np.abs(v - raw[:, (H_q + H_kv) * d_h:].reshape(n, H_kv, d_h)).max() < 1e-12
+    q1, k1, _ = O.recompute_qkv_qknorm(x, w, pos, H_q, H_kv, d_h, 10000.0, ones, ones, 0.0)
+    q3, k3, _ = O.recompute_qkv_qknorm(3.0 * x, w, pos, H_q, H_kv, d_h, 10000.0, ones, ones, 0.0)
+    assert np.abs(q1 - q3).max() < 1e-10 and np.abs(k1 - k3).max() < 1e-10
+
+
+def pin_qknorm_gain_before_rotation():
+    """The gains act before the rotation: a head's norm does not depend on its position even with
+    uneven gains, and at position 0 a gain that keeps one channel keeps only that channel."""
+    rng = _rng(73)
+    H_q, H_kv, d_h, D = 1, 1, 8, 9
+    x = np.repeat(rng.standard_normal((1, D)), 3, axis=0)
+    w = rng.standard_normal(((H_q + 2 * H_kv) * d_h, D))
+    g = rng.uniform(0.2, 3.0, d_h)
+    q, k, _ = O.recompute_qkv_qknorm(x, w, np.array([0, 9, 4000]), H_q, H_kv, d_h, 10000.0, g, g[::-1], 1e-6)
+    for t in (q, k):
+        nrm = np.linalg.norm(t, axis=-1)
+        assert np.abs(nrm - nrm[0]).max() < 1e-10
+    e = np.zeros(d_h)
+    e[3] = 2.0
+    q0, _, _ = O.recompute_qkv_qknorm(x[:1], w, np.array([0]), H_q, H_kv, d_h, 10000.0, e, g, 1e-6)
+    assert np.count_nonzero(np.abs(q0) > 1e-14) == 1 and abs(q0[0, 0, 3]) > 0
+
+
 def pin_recompute_identity_weights():
     """w_qkv made of identity blocks returns the hidden rows themselves (q, k rotated)."""
     rng = _rng(15)
@@ -1008,6 +1050,20 @@ def _mut_normalized_mean_of_layers(Y, u):
     return acc / L
 
 
+def _mut_qknorm_gain_after_rope(x_rows, w_qkv, pos, H_q, H_kv, d_h, base, q_gain, k_gain, eps):
+    q, k, v = O.recompute_qkv(x_rows, w_qkv, pos, H_q, H_kv, d_h, base)
+    return (O.rmsnorm(q, np.ones(d_h), eps) * q_gain, O.rmsnorm(k, np.ones(d_h), eps) * k_gain, v)
+
+
+def _mut_qknorm_over_all_heads(x_rows, w_qkv, pos, H_q, H_kv, d_h, base, q_gain, k_gain, eps):
+    qkv = x_rows @ w_qkv.T
+    n = x_rows.shape[0]
+    q = O.rmsnorm(qkv[:, :H_q * d_h], np.tile(q_gain, H_q), eps).reshape(n, H_q, d_h)
+    k = O.rmsnorm(qkv[:, H_q * d_h:(H_q + H_kv) * d_h], np.tile(k_gain, H_kv), eps).reshape(n, H_kv, d_h)
+    v = qkv[:, (H_q + H_kv) * d_h:].reshape(n, H_kv, d_h)
+    return O.rope(q, np.asarray(pos)[:, None], base), O.rope(k, np.asarray(pos)[:, None], base), v
+
+
 MUTANTS = {
     "rope_sign": ("rope", _mut_rope_sign),
     "rope_interleaved": ("rope", _mut_rope_interleaved),
@@ -1034,6 +1090,8 @@ MUTANTS = {
     "scatter_kv_swapped": ("scatter", _mut_scatter_kv_swapped),
     "scatter_shifted": ("scatter", _mut_scatter_shifted),
     "recompute_v_rotated": ("recompute_qkv", _mut_recompute_v_rotated),
+    "qknorm_gain_after_rope": ("recompute_qkv_qknorm", _mut_qknorm_gain_after_rope),
+    "qknorm_over_all_heads": ("recompute_qkv_qknorm", _mut_qknorm_over_all_heads),
     "recompute_rank_positions": ("recompute_qkv", _mut_recompute_rank_positions),
     "chained_from_input": ("chained_layers", _mut_chained_from_input),
     "first_token_one_layer": ("first_token", _mut_first_token_one_layer),
