@@ -652,6 +652,30 @@ def main():
     torch.cuda.synchronize()
     normalized = {"kernel": "score_select_normalized (two score GEMMs and one select), outside the timed step",
                   "ms": round(n0.elapsed_time(n1) / 10, 5)}
+    # the projection with QK-norm (q and k normalised per head before the rotation) on one layer
+    # of the step's rows, beside the same projection without it (both whole tiles, no split)
+    gq = torch.ones(wl.d_h, dtype=torch.float32, device=dev)
+    def time_qkv(qk, reps=10):
+        def run():
+            if qk:
+                kvx.qkv_rope_scatter_qknorm(0, inp.x_l[0], inp.w_qkv[0], wl.H_q, wl.H_kv, wl.d_h, gq, gq, 1e-6, h.rope,
+                                            h.batch, h.S, h.cache, qkv)
+            else:
+                kvx.qkv_rope_scatter_layers(0, inp.x_l[0:1], inp.w_qkv[0:1], wl.H_q, wl.H_kv, wl.d_h, h.rope, h.batch,
+                                            h.S, h.cache, qkv.view(1, *qkv.shape))
+        for _ in range(2):
+            run()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record(stream)
+        for _ in range(reps):
+            run()
+        q1.record(stream)
+        torch.cuda.synchronize()
+        return q0.elapsed_time(q1) / reps
+    qk_plain_ms, qk_norm_ms = time_qkv(False), time_qkv(True)
+    qknorm = {"kernel": "qkv_rope_scatter_qknorm on one layer (whole tiles), outside the timed step",
+              "ms": round(qk_norm_ms, 5), "plain_ms": round(qk_plain_ms, 5),
+              "tflops": round(2.0 * k * wl.D * wl.n_qkv / (qk_norm_ms * 1e-3) / 1e12, 2)}
     rec_flops = work["reconstruct"]["flops"]
     rotated_keys = {"kernel": "reconstruct with rotated translated keys (kvx_reconstruct_rope), outside the timed step",
                     "ms": round(rec_rope_ms, 5), "tflops": round(rec_flops / (rec_rope_ms * 1e-3) / 1e12, 2),
@@ -715,6 +739,7 @@ def main():
         "scatter_standalone": scatter,
         "reconstruct_rotated_keys": rotated_keys,
         "score_select_normalized": normalized,
+        "qkv_qknorm": qknorm,
         "graph": graph,
         "measured_peaks": peaks,
     }

@@ -301,6 +301,15 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
         const bool is_k = ng >= a.q_cols && cc < a.hd;
         const int j0 = (cc % a.d_h) % half;           // rotation index of the first column
         const bool lo = (cc % a.d_h) < half;
+        // QK-norm: q and k heads normalised over their d_h columns (16 lanes at d_h = 128, 8 at 64)
+        const bool is_q = ng < a.q_cols;
+        const bool norm = a.qk_gain_q && (is_q || is_k);
+        float gn[8];
+        if (a.qk_gain_q) {
+            const float* gsrc = (is_q ? a.qk_gain_q : a.qk_gain_k) + (ng % a.d_h);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) gn[j] = is_q || is_k ? gsrc[j] : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -309,6 +318,19 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
                 float x[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[j] = (float)(bf16)acc[i][j][v];
+                if (a.qk_gain_q) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
+                    ss += __shfl_xor(ss, 1);
+                    ss += __shfl_xor(ss, 2);
+                    ss += __shfl_xor(ss, 4);
+                    if (a.d_h == 128) ss += __shfl_xor(ss, 8);
+                    const float inv = 1.f / sqrtf(ss / (float)a.d_h + a.qk_eps);
+                    if (norm)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) x[j] = x[j] * inv * gn[j];
+                }
                 float y[8];
                 if (k_slab) {
 #pragma unroll

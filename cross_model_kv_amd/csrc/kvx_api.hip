@@ -807,7 +807,8 @@ hipError_t run_scatter(hipStream_t s, int32_t dtype, int32_t layer, const void* 
 hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, const void* x_l, const void* w_qkv,
                                 int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h, const float* rope,
                                 const kvx_batch* batch, const BatchInfo& bi, const int32_t* sel,
-                                const kvx_cache* cache, void* qkv, void* split_ws, bool compact_rows = false) {
+                                const kvx_cache* cache, void* qkv, void* split_ws, bool compact_rows = false,
+                                const float* q_gain = nullptr, const float* k_gain = nullptr, float eps = 0.f) {
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     if (dtype != KVX_BF16) {
         if (hipError_t e = run_qkv(s, dtype, x_l, w_qkv, D, n_qkv, batch, bi, sel, qkv, split_ws)) return e;
@@ -826,6 +827,10 @@ hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, con
     a.hd = hd; a.slots = slot_map(cache, batch);
     a.rope = rope; a.q_cols = H_q * d_h; a.d_h = d_h;
     a.split_ws = (float*)split_ws;
+    if (q_gain) {                    // QK-norm: whole tiles only (the split reduce has no normalisation)
+        a.qk_gain_q = q_gain; a.qk_gain_k = k_gain; a.qk_eps = eps;
+        a.split_ws = nullptr;
+    }
     return launch_gemm_bf16(a, s);
 }
 
@@ -1047,6 +1052,31 @@ kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t layer, cons
     return hip_status(run_qkv_rope_scatter((hipStream_t)stream, dtype, layer, x_l, w_qkv, D, H_q, H_kv, d_h, rope,
                                            batch, bi, sel, cache, qkv, need ? ws : nullptr),
                       "qkv_rope_scatter");
+}
+
+kvx_status kvx_qkv_rope_scatter_qknorm(void* stream, int32_t dtype, int32_t layer, const void* x_l,
+                                       const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv, int32_t d_h,
+                                       const float* q_gain, const float* k_gain, float eps, const float* rope,
+                                       int32_t max_pos, const kvx_batch* batch, const int32_t* sel,
+                                       const kvx_cache* cache, void* qkv) {
+    if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
+    if (dtype != KVX_BF16) return fail(KVX_ERR_UNSUPPORTED, "qkv_rope_scatter_qknorm supports KVX_BF16 only");
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE_PTR(x_l, "x_l");
+    KVX_REQUIRE_PTR(w_qkv, "w_qkv");
+    KVX_REQUIRE(q_gain && k_gain, "q_gain and k_gain must not be null");
+    KVX_REQUIRE(eps >= 0.f && eps < INFINITY, "eps must be finite and >= 0");
+    KVX_REQUIRE(D > 0 && D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
+    if (bi.n_sel == 0) return ok();
+    KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");
+    KVX_REQUIRE_PTR(sel, "sel");
+    if (kvx_status st = check_positions_debug(sel, batch, false, "sel")) return st;
+    KVX_REQUIRE_PTR(qkv, "qkv");
+    return hip_status(run_qkv_rope_scatter((hipStream_t)stream, dtype, layer, x_l, w_qkv, D, H_q, H_kv, d_h, rope,
+                                           batch, bi, sel, cache, qkv, nullptr, false, q_gain, k_gain, eps),
+                      "qkv_rope_scatter_qknorm");
 }
 
 kvx_status kvx_sparse_attention(void* stream, int32_t dtype, int32_t layer, const void* qkv, int32_t H_q,

@@ -144,6 +144,10 @@ struct GemmArgs {
     // position) and written with the V columns to the layer's cache slots (kc, vc, hd, slots).
     // EPI_CACHE with rope set: the K columns [0, hd) rotated the same way before they are stored
     const float* rope; int32_t q_cols; int32_t d_h;
+    // EPI_QKV with qk_gain_q set (QK-norm): every q and k head RMS-normalised over its d_h
+    // channels (mean square + qk_eps) with the per-channel gains qk_gain_q / qk_gain_k [d_h]
+    // before the rotation (the value rounded to bf16 first, as without the normalisation)
+    const float* qk_gain_q; const float* qk_gain_k; float qk_eps;
     // EPI_RESID: C[m][n] = R[m][n] + acc (C may be R: every element is read, then written, by
     // one thread)
     const bf16* R; int64_t ldr;

@@ -73,6 +73,8 @@ _SIGS = {
                        _I32),
     "kvx_fit_calibration_workspace": ([_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_fit_calibration": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ], _I32),
+    "kvx_qkv_rope_scatter_qknorm": ([_P, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, ctypes.c_float, _P,
+                                     _I32, ctypes.POINTER(_Batch), _P, ctypes.POINTER(_Cache), _P], _I32),
     "kvx_reconstruct_rope": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch), _P,
                               ctypes.POINTER(_Cache)], _I32),
     "kvx_reconstruct": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_Batch), _P,
@@ -493,6 +495,22 @@ def qkv_rope_scatter(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: in
         _stream(dev), dt, layer, _ptr(x_l), _ptr(w_qkv), D, H_q, H_kv, d_h, _ptr(rope), rope.shape[0],
         ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None, ctypes.byref(cache.c), _ptr(qkv),
         _ptr(ws) if need else None, ws.numel() if need else 0))
+    return qkv
+
+
+def qkv_rope_scatter_qknorm(layer: int, x_l: torch.Tensor, w_qkv: torch.Tensor, H_q: int, H_kv: int, d_h: int,
+                            q_gain: torch.Tensor, k_gain: torch.Tensor, eps: float, rope: torch.Tensor, batch: Batch,
+                            sel: torch.Tensor, cache: Cache, qkv: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Steps 1-3 with q and k normalised per head before the rotation (QK-norm); returns qkv."""
+    dev = x_l.device
+    D = x_l.shape[1]
+    n_qkv = (H_q + 2 * H_kv) * d_h
+    if qkv is None:
+        qkv = torch.empty((max(batch.total_sel, 1), n_qkv), dtype=x_l.dtype, device=dev)
+    _check("kvx_qkv_rope_scatter_qknorm", lib().kvx_qkv_rope_scatter_qknorm(
+        _stream(dev), _dtype(x_l), layer, _ptr(x_l), _ptr(w_qkv), D, H_q, H_kv, d_h, _ptr(q_gain), _ptr(k_gain),
+        float(eps), _ptr(rope), rope.shape[0], ctypes.byref(batch.c), _ptr(sel) if sel.numel() else None,
+        ctypes.byref(cache.c), _ptr(qkv)))
     return qkv
 
 

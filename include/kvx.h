@@ -338,6 +338,21 @@ KVX_API kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t lay
                                         const kvx_cache* cache, void* qkv, void* ws,
                                         size_t ws_bytes);
 
+/* kvx_qkv_rope_scatter_qknorm: steps 1-3 for a target whose layers normalise q and k per head
+ * before the rotation (QK-norm; one of the target families the pages name does, the pages do not
+ * describe the block): every q and every k head is divided by the root of its mean square over its
+ * d_h channels plus eps and multiplied by the layer's per-channel gain (q_gain, k_gain (device)
+ * [d_h] fp32, shared by the layer's heads), k is then rotated and written to the cache with v, and
+ * the normalised q is left in qkv for kvx_sparse_attention (which rotates it).  Each value is
+ * rounded to bf16 before the normalisation, as the plain projection stores it.  bf16 only; whole
+ * output tiles (no workspace); other arguments as in kvx_qkv_rope_scatter. */
+KVX_API kvx_status kvx_qkv_rope_scatter_qknorm(void* stream, int32_t dtype, int32_t layer, const void* x_l,
+                                               const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv,
+                                               int32_t d_h, const float* q_gain, const float* k_gain,
+                                               float eps, const float* rope, int32_t max_pos,
+                                               const kvx_batch* batch, const int32_t* sel,
+                                               const kvx_cache* cache, void* qkv);
+
 /* kvx_sparse_attention: step 4, causal attention of the selected queries (the q part of
  * the qkv rows, rotated at their true positions inside the kernel) over layer `layer` of
  * the cache; out and lse as in kvx_recompute_attn.  d_h must be 64 or 128.

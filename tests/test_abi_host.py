@@ -283,6 +283,19 @@ def test_qkv_rope_scatter_validation():
     status(call(dtype=3), UNSUPPORTED, "dtype")
 
 
+def test_qknorm_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    c = cache(n_layers=1)
+    args = lambda dt=1, gq=A16, eps=1e-6, d_h=128: (None, dt, 0, A16, A16, 256, 8, 2, d_h, gq, A16B,
+                                                    ctypes.c_float(eps), A16, 100, ctypes.byref(bt.c), A16,
+                                                    ctypes.byref(c), A16)
+    status(L.kvx_qkv_rope_scatter_qknorm(*args(dt=0)), UNSUPPORTED, "BF16")
+    status(L.kvx_qkv_rope_scatter_qknorm(*args(gq=None)), INVALID, "gain")
+    status(L.kvx_qkv_rope_scatter_qknorm(*args(eps=-1.0)), INVALID, "eps")
+    status(L.kvx_qkv_rope_scatter_qknorm(*args(d_h=96)), UNSUPPORTED, "d_h")
+
+
 def test_chaining_validation():
     L = kvx.lib()
     bt = FakeBatch([100, 50], [30, 15])
