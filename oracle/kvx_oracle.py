@@ -32,6 +32,10 @@ plain pre-norm decoder layer those families share - RMS normalisation with a per
 gain, the recomputed attention, an output projection and a residual add, a second RMS
 normalisation, a SiLU-gated MLP and a second residual add - with no norm on q or k.
 
+Variants (unranked on the pages' list of next steps, each its own function): the score as a share
+of the token's energy, the keys of a mapper without rotary phase, QK-norm on the recomputed q and
+k, the score taken directly from a stored cache layer by layer, and per-layer selection sets.
+
 Fitting (before the path): the mapper is fitted in closed form to paired calibration KV of the
 two models - reduced-rank ridge regression, the rank-r least-squares map from source KV to the
 target KV of all layers, factored into the shared projection and the per-layer reconstructions -
@@ -135,6 +139,33 @@ def rank_disagreement_normalized(Y: np.ndarray, u: np.ndarray) -> np.ndarray:
     nz = total > 0
     out[nz] = outside[nz] / total[nz]
     return out
+
+
+def layer_disagreement(K: np.ndarray, V: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """The rank-disagreement energy scored directly from a stored target cache, layer by layer
+    (an unranked variant of the RaReCache abstract's score, for a mapper that is not linear, whose
+    cache has no latent form): for layer l and position t, the squared norm of the part of the
+    stored vector y = [K heads | V heads] (head-major, the order reconstruct splits) outside
+    span(U_l).  K, V [L_t, T, H_kv, d_h] as stored, u [L_t, d_t, c] with orthonormal columns.
+    Returns E [L_t, T]; its sum over the layers is the summed score of those stored values."""
+    L, T = K.shape[0], K.shape[1]
+    E = np.zeros((L, T))
+    for l in range(L):
+        y = np.concatenate([K[l].reshape(T, -1), V[l].reshape(T, -1)], axis=1)
+        res = y - (y @ u[l]) @ u[l].T
+        E[l] = np.sum(res * res, axis=1)
+    return E
+
+
+def select_per_layer(E: np.ndarray, k: int):
+    """Per-layer selection sets (an unranked variant): every layer takes its own k positions of
+    largest energy E[l], with select's rule for ties.  Returns S [L_t, k] and C [L_t, T - k],
+    each row ascending."""
+    sets = [select(E[l], k) for l in range(E.shape[0])]
+    T = E.shape[1]
+    S = np.array([s for s, _ in sets], dtype=np.int64).reshape(E.shape[0], k)
+    C = np.array([c for _, c in sets], dtype=np.int64).reshape(E.shape[0], T - k)
+    return S, C
 
 
 def select(s: np.ndarray, k: int):
@@ -281,6 +312,34 @@ def handoff_request(x_src: np.ndarray, w_s: np.ndarray, w_l: np.ndarray, u: np.n
         K[l], V[l] = scatter(K[l], V[l], S, kk, vv)
         O[l], LSE[l] = sparse_causal_attention(q, K[l], V[l], S)
     return dict(z=z, K_tr=K_tr, V_tr=V_tr, s=s, S=S, C=C, K=K, V=V, O=O, LSE=LSE)
+
+
+def handoff_request_layer_sets(x_src: np.ndarray, w_s: np.ndarray, w_l: np.ndarray, u: np.ndarray,
+                               x_l: np.ndarray, w_qkv: np.ndarray, pct: int, H_q: int, H_kv: int,
+                               d_h: int, base: float = 10000.0) -> Dict[str, np.ndarray]:
+    """One request with per-layer selection sets, scored directly from the stored cache (the two
+    unranked variants together): map, translate every position of every layer, score each layer
+    from its own stored K/V (layer_disagreement), and let layer l recompute its own top-k set S_l,
+    scatter there and attend with the queries of S_l.  The budget k is the same for every layer.
+    Returns z, the translated cache (K_tr, V_tr), E [L_t, T], S [L_t, k], C [L_t, T - k], the
+    mixed cache (K, V) and O [L_t, k, H_q, d_h], LSE [L_t, k, H_q] (row i of layer l is S[l][i])."""
+    T = x_src.shape[0]
+    L = w_l.shape[0]
+    z = map_latent(x_src, w_s)
+    K_tr, V_tr, _ = reconstruct(z, w_l, H_kv, d_h)
+    E = layer_disagreement(K_tr, V_tr, u)
+    k = budget(T, pct)
+    S, C = select_per_layer(E, k)
+    K = K_tr.copy()
+    V = V_tr.copy()
+    O = np.zeros((L, k, H_q, d_h))
+    LSE = np.zeros((L, k, H_q))
+    for l in range(L):
+        q, kk, vv = recompute_qkv(x_l[l][S[l]], w_qkv[l], S[l], H_q, H_kv, d_h, base)
+        K[l], V[l] = scatter(K[l], V[l], S[l], kk, vv)
+        if k:
+            O[l], LSE[l] = sparse_causal_attention(q, K[l], V[l], S[l])
+    return dict(z=z, K_tr=K_tr, V_tr=V_tr, E=E, S=S, C=C, K=K, V=V, O=O, LSE=LSE)
 
 
 # ------------------------------------------------------------------------------------

@@ -828,6 +828,156 @@ def pin_calibration_energy_is_discarded_spectrum():
     assert abs(total - want) <= 1e-9 * want
 
 
+# ------------------------------------------------------------------------- direct scoring of a stored cache, per-layer sets
+
+def _split_kv(y, H_kv, d_h):
+    """[L, T, 2 H_kv d_h] rows in the reconstruction's channel order -> stored K, V [L, T, H_kv, d_h]."""
+    L, T = y.shape[:2]
+    hd = H_kv * d_h
+    return y[..., :hd].reshape(L, T, H_kv, d_h), y[..., hd:].reshape(L, T, H_kv, d_h)
+
+
+def pin_layer_disagreement_closed_forms():
+    """Layer by layer, with each layer's own basis (the first c columns of a full orthogonal
+    matrix Q_l): a stored vector inside span(U_l) scores 0, one built from Q_l's other columns
+    scores its squared norm, and their sum scores the second part only.  The same stored vector in
+    two layers scores 0 in the layer whose span holds it and the squared norm of its coordinates
+    on the other layer's remaining columns there.  A basis of K channels only ignores K and scores
+    all of V (the K heads come first in the stored vector)."""
+    rng = _rng(80)
+    L, T, H_kv, d_h, c = 2, 5, 2, 4, 3
+    d_t = 2 * H_kv * d_h
+    Q = np.stack([np.linalg.qr(rng.standard_normal((d_t, d_t)))[0] for _ in range(L)])
+    u = Q[:, :, :c]
+    a = rng.standard_normal((L, T, c))
+    b = rng.standard_normal((L, T, d_t - c))
+    inside = np.einsum("ldc,ltc->ltd", Q[:, :, :c], a)
+    outside = np.einsum("ldc,ltc->ltd", Q[:, :, c:], b)
+    E_in = O.layer_disagreement(*_split_kv(inside, H_kv, d_h), u)
+    E_out = O.layer_disagreement(*_split_kv(outside, H_kv, d_h), u)
+    E_sum = O.layer_disagreement(*_split_kv(inside + outside, H_kv, d_h), u)
+    want = np.sum(b * b, axis=2)
+    assert E_in.shape == (L, T) and np.abs(E_in).max() < 1e-24 + 1e-12 * np.sum(a * a)
+    assert np.abs(E_out - want).max() <= 1e-12 * want.max()
+    assert np.abs(E_sum - want).max() <= 1e-12 * want.max()
+    # one vector in both layers, inside layer 0's span
+    y = np.stack([inside[0], inside[0]])
+    E = O.layer_disagreement(*_split_kv(y, H_kv, d_h), u)
+    other = np.einsum("dc,td->tc", Q[1, :, c:], inside[0])
+    assert np.abs(E[0]).max() <= 1e-12 * np.sum(inside[0] ** 2)
+    assert np.abs(E[1] - np.sum(other ** 2, axis=1)).max() <= 1e-12 * np.sum(inside[0] ** 2)
+    assert E[1].min() > 1e-3
+    # a basis of the first c K channels
+    e = np.zeros((1, d_t, c))
+    e[0, np.arange(c), np.arange(c)] = 1.0
+    yk = np.zeros((1, T, d_t))
+    yk[0, :, :c] = rng.standard_normal((T, c))
+    yk[0, :, H_kv * d_h:] = rng.standard_normal((T, H_kv * d_h))
+    Ek = O.layer_disagreement(*_split_kv(yk, H_kv, d_h), e)
+    assert np.abs(Ek[0] - np.sum(yk[0, :, H_kv * d_h:] ** 2, axis=1)).max() <= 1e-12 * np.sum(yk ** 2)
+
+
+def pin_layer_disagreement_sums_to_score():
+    """Scored from the translated cache the reconstruction writes, the layers' energies add up to
+    the rank-disagreement score of the same mapped vectors."""
+    rng = _rng(81)
+    L, T, r, H_kv, d_h, c = 3, 11, 6, 2, 4, 5
+    d_t = 2 * H_kv * d_h
+    z = rng.standard_normal((T, r))
+    w_l = rng.standard_normal((L, d_t, r))
+    u = np.stack([_orthonormal(rng, d_t, c) for _ in range(L)])
+    K, V, Y = O.reconstruct(z, w_l, H_kv, d_h)
+    E = O.layer_disagreement(K, V, u)
+    s = O.rank_disagreement(Y, u)
+    assert E.shape == (L, T) and (E >= 0).all()
+    assert np.abs(E.sum(axis=0) - s).max() <= 1e-12 * s.max()
+
+
+def pin_select_per_layer_hand():
+    """Every layer its own top-k, ties to the lower position (worked by hand)."""
+    E = np.array([[3.0, 1.0, 2.0, 2.0, 0.0],
+                  [0.0, 5.0, 5.0, 1.0, 7.0],
+                  [1.0, 1.0, 1.0, 1.0, 1.0]])
+    S, C = O.select_per_layer(E, 2)
+    assert S.tolist() == [[0, 2], [1, 4], [0, 1]]
+    assert C.tolist() == [[1, 3, 4], [0, 2, 3], [2, 3, 4]]
+    S0, C0 = O.select_per_layer(E, 0)
+    assert S0.shape == (3, 0) and C0.tolist() == [[0, 1, 2, 3, 4]] * 3
+
+
+def _layer_sets_case(rng, L, T, H_q, H_kv, d_h, D, same_layers=False):
+    d_src, r, c = 10, 2 * H_kv * d_h * L, 3
+    d_t = 2 * H_kv * d_h
+    x_src = rng.standard_normal((T, d_src))
+    w_s = rng.standard_normal((r, d_src))
+    w_l = rng.standard_normal((L, d_t, r))
+    u = np.stack([_orthonormal(rng, d_t, c) for _ in range(L)])
+    if same_layers:
+        w_l[:] = w_l[0]
+        u[:] = u[0]
+    x_l = rng.standard_normal((L, T, D))
+    w_qkv = rng.standard_normal((L, (H_q + 2 * H_kv) * d_h, D))
+    return x_src, w_s, w_l, u, x_l, w_qkv
+
+
+def pin_layer_sets_hand():
+    """Each layer recomputes the positions of its own largest energies: layer l's reconstruction
+    reads only block l of the latent, so energies planted in block 0 at positions 1 and 4 and in
+    block 1 at 2 and 7 select {1, 4} in layer 0 and {2, 7} in layer 1 (a set shared by both
+    layers, from the summed score, would be {1, 2})."""
+    L, T, H_kv, d_h = 2, 8, 1, 2
+    d_t = 2 * H_kv * d_h
+    z = np.full((T, L * d_t), 1e-3)
+    z[1, 0], z[4, 1], z[2, d_t], z[7, d_t + 2] = 10.0, 9.5, 9.7, 9.0
+    w_l = np.zeros((L, d_t, L * d_t))
+    for l in range(L):
+        w_l[l][:, l * d_t:(l + 1) * d_t] = np.eye(d_t)
+    u = np.zeros((L, d_t, 0))                   # empty calibration span: the energy is the squared norm
+    H_q, D = 2, 4
+    rng = _rng(82)
+    out = O.handoff_request_layer_sets(z, np.eye(L * d_t), w_l, u, rng.standard_normal((L, T, D)),
+                                       rng.standard_normal((L, (H_q + 2 * H_kv) * d_h, D)), 25, H_q, H_kv, d_h)
+    assert out["S"].tolist() == [[1, 4], [2, 7]]
+    assert out["C"].tolist() == [[0, 2, 3, 5, 6, 7], [0, 1, 3, 4, 5, 6]]
+
+
+def pin_layer_sets_shared_when_layers_agree():
+    """With every layer's reconstruction and basis equal, every layer's energies are the same, so
+    every layer's set is the shared set of the summed score and the variant's cache and outputs
+    are the plain handoff's."""
+    rng = _rng(83)
+    L, T, H_q, H_kv, d_h, D = 3, 30, 4, 2, 4, 12
+    args = _layer_sets_case(rng, L, T, H_q, H_kv, d_h, D, same_layers=True)
+    a = O.handoff_request_layer_sets(*args, 30, H_q, H_kv, d_h)
+    b = O.handoff_request(*args, 30, H_q, H_kv, d_h)
+    for l in range(L):
+        assert a["S"][l].tolist() == b["S"].tolist()
+    for key in ("K", "V", "O", "LSE"):
+        assert np.abs(a[key] - b[key]).max() <= 1e-12 * np.abs(b[key]).max(), key
+
+
+def pin_layer_sets_complement_and_layer_order():
+    """Layer l writes recomputed K/V only at its own set: its complement rows keep the translated
+    values, and its set's rows change.  Reordering the layers (weights, bases, inputs) reorders the
+    energies, sets, cache and outputs the same way."""
+    rng = _rng(84)
+    L, T, H_q, H_kv, d_h, D = 3, 30, 4, 2, 4, 12
+    args = _layer_sets_case(rng, L, T, H_q, H_kv, d_h, D)
+    out = O.handoff_request_layer_sets(*args, 30, H_q, H_kv, d_h)
+    assert any(out["S"][0].tolist() != out["S"][l].tolist() for l in range(1, L))
+    for l in range(L):
+        Cl, Sl = out["C"][l], out["S"][l]
+        assert np.array_equal(out["K"][l][Cl], out["K_tr"][l][Cl])
+        assert np.array_equal(out["V"][l][Cl], out["V_tr"][l][Cl])
+        assert np.abs(out["K"][l][Sl] - out["K_tr"][l][Sl]).min(axis=(1, 2)).max() > 0
+    perm = np.array([2, 0, 1])
+    x_src, w_s, w_l, u, x_l, w_qkv = args
+    po = O.handoff_request_layer_sets(x_src, w_s, w_l[perm], u[perm], x_l[perm], w_qkv[perm], 30, H_q, H_kv, d_h)
+    assert np.array_equal(po["S"], out["S"][perm])
+    for key in ("E", "K", "V", "O", "LSE"):
+        assert np.abs(po[key] - out[key][perm]).max() <= 1e-12 * np.abs(out[key]).max(), key
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 
@@ -1064,6 +1214,31 @@ def _mut_qknorm_over_all_heads(x_rows, w_qkv, pos, H_q, H_kv, d_h, base, q_gain,
     return O.rope(q, np.asarray(pos)[:, None], base), O.rope(k, np.asarray(pos)[:, None], base), v
 
 
+_ORIG = {name: getattr(O, name) for name in ("layer_disagreement", "select_per_layer")}
+
+
+def _mut_direct_v_then_k(K, V, u):
+    L, T = K.shape[:2]
+    E = np.zeros((L, T))
+    for l in range(L):
+        y = np.concatenate([V[l].reshape(T, -1), K[l].reshape(T, -1)], axis=1)
+        res = y - (y @ u[l]) @ u[l].T
+        E[l] = np.sum(res * res, axis=1)
+    return E
+
+
+def _mut_direct_first_basis(K, V, u):
+    return _ORIG["layer_disagreement"](K, V, np.stack([u[0]] * u.shape[0]))
+
+
+def _mut_per_layer_summed(E, k):
+    return _ORIG["select_per_layer"](np.stack([E.sum(axis=0)] * E.shape[0]), k)
+
+
+def _mut_per_layer_first_set(E, k):
+    return _ORIG["select_per_layer"](np.stack([E[0]] * E.shape[0]), k)
+
+
 MUTANTS = {
     "rope_sign": ("rope", _mut_rope_sign),
     "rope_interleaved": ("rope", _mut_rope_interleaved),
@@ -1101,6 +1276,10 @@ MUTANTS = {
     "fit_trailing_directions": ("fit_mapper", _mut_fit_trailing),
     "calibration_trailing_directions": ("calibration_basis", _mut_calibration_trailing),
     "calibration_without_latents": ("calibration_basis", _mut_calibration_no_latent),
+    "direct_score_v_then_k": ("layer_disagreement", _mut_direct_v_then_k),
+    "direct_score_first_basis": ("layer_disagreement", _mut_direct_first_basis),
+    "layer_sets_from_summed_score": ("select_per_layer", _mut_per_layer_summed),
+    "layer_sets_first_layer_everywhere": ("select_per_layer", _mut_per_layer_first_set),
 }
 
 
