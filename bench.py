@@ -676,6 +676,38 @@ def main():
     qknorm = {"kernel": "qkv_rope_scatter_qknorm on one layer (whole tiles), outside the timed step",
               "ms": round(qk_norm_ms, 5), "plain_ms": round(qk_plain_ms, 5),
               "tflops": round(2.0 * k * wl.D * wl.n_qkv / (qk_norm_ms * 1e-3) / 1e12, 2)}
+    # direct scoring of the stored cache (every layer's K/V of every position, against the
+    # calibration bases), summed and selected, and per layer with every layer's own top-k
+    cop = kvx.score_cache_prepare(inp.u, kvx.BF16)
+    cws = torch.empty(4 * wl.L_t * -(-wl.c // 256) * T + 256, dtype=torch.uint8, device=dev)
+    cbuf = (torch.empty_like(h.scores), torch.empty_like(h.sel), torch.empty_like(h.rest))
+    energy = torch.empty((wl.L_t, T), dtype=torch.float32, device=dev)
+    lbuf = (torch.empty((wl.L_t, k), dtype=torch.int32, device=dev),
+            torch.empty((wl.L_t, T - k), dtype=torch.int32, device=dev))
+    def time_direct(per_layer, reps=5):
+        def run():
+            if per_layer:
+                kvx.score_cache(h.cache, 0, wl.H_kv, wl.d_h, cop, h.batch, energy=energy, ws=cws)
+                kvx.select_topk_layers(energy, h.batch, out=lbuf)
+            else:
+                kvx.score_cache_select(h.cache, 0, wl.H_kv, wl.d_h, cop, h.batch, inp.pcts, ws=cws, out=cbuf)
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    dsum_ms, dlay_ms = time_direct(False), time_direct(True)
+    d_t = 2 * wl.H_kv * wl.d_h
+    dflops = 2.0 * T * d_t * 2 * wl.c * wl.L_t              # hi and lo halves of the basis
+    direct_score = {"kernel": "score_cache_select (direct scoring of the stored cache, all layers) and score_cache + "
+                              "select_topk_layers (per-layer sets), outside the timed step",
+                    "ms": round(dsum_ms, 5), "per_layer_sets_ms": round(dlay_ms, 5), "bound": "mfma",
+                    "tflops_executed": round(dflops / (dsum_ms * 1e-3) / 1e12, 2),
+                    "cache_gbs": round(2.0 * T * d_t * wl.L_t / (dsum_ms * 1e-3) / 1e9, 1)}
+    del cop, cws, cbuf, energy, lbuf
     rec_flops = work["reconstruct"]["flops"]
     rotated_keys = {"kernel": "reconstruct with rotated translated keys (kvx_reconstruct_rope), outside the timed step",
                     "ms": round(rec_rope_ms, 5), "tflops": round(rec_flops / (rec_rope_ms * 1e-3) / 1e12, 2),
@@ -740,6 +772,7 @@ def main():
         "reconstruct_rotated_keys": rotated_keys,
         "score_select_normalized": normalized,
         "qkv_qknorm": qknorm,
+        "direct_score": direct_score,
         "graph": graph,
         "measured_peaks": peaks,
     }

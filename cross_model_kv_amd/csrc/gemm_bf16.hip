@@ -85,7 +85,7 @@ __device__ __forceinline__ void group_order() {
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool SQ>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xcd) {
     constexpr int NW = WM * WN;
@@ -99,6 +99,7 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
     __shared__ int64_t s_slot[BM];
     __shared__ int s_pos[BM];
     __shared__ float s_red[WN][BM];
+    __shared__ float s_yy[SQ ? BM : 1];             // EPI_SQNORM: squared norm of every A row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -132,7 +133,7 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
         if (m < a.M) {
             const RowInfo ri = row_info(a.rows, m);
             src = ri.src;
-            if (a.epi == EPI_CACHE || a.epi == EPI_QKV) slot = a.slots.slot(ri.b, ri.pos);
+            if (a.epi == EPI_CACHE || a.epi == EPI_QKV || SQ) slot = a.slots.slot(ri.b, ri.pos);
             pos = ri.pos;
         }
         s_src[r] = src;
@@ -154,8 +155,12 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
     for (int c = 0; c < A_L; ++c) {
         const int P = (c * NL + lw) * 64 + lane;
         const int row = P >> 3, ch = (P & 7) ^ swz(row);
-        const int src = max(s_src[row], 0);
-        asrc[c] = a.A + (int64_t)t.group * a.a_group_stride + (int64_t)src * a.lda + ch * 8;
+        if constexpr (SQ) {              // the row's cache slot (rows past M read slot 0)
+            asrc[c] = a.A + (int64_t)t.group * a.a_group_stride + s_slot[row] * a.lda + ch * 8;
+        } else {
+            const int src = max(s_src[row], 0);
+            asrc[c] = a.A + (int64_t)t.group * a.a_group_stride + (int64_t)src * a.lda + ch * 8;
+        }
     }
 #pragma unroll
     for (int c = 0; c < B_L; ++c) {
@@ -171,10 +176,18 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
     }
     auto issue = [&](bf16* st, int kt) {
         if (wave >= NL) return;
-        const int ka = (kt * BK) % a.K_a;
+        if constexpr (SQ) {
+            int64_t ka = (kt >> 1) * BK;
+            if (ka >= a.kv_split) ka += a.kv_delta - a.kv_split;
 #pragma unroll
-        for (int c = 0; c < A_L; ++c)
-            lds_dma16(asrc[c] + ka, st + (c * NL + lw) * 512);
+            for (int c = 0; c < A_L; ++c)
+                lds_dma16(asrc[c] + ka, st + (c * NL + lw) * 512);
+        } else {
+            const int ka = (kt * BK) % a.K_a;
+#pragma unroll
+            for (int c = 0; c < A_L; ++c)
+                lds_dma16(asrc[c] + ka, st + (c * NL + lw) * 512);
+        }
 #pragma unroll
         for (int c = 0; c < B_L; ++c)
             lds_dma16(bsrc[c] + kt * BK, st + BM * BK + (c * NL + lw) * 512);
@@ -187,6 +200,12 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int lr = lane & 15, lq = lane >> 4;
+    // EPI_SQNORM: the first column tile's wn == 0 waves square the A fragments they read on the even
+    // K steps (each A chunk once); lane holds row wm*WTM + i*16 + lr, k chunk ks*4 + lq
+    float sq[SQ ? FM : 1];
+#pragma unroll
+    for (int i = 0; i < (SQ ? FM : 1); ++i) sq[i] = 0.f;
+    bool sq_on = false;
     // One stage = two 32-deep substeps = 2*FM groups of FN MFMAs (group g: A fragment g % FM of
     // substep g / FM against the substep's FN B fragments).  Reads run one group ahead: before
     // group g the A fragment of group g+1 is read, and during the first substep's groups the
@@ -219,12 +238,24 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[g & 1], ks ? b1[j] : b0[j], acc[i][j], 0, 0, 0);
+            if constexpr (SQ) {
+                if (sq_on) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float f = (float)af[g & 1][e];
+                        sq[i] = __builtin_fmaf(f, f, sq[i]);
+                    }
+                }
+            }
         }
         // issue order: the first reads, then per group its look-ahead reads and its MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);
         group_order<0, FM, FN>();
     };
 
+    // SQ: K steps alternate high and low halves of the basis on the same A chunk, so stage lds0
+    // (even steps) carries each chunk once
+    if constexpr (SQ) sq_on = t.tn == 0 && wn == 0;
     issue(lds0, k_first);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -235,7 +266,8 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
         __syncthreads();
         if (kt + 1 < nk) {
             if (kt + 2 < nk) issue(lds0, k_first + kt + 2);
-            compute(lds1);
+            if constexpr (SQ) { const bool on = sq_on; sq_on = false; compute(lds1); sq_on = on; }
+            else compute(lds1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -257,6 +289,44 @@ void gemm_bf16_kernel(GemmArgs a, int mt, int nt, int gm, SplitPlan sp, int n_xc
                     *(f32x4*)(pt + ml * BN + nl0 + j) =
                         f32x4{acc[i][j][v], acc[i][j + 1][v], acc[i][j + 2][v], acc[i][j + 3][v]};
             }
+        return;
+    }
+    if constexpr (SQ) {
+        if (t.tn == 0 && wn == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                float v = sq[i];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (lq == 0) s_yy[wm * WTM + i * 16 + lr] = v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ml = wm * WTM + i * 16 + 4 * lq + v;
+                float p = 0.f;
+                if (s_src[ml] >= 0 && ng < a.N) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) p = __builtin_fmaf(acc[i][j][v], acc[i][j][v], p);
+                }
+                p += __shfl_xor(p, 1);
+                p += __shfl_xor(p, 2);
+                p += __shfl_xor(p, 4);
+                p += __shfl_xor(p, 8);
+                if (lr == 0) s_red[wn][ml] = p;
+            }
+        }
+        __syncthreads();
+        float* out = a.partial + ((int64_t)t.group * nt + t.tn) * a.M + m0;
+        for (int r = tid; r < BM; r += NW * 64) {
+            if (m0 + r >= a.M) continue;
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) s += s_red[w][r];
+            out[r] = (t.tn == 0 ? s_yy[r] : 0.f) - s;
+        }
         return;
     }
     if (a.epi == EPI_SCORE) {
@@ -787,7 +857,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     // once while the row operand stays resident in the last-level cache (measured fastest).
     const DeviceShape dv = device_shape();
     const bool indep = a.a_group_stride != 0;
-    if (indep && (a.epi != EPI_QKV || a.split_ws)) return hipErrorInvalidValue;
+    if (indep && ((a.epi != EPI_QKV && a.epi != EPI_SQNORM) || a.split_ws)) return hipErrorInvalidValue;
+    if ((a.epi == EPI_SQNORM) != (indep && a.K == 2 * a.K_a && a.kv_split > 0 && a.kv_split % BK == 0 &&
+                                  a.K_a % BK == 0))
+        return hipErrorInvalidValue;
     const int gm = a.groups > 1 && !indep ? mt
                                           : pick_group_rows(mt, nt * (indep ? 1 : a.groups), 256.0 * a.K_a,
                                                             256.0 * a.K, std::max(1, dv.cus / dv.xcds));
@@ -806,8 +879,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     SplitPlan sp = plan_split(a.M, a.N, a.K, a.groups, a.epi);
     if (sp.rem && !a.split_ws) sp = SplitPlan{sp.full + sp.rem, 0, 1};   // no workspace: whole tiles
     const int64_t grid = (int64_t)sp.full + (int64_t)sp.rem * sp.split;
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2>), dim3((unsigned)grid), dim3(512), 0, s, a, mt, nt, gm, sp,
-                       dv.xcds);
+    if (a.epi == EPI_SQNORM)
+        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2, true>), dim3((unsigned)grid), dim3(512), 0, s, a, mt, nt,
+                           gm, sp, dv.xcds);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 2, false>), dim3((unsigned)grid), dim3(512), 0, s, a, mt, nt,
+                           gm, sp, dv.xcds);
     if (sp.rem) {
         if (hipError_t e = hipGetLastError()) return e;
         hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3(65536 / (256 * 8), sp.rem), dim3(256), 0, s, a, mt, nt, gm, sp);

@@ -90,6 +90,101 @@ __global__ void pack_operator_kernel(const double* A, int r, int dtype, void* op
     o[r + col] = lo;
 }
 
+// =========================================================================== direct scoring of a stored cache
+// Calibration basis for the direct scoring: u [L][d_t][c] fp32 (columns orthonormal).  bf16: the
+// score GEMM's B operand [L][c][2 d_t], row j = direction j, its columns in 128-wide pairs of
+// chunks: [128 q, 128 q + 64) the bf16-rounded u[64 q + e][j] and [128 q + 64, 128 q + 128) the
+// bf16 rounding of what is left (so hi + lo carries u to about 2^-17); fp32: u copied as is.
+__global__ void pack_cache_basis_kernel(const float* u, int d_t, int c, int64_t n, int dtype, void* op) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float x = u[i];
+    if (dtype == KVX_F32) {
+        ((float*)op)[i] = x;
+        return;
+    }
+    const int64_t l = i / ((int64_t)d_t * c);
+    const int rem = (int)(i - l * d_t * c);
+    const int ch = rem / c, j = rem % c;
+    const bf16 hi = (bf16)x;
+    const bf16 lo = (bf16)(x - (float)hi);
+    bf16* o = (bf16*)op + (l * c + j) * 2 * d_t + (ch >> 6) * 128 + (ch & 63);
+    o[0] = hi;
+    o[64] = lo;
+}
+
+// fp32 cache: one 256-thread block per (position, layer).  The stored vector y = [K heads | V
+// heads] of the position's slot goes to LDS; the block sums y_i^2 and, one direction per thread
+// in turn, p_j = sum_i y_i u[i][j] (reads of u coalesced over j), then p_j^2; both block sums in
+// a fixed order.  energy[l][m] = |y|^2 - |p|^2.
+constexpr int DSC_THREADS = 256;
+__global__ __launch_bounds__(DSC_THREADS) void score_cache_f32_kernel(const float* kc, const float* vc,
+                                                                      int64_t layer_elems, int hd, SlotMap slots,
+                                                                      int n_req, const float* u, int c, float* energy,
+                                                                      int64_t M) {
+    extern __shared__ float s_y[];
+    __shared__ float red[2][DSC_THREADS / 64];
+    const int m = blockIdx.x, l = blockIdx.y;
+    const int b = find_request(slots.cu_tok, n_req, m);
+    const int64_t slot = slots.slot(b, m - slots.cu_tok[b]);
+    const int d_t = 2 * hd;
+    const float* kr = kc + l * layer_elems + slot * hd;
+    const float* vr = vc + l * layer_elems + slot * hd;
+    float yy = 0.f;
+    for (int i = threadIdx.x; i < hd; i += DSC_THREADS) {
+        const float a = kr[i], v = vr[i];
+        s_y[i] = a;
+        s_y[hd + i] = v;
+        yy = fmaf(a, a, yy);
+        yy = fmaf(v, v, yy);
+    }
+    __syncthreads();
+    const float* ul = u + (int64_t)l * d_t * c;
+    float pp = 0.f;
+    for (int j = threadIdx.x; j < c; j += DSC_THREADS) {
+        float p = 0.f;
+        for (int i = 0; i < d_t; ++i) p = fmaf(s_y[i], ul[(int64_t)i * c + j], p);
+        pp = fmaf(p, p, pp);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        yy += __shfl_xor(yy, o);
+        pp += __shfl_xor(pp, o);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = yy;
+        red[1][threadIdx.x >> 6] = pp;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float ty = 0.f, tp = 0.f;
+#pragma unroll
+        for (int w = 0; w < DSC_THREADS / 64; ++w) {
+            ty += red[0][w];
+            tp += red[1][w];
+        }
+        energy[(int64_t)l * M + m] = ty - tp;
+    }
+}
+
+// out[o][m] = sum_{i < n_inner} parts[(o * n_inner + i) * M + m] for o < n_outer (per_outer), or
+// out[m] = the sum over every o and i (both in ascending order, so the result is deterministic)
+__global__ void sum_parts_kernel(const float* parts, int n_outer, int n_inner, int64_t M, int per_outer,
+                                 float* out) {
+    const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M) return;
+    if (per_outer) {
+        const int o = blockIdx.y;
+        float s = 0.f;
+        for (int i = 0; i < n_inner; ++i) s += parts[((int64_t)o * n_inner + i) * M + m];
+        out[(int64_t)o * M + m] = s;
+        return;
+    }
+    float s = 0.f;
+    for (int j = 0; j < n_outer * n_inner; ++j) s += parts[(int64_t)j * M + m];
+    out[m] = s;
+}
+
 // =========================================================================== select
 // One workgroup of 1024 threads per request.  Keys are the fp32 score bits made
 // order-preserving as unsigned integers (-0.0 folded onto +0.0).  The k-th largest key is
@@ -141,7 +236,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
                                                             int64_t n_rows, float* scores,
                                                             const int32_t* cu_tok,
                                                             const int32_t* cu_sel, int32_t* sel,
-                                                            int32_t* rest) {
+                                                            int32_t* rest, int64_t n_sel_all) {
     __shared__ int hist[SEL_WAVES][256];
     __shared__ uint32_t s_key[SEL_CAP];
     __shared__ int s_wave[SEL_WAVES];
@@ -149,6 +244,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* partia
     __shared__ int s_bc[2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = blockIdx.x;
+    // blockIdx.y: the layer of per-layer scores (no partials then), each with its own outputs
+    scores += (int64_t)blockIdx.y * n_rows;
+    sel += (int64_t)blockIdx.y * n_sel_all;
+    rest += (int64_t)blockIdx.y * (n_rows - n_sel_all);
     const int base = cu_tok[b], T = cu_tok[b + 1] - base;
     const int k = cu_sel[b + 1] - cu_sel[b];
     int32_t* so = sel + cu_sel[b];
@@ -682,10 +781,12 @@ hipError_t launch_pack_operator(const double* A, int r, int dtype, void* op, hip
 
 hipError_t launch_select(const float* partial, int n_part, int64_t n_rows, float* scores,
                          const int32_t* cu_tok, const int32_t* cu_sel, int n_req, int32_t* sel,
-                         int32_t* rest, hipStream_t s, const float* partial2, int n_part2) {
-    if (n_req == 0) return hipSuccess;
-    hipLaunchKernelGGL(select_kernel, dim3(n_req), dim3(SEL_THREADS), 0, s, partial, n_part, partial2, n_part2,
-                       n_rows, scores, cu_tok, cu_sel, sel, rest);
+                         int32_t* rest, hipStream_t s, const float* partial2, int n_part2, int n_layers,
+                         int64_t n_sel_all) {
+    if (n_req == 0 || n_layers == 0) return hipSuccess;
+    if (n_layers > 1 && (n_part > 0 || n_part2 > 0)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(select_kernel, dim3(n_req, n_layers), dim3(SEL_THREADS), 0, s, partial, n_part, partial2,
+                       n_part2, n_rows, scores, cu_tok, cu_sel, sel, rest, n_sel_all);
     return hipGetLastError();
 }
 
@@ -722,6 +823,30 @@ hipError_t launch_gemm_f32(const GemmF32Args& a, hipStream_t s) {
 hipError_t launch_rowdot_f32(const float* P, const float* Z, int64_t n, int r, float* out, hipStream_t s) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(rowdot_f32_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, P, Z, n, r, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_cache_basis(const float* u, int L, int d_t, int c, int dtype, void* op, hipStream_t s) {
+    const int64_t n = (int64_t)L * d_t * c;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_cache_basis_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, u, d_t, c, n, dtype,
+                       op);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_cache_f32(const float* kc, const float* vc, int64_t layer_elems, int hd, const SlotMap& slots,
+                                  int n_req, int64_t M, int L, const float* u, int c, float* energy, hipStream_t s) {
+    if (M == 0 || L == 0) return hipSuccess;
+    hipLaunchKernelGGL(score_cache_f32_kernel, dim3((unsigned)M, (unsigned)L), dim3(DSC_THREADS),
+                       (size_t)2 * hd * sizeof(float), s, kc, vc, layer_elems, hd, slots, n_req, u, c, energy, M);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const float* parts, int n_outer, int n_inner, int64_t M, bool per_outer, float* out,
+                            hipStream_t s) {
+    if (M == 0 || n_outer == 0) return hipSuccess;
+    hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((M + 255) / 256), per_outer ? n_outer : 1), dim3(256), 0, s,
+                       parts, n_outer, n_inner, M, per_outer ? 1 : 0, out);
     return hipGetLastError();
 }
 

@@ -435,6 +435,19 @@ kvx_status kvx_score_select_workspace(int32_t dtype, int32_t r, int64_t n, size_
 
 namespace {
 
+// Every request's selected count is the budget of its percentage.
+kvx_status check_budgets(const kvx_batch* batch, const BatchInfo& bi, const int32_t* budget_pct) {
+    for (int b = 0; b < bi.n_req; ++b) {
+        const int T = batch->cu_tokens_h[b + 1] - batch->cu_tokens_h[b];
+        const int k = batch->cu_sel_h[b + 1] - batch->cu_sel_h[b];
+        KVX_REQUIRE(budget_pct[b] >= 0 && budget_pct[b] <= 100, "budget_pct[%d] = %d outside [0, 100]", b,
+                    budget_pct[b]);
+        KVX_REQUIRE(k == budget_of(T, budget_pct[b]), "request %d: cu_sel gives %d positions but the "
+                    "budget of %d%% of %d is %d", b, k, budget_pct[b], T, budget_of(T, budget_pct[b]));
+    }
+    return KVX_OK;
+}
+
 // Arguments of kvx_score_select other than its workspace.
 kvx_status check_score_select(int32_t dtype, const void* z, const void* op, int32_t r, const kvx_batch* batch,
                               const int32_t* budget_pct, const float* scores, const int32_t* sel,
@@ -450,14 +463,7 @@ kvx_status check_score_select(int32_t dtype, const void* z, const void* op, int3
     if (dtype == KVX_BF16) KVX_REQUIRE(r % 64 == 0, "bf16 needs r %% 64 == 0 (got %d)", r);
     if (bi.n_sel > 0) KVX_REQUIRE_PTR(sel, "sel");
     if (bi.n_rest > 0) KVX_REQUIRE_PTR(rest, "rest");
-    for (int b = 0; b < bi.n_req; ++b) {
-        const int T = batch->cu_tokens_h[b + 1] - batch->cu_tokens_h[b];
-        const int k = batch->cu_sel_h[b + 1] - batch->cu_sel_h[b];
-        KVX_REQUIRE(budget_pct[b] >= 0 && budget_pct[b] <= 100, "budget_pct[%d] = %d outside [0, 100]", b,
-                    budget_pct[b]);
-        KVX_REQUIRE(k == budget_of(T, budget_pct[b]), "request %d: cu_sel gives %d positions but the "
-                    "budget of %d%% of %d is %d", b, k, budget_pct[b], T, budget_of(T, budget_pct[b]));
-    }
+    if (kvx_status st = check_budgets(batch, bi, budget_pct)) return st;
     KVX_REQUIRE(bi.n_tokens <= INT32_MAX, "too many rows");
     return KVX_OK;
 }
@@ -1468,6 +1474,157 @@ kvx_status kvx_argmax(void* stream, int32_t dtype, const void* logits, int64_t n
     KVX_REQUIRE_PTR(logits, "logits");
     KVX_REQUIRE(out && aligned16(out), "out must be a 16-byte aligned pointer");
     return hip_status(launch_argmax_bf16((const bf16*)logits, n, V, out, (hipStream_t)stream), "argmax");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Arguments of the direct scoring calls other than the outputs and the workspace.
+kvx_status check_score_cache(int32_t dtype, const kvx_cache* cache, int32_t layer0, int32_t n_layers, int32_t H_kv,
+                             int32_t d_h, const void* op, int32_t c, const kvx_batch* batch, BatchInfo* bi) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    if (kvx_status st = check_batch(batch, bi)) return st;
+    KVX_REQUIRE(layer0 >= 0 && n_layers >= 1 && n_layers <= 65535, "need layer0 >= 0 and n_layers in [1, 65535] "
+                "(got %d, %d)", layer0, n_layers);
+    KVX_REQUIRE(H_kv > 0 && d_h > 0 && d_h % 8 == 0, "H_kv must be positive and d_h a positive multiple of 8");
+    KVX_REQUIRE((int64_t)H_kv * d_h <= (1 << 20), "H_kv * d_h too large");
+    const int d_t = 2 * H_kv * d_h;
+    KVX_REQUIRE(c >= 1 && c <= d_t, "c must be in [1, d_t = %d] (got %d)", d_t, c);
+    if (dtype == KVX_BF16) {
+        KVX_REQUIRE((H_kv * d_h) % 64 == 0, "bf16 needs H_kv * d_h %% 64 == 0 (got %d)", H_kv * d_h);
+        KVX_REQUIRE(c % 8 == 0, "bf16 needs c %% 8 == 0 (got %d)", c);
+    } else {
+        KVX_REQUIRE(d_t <= 8192, "fp32 needs d_t <= 8192 (got %d)", d_t);
+    }
+    KVX_REQUIRE_PTR(op, "op");
+    if (kvx_status st = check_cache(cache, *bi, dtype, H_kv, d_h, 1)) return st;
+    KVX_REQUIRE((int64_t)layer0 + n_layers <= cache->n_layers, "layers [%d, %d) outside the cache's %d layers",
+                layer0, layer0 + n_layers, cache->n_layers);
+    KVX_REQUIRE(bi->n_tokens <= INT32_MAX, "too many rows");
+    KVX_REQUIRE((uintptr_t)cache->k % 16 == 0 && (uintptr_t)cache->v % 16 == 0, "cache.k and cache.v must be "
+                "16-byte aligned");
+    return check_page_table_debug(cache, batch);
+}
+
+size_t score_cache_ws_bytes(int32_t dtype, int32_t n_layers, int32_t c, int64_t n) {
+    const int64_t inner = dtype == KVX_BF16 ? cdiv(c, gemm_bf16_block_n()) : 1;
+    return round256((size_t)n_layers * inner * n * 4);
+}
+
+// Per-layer energies of the scored layers as partials in ws: [n_layers][*n_inner][N].
+hipError_t score_cache_parts(hipStream_t s, int32_t dtype, const kvx_cache* cache, int32_t layer0, int32_t n_layers,
+                             int32_t H_kv, int32_t d_h, const void* op, int32_t c, const kvx_batch* batch,
+                             const BatchInfo& bi, float* parts, int* n_inner) {
+    const int hd = H_kv * d_h, d_t = 2 * hd;
+    const int64_t layer_elems = cache->n_slots * hd;
+    const SlotMap slots = slot_map(cache, batch);
+    if (dtype == KVX_F32) {
+        *n_inner = 1;
+        return launch_score_cache_f32((const float*)cache->k + layer0 * layer_elems,
+                                      (const float*)cache->v + layer0 * layer_elems, layer_elems, hd, slots, bi.n_req,
+                                      bi.n_tokens, n_layers, (const float*)op, c, parts, s);
+    }
+    GemmArgs a{};
+    a.A = (const bf16*)cache->k + layer0 * layer_elems; a.lda = hd; a.K_a = d_t;
+    a.kv_delta = ((int64_t)(uintptr_t)cache->v - (int64_t)(uintptr_t)cache->k) / (int64_t)sizeof(bf16);
+    a.kv_split = hd;
+    a.a_group_stride = layer_elems;
+    a.B = (const bf16*)op; a.ldb = 2 * d_t; a.b_group_stride = (int64_t)c * 2 * d_t;
+    a.M = (int)bi.n_tokens; a.N = c; a.K = 2 * d_t; a.groups = n_layers;
+    a.rows.mode = 1; a.rows.cu_tok = batch->cu_tokens_d; a.rows.cu_sel = batch->cu_sel_d; a.rows.n_req = bi.n_req;
+    a.slots = slots;
+    a.epi = EPI_SQNORM; a.partial = parts;
+    *n_inner = cdiv(c, gemm_bf16_block_n());
+    return launch_gemm_bf16(a, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvx_status kvx_score_cache_prepare(void* stream, int32_t dtype, const float* u, int32_t n_layers, int32_t d_t,
+                                   int32_t c, void* op) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    KVX_REQUIRE(n_layers >= 1 && d_t >= 1 && c >= 1 && c <= d_t, "need n_layers >= 1 and 1 <= c <= d_t "
+                "(got %d, %d, %d)", n_layers, c, d_t);
+    KVX_REQUIRE((int64_t)n_layers * d_t * c <= ((int64_t)1 << 40), "basis too large");
+    if (dtype == KVX_BF16) {
+        KVX_REQUIRE(d_t % 128 == 0, "bf16 needs d_t %% 128 == 0 (got %d)", d_t);
+        KVX_REQUIRE(c % 8 == 0, "bf16 needs c %% 8 == 0 (got %d)", c);
+    }
+    KVX_REQUIRE_PTR(u, "u");
+    KVX_REQUIRE_PTR(op, "op");
+    return hip_status(launch_pack_cache_basis(u, n_layers, d_t, c, dtype, op, (hipStream_t)stream),
+                      "score_cache_prepare");
+}
+
+kvx_status kvx_score_cache_workspace(int32_t dtype, int32_t n_layers, int32_t c, int64_t n, size_t* bytes) {
+    if (kvx_status st = check_dtype(dtype)) return st;
+    KVX_REQUIRE(bytes, "bytes must not be null");
+    KVX_REQUIRE(n_layers >= 1 && c >= 1 && n >= 0 && n <= INT32_MAX, "need n_layers >= 1, c >= 1 and n in [0, 2^31)");
+    *bytes = score_cache_ws_bytes(dtype, n_layers, c, n);
+    return ok();
+}
+
+kvx_status kvx_score_cache(void* stream, int32_t dtype, const kvx_cache* cache, int32_t layer0, int32_t n_layers,
+                           int32_t H_kv, int32_t d_h, const void* op, int32_t c, const kvx_batch* batch,
+                           float* energy, void* ws, size_t ws_bytes) {
+    BatchInfo bi;
+    if (kvx_status st = check_score_cache(dtype, cache, layer0, n_layers, H_kv, d_h, op, c, batch, &bi)) return st;
+    if (bi.n_tokens == 0) return ok();
+    KVX_REQUIRE_PTR(energy, "energy");
+    const size_t need = score_cache_ws_bytes(dtype, n_layers, c, bi.n_tokens);
+    if (kvx_status st = check_ws(need, ws, ws_bytes, "score_cache")) return st;
+    hipStream_t s = (hipStream_t)stream;
+    int inner = 0;
+    if (dtype == KVX_F32)       // one partial per layer: the energies are written in place
+        return hip_status(score_cache_parts(s, dtype, cache, layer0, n_layers, H_kv, d_h, op, c, batch, bi, energy,
+                                            &inner),
+                          "score_cache");
+    KVX_TRY_HIP(score_cache_parts(s, dtype, cache, layer0, n_layers, H_kv, d_h, op, c, batch, bi, (float*)ws, &inner),
+                "score_cache");
+    return hip_status(launch_sum_parts((const float*)ws, n_layers, inner, bi.n_tokens, true, energy, s),
+                      "score_cache (layer sums)");
+}
+
+kvx_status kvx_score_cache_select(void* stream, int32_t dtype, const kvx_cache* cache, int32_t layer0,
+                                  int32_t n_layers, int32_t H_kv, int32_t d_h, const void* op, int32_t c,
+                                  const kvx_batch* batch, const int32_t* budget_pct, float* scores, int32_t* sel,
+                                  int32_t* rest, void* ws, size_t ws_bytes) {
+    BatchInfo bi;
+    if (kvx_status st = check_score_cache(dtype, cache, layer0, n_layers, H_kv, d_h, op, c, batch, &bi)) return st;
+    KVX_REQUIRE(budget_pct, "budget_pct must not be null");
+    if (kvx_status st = check_budgets(batch, bi, budget_pct)) return st;
+    if (bi.n_tokens == 0) return ok();
+    KVX_REQUIRE_PTR(scores, "scores");
+    if (bi.n_sel > 0) KVX_REQUIRE_PTR(sel, "sel");
+    if (bi.n_rest > 0) KVX_REQUIRE_PTR(rest, "rest");
+    const size_t need = score_cache_ws_bytes(dtype, n_layers, c, bi.n_tokens);
+    if (kvx_status st = check_ws(need, ws, ws_bytes, "score_cache_select")) return st;
+    hipStream_t s = (hipStream_t)stream;
+    int inner = 0;
+    KVX_TRY_HIP(score_cache_parts(s, dtype, cache, layer0, n_layers, H_kv, d_h, op, c, batch, bi, (float*)ws, &inner),
+                "score_cache");
+    KVX_TRY_HIP(launch_sum_parts((const float*)ws, n_layers, inner, bi.n_tokens, false, scores, s),
+                "score_cache (sums)");
+    return hip_status(launch_select(nullptr, 0, bi.n_tokens, scores, batch->cu_tokens_d, batch->cu_sel_d, bi.n_req,
+                                    sel, rest, s),
+                      "select");
+}
+
+kvx_status kvx_select_topk_layers(void* stream, const float* scores, int32_t n_layers, const kvx_batch* batch,
+                                  int32_t* sel, int32_t* rest) {
+    BatchInfo bi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    KVX_REQUIRE(n_layers >= 1 && n_layers <= 65535, "n_layers must be in [1, 65535] (got %d)", n_layers);
+    if (bi.n_tokens == 0) return ok();
+    KVX_REQUIRE_PTR(scores, "scores");
+    if (bi.n_sel > 0) KVX_REQUIRE_PTR(sel, "sel");
+    if (bi.n_rest > 0) KVX_REQUIRE_PTR(rest, "rest");
+    return hip_status(launch_select(nullptr, 0, bi.n_tokens, (float*)scores, batch->cu_tokens_d, batch->cu_sel_d,
+                                    bi.n_req, sel, rest, (hipStream_t)stream, nullptr, 0, n_layers, bi.n_sel),
+                      "select_topk_layers");
 }
 
 }  // extern "C"

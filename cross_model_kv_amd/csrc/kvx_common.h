@@ -118,7 +118,8 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& rm, int m) {
     return r;
 }
 
-enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2, EPI_QKV = 3, EPI_RESID = 4, EPI_SWIGLU = 5, EPI_F32 = 6 };
+enum EpiKind { EPI_STORE = 0, EPI_CACHE = 1, EPI_SCORE = 2, EPI_QKV = 3, EPI_RESID = 4, EPI_SWIGLU = 5, EPI_F32 = 6,
+               EPI_SQNORM = 7 };
 
 struct GemmArgs {
     // C[m][n] = sum_k A[src(m)][k mod K_a] * B[n][k]
@@ -154,6 +155,13 @@ struct GemmArgs {
     // EPI_SWIGLU: B row n is row (n/16)*8 + n%8 of the gate weight B (n/8 even) or of the up
     // weight B2 (n/8 odd); C[m][f] = silu(gate_f) * up_f for f = (n/16)*8 + n%8, N = 2F
     const bf16* B2;
+    // EPI_SQNORM (direct scoring of a stored cache, independent groups = layers): A row m is the
+    // stored vector of row m's cache slot, its columns [0, kv_split) in the K array at A and
+    // [kv_split, K_a) in the V array at A + kv_delta (elements); K = 2 K_a, and K step kt reads A
+    // columns [(kt/2) BK, (kt/2 + 1) BK) against B columns [kt BK, (kt + 1) BK) (each A chunk
+    // twice, once against the high and once against the low bf16 half of the basis).
+    // partial[(g * nt + tn) * M + m] = (tn == 0 ? sum_k A[m][k]^2 : 0) - sum_{n in tile} C[m][n]^2
+    int64_t kv_delta; int32_t kv_split;
 };
 
 // Rotate-half of one pair, in the order every kernel uses (results are bit-identical):

@@ -29,9 +29,21 @@ hipError_t launch_fit_calibration(hipStream_t s, int dtype, const void* z, const
 // ---- selection: scores[t] = sum_p partial[p][t] (when n_part > 0; divided by
 //      sum_p partial2[p][t] when n_part2 > 0, 0 where that is 0), then the k_b largest per
 //      request (ties to the lower position) written ascending to sel, the rest to rest.
+//      n_layers > 1 (scores only, no partials): scores [n_layers][n_rows], every layer selected
+//      on its own into sel [n_layers][n_sel_all] and rest [n_layers][n_rows - n_sel_all].
 hipError_t launch_select(const float* partial, int n_part, int64_t n_rows, float* scores,
                          const int32_t* cu_tok, const int32_t* cu_sel, int n_req, int32_t* sel,
-                         int32_t* rest, hipStream_t s, const float* partial2 = nullptr, int n_part2 = 0);
+                         int32_t* rest, hipStream_t s, const float* partial2 = nullptr, int n_part2 = 0,
+                         int n_layers = 1, int64_t n_sel_all = 0);
+
+// ---- direct scoring of a stored cache: the calibration bases packed for the score GEMM (bf16:
+//      hi/lo pairs of 64-column chunks, [L][c][2 d_t]; fp32: a copy of u [L][d_t][c]), the fp32
+//      path's per-layer energies, and fixed-order sums of per-tile partials
+hipError_t launch_pack_cache_basis(const float* u, int L, int d_t, int c, int dtype, void* op, hipStream_t s);
+hipError_t launch_score_cache_f32(const float* kc, const float* vc, int64_t layer_elems, int hd, const SlotMap& slots,
+                                  int n_req, int64_t M, int L, const float* u, int c, float* energy, hipStream_t s);
+hipError_t launch_sum_parts(const float* parts, int n_outer, int n_inner, int64_t M, bool per_outer, float* out,
+                            hipStream_t s);
 
 // ---- rotary table [max_pos][d_h/2][2] (cos, sin), angles in fp64
 hipError_t launch_rope_table(double base, int d_h, int max_pos, float* table, hipStream_t s);

@@ -68,6 +68,13 @@ _SIGS = {
     "kvx_score_select_normalized_workspace": ([_I32, _I32, ctypes.c_int64, ctypes.POINTER(_SZ)], _I32),
     "kvx_score_select_normalized": ([_P, _I32, _P, _P, _P, _I32, ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P,
                                      _P, _P, _P, _SZ], _I32),
+    "kvx_score_cache_prepare": ([_P, _I32, _P, _I32, _I32, _I32, _P], _I32),
+    "kvx_score_cache_workspace": ([_I32, _I32, _I32, _I64, ctypes.POINTER(_SZ)], _I32),
+    "kvx_score_cache": ([_P, _I32, ctypes.POINTER(_Cache), _I32, _I32, _I32, _I32, _P, _I32, ctypes.POINTER(_Batch),
+                         _P, _P, _SZ], _I32),
+    "kvx_score_cache_select": ([_P, _I32, ctypes.POINTER(_Cache), _I32, _I32, _I32, _I32, _P, _I32,
+                                ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P, _P, _P, _P, _SZ], _I32),
+    "kvx_select_topk_layers": ([_P, _P, _I32, ctypes.POINTER(_Batch), _P, _P], _I32),
     "kvx_fit_mapper_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_fit_mapper": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _I32, _P, _P, _P, _SZ],
                        _I32),
@@ -307,6 +314,83 @@ def score_select(z: torch.Tensor, op: torch.Tensor, batch: Batch, pcts: Sequence
                                                       ctypes.byref(batch.c), pct, _ptr(scores), _ptr(sel),
                                                       _ptr(rest), _ptr(ws), need))
     return scores, sel[:batch.total_sel], rest[:batch.total_rest]
+
+
+def score_cache_prepare(u: torch.Tensor, dtype: int) -> torch.Tensor:
+    """Calibration bases u [n_layers][d_t][c] fp32 packed for the direct scoring of a cache of
+    storage dtype `dtype` (BF16 or F32)."""
+    L, d_t, c = u.shape
+    op = (torch.empty((L, c, 2 * d_t), dtype=torch.bfloat16, device=u.device) if dtype == BF16
+          else torch.empty((L, d_t, c), dtype=torch.float32, device=u.device))
+    _check("kvx_score_cache_prepare", lib().kvx_score_cache_prepare(_stream(u.device), dtype, _ptr(u), L, d_t, c,
+                                                                    _ptr(op)))
+    return op
+
+
+def _score_cache_ws(dt: int, n_layers: int, c: int, n: int, ws, dev):
+    b = _SZ()
+    _check("kvx_score_cache_workspace", lib().kvx_score_cache_workspace(dt, n_layers, c, n, ctypes.byref(b)))
+    if ws is None or ws.numel() < b.value:
+        ws = torch.empty(max(b.value, 16), dtype=torch.uint8, device=dev)
+    return ws
+
+
+def _op_shape(op: torch.Tensor):
+    """(n_layers, c) of a packed basis."""
+    return (op.shape[0], op.shape[1]) if op.dtype == torch.bfloat16 else (op.shape[0], op.shape[2])
+
+
+def score_cache(cache: Cache, layer0: int, H_kv: int, d_h: int, op: torch.Tensor, batch: Batch,
+                energy: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Energy outside the calibration subspace of every position's stored K/V, per scored layer:
+    [n_layers][N] fp32 for the layers [layer0, layer0 + n_layers) of `cache`."""
+    dev = cache.k.device
+    dt = _dtype(cache.k)
+    n_layers, c = _op_shape(op)
+    if energy is None:
+        energy = torch.empty((n_layers, max(batch.n_tokens, 1)), dtype=torch.float32, device=dev)
+    ws = _score_cache_ws(dt, n_layers, c, batch.n_tokens, ws, dev)
+    _check("kvx_score_cache", lib().kvx_score_cache(_stream(dev), dt, ctypes.byref(cache.c), layer0, n_layers, H_kv,
+                                                    d_h, _ptr(op), c, ctypes.byref(batch.c), _ptr(energy), _ptr(ws),
+                                                    ws.numel()))
+    return energy[:, :batch.n_tokens]
+
+
+def score_cache_select(cache: Cache, layer0: int, H_kv: int, d_h: int, op: torch.Tensor, batch: Batch,
+                       pcts: Sequence[int], ws: Optional[torch.Tensor] = None, out=None):
+    """Scores summed over the scored layers' stored K/V and their top-budget selection."""
+    dev = cache.k.device
+    dt = _dtype(cache.k)
+    n_layers, c = _op_shape(op)
+    ws = _score_cache_ws(dt, n_layers, c, batch.n_tokens, ws, dev)
+    if out is None:
+        scores = torch.empty(max(batch.n_tokens, 1), dtype=torch.float32, device=dev)
+        sel = torch.empty(max(batch.total_sel, 1), dtype=torch.int32, device=dev)
+        rest = torch.empty(max(batch.total_rest, 1), dtype=torch.int32, device=dev)
+    else:
+        scores, sel, rest = out
+    pct = (ctypes.c_int32 * batch.n_req)(*[int(p) for p in pcts])
+    _check("kvx_score_cache_select", lib().kvx_score_cache_select(
+        _stream(dev), dt, ctypes.byref(cache.c), layer0, n_layers, H_kv, d_h, _ptr(op), c, ctypes.byref(batch.c), pct,
+        _ptr(scores), _ptr(sel), _ptr(rest), _ptr(ws), ws.numel()))
+    return scores[:batch.n_tokens], sel[:batch.total_sel], rest[:batch.total_rest]
+
+
+def select_topk_layers(scores: torch.Tensor, batch: Batch, out=None):
+    """Every layer's own top-k: scores [n_layers][N] -> sel [n_layers][K], rest [n_layers][N - K]."""
+    dev = scores.device
+    n_layers = scores.shape[0]
+    if out is None:
+        sel = torch.empty((n_layers, max(batch.total_sel, 1)), dtype=torch.int32, device=dev)
+        rest = torch.empty((n_layers, max(batch.total_rest, 1)), dtype=torch.int32, device=dev)
+    else:
+        sel, rest = out
+    assert scores.is_contiguous() and scores.shape[1] == batch.n_tokens
+    assert sel.shape[1] == batch.total_sel or batch.total_sel == 0
+    assert rest.shape[1] == batch.total_rest or batch.total_rest == 0
+    _check("kvx_select_topk_layers", lib().kvx_select_topk_layers(_stream(dev), _ptr(scores), n_layers,
+                                                                  ctypes.byref(batch.c), _ptr(sel), _ptr(rest)))
+    return sel[:, :batch.total_sel], rest[:, :batch.total_rest]
 
 
 def score_select_normalized(z: torch.Tensor, op: torch.Tensor, op_total: torch.Tensor, batch: Batch,

@@ -203,6 +203,49 @@ KVX_API kvx_status kvx_score_select_normalized(void* stream, int32_t dtype, cons
                                                const int32_t* budget_pct, float* scores, int32_t* sel,
                                                int32_t* rest, void* ws, size_t ws_bytes);
 
+/* Direct scoring of a stored cache (an unranked variant of the RaReCache abstract's score, for a
+ * mapper that is not linear, whose cache has no latent form).  For every scored layer l and every
+ * position t of the batch, with y = [K heads | V heads] of t's slot in cache layer layer0 + l (the
+ * order kvx_reconstruct splits), the energy outside the calibration subspace:
+ *   E[l][t] = |y|^2 - |U_l^T y|^2   (= |(I - U_l U_l^T) y|^2 for orthonormal U_l).
+ * kvx_score_cache_prepare packs the bases once:
+ *   u (device) [n_layers][d_t][c] fp32, orthonormal columns (the bases of the scored layers, in
+ *   order); op (device, out) of 4 * n_layers * d_t * c bytes:
+ *     bf16: [n_layers][c][2 d_t] bf16, row j: for every 64-channel chunk q the 64 values bf16(u)
+ *           then the 64 values bf16(u - bf16(u)) (the two halves of the score GEMM's operand);
+ *     f32:  a copy of u.
+ *   bf16 needs d_t % 128 == 0 and c % 8 == 0; c in [1, d_t].
+ * kvx_score_cache: energy (device, out) [n_layers][N] fp32.  bf16: one matrix-core GEMM over all
+ *   scored layers (the stored rows gathered by slot straight from the cache, each 64-channel chunk
+ *   against both halves of the basis; |y|^2 from the same fragments), then a fixed-order sum of its
+ *   per-256-direction partials; fp32: one block per (position, layer).  Deterministic.
+ *   cache as in kvx_reconstruct (contiguous or paged), layers [layer0, layer0 + n_layers) inside
+ *   it; H_kv * d_h = d_t / 2 (bf16: a multiple of 64; fp32: d_t <= 8192); op from
+ *   kvx_score_cache_prepare with the same dtype, n_layers, d_t and c; ws (device) of
+ *   kvx_score_cache_workspace() bytes (bf16: 4 * n_layers * ceil(c / 256) * N rounded up to 256;
+ *   fp32: 4 * n_layers * N rounded up).
+ * kvx_score_cache_select: scores (device, out) [N] = sum over the scored layers of E (in layer
+ *   order), then the selection of kvx_score_select (budget_pct, sel, rest as there). */
+KVX_API kvx_status kvx_score_cache_prepare(void* stream, int32_t dtype, const float* u, int32_t n_layers,
+                                           int32_t d_t, int32_t c, void* op);
+KVX_API kvx_status kvx_score_cache_workspace(int32_t dtype, int32_t n_layers, int32_t c, int64_t n, size_t* bytes);
+KVX_API kvx_status kvx_score_cache(void* stream, int32_t dtype, const kvx_cache* cache, int32_t layer0,
+                                   int32_t n_layers, int32_t H_kv, int32_t d_h, const void* op, int32_t c,
+                                   const kvx_batch* batch, float* energy, void* ws, size_t ws_bytes);
+KVX_API kvx_status kvx_score_cache_select(void* stream, int32_t dtype, const kvx_cache* cache, int32_t layer0,
+                                          int32_t n_layers, int32_t H_kv, int32_t d_h, const void* op, int32_t c,
+                                          const kvx_batch* batch, const int32_t* budget_pct, float* scores,
+                                          int32_t* sel, int32_t* rest, void* ws, size_t ws_bytes);
+
+/* Per-layer selection sets (an unranked variant: every layer recomputes its own positions): the
+ * selection of kvx_select_topk applied to each layer's scores on its own.  scores (device)
+ * [n_layers][N] fp32, finite (e.g. kvx_score_cache's energies); sel (device, out)
+ * [n_layers][cu_sel[n_req]] and rest (device, out) [n_layers][N - cu_sel[n_req]], row l laid out
+ * as kvx_select_topk lays out its single set.  Every layer takes cu_sel[b+1] - cu_sel[b] positions
+ * of request b.  Row l of sel then serves as the `sel` of layer l's kvx_recompute_attn. */
+KVX_API kvx_status kvx_select_topk_layers(void* stream, const float* scores, int32_t n_layers,
+                                          const kvx_batch* batch, int32_t* sel, int32_t* rest);
+
 /* Top-k of given scores per request: the k_b largest scores of request b, ties to the
  * lower position, -0.0 equal to +0.0.  scores (device) [N] fp32, finite.
  * sel (device, out) [cu_sel[n_req]] request-local positions, ascending per request;

@@ -191,6 +191,51 @@ def test_score_select_normalized_validation():
     status(L.kvx_score_select_normalized(*args(wsb=need.value - 1)), WORKSPACE)
 
 
+def test_score_cache_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    pct = (ctypes.c_int32 * 2)(30, 30)
+    c = cache(n_layers=3)
+    # prepare: shapes of the packed basis
+    status(L.kvx_score_cache_prepare(None, 1, A16, 2, 192, 16, A16B), INVALID, "d_t % 128")
+    status(L.kvx_score_cache_prepare(None, 1, A16, 2, 256, 12, A16B), INVALID, "c % 8")
+    status(L.kvx_score_cache_prepare(None, 1, A16, 2, 256, 300, A16B), INVALID, "c <= d_t")
+    status(L.kvx_score_cache_prepare(None, 1, None, 2, 256, 16, A16B), INVALID, "u")
+    status(L.kvx_score_cache_prepare(None, 3, A16, 2, 256, 16, A16B), UNSUPPORTED, "dtype")
+    # workspace: bf16 one partial per 256 directions and layer, fp32 one per layer
+    b16, b32 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.kvx_score_cache_workspace(1, 2, 300, 150, ctypes.byref(b16)) == 0 and b16.value == -(-2 * 2 * 150 * 4 // 256) * 256
+    assert L.kvx_score_cache_workspace(0, 2, 300, 150, ctypes.byref(b32)) == 0 and b32.value == -(-2 * 150 * 4 // 256) * 256
+    need = ctypes.c_size_t()
+    assert L.kvx_score_cache_workspace(1, 2, 64, 150, ctypes.byref(need)) == 0
+
+    def call(dt=1, l0=0, n=2, H_kv=2, d_h=64, op=A16B, cc=64, cch=c, energy=A16, ws=A16, wsb=None):
+        return L.kvx_score_cache(None, dt, ctypes.byref(cch), l0, n, H_kv, d_h, op, cc, ctypes.byref(bt.c), energy,
+                                 ws, need.value if wsb is None else wsb)
+    status(call(l0=2), INVALID, "outside the cache")
+    status(call(n=0), INVALID, "n_layers")
+    status(call(H_kv=1, d_h=40), INVALID, "% 64")
+    status(call(cc=12), INVALID, "c % 8")
+    status(call(cc=257), INVALID, "c must be in")
+    status(call(op=None), INVALID, "op")
+    status(call(energy=None), INVALID, "energy")
+    status(call(ws=None), WORKSPACE)
+    status(call(wsb=need.value - 1), WORKSPACE)
+    status(call(cch=cache(n_layers=3, n_slots=100)), INVALID, "n_slots")
+    status(call(dt=0, H_kv=64, d_h=80), INVALID, "d_t <= 8192")
+    # the summed score and its selection: budgets as in kvx_score_select
+    bad = (ctypes.c_int32 * 2)(30, 40)
+    sargs = lambda p=pct, wsb=need.value: (None, 1, ctypes.byref(c), 0, 2, 2, 64, A16B, 64, ctypes.byref(bt.c), p,
+                                           A16, A16, A16, A16, wsb)
+    status(L.kvx_score_cache_select(*sargs(p=bad)), INVALID, "budget")
+    status(L.kvx_score_cache_select(*sargs(p=None)), INVALID, "budget_pct")
+    status(L.kvx_score_cache_select(*sargs(wsb=need.value - 1)), WORKSPACE)
+    # per-layer selection
+    status(L.kvx_select_topk_layers(None, A16, 0, ctypes.byref(bt.c), A16, A16), INVALID, "n_layers")
+    status(L.kvx_select_topk_layers(None, None, 2, ctypes.byref(bt.c), A16, A16), INVALID, "scores")
+    status(L.kvx_select_topk_layers(None, A16, 2, ctypes.byref(bt.c), None, A16), INVALID, "sel")
+
+
 def test_reconstruct_validation():
     L = kvx.lib()
     bt = FakeBatch([100, 50], [30, 15])
