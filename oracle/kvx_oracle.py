@@ -34,7 +34,8 @@ normalisation, a SiLU-gated MLP and a second residual add - with no norm on q or
 
 Variants (unranked on the pages' list of next steps, each its own function): the score as a share
 of the token's energy, the keys of a mapper without rotary phase, QK-norm on the recomputed q and
-k, the score taken directly from a stored cache layer by layer, and per-layer selection sets.
+k, the score taken directly from a stored cache layer by layer, per-layer selection sets, and
+selection of whole pages of positions.
 
 Fitting (before the path): the mapper is fitted in closed form to paired calibration KV of the
 two models - reduced-rank ridge regression, the rank-r least-squares map from source KV to the
@@ -186,6 +187,29 @@ def select(s: np.ndarray, k: int):
 # ------------------------------------------------------------------------------------
 # contextual recomputation of the selected positions
 # ------------------------------------------------------------------------------------
+
+def page_scores(s: np.ndarray, page_size: int) -> np.ndarray:
+    """Page-granular scoring (an unranked variant, after the block-rounded repair sets of the PatchKV
+    abstract on the CacheReforge card): a request's positions fall into pages of page_size
+    consecutive positions, page j holding [j * page_size, min((j + 1) * page_size, T)) (the last
+    page may be short); a page's score is the sum of its positions' scores."""
+    T = s.shape[0]
+    n_pages = -(-T // page_size)
+    return np.array([np.sum(s[j * page_size:min((j + 1) * page_size, T)]) for j in range(n_pages)])
+
+
+def select_pages(ps: np.ndarray, T: int, page_size: int, k_pages: int):
+    """The k_pages pages of largest page score (select's rule: ties to the lower page), recomputed
+    whole.  Returns (S, C, P): the selected positions and their complement (ascending, inside
+    [0, T)) and the selected pages (ascending).  |S| is k_pages * page_size less the shortfall of
+    the last page when that page is selected."""
+    P, _ = select(ps, k_pages)
+    chosen = np.zeros(T, dtype=bool)
+    for j in P:
+        chosen[j * page_size:min((j + 1) * page_size, T)] = True
+    t = np.arange(T)
+    return t[chosen].astype(np.int64), t[~chosen].astype(np.int64), P
+
 
 def rope_angles(pos: np.ndarray, d_h: int, base: float) -> np.ndarray:
     """Angles pos * base**(-2j/d_h) for j < d_h/2, in float64; shape pos.shape + (d_h/2,)."""

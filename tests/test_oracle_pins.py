@@ -978,6 +978,59 @@ def pin_layer_sets_complement_and_layer_order():
         assert np.abs(po[key] - out[key][perm]).max() <= 1e-12 * np.abs(out[key]).max(), key
 
 
+# ------------------------------------------------------------------------- page-granular selection
+
+def pin_page_selection_hand():
+    """Worked by hand: T = 10, pages of 4 ([0,4), [4,8), [8,10)); the short last page competes
+    with its two positions' sum."""
+    s = np.array([1.0, 0.0, 0.0, 1.0, 0.5, 0.5, 0.5, 0.0, 3.0, 0.2])
+    ps = O.page_scores(s, 4)
+    assert np.allclose(ps, [2.0, 1.5, 3.2], rtol=0, atol=1e-15)
+    S, C, P = O.select_pages(ps, 10, 4, 2)
+    assert P.tolist() == [0, 2] and S.tolist() == [0, 1, 2, 3, 8, 9] and C.tolist() == [4, 5, 6, 7]
+    S1, C1, P1 = O.select_pages(ps, 10, 4, 1)
+    assert P1.tolist() == [2] and S1.tolist() == [8, 9] and len(C1) == 8
+    # equal page scores: the lower page
+    S2, _, P2 = O.select_pages(np.array([1.0, 1.0, 1.0]), 10, 4, 1)
+    assert P2.tolist() == [0] and S2.tolist() == [0, 1, 2, 3]
+
+
+def pin_page_selection_unit_pages():
+    """Pages of one position are positions: the page scores are the scores and the selection is
+    the position selection with the same count."""
+    rng = _rng(90)
+    for T in (1, 7, 64, 300):
+        s = rng.standard_normal(T)
+        ps = O.page_scores(s, 1)
+        assert np.array_equal(ps, s)
+        for k in (0, 1, T // 3, T):
+            S, C, P = O.select_pages(ps, T, 1, k)
+            S0, C0 = O.select(s, k)
+            assert np.array_equal(S, S0) and np.array_equal(C, C0) and np.array_equal(P, S0)
+
+
+def pin_page_selection_whole_pages():
+    """Every selected set is a union of whole pages inside [0, T) (the last one possibly short),
+    with |S| = k_pages * page_size less the last page's shortfall when it is chosen; the page
+    scores add up to the total score; a page made to dominate is chosen."""
+    rng = _rng(91)
+    for T, ps_, kp in ((100, 16, 3), (37, 8, 2), (64, 16, 4), (5, 16, 1)):
+        s = rng.uniform(0, 1, T)
+        pg = O.page_scores(s, ps_)
+        assert len(pg) == -(-T // ps_) and abs(pg.sum() - s.sum()) <= 1e-12 * s.sum()
+        S, C, P = O.select_pages(pg, T, ps_, kp)
+        assert np.array_equal(np.sort(np.concatenate([S, C])), np.arange(T))
+        short = (-T) % ps_ if (len(pg) - 1) in P.tolist() else 0
+        assert len(S) == kp * ps_ - short
+        for j in P:
+            assert set(range(j * ps_, min((j + 1) * ps_, T))) <= set(S.tolist())
+        s2 = s.copy()
+        last = len(pg) - 1
+        s2[last * ps_] = 1e6
+        _, _, P2 = O.select_pages(O.page_scores(s2, ps_), T, ps_, kp)
+        assert last in P2.tolist()
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 
@@ -1214,7 +1267,25 @@ def _mut_qknorm_over_all_heads(x_rows, w_qkv, pos, H_q, H_kv, d_h, base, q_gain,
     return O.rope(q, np.asarray(pos)[:, None], base), O.rope(k, np.asarray(pos)[:, None], base), v
 
 
-_ORIG = {name: getattr(O, name) for name in ("layer_disagreement", "select_per_layer")}
+_ORIG = {name: getattr(O, name) for name in ("layer_disagreement", "select_per_layer", "page_scores",
+                                             "select_pages")}
+
+
+def _mut_page_score_max(s, page_size):
+    T = s.shape[0]
+    return np.array([np.max(s[j * page_size:min((j + 1) * page_size, T)]) for j in range(-(-T // page_size))])
+
+
+def _mut_page_last_full(ps, T, page_size, k_pages):
+    P, _ = O.select(ps, k_pages)
+    S = np.sort(np.concatenate([np.arange(j * page_size, (j + 1) * page_size) for j in P])) if len(P) else \
+        np.zeros(0, dtype=np.int64)
+    C = np.setdiff1d(np.arange(T), S)
+    return S.astype(np.int64), C.astype(np.int64), P
+
+
+def _mut_page_ties_high(ps, T, page_size, k_pages):
+    return _ORIG["select_pages"](ps + 1e-9 * np.arange(len(ps)), T, page_size, k_pages)
 
 
 def _mut_direct_v_then_k(K, V, u):
@@ -1280,6 +1351,9 @@ MUTANTS = {
     "direct_score_first_basis": ("layer_disagreement", _mut_direct_first_basis),
     "layer_sets_from_summed_score": ("select_per_layer", _mut_per_layer_summed),
     "layer_sets_first_layer_everywhere": ("select_per_layer", _mut_per_layer_first_set),
+    "page_score_max": ("page_scores", _mut_page_score_max),
+    "page_last_counted_full": ("select_pages", _mut_page_last_full),
+    "page_ties_high": ("select_pages", _mut_page_ties_high),
 }
 
 
