@@ -185,6 +185,65 @@ __global__ void sum_parts_kernel(const float* parts, int n_outer, int n_inner, i
     out[m] = s;
 }
 
+// =========================================================================== page-granular selection
+// Page j of request b holds positions [j ps, min((j + 1) ps, T_b)); one thread per page sums its
+// positions' scores in position order.
+__global__ void page_scores_kernel(const float* scores, const int32_t* cu_tok, const int32_t* cu_pages, int n_req,
+                                   int ps, int64_t total_pages, float* out) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= total_pages) return;
+    const int b = find_request(cu_pages, n_req, (int)g);
+    const int j = (int)g - cu_pages[b];
+    const int T = cu_tok[b + 1] - cu_tok[b];
+    const int p0 = j * ps, p1 = min(p0 + ps, T);
+    const float* sb = scores + cu_tok[b];
+    float sum = 0.f;
+    for (int p = p0; p < p1; ++p) sum += sb[p];
+    out[g] = sum;
+}
+
+// cu_sel[b + 1] = cu_sel[b] + positions of request b's selected pages (the last page of a request
+// may be short; it is the last of the ascending selected pages when it is selected).  One thread.
+__global__ void page_counts_kernel(const int32_t* cu_tok, const int32_t* cu_pages, const int32_t* cu_kpages,
+                                   const int32_t* sel_pages, int n_req, int ps, int32_t* cu_sel) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int acc = 0;
+    cu_sel[0] = 0;
+    for (int b = 0; b < n_req; ++b) {
+        const int kp = cu_kpages[b + 1] - cu_kpages[b];
+        const int np = cu_pages[b + 1] - cu_pages[b];
+        const int T = cu_tok[b + 1] - cu_tok[b];
+        int cnt = kp * ps;
+        if (kp > 0 && sel_pages[cu_kpages[b] + kp - 1] == np - 1) cnt -= np * ps - T;
+        acc += cnt;
+        cu_sel[b + 1] = acc;
+    }
+}
+
+// Positions of request b's selected pages (ascending) at sel + cu_sel[b] and of its other pages at
+// rest + cu_tok[b] - cu_sel[b]; entry i * ps + e is position e of the i-th page (only a request's
+// last page can be short, and it comes last in either list).  One block per request.
+__global__ void expand_pages_kernel(const int32_t* cu_tok, const int32_t* cu_pages, const int32_t* cu_kpages,
+                                    const int32_t* sel_pages, const int32_t* rest_pages, const int32_t* cu_sel, int ps,
+                                    int32_t* sel, int32_t* rest) {
+    const int b = blockIdx.x;
+    const int T = cu_tok[b + 1] - cu_tok[b];
+    const int kp = cu_kpages[b + 1] - cu_kpages[b];
+    const int nr = cu_pages[b + 1] - cu_pages[b] - kp;
+    const int32_t* sp = sel_pages + cu_kpages[b];
+    const int32_t* rp = rest_pages + (cu_pages[b] - cu_kpages[b]);
+    int32_t* so = sel + cu_sel[b];
+    int32_t* ro = rest + (cu_tok[b] - cu_sel[b]);
+    for (int64_t i = threadIdx.x; i < (int64_t)kp * ps; i += blockDim.x) {
+        const int pos = sp[i / ps] * ps + (int)(i % ps);
+        if (pos < T) so[i] = pos;
+    }
+    for (int64_t i = threadIdx.x; i < (int64_t)nr * ps; i += blockDim.x) {
+        const int pos = rp[i / ps] * ps + (int)(i % ps);
+        if (pos < T) ro[i] = pos;
+    }
+}
+
 // =========================================================================== select
 // One workgroup of 1024 threads per request.  Keys are the fp32 score bits made
 // order-preserving as unsigned integers (-0.0 folded onto +0.0).  The k-th largest key is
@@ -847,6 +906,26 @@ hipError_t launch_sum_parts(const float* parts, int n_outer, int n_inner, int64_
     if (M == 0 || n_outer == 0) return hipSuccess;
     hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((M + 255) / 256), per_outer ? n_outer : 1), dim3(256), 0, s,
                        parts, n_outer, n_inner, M, per_outer ? 1 : 0, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_pages(const float* scores, const int32_t* cu_tok, int n_req, int ps, const int32_t* cu_pages,
+                               const int32_t* cu_kpages, int64_t total_pages, float* page_scores, int32_t* sel_pages,
+                               int32_t* rest_pages, int32_t* cu_sel, int32_t* sel, int32_t* rest, hipStream_t s) {
+    if (n_req == 0) return hipSuccess;
+    if (total_pages > 0) {
+        hipLaunchKernelGGL(page_scores_kernel, dim3((unsigned)((total_pages + 255) / 256)), dim3(256), 0, s, scores,
+                           cu_tok, cu_pages, n_req, ps, total_pages, page_scores);
+        if (hipError_t e = hipGetLastError()) return e;
+        if (hipError_t e = launch_select(nullptr, 0, total_pages, page_scores, cu_pages, cu_kpages, n_req, sel_pages,
+                                         rest_pages, s))
+            return e;
+    }
+    hipLaunchKernelGGL(page_counts_kernel, dim3(1), dim3(64), 0, s, cu_tok, cu_pages, cu_kpages, sel_pages, n_req, ps,
+                       cu_sel);
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL(expand_pages_kernel, dim3(n_req), dim3(256), 0, s, cu_tok, cu_pages, cu_kpages, sel_pages,
+                       rest_pages, cu_sel, ps, sel, rest);
     return hipGetLastError();
 }
 

@@ -1627,4 +1627,37 @@ kvx_status kvx_select_topk_layers(void* stream, const float* scores, int32_t n_l
                       "select_topk_layers");
 }
 
+kvx_status kvx_select_pages(void* stream, const float* scores, const kvx_batch* batch, int32_t page_size,
+                            const kvx_batch* pages, float* page_scores, int32_t* sel_pages, int32_t* rest_pages,
+                            int32_t* cu_sel, int32_t* sel, int32_t* rest) {
+    BatchInfo bi, pi;
+    if (kvx_status st = check_batch(batch, &bi)) return st;
+    if (kvx_status st = check_batch(pages, &pi)) return st;
+    KVX_REQUIRE(page_size >= 1, "page_size must be >= 1 (got %d)", page_size);
+    KVX_REQUIRE(pages->n_req == batch->n_req, "pages has %d requests, batch %d", pages->n_req, batch->n_req);
+    for (int b = 0; b < bi.n_req; ++b) {
+        const int64_t T = batch->cu_tokens_h[b + 1] - batch->cu_tokens_h[b];
+        const int64_t np = pages->cu_tokens_h[b + 1] - pages->cu_tokens_h[b];
+        KVX_REQUIRE(np == (T + page_size - 1) / page_size, "request %d: %lld positions make %lld pages of %d, "
+                    "pages gives %lld", b, (long long)T, (long long)((T + page_size - 1) / page_size), page_size,
+                    (long long)np);
+    }
+    KVX_REQUIRE(pi.n_sel * (int64_t)page_size <= INT32_MAX, "too many selected positions");
+    KVX_REQUIRE_PTR(cu_sel, "cu_sel");
+    if (bi.n_tokens > 0) KVX_REQUIRE_PTR(scores, "scores");
+    if (pi.n_tokens > 0) KVX_REQUIRE_PTR(page_scores, "page_scores");
+    if (pi.n_sel > 0) {
+        KVX_REQUIRE_PTR(sel_pages, "sel_pages");
+        KVX_REQUIRE_PTR(sel, "sel");
+    }
+    if (pi.n_rest > 0) {
+        KVX_REQUIRE_PTR(rest_pages, "rest_pages");
+        KVX_REQUIRE_PTR(rest, "rest");
+    }
+    return hip_status(launch_select_pages(scores, batch->cu_tokens_d, bi.n_req, page_size, pages->cu_tokens_d,
+                                          pages->cu_sel_d, pi.n_tokens, page_scores, sel_pages, rest_pages, cu_sel, sel,
+                                          rest, (hipStream_t)stream),
+                      "select_pages");
+}
+
 }  // extern "C"

@@ -45,6 +45,12 @@ hipError_t launch_score_cache_f32(const float* kc, const float* vc, int64_t laye
 hipError_t launch_sum_parts(const float* parts, int n_outer, int n_inner, int64_t M, bool per_outer, float* out,
                             hipStream_t s);
 
+// ---- page-granular selection: page scores (sums over aligned pages of ps positions), the top
+//      pages per request (select over pages), the selected position counts and the positions
+hipError_t launch_select_pages(const float* scores, const int32_t* cu_tok, int n_req, int ps, const int32_t* cu_pages,
+                               const int32_t* cu_kpages, int64_t total_pages, float* page_scores, int32_t* sel_pages,
+                               int32_t* rest_pages, int32_t* cu_sel, int32_t* sel, int32_t* rest, hipStream_t s);
+
 // ---- rotary table [max_pos][d_h/2][2] (cos, sin), angles in fp64
 hipError_t launch_rope_table(double base, int d_h, int max_pos, float* table, hipStream_t s);
 

@@ -75,6 +75,8 @@ _SIGS = {
     "kvx_score_cache_select": ([_P, _I32, ctypes.POINTER(_Cache), _I32, _I32, _I32, _I32, _P, _I32,
                                 ctypes.POINTER(_Batch), ctypes.POINTER(_I32), _P, _P, _P, _P, _SZ], _I32),
     "kvx_select_topk_layers": ([_P, _P, _I32, ctypes.POINTER(_Batch), _P, _P], _I32),
+    "kvx_select_pages": ([_P, _P, ctypes.POINTER(_Batch), _I32, ctypes.POINTER(_Batch), _P, _P, _P, _P, _P, _P],
+                         _I32),
     "kvx_fit_mapper_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "kvx_fit_mapper": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _I32, _P, _P, _P, _SZ],
                        _I32),
@@ -391,6 +393,30 @@ def select_topk_layers(scores: torch.Tensor, batch: Batch, out=None):
     _check("kvx_select_topk_layers", lib().kvx_select_topk_layers(_stream(dev), _ptr(scores), n_layers,
                                                                   ctypes.byref(batch.c), _ptr(sel), _ptr(rest)))
     return sel[:, :batch.total_sel], rest[:, :batch.total_rest]
+
+
+def select_pages(scores: torch.Tensor, batch: Batch, page_size: int, pcts: Sequence[int]):
+    """Whole pages of page_size positions by the sum of their scores; request b keeps
+    kvx_budget(ceil(T_b / page_size), pcts[b]) pages.  The selected count depends on the data (a
+    short last page), so this call waits for the device to read it.  Returns (sel, rest, sel_batch,
+    page_scores, sel_pages): sel_batch is the batch of the positions with the selected counts."""
+    dev = scores.device
+    n_pages = [-(-t // page_size) for t in batch.lengths]
+    pages = Batch.for_budgets(n_pages, pcts, dev)
+    page_scores = torch.empty(max(pages.n_tokens, 1), dtype=torch.float32, device=dev)
+    sel_pages = torch.empty(max(pages.total_sel, 1), dtype=torch.int32, device=dev)
+    rest_pages = torch.empty(max(pages.total_rest, 1), dtype=torch.int32, device=dev)
+    cu_sel = torch.empty(batch.n_req + 1, dtype=torch.int32, device=dev)
+    sel = torch.empty(max(pages.total_sel * page_size, 1), dtype=torch.int32, device=dev)
+    rest = torch.empty(max(batch.n_tokens, 1), dtype=torch.int32, device=dev)
+    _check("kvx_select_pages", lib().kvx_select_pages(_stream(dev), _ptr(scores), ctypes.byref(batch.c), page_size,
+                                                      ctypes.byref(pages.c), _ptr(page_scores), _ptr(sel_pages),
+                                                      _ptr(rest_pages), _ptr(cu_sel), _ptr(sel), _ptr(rest)))
+    cu = cu_sel.cpu().tolist()
+    counts = [cu[b + 1] - cu[b] for b in range(batch.n_req)]
+    sel_batch = Batch(batch.lengths, counts, dev)
+    return (sel[:cu[-1]], rest[:batch.n_tokens - cu[-1]], sel_batch, page_scores[:pages.n_tokens],
+            sel_pages[:pages.total_sel])
 
 
 def score_select_normalized(z: torch.Tensor, op: torch.Tensor, op_total: torch.Tensor, batch: Batch,

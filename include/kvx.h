@@ -246,6 +246,28 @@ KVX_API kvx_status kvx_score_cache_select(void* stream, int32_t dtype, const kvx
 KVX_API kvx_status kvx_select_topk_layers(void* stream, const float* scores, int32_t n_layers,
                                           const kvx_batch* batch, int32_t* sel, int32_t* rest);
 
+/* Page-granular selection (an unranked variant, after the block-rounded repair sets of the
+ * PatchKV abstract on the CacheReforge card): request b's positions fall into pages of page_size
+ * consecutive positions (page j = [j * page_size, min((j + 1) * page_size, T_b)), the last one
+ * possibly short); a page's score is the sum of its positions' scores (fp32, in position order);
+ * the request's k_b pages of largest score (ties to the lower page) are recomputed whole.
+ *   scores (device) [N] fp32 position scores, finite; batch: the positions (its cu_sel is not read);
+ *   page_size >= 1; pages: a batch over pages with the same n_req, request b holding
+ *     ceil(T_b / page_size) pages of which cu_sel gives the k_b selected ones;
+ *   page_scores (device, out) [pages.cu_tokens[n_req]] fp32;
+ *   sel_pages (device, out) [pages.cu_sel[n_req]], rest_pages (device, out) [the other pages], laid
+ *     out as kvx_select_topk lays out positions;
+ *   cu_sel (device, out) [n_req + 1]: cu_sel[0] = 0, cu_sel[b + 1] - cu_sel[b] = the positions of
+ *     request b's selected pages (k_b * page_size less the shortfall of its last page when that page
+ *     is selected), so the selected count is known on the device only;
+ *   sel (device, out), room for sum_b k_b * page_size entries: request b's selected positions,
+ *     ascending, at cu_sel[b]; rest (device, out), room for N entries: its other positions, ascending,
+ *     at cu_tokens[b] - cu_sel[b].
+ * A caller copies cu_sel to the host to build the kvx_batch of the following steps. */
+KVX_API kvx_status kvx_select_pages(void* stream, const float* scores, const kvx_batch* batch, int32_t page_size,
+                                    const kvx_batch* pages, float* page_scores, int32_t* sel_pages,
+                                    int32_t* rest_pages, int32_t* cu_sel, int32_t* sel, int32_t* rest);
+
 /* Top-k of given scores per request: the k_b largest scores of request b, ties to the
  * lower position, -0.0 equal to +0.0.  scores (device) [N] fp32, finite.
  * sel (device, out) [cu_sel[n_req]] request-local positions, ascending per request;

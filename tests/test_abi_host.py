@@ -236,6 +236,21 @@ def test_score_cache_validation():
     status(L.kvx_select_topk_layers(None, A16, 2, ctypes.byref(bt.c), None, A16), INVALID, "sel")
 
 
+def test_select_pages_validation():
+    L = kvx.lib()
+    bt = FakeBatch([100, 50], [30, 15])
+    pg = FakeBatch([7, 4], [3, 2])              # ceil(100 / 16) = 7, ceil(50 / 16) = 4
+    bad = FakeBatch([7, 3], [3, 2])
+    one = FakeBatch([7], [3])
+    args = lambda ps=16, pages=pg, cu=A16: (None, A16, ctypes.byref(bt.c), ps, ctypes.byref(pages.c), A16, A16,
+                                            A16B, cu, A16, A16B)
+    status(L.kvx_select_pages(*args(ps=0)), INVALID, "page_size")
+    status(L.kvx_select_pages(*args(pages=bad)), INVALID, "pages")
+    status(L.kvx_select_pages(*args(pages=one)), INVALID, "requests")
+    status(L.kvx_select_pages(*args(ps=8)), INVALID, "pages of 8")
+    status(L.kvx_select_pages(*args(cu=None)), INVALID, "cu_sel")
+
+
 def test_reconstruct_validation():
     L = kvx.lib()
     bt = FakeBatch([100, 50], [30, 15])
