@@ -66,8 +66,8 @@ def _stored_rows(cache, layers, batch, lengths, page_table, positions=None):
     return K, V
 
 
-def _setup(wl, seed, mostly_inside=False):
-    inp = synth.generate(wl, seed, DEV)
+def _setup(wl, seed, mostly_inside=False, lengths=None, pcts=None):
+    inp = synth.generate(wl, seed, DEV, lengths=lengths, pcts=pcts)
     h = Handoff(inp, DEV)
     h.map()
     kvx.reconstruct(h.z, inp.w_l, wl.H_kv, wl.d_h, h.batch, h.cache)          # every position
@@ -86,11 +86,20 @@ def _setup(wl, seed, mostly_inside=False):
     return inp, h, u
 
 
-@pytest.mark.parametrize("name", list(CASES))
+# requests of length 0 among others (lengths, budgets)
+EMPTY = ([0, 257, 0, 64], [30, 30, 40, 100])
+
+
+@pytest.mark.parametrize("name", list(CASES) + ["bf16-empty-requests"])
 def test_score_cache_matches_oracle(name):
-    wl, l0, n = CASES[name]
+    lengths = pcts = None
+    if name == "bf16-empty-requests":
+        wl, l0, n = small("bf16-empty", n_req=4, t_min=1, t_max=300, pct_choices=(30,)), 0, 3
+        lengths, pcts = EMPTY
+    else:
+        wl, l0, n = CASES[name]
     print(f"[score cache] {name}", flush=True)
-    inp, h, u = _setup(wl, 71, mostly_inside=name == "bf16-mostly-inside")
+    inp, h, u = _setup(wl, 71, mostly_inside=name == "bf16-mostly-inside", lengths=lengths, pcts=pcts)
     dt = kvx.BF16 if wl.dtype == "bf16" else kvx.F32
     op = kvx.score_cache_prepare(u[l0:l0 + n].contiguous(), dt)
     energy = kvx.score_cache(h.cache, l0, wl.H_kv, wl.d_h, op, h.batch)

@@ -32,6 +32,7 @@ CASES = [
     ("ps1-positions", [200, 17], [30, 40], 1, "normal"),
     ("ps16-long", [40000], [30], 16, "normal"),
     ("ps1-long", [40000], [40], 1, "ties"),
+    ("ps16-empty-requests", [0, 40, 0, 17], [30, 40, 30, 100], 16, "normal"),
 ]
 
 
