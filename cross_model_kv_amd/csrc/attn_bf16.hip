@@ -31,7 +31,8 @@
 //    partial sums, since one serial chain of 16 dependent dot products measured 2.5% slower),
 //    kept per lane until the end.  The common tile is exp2, bf16 packing and 16 dot products; only when a
 //    lane sum exceeds 2^16 (a score far above m_ref) does a slow path take the true maximum
-//    and rescale O and l (the ratio O / l does not depend on the reference used).
+//    and rescale O and l (the ratio O / l does not depend on the reference used); a wave's
+//    first tile, with no reference yet, goes to that path directly.
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
 //    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
 //  * With fewer blocks than CUs the keys of the long blocks are cut into runs counted back
@@ -332,8 +333,16 @@ void attn_bf16_kernel(AttnArgs a) {
                 }
             return (rs[0] + rs[1]) + (rs[2] + rs[3]);
         };
-        float rs = exp_pack(false, 0.f);
-        if (__any(!have_ref || !(rs <= 65536.f))) {   // no reference yet, or a score far above it (rare)
+        // a wave with a row that has no reference yet (its first tile) goes straight to the slow
+        // path; otherwise the common path, and the slow one only if a score is far above m_ref
+        float rs = 0.f;
+        const bool no_ref = __any(!have_ref);
+        bool slow = no_ref;
+        if (!no_ref) {
+            rs = exp_pack(false, 0.f);
+            slow = __any(!(rs <= 65536.f));
+        }
+        if (slow) {
             asm volatile("");
             float mx = sacc[0][0];
 #pragma unroll
@@ -345,12 +354,15 @@ void attn_bf16_kernel(AttnArgs a) {
             // past the row's position) keeps its reference: its P is 0
             const bool none = !(mx > -INFINITY);
             const float m_new = none ? m_ref : have_ref ? fmaxf(m_ref, mx) : mx;
-            const float corr = have_ref ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
-            l_lane *= corr;
+            // rows without a reference hold O = 0 and l = 0: a wave without any reference skips the rescale
+            if (__any(have_ref)) {
+                const float corr = have_ref ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
+                l_lane *= corr;
 #pragma unroll
-            for (int d = 0; d < DB; ++d)
+                for (int d = 0; d < DB; ++d)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
+                    for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
+            }
             rs = exp_pack(true, m_ref - m_new);
             m_ref = m_new;
             have_ref = have_ref || !none;
