@@ -185,6 +185,51 @@ __global__ void sum_parts_kernel(const float* parts, int n_outer, int n_inner, i
     out[m] = s;
 }
 
+// =========================================================================== fp32 variants
+// QK-norm on fp32 projection rows: one wave per (row, q or k head); the head's sum of squares over
+// its d_h channels (lanes stride the channels, then a wave tree), x = x * inv * gain with
+// inv = 1 / sqrt(mean square + eps), in place; v is left as it is.
+__global__ __launch_bounds__(256) void qknorm_rows_f32_kernel(float* qkv, int64_t n_rows, int n_qkv, int H_q,
+                                                              int H_kv, int d_h, const float* gq, const float* gk,
+                                                              float eps) {
+    const int heads = H_q + H_kv;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (item >= n_rows * heads) return;
+    const int64_t row = item / heads;
+    const int hs = (int)(item - row * heads);
+    float* x = qkv + row * n_qkv + (int64_t)hs * d_h;
+    const float* g = hs < H_q ? gq : gk;
+    float ss = 0.f;
+    for (int j = lane; j < d_h; j += 64) ss = fmaf(x[j], x[j], ss);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float inv = 1.f / sqrtf(ss / (float)d_h + eps);
+    for (int j = lane; j < d_h; j += 64) x[j] = x[j] * inv * g[j];
+}
+
+// Keys of the listed rows rotated in place in every layer of an fp32 cache (the rotary phase of
+// a mapper whose keys carry none): thread per (row, layer, rotation pair of one head), rope_lo /
+// rope_hi with the table's (cos, sin) at the row's position.
+__global__ void rope_cache_rows_f32_kernel(float* kc, int64_t layer_elems, int L, int hd, int d_h, const float* rope,
+                                           RowMap rm, SlotMap sl, int64_t M) {
+    const int half = d_h / 2, pairs = hd / 2;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * L * pairs) return;
+    const int p = (int)(i % pairs);
+    const int64_t ml = i / pairs;
+    const int l = (int)(ml % L);
+    const int m = (int)(ml / L);
+    const RowInfo ri = row_info(rm, m);
+    const int64_t slot = sl.slot(ri.b, ri.pos);
+    const int h = p / half, j = p % half;
+    float* base = kc + l * layer_elems + slot * hd + (int64_t)h * d_h;
+    const float* cs = rope + ((int64_t)ri.pos * half + j) * 2;
+    const float x1 = base[j], x2 = base[j + half];
+    base[j] = rope_lo(x1, x2, cs[0], cs[1]);
+    base[j + half] = rope_hi(x1, x2, cs[0], cs[1]);
+}
+
 // =========================================================================== page-granular selection
 // Page j of request b holds positions [j ps, min((j + 1) ps, T_b)); one thread per page sums its
 // positions' scores in position order.
@@ -926,6 +971,24 @@ hipError_t launch_select_pages(const float* scores, const int32_t* cu_tok, int n
     if (hipError_t e = hipGetLastError()) return e;
     hipLaunchKernelGGL(expand_pages_kernel, dim3(n_req), dim3(256), 0, s, cu_tok, cu_pages, cu_kpages, sel_pages,
                        rest_pages, cu_sel, ps, sel, rest);
+    return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rows_f32(float* qkv, int64_t n_rows, int n_qkv, int H_q, int H_kv, int d_h, const float* gq,
+                                  const float* gk, float eps, hipStream_t s) {
+    const int64_t items = n_rows * (H_q + H_kv);
+    if (items == 0) return hipSuccess;
+    hipLaunchKernelGGL(qknorm_rows_f32_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, qkv, n_rows, n_qkv,
+                       H_q, H_kv, d_h, gq, gk, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_cache_rows_f32(float* kc, int64_t layer_elems, int L, int hd, int d_h, const float* rope,
+                                      const RowMap& rm, const SlotMap& sl, int64_t M, hipStream_t s) {
+    const int64_t n = M * L * (hd / 2);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_cache_rows_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kc, layer_elems,
+                       L, hd, d_h, rope, rm, sl, M);
     return hipGetLastError();
 }
 

@@ -655,7 +655,10 @@ kvx_status run_reconstruct(void* stream, int32_t dtype, const void* z, const voi
     a.epi = EPI_CACHE;
     a.kc = (float*)cache->k; a.vc = (float*)cache->v;
     a.layer_elems = cache->n_slots * hd; a.hd = hd; a.slots = slot_map(cache, batch);
-    return hip_status(launch_gemm_f32(a, s), "reconstruct");
+    if (!rope) return hip_status(launch_gemm_f32(a, s), "reconstruct");
+    KVX_TRY_HIP(launch_gemm_f32(a, s), "reconstruct");
+    return hip_status(launch_rope_cache_rows_f32((float*)cache->k, a.layer_elems, L_t, hd, d_h, rope, rm, a.slots, M, s),
+                      "reconstruct (key rotation)");
 }
 
 }  // namespace
@@ -673,8 +676,8 @@ kvx_status kvx_reconstruct_rope(void* stream, int32_t dtype, const void* z, cons
                                 int32_t r, int32_t H_kv, int32_t d_h, const float* rope, int32_t max_pos,
                                 const kvx_batch* batch, const int32_t* rows, const kvx_cache* cache) {
     if (kvx_status st = check_dtype(dtype)) return st;
-    if (dtype != KVX_BF16) return fail(KVX_ERR_UNSUPPORTED, "reconstruct_rope supports KVX_BF16 only");
-    if (d_h != 64 && d_h != 128) return fail(KVX_ERR_UNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+    if (dtype == KVX_BF16 && d_h != 64 && d_h != 128)
+        return fail(KVX_ERR_UNSUPPORTED, "bf16 needs d_h 64 or 128 (got %d)", d_h);
     KVX_REQUIRE_PTR(rope, "rope");
     BatchInfo bi;
     if (kvx_status st = check_batch(batch, &bi)) return st;
@@ -818,6 +821,10 @@ hipError_t run_qkv_rope_scatter(hipStream_t s, int32_t dtype, int32_t layer, con
     const int n_qkv = (H_q + 2 * H_kv) * d_h;
     if (dtype != KVX_BF16) {
         if (hipError_t e = run_qkv(s, dtype, x_l, w_qkv, D, n_qkv, batch, bi, sel, qkv, split_ws)) return e;
+        if (q_gain)                      // QK-norm: q and k heads normalised in place before the rotation
+            if (hipError_t e = launch_qknorm_rows_f32((float*)qkv, bi.n_sel, n_qkv, H_q, H_kv, d_h, q_gain, k_gain,
+                                                      eps, s))
+                return e;
         return run_scatter(s, dtype, layer, qkv, H_q, H_kv, d_h, rope, batch, bi, sel, cache);
     }
     const int hd = H_kv * d_h;
@@ -1066,14 +1073,14 @@ kvx_status kvx_qkv_rope_scatter_qknorm(void* stream, int32_t dtype, int32_t laye
                                        int32_t max_pos, const kvx_batch* batch, const int32_t* sel,
                                        const kvx_cache* cache, void* qkv) {
     if (kvx_status st = check_heads(dtype, H_q, H_kv, d_h)) return st;
-    if (dtype != KVX_BF16) return fail(KVX_ERR_UNSUPPORTED, "qkv_rope_scatter_qknorm supports KVX_BF16 only");
     BatchInfo bi;
     if (kvx_status st = check_batch(batch, &bi)) return st;
     KVX_REQUIRE_PTR(x_l, "x_l");
     KVX_REQUIRE_PTR(w_qkv, "w_qkv");
     KVX_REQUIRE(q_gain && k_gain, "q_gain and k_gain must not be null");
     KVX_REQUIRE(eps >= 0.f && eps < INFINITY, "eps must be finite and >= 0");
-    KVX_REQUIRE(D > 0 && D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    if (dtype == KVX_BF16) KVX_REQUIRE(D > 0 && D % 64 == 0, "bf16 needs D %% 64 == 0 (got %d)", D);
+    else KVX_REQUIRE(D > 0, "D must be positive (got %d)", D);
     if (kvx_status st = check_layer_cache(cache, batch, bi, dtype, H_kv, d_h, layer, rope, max_pos)) return st;
     if (bi.n_sel == 0) return ok();
     KVX_REQUIRE(bi.n_sel <= INT32_MAX, "too many selected rows");

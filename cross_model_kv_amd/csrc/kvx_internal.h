@@ -45,6 +45,13 @@ hipError_t launch_score_cache_f32(const float* kc, const float* vc, int64_t laye
 hipError_t launch_sum_parts(const float* parts, int n_outer, int n_inner, int64_t M, bool per_outer, float* out,
                             hipStream_t s);
 
+// ---- fp32 variants: QK-norm of the projection rows in place; keys of the listed rows of every
+//      layer rotated in place at their positions
+hipError_t launch_qknorm_rows_f32(float* qkv, int64_t n_rows, int n_qkv, int H_q, int H_kv, int d_h, const float* gq,
+                                  const float* gk, float eps, hipStream_t s);
+hipError_t launch_rope_cache_rows_f32(float* kc, int64_t layer_elems, int L, int hd, int d_h, const float* rope,
+                                      const RowMap& rm, const SlotMap& sl, int64_t M, hipStream_t s);
+
 // ---- page-granular selection: page scores (sums over aligned pages of ps positions), the top
 //      pages per request (select over pages), the selected position counts and the positions
 hipError_t launch_select_pages(const float* scores, const int32_t* cu_tok, int n_req, int ps, const int32_t* cu_pages,

@@ -322,9 +322,10 @@ KVX_API kvx_status kvx_reconstruct(void* stream, int32_t dtype, const void* z, c
  * every layer is rotated at its row's position as recomputed keys are (rotate-half, pair
  * (j, j + d_h/2) by angle p * base^(-2j/d_h), the table of kvx_rope_table), V unchanged:
  *   K_l[slot(b,p)] = rope(y[0 : H_kv d_h], p) head by head,  V_l[slot(b,p)] = y[H_kv d_h : ].
- * Each key value is rounded to bf16, rotated in fp32 with its partner and rounded again (the
- * order of the fused QKV projection).  bf16 only (KVX_ERR_UNSUPPORTED for KVX_F32); d_h 64 or
- * 128; rope (device) with max_pos >= every T_b; other arguments as in kvx_reconstruct. */
+ * bf16: each key value is rounded to bf16, rotated in fp32 with its partner and rounded again
+ * (the order of the fused QKV projection), in the reconstruction's epilogue; d_h 64 or 128.
+ * fp32: the reconstruction, then the listed rows' keys rotated in place in fp32.  rope (device)
+ * with max_pos >= every T_b; other arguments as in kvx_reconstruct. */
 KVX_API kvx_status kvx_reconstruct_rope(void* stream, int32_t dtype, const void* z, const void* w_l,
                                         int32_t L_t, int32_t r, int32_t H_kv, int32_t d_h,
                                         const float* rope, int32_t max_pos, const kvx_batch* batch,
@@ -408,9 +409,11 @@ KVX_API kvx_status kvx_qkv_rope_scatter(void* stream, int32_t dtype, int32_t lay
  * describe the block): every q and every k head is divided by the root of its mean square over its
  * d_h channels plus eps and multiplied by the layer's per-channel gain (q_gain, k_gain (device)
  * [d_h] fp32, shared by the layer's heads), k is then rotated and written to the cache with v, and
- * the normalised q is left in qkv for kvx_sparse_attention (which rotates it).  Each value is
- * rounded to bf16 before the normalisation, as the plain projection stores it.  bf16 only; whole
- * output tiles (no workspace); other arguments as in kvx_qkv_rope_scatter. */
+ * the normalised q is left in qkv for kvx_sparse_attention (which rotates it).  bf16: in the
+ * projection's epilogue, each value rounded to bf16 before the normalisation as the plain projection
+ * stores it, whole output tiles (no workspace); fp32: the projection, then the q and k heads of the
+ * rows normalised in place, then the rotation and scatter.  Other arguments as in
+ * kvx_qkv_rope_scatter. */
 KVX_API kvx_status kvx_qkv_rope_scatter_qknorm(void* stream, int32_t dtype, int32_t layer, const void* x_l,
                                                const void* w_qkv, int32_t D, int32_t H_q, int32_t H_kv,
                                                int32_t d_h, const float* q_gain, const float* k_gain,

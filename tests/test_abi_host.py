@@ -282,8 +282,8 @@ def test_reconstruct_rope_validation():
     c = cache()
     args = lambda dt=1, d_h=64, rope=A16B, max_pos=100: (None, dt, A16, A16, 2, 128, 2, d_h, rope, max_pos,
                                                           ctypes.byref(bt.c), None, ctypes.byref(c))
-    status(L.kvx_reconstruct_rope(*args(dt=0)), UNSUPPORTED, "BF16")
     status(L.kvx_reconstruct_rope(*args(d_h=96)), UNSUPPORTED, "d_h")
+    status(L.kvx_reconstruct_rope(*args(dt=0, d_h=96, rope=None)), INVALID, "rope")   # fp32: any d_h % 8 == 0
     status(L.kvx_reconstruct_rope(*args(rope=None)), INVALID, "rope")
     status(L.kvx_reconstruct_rope(*args(max_pos=99)), INVALID, "positions")
 
@@ -350,8 +350,8 @@ def test_qknorm_validation():
     args = lambda dt=1, gq=A16, eps=1e-6, d_h=128: (None, dt, 0, A16, A16, 256, 8, 2, d_h, gq, A16B,
                                                     ctypes.c_float(eps), A16, 100, ctypes.byref(bt.c), A16,
                                                     ctypes.byref(c), A16)
-    status(L.kvx_qkv_rope_scatter_qknorm(*args(dt=0)), UNSUPPORTED, "BF16")
     status(L.kvx_qkv_rope_scatter_qknorm(*args(gq=None)), INVALID, "gain")
+    status(L.kvx_qkv_rope_scatter_qknorm(*args(dt=0, gq=None)), INVALID, "gain")
     status(L.kvx_qkv_rope_scatter_qknorm(*args(eps=-1.0)), INVALID, "eps")
     status(L.kvx_qkv_rope_scatter_qknorm(*args(d_h=96)), UNSUPPORTED, "d_h")
 

@@ -5,8 +5,9 @@ plus eps, per-channel gains) before the rotation; v as it is.
 Checks per case: the normalised q rows the projection leaves in qkv (not rotated yet), the
 recomputed k and v rows in the cache at the selected positions, and the attention output over
 the mixed cache, each within the bf16 bars of the other recompute tests (2e-2 normwise and
-max-abs, attention rows at least 0.999 cosine).  Cases: d_h 128 and 64 (g = 4 and 5), one
-request and a paged batch of three.
+max-abs, attention rows at least 0.999 cosine; fp32 storage: 1e-4).  Cases: d_h 128 and 64
+(g = 4 and 5), one request and paged batches, bf16 (normalisation in the projection's epilogue) and
+fp32 (the projection, then the heads normalised in place).
 """
 import numpy as np
 import pytest
@@ -19,23 +20,27 @@ from oracle import kvx_oracle as O
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
-# (name, lengths, pcts, H_q, H_kv, d_h, D, paged)
+# (name, lengths, pcts, H_q, H_kv, d_h, D, paged, storage)
 CASES = [
-    ("d128-one", [700], [30], 8, 2, 128, 256, False),
-    ("d64-g5-one", [500], [40], 10, 2, 64, 192, False),
-    ("d128-batched-paged", [300, 900, 77], [20, 30, 40], 16, 4, 128, 256, True),
+    ("d128-one", [700], [30], 8, 2, 128, 256, False, "bf16"),
+    ("d64-g5-one", [500], [40], 10, 2, 64, 192, False, "bf16"),
+    ("d128-batched-paged", [300, 900, 77], [20, 30, 40], 16, 4, 128, 256, True, "bf16"),
+    ("f32-d64-batched-paged", [260, 90], [30, 40], 8, 2, 64, 200, True, "f32"),
+    ("f32-d128-one", [300], [30], 4, 1, 128, 96, False, "f32"),
 ]
 
 
-@pytest.mark.parametrize("name,lengths,pcts,H_q,H_kv,d_h,D,paged", CASES, ids=[c[0] for c in CASES])
-def test_qknorm_recompute(name, lengths, pcts, H_q, H_kv, d_h, D, paged):
+@pytest.mark.parametrize("name,lengths,pcts,H_q,H_kv,d_h,D,paged,storage", CASES, ids=[c[0] for c in CASES])
+def test_qknorm_recompute(name, lengths, pcts, H_q, H_kv, d_h, D, paged, storage):
     print(f"[qknorm] {name}", flush=True)
     rng = np.random.default_rng(93)
     batch = kvx.Batch.for_budgets(lengths, pcts, DEV)
     N = batch.n_tokens
     n_qkv = (H_q + 2 * H_kv) * d_h
-    x = synth.cache_fill((N, D), 93, device=DEV)
-    w = (synth.cache_fill((n_qkv, D), 94, device=DEV).float() / np.sqrt(D)).to(torch.bfloat16)
+    dt = torch.float32 if storage == "f32" else torch.bfloat16
+    bar = 1e-4 if storage == "f32" else 2e-2
+    x = synth.cache_fill((N, D), 93, dtype=dt, device=DEV)
+    w = (synth.cache_fill((n_qkv, D), 94, device=DEV).float() / np.sqrt(D)).to(dt)
     gq = torch.from_numpy(rng.uniform(0.5, 1.5, d_h).astype(np.float32)).to(DEV)
     gk = torch.from_numpy(rng.uniform(0.5, 1.5, d_h).astype(np.float32)).to(DEV)
     eps = 1e-6
@@ -52,16 +57,16 @@ def test_qknorm_recompute(name, lengths, pcts, H_q, H_kv, d_h, D, paged):
             pt[b, :n] = perm[pos_:pos_ + n]
             pos_ += n
         shape = (1, n_pages * 16, H_kv, d_h)
-        cache = kvx.Cache(synth.cache_fill(shape, 95, device=DEV), synth.cache_fill(shape, 96, device=DEV), 1,
+        cache = kvx.Cache(synth.cache_fill(shape, 95, dtype=dt, device=DEV), synth.cache_fill(shape, 96, dtype=dt, device=DEV), 1,
                           n_pages * 16, page_table=torch.from_numpy(pt).to(DEV), page_size=16)
     else:
         pt = None
         shape = (1, N, H_kv, d_h)
-        cache = kvx.Cache(synth.cache_fill(shape, 95, device=DEV), synth.cache_fill(shape, 96, device=DEV), 1, N)
+        cache = kvx.Cache(synth.cache_fill(shape, 95, dtype=dt, device=DEV), synth.cache_fill(shape, 96, dtype=dt, device=DEV), 1, N)
     K0 = [np.stack([logical(cache.k, 0, b, t, batch.cu_tokens, pt, 16)]) for b, t in enumerate(lengths)]
     V0 = [np.stack([logical(cache.v, 0, b, t, batch.cu_tokens, pt, 16)]) for b, t in enumerate(lengths)]
     qkv = kvx.qkv_rope_scatter_qknorm(0, x, w, H_q, H_kv, d_h, gq, gk, eps, rope, batch, sel, cache)
-    out = torch.empty((max(batch.total_sel, 1), H_q, d_h), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((max(batch.total_sel, 1), H_q, d_h), dtype=dt, device=DEV)
     kvx.sparse_attention(0, qkv, H_q, H_kv, d_h, rope, batch, sel, cache, out)
     torch.cuda.synchronize()
     cs = batch.cu_sel
@@ -71,13 +76,13 @@ def test_qknorm_recompute(name, lengths, pcts, H_q, H_kv, d_h, D, paged):
         q0, _, _ = O.recompute_qkv_qknorm(xb[S], f64(w), np.zeros(len(S)), H_q, H_kv, d_h, 10000.0, f64(gq),
                                           f64(gk), eps)
         q, k, v = O.recompute_qkv_qknorm(xb[S], f64(w), S, H_q, H_kv, d_h, 10000.0, f64(gq), f64(gk), eps)
-        assert_close(f64(qkv[cs[b]:cs[b + 1], :H_q * d_h]).reshape(len(S), H_q, d_h), q0, 2e-2, "normalised q")
+        assert_close(f64(qkv[cs[b]:cs[b + 1], :H_q * d_h]).reshape(len(S), H_q, d_h), q0, bar, "normalised q")
         K, V = O.scatter(K0[b][0], V0[b][0], S, k, v)
         Kg = logical(cache.k, 0, b, T, batch.cu_tokens, pt, 16)
         Vg = logical(cache.v, 0, b, T, batch.cu_tokens, pt, 16)
-        assert_close(Kg[S], K[S], 2e-2, "recomputed k")
-        assert_close(Vg[S], V[S], 2e-2, "recomputed v")
+        assert_close(Kg[S], K[S], bar, "recomputed k")
+        assert_close(Vg[S], V[S], bar, "recomputed v")
         o_ref, _ = O.sparse_causal_attention(q, K, V, S)
         o = f64(out[cs[b]:cs[b + 1]])
         assert min_row_cosine(o.reshape(-1, d_h), o_ref.reshape(-1, d_h)) >= 0.999
-        assert_close(o, o_ref, 2e-2, "attention")
+        assert_close(o, o_ref, bar, "attention")

@@ -8,7 +8,8 @@ inside one wave's 128 output columns, and the last column tile is half empty).  
 within the bf16 bar (2e-2 normwise and max-abs, per request and tensor: the value is rounded to
 bf16 once before the rotation and once after, like the fused projection), the values bit for bit
 equal to kvx_reconstruct's, the paged cache equal to the contiguous one, and rows outside the list
-untouched.
+untouched.  fp32 (the reconstruction, then the keys rotated in place): bar 1e-4, with d_h 64 and 96
+(no lane layout ties the fp32 path to 64 or 128).
 """
 import numpy as np
 import pytest
@@ -36,6 +37,9 @@ CASES = {
                                     t_max=600, pct_choices=(20, 40), paged=True, page_size=16),
     "d128-batched-paged": small("d128-batched-paged", H_kv=4, H_q=16, n_req=3, t_min=100, t_max=500,
                                 pct_choices=(30,), paged=True, page_size=16),
+    "f32-d64-batched-paged": small("f32-d64-batched-paged", dtype="f32", d_h=64, H_kv=2, H_q=8, n_req=2, t_min=60,
+                                   t_max=300, pct_choices=(30,), paged=True, page_size=16),
+    "f32-d96-one-request": small("f32-d96-one-request", dtype="f32", d_h=96, H_kv=1, H_q=4),
 }
 
 
@@ -47,24 +51,26 @@ def test_reconstruct_rope(name, all_rows):
     inp = synth.generate(wl, 81, DEV)
     batch = kvx.Batch.for_budgets(inp.lengths, inp.pcts, DEV)
     N = batch.n_tokens
-    z = synth.latent(N, wl.r, 81, dtype=torch.bfloat16, device=DEV)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    bar = 1e-4 if wl.dtype == "f32" else 2e-2
+    z = synth.latent(N, wl.r, 81, dtype=dt, device=DEV)
     S_list = [synth.random_subset(t, k, 81 + b) for b, (t, k) in enumerate(zip(inp.lengths, batch.n_sel))]
     C_list = [np.setdiff1d(np.arange(t), S) for t, S in zip(inp.lengths, S_list)]
     rest = None if all_rows else torch.from_numpy(np.concatenate(C_list).astype(np.int32)).to(DEV)
     rope = kvx.rope_table(wl.rope_base, wl.d_h, max(inp.lengths), DEV)
     shape = (wl.L_t, N, wl.H_kv, wl.d_h)
-    cont = kvx.Cache(torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV),
-                     torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV), wl.L_t, N)
-    plain = kvx.Cache(torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV),
-                      torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV), wl.L_t, N)
+    cont = kvx.Cache(torch.full(shape, 7.0, dtype=dt, device=DEV),
+                     torch.full(shape, 7.0, dtype=dt, device=DEV), wl.L_t, N)
+    plain = kvx.Cache(torch.full(shape, 7.0, dtype=dt, device=DEV),
+                      torch.full(shape, 7.0, dtype=dt, device=DEV), wl.L_t, N)
     kvx.reconstruct(z, inp.w_l, wl.H_kv, wl.d_h, batch, cont, rows=rest, rope=rope)
     kvx.reconstruct(z, inp.w_l, wl.H_kv, wl.d_h, batch, plain, rows=rest)
     pt = None
     if wl.paged:
         n_slots = inp.n_pages * wl.page_size
         ps = (wl.L_t, n_slots, wl.H_kv, wl.d_h)
-        paged = kvx.Cache(torch.full(ps, 7.0, dtype=torch.bfloat16, device=DEV),
-                          torch.full(ps, 7.0, dtype=torch.bfloat16, device=DEV), wl.L_t, n_slots,
+        paged = kvx.Cache(torch.full(ps, 7.0, dtype=dt, device=DEV),
+                          torch.full(ps, 7.0, dtype=dt, device=DEV), wl.L_t, n_slots,
                           page_table=inp.page_table, page_size=wl.page_size)
         kvx.reconstruct(z, inp.w_l, wl.H_kv, wl.d_h, batch, paged, rows=rest, rope=rope)
         pt = inp.page_table.cpu().numpy()
@@ -82,7 +88,7 @@ def test_reconstruct_rope(name, all_rows):
             assert np.all(K[:, S_list[b]] == 7.0), "selected rows were written"
         zb = f64(z[batch.cu_tokens[b]:batch.cu_tokens[b + 1]])
         K_ref, _, _ = O.reconstruct_rotated(zb, f64(inp.w_l), wl.H_kv, wl.d_h, np.arange(T), wl.rope_base)
-        assert_close(K[:, rows], K_ref[:, rows], 2e-2, f"rotated keys, request {b}")
+        assert_close(K[:, rows], K_ref[:, rows], bar, f"rotated keys, request {b}")
         # the rotation moved them: the plain keys are far from the rotated ones past position 0
         K_plain = np.stack([logical(plain.k, l, b, T, batch.cu_tokens) for l in range(wl.L_t)])
         late = rows[rows > 8]
