@@ -33,6 +33,10 @@
 //    lane sum exceeds 2^16 (a score far above m_ref) does a slow path take the true maximum
 //    and rescale O and l (the ratio O / l does not depend on the reference used); a wave's
 //    first tile, with no reference yet, goes to that path directly.
+//  * Paged caches run their own instance (PG): the request's page-table entries are staged in
+//    LDS once and each tile's block pages are read from there by the instance whose loads know
+//    it is LDS (a pointer that could be either LDS or global memory is read with flat loads,
+//    which wait on both memory counters); contiguous caches keep their instance unchanged.
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
 //    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
 //  * With fewer blocks than CUs the keys of the long blocks are cut into runs counted back
@@ -63,7 +67,7 @@ __device__ __forceinline__ int kv_swz(int key) {
     else return swz(key);
 }
 
-template <int D_H, int W>
+template <int D_H, int W, bool PG>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
     constexpr int NT = W * 64;
@@ -174,7 +178,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const int tok0 = a.slots.cu_tok[b];
     const int32_t* ptab = a.slots.page_table + (int64_t)b * a.slots.max_pages;
     const int psz = a.slots.page_size, psh = a.slots.page_shift;
-    const bool paged = a.slots.paged != 0;
+    const bool paged = PG || a.slots.paged != 0;   // PG: the paged instance (known at compile time)
     // the pages this block's tiles touch, staged in LDS once (made visible by the first barrier)
     const int n_tiles_pt = p_max / KT + 1;
     const int n_pages = !paged ? 0 : psh >= 0 ? ((min(n_tiles_pt * KT, T_b) - 1) >> psh) + 1
@@ -190,21 +194,13 @@ void attn_bf16_kernel(AttnArgs a) {
     const int key0 = (w % (NBLK / 2)) * KPB + lane / NCH;
     const bf16* lane0 = kbase + ((int64_t)(lane / NCH) * H_kv + hk) * D_H + (((lane % NCH) ^ kv_swz<D_H>(key0)) << 3);
     const int64_t tile_stride = (int64_t)KT * H_kv * D_H;
-    auto issue = [&](bf16* st, int kt) {
-        if (UNIFORM && !paged && (kt + 1) * KT <= T_b) {
-            const bf16* base = lane0 + (int64_t)(tok0 + (w % (NBLK / 2)) * KPB) * H_kv * D_H + kt * tile_stride;
-#pragma unroll
-            for (int c = 0; c < NBW; ++c) {
-                const int q = w + c * W;
-                const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
-                const int64_t d = (int64_t)(ql - w % (NBLK / 2)) * KPB * H_kv * D_H + (kv ? vdelta : 0);
-                lds_dma16(base + d, st + kv * TILE + ql * 512);
-            }
-            return;
-        }
+    // the paged and general paths read page-table entries through page_of: the staged copy in LDS
+    // or the table in global memory, each in its own instance (a pointer that could point to either
+    // is read with flat loads, which wait on both memory counters)
+    auto issue_with = [&](bf16* st, int kt, auto page_of) __attribute__((always_inline)) {
         if (UNIFORM && paged && psh >= 0 && psz >= KPB && (kt + 1) * KT <= T_b) {
             // each 1 KB block holds KPB consecutive keys of one page: one wave-uniform
-            // page-table read per block (a scalar load), the lane's key and chunk added on top
+            // page-table read per block, the lane's key and chunk added on top
             // (all page-table reads before the first load: the loads' asm orders memory accesses)
             int64_t o[NBW];
 #pragma unroll
@@ -212,7 +208,7 @@ void attn_bf16_kernel(AttnArgs a) {
                 const int q = w + c * W;
                 const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
                 const int j0 = kt * KT + ql * KPB;
-                const int page = ptab[__builtin_amdgcn_readfirstlane(j0 >> psh)];
+                const int page = page_of(__builtin_amdgcn_readfirstlane(j0 >> psh));
                 const int64_t slot0 = (int64_t)page * psz + (j0 & (psz - 1));
                 // same swizzle as the wave's first block: the blocks' keys differ by multiples of 16
                 o[c] = slot0 * H_kv * D_H + (kv ? vdelta : 0);
@@ -238,7 +234,7 @@ void attn_bf16_kernel(AttnArgs a) {
             if (paged) {
                 const int pi = psh >= 0 ? j >> psh : j / psz;
                 const int po = psh >= 0 ? j & (psz - 1) : j % psz;
-                slot = (int64_t)(pt_lds ? s_pt[pi] : ptab[pi]) * psz + po;
+                slot = (int64_t)page_of(pi) * psz + po;
             } else {
                 slot = tok0 + j;
             }
@@ -250,6 +246,74 @@ void attn_bf16_kernel(AttnArgs a) {
             if (NBLK % W == 0 || q < NBLK) {
                 const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
                 lds_dma16(kbase + off[c], st + kv * TILE + ql * 512);
+            }
+        }
+    };
+    auto issue = [&](bf16* st, int kt) {
+        if constexpr (PG) {            // paged caches: the page table read from LDS when staged there
+            if (pt_lds) issue_with(st, kt, [&](int i) { return s_pt[i]; });
+            else issue_with(st, kt, [&](int i) { return ptab[i]; });
+        } else {
+            if (UNIFORM && !paged && (kt + 1) * KT <= T_b) {
+                const bf16* base = lane0 + (int64_t)(tok0 + (w % (NBLK / 2)) * KPB) * H_kv * D_H + kt * tile_stride;
+    #pragma unroll
+                for (int c = 0; c < NBW; ++c) {
+                    const int q = w + c * W;
+                    const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                    const int64_t d = (int64_t)(ql - w % (NBLK / 2)) * KPB * H_kv * D_H + (kv ? vdelta : 0);
+                    lds_dma16(base + d, st + kv * TILE + ql * 512);
+                }
+                return;
+            }
+            if (UNIFORM && paged && psh >= 0 && psz >= KPB && (kt + 1) * KT <= T_b) {
+                // each 1 KB block holds KPB consecutive keys of one page: one wave-uniform
+                // page-table read per block (a scalar load), the lane's key and chunk added on top
+                // (all page-table reads before the first load: the loads' asm orders memory accesses)
+                int64_t o[NBW];
+    #pragma unroll
+                for (int c = 0; c < NBW; ++c) {
+                    const int q = w + c * W;
+                    const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                    const int j0 = kt * KT + ql * KPB;
+                    const int page = ptab[__builtin_amdgcn_readfirstlane(j0 >> psh)];
+                    const int64_t slot0 = (int64_t)page * psz + (j0 & (psz - 1));
+                    // same swizzle as the wave's first block: the blocks' keys differ by multiples of 16
+                    o[c] = slot0 * H_kv * D_H + (kv ? vdelta : 0);
+                }
+    #pragma unroll
+                for (int c = 0; c < NBW; ++c) {
+                    const int q = w + c * W;
+                    const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                    lds_dma16(lane0 + o[c], st + kv * TILE + ql * 512);
+                }
+                return;
+            }
+            int64_t off[NBW];
+    #pragma unroll
+            for (int c = 0; c < NBW; ++c) {
+                const int q = w + c * W;
+                const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                const int key = ql * KPB + lane / NCH;
+                const int ch = (lane % NCH) ^ kv_swz<D_H>(key);
+                int j = kt * KT + key;
+                if (j >= T_b) j = 0;
+                int64_t slot;
+                if (paged) {
+                    const int pi = psh >= 0 ? j >> psh : j / psz;
+                    const int po = psh >= 0 ? j & (psz - 1) : j % psz;
+                    slot = (int64_t)(pt_lds ? s_pt[pi] : ptab[pi]) * psz + po;
+                } else {
+                    slot = tok0 + j;
+                }
+                off[c] = (slot * H_kv + hk) * D_H + ch * 8 + (kv ? vdelta : 0);
+            }
+    #pragma unroll
+            for (int c = 0; c < NBW; ++c) {
+                const int q = w + c * W;
+                if (NBLK % W == 0 || q < NBLK) {
+                    const int kv = q / (NBLK / 2), ql = q % (NBLK / 2);
+                    lds_dma16(kbase + off[c], st + kv * TILE + ql * 512);
+                }
             }
         }
     };
@@ -549,7 +613,10 @@ hipError_t launch_dh(const AttnArgs& a, int W, hipStream_t s) {
     const int64_t wgs = (int64_t)a.n_blocks * a.n_split * a.H_kv * a.n_layers;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8>), grid, dim3(8 * 64), 0, s, a);
+    if (a.slots.paged)
+        hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8, true>), grid, dim3(8 * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<D_H, 8, false>), grid, dim3(8 * 64), 0, s, a);
     if (a.n_split == 1) return hipGetLastError();
     if (hipError_t e = hipGetLastError()) return e;
     const int64_t rows = a.n_rows_total * a.H_q;   // (selected row, query head) rows
