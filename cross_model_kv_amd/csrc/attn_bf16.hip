@@ -37,6 +37,10 @@
 //    LDS once and each tile's block pages are read from there by the instance whose loads know
 //    it is LDS (a pointer that could be either LDS or global memory is read with flat loads,
 //    which wait on both memory counters); contiguous caches keep their instance unchanged.
+//  * The normalised output rows leave through LDS: each wave writes its 32 rows into its own
+//    slice of the idle K/V stages and stores whole rows, 16 bytes per lane (the accumulator
+//    layout would store 8 bytes to each of 32 rows per instruction, which measured slower for
+//    the short workgroups of 4K requests).
 //  * Query blocks are issued longest-first, and the KV head is the fastest-varying workgroup
 //    index so that, with 8 KV heads, every XCD streams one head's K/V through its own L2.
 //  * With fewer blocks than CUs the keys of the long blocks are cut into runs counted back
@@ -148,15 +152,24 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qf[c][e] = (bf16)0.f;
         }
-        constexpr int HC = QC / 2;     // chunks of the first half of the dims
+    }
+    constexpr int HC = QC / 2;     // chunks of the first half of the dims
+    float4 rt[HC][4];
+    {
         const float* rp = a.rope + (int64_t)p_row * D_H;   // [d_h/2][2] per position
 #pragma unroll
+        for (int c = 0; c < HC; ++c)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) rt[c][e2] = ((const float4*)(rp + 2 * (16 * c + 8 * hf)))[e2];
+    }
+    // the rotation runs after the first tile's loads are issued (its table reads are in flight
+    // with them)
+    auto rotate_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
         for (int c = 0; c < HC; ++c) {
-            const int j0 = 16 * c + 8 * hf;
-            const float4* cs = (const float4*)(rp + 2 * j0);
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                const float4 t = cs[e2];       // (cos, sin) of j0+2e2 and j0+2e2+1
+                const float4 t = rt[c][e2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int e = 2 * e2 + u;
@@ -167,7 +180,7 @@ void attn_bf16_kernel(AttnArgs a) {
                 }
             }
         }
-    }
+    };
 
     // ---- K/V tile staging: block q of a tile holds KPB consecutive keys of K (q < NBLK/2) or V
     const bf16* kbase = (const bf16*)a.kc + layer * a.kv_layer_elems;
@@ -470,8 +483,9 @@ void attn_bf16_kernel(AttnArgs a) {
     };
 
     if (paged && pt_lds) __syncthreads();      // the staged page table, before the first loads
+    if (t_lo < t_hi) issue(lds0, t_lo);
+    rotate_q();
     if (t_lo < t_hi) {
-        issue(lds0, t_lo);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -495,42 +509,61 @@ void attn_bf16_kernel(AttnArgs a) {
     asm volatile("" : "+v"(lane_e));
     const int row_e = w * 32 + (lane_e & 31);
     const int qi_e = row_e / g;
-    if (qi_e >= nq) return;
-    const int64_t out_row = (int64_t)(i0 + qi_e) * a.H_q + hk * g + (row_e - qi_e * g);
-    if (!whole) {                  // partial rows of this chunk: unnormalised O, m (log2), l
-        // rows without keys in the chunk leave only l = 0 (the merge skips their output)
-        const bool has = active;
-        const int64_t prow = out_row * a.n_split + chunk;
-        float* po = a.part + prow * D_H;
-        if (has)
+    if (whole) {
+        // final rows: staged in this wave's own 32-row slice of the (now idle) K/V stages
+        // (16-byte chunks XOR-swizzled by row), then written 16 bytes per lane, whole rows per
+        // store (4 at d_h = 128): a store of the accumulator layout touches 32 rows, 8 bytes each
+        const float inv = 1.f / l_run;
+        bf16* so = (w < 4 ? lds0 : lds1) + (w & 3) * 32 * D_H;
+        const int rr = lane_e & 31, hh2 = lane_e >> 5;
 #pragma unroll
-            for (int d = 0; d < DB; ++d)
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    f32x4 o;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                bf16x4 o;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) o[v] = oacc[d][4 * q4 + v];
-                    *(f32x4*)(po + d * 32 + 8 * q4 + 4 * hf) = o;
-                }
-        if (hf == 0) {
-            a.part_ml[prow * 2] = m_ref;
-            a.part_ml[prow * 2 + 1] = has ? l_run : 0.f;
+                for (int v = 0; v < 4; ++v) o[v] = (bf16)(oacc[d][4 * q4 + v] * inv);
+                const int c16 = (d * 4 + q4) ^ (rr & (NCH - 1));
+                *(bf16x4*)(so + rr * D_H + c16 * 8 + 4 * hh2) = o;
+            }
+        constexpr int RPS = 64 / NCH;               // rows per store
+#pragma unroll
+        for (int it = 0; it < 32 / RPS; ++it) {
+            const int r = it * RPS + lane_e / NCH, ch = lane_e % NCH;
+            const bf16x8 v = *(const bf16x8*)(so + r * D_H + ((ch ^ (r & (NCH - 1))) << 3));
+            const int row2 = w * 32 + r, qi2 = row2 / g;
+            if (qi2 < nq) {
+                const int64_t orow2 = (int64_t)(i0 + qi2) * a.H_q + hk * g + (row2 - qi2 * g);
+                *(bf16x8*)((bf16*)a.out + layer * a.out_layer_stride + orow2 * D_H + ch * 8) = v;
+            }
         }
+        if (qi_e >= nq) return;
+        const int64_t out_row = (int64_t)(i0 + qi_e) * a.H_q + hk * g + (row_e - qi_e * g);
+        if (a.lse && hf == 0)
+            a.lse[layer * a.lse_layer_stride + out_row] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
         return;
     }
-    const float inv = 1.f / l_run;
-    bf16* orow = (bf16*)a.out + layer * a.out_layer_stride + out_row * D_H;
+    // partial rows of this chunk: unnormalised O, m (log2), l
+    if (qi_e >= nq) return;
+    const int64_t out_row = (int64_t)(i0 + qi_e) * a.H_q + hk * g + (row_e - qi_e * g);
+    // rows without keys in the chunk leave only l = 0 (the merge skips their output)
+    const bool has = active;
+    const int64_t prow = out_row * a.n_split + chunk;
+    float* po = a.part + prow * D_H;
+    if (has)
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            bf16x4 o;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4 o;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) o[v] = (bf16)(oacc[d][4 * q4 + v] * inv);
-            *(bf16x4*)(orow + d * 32 + 8 * q4 + 4 * hf) = o;
-        }
-    if (a.lse && hf == 0)
-        a.lse[layer * a.lse_layer_stride + out_row] = (m_ref + __log2f(l_run)) * 0.6931471805599453f;
+                for (int v = 0; v < 4; ++v) o[v] = oacc[d][4 * q4 + v];
+                *(f32x4*)(po + d * 32 + 8 * q4 + 4 * hf) = o;
+            }
+    if (hf == 0) {
+        a.part_ml[prow * 2] = m_ref;
+        a.part_ml[prow * 2 + 1] = has ? l_run : 0.f;
+    }
 }
 
 // Merge of a split attention: out = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over the
