@@ -23,6 +23,8 @@
 //    the LDS counter and the look-ahead reads are waited for one at a time.
 //  * q is rotated (rotate-half, table angles at the query's true position) and scaled by
 //    log2(e)/sqrt(d_h) while it is loaded; k was rotated when it was scattered into the cache.
+//    The q rows arrive whole (16 bytes per lane, several rows per load) through LDS rather than
+//    as fragments, which would read 32 bytes of each of 32 rows per load.
 //  * VALU work per tile is kept small, because on gfx950 a wave's VALU instructions do not
 //    overlap its own MFMAs: the causal mask runs only on tiles that reach past the smallest
 //    query position of the wave; the scores leave the MFMAs already shifted by a reference
@@ -84,6 +86,7 @@ void attn_bf16_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) bf16 lds0[2 * TILE];
     __shared__ __attribute__((aligned(1024))) bf16 lds1[2 * TILE];
     __shared__ int32_t s_pt[PT_MAX];           // the request's page table (paged caches)
+    __shared__ __attribute__((aligned(16))) bf16 s_q[W * 32 * D_H];   // q rows on their way to the fragments
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -143,15 +146,32 @@ void attn_bf16_kernel(AttnArgs a) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)D_H);
     bf16x8 qf[QC];
     {
-        const bf16* qrow = (const bf16*)a.qkv + layer * a.q_layer_stride + (int64_t)(i0 + (valid ? qi : 0)) * a.ld +
-                           (int64_t)h * D_H;
+        // whole q rows, 16 bytes per lane, through this wave's slice of s_q (16-byte chunks
+        // XOR-swizzled by row), then read back in the fragment layout
+        bf16* sq = s_q + w * 32 * D_H;
+        constexpr int RPS = 64 / NCH;
+        bf16x8 tmp[32 / RPS];
 #pragma unroll
-        for (int c = 0; c < QC; ++c) {
-            if (valid) qf[c] = *(const bf16x8*)(qrow + 16 * c + 8 * hf);
-            else
+        for (int it = 0; it < 32 / RPS; ++it) {
+            const int r = it * RPS + lane / NCH, ch = lane % NCH;
+            const int row2 = w * 32 + r, qi2 = row2 / g;
+            if (qi2 < nq) {
+                const int h2 = hk * g + (row2 - qi2 * g);
+                tmp[it] = *(const bf16x8*)((const bf16*)a.qkv + layer * a.q_layer_stride + (int64_t)(i0 + qi2) * a.ld +
+                                           (int64_t)h2 * D_H + ch * 8);
+            } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qf[c][e] = (bf16)0.f;
+                for (int e = 0; e < 8; ++e) tmp[it][e] = (bf16)0.f;
+            }
         }
+#pragma unroll
+        for (int it = 0; it < 32 / RPS; ++it) {
+            const int r = it * RPS + lane / NCH, ch = lane % NCH;
+            *(bf16x8*)(sq + r * D_H + ((ch ^ (r & (NCH - 1))) << 3)) = tmp[it];
+        }
+#pragma unroll
+        for (int c = 0; c < QC; ++c)
+            qf[c] = *(const bf16x8*)(sq + lr * D_H + (((2 * c + hf) ^ (lr & (NCH - 1))) << 3));
     }
     constexpr int HC = QC / 2;     // chunks of the first half of the dims
     float4 rt[HC][4];
